@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the C2KV hot path on one MI355X.
+
+One step = one pass of the whole hot path over the Llama3.1-8B-shaped
+single-layer workload (bf16, 32 query / 8 KV heads, head_dim 128, RoPE theta
+5e5): structured-flow extraction attention of 8 documents x 4096 tokens at
+k = 4 (1024 slots each, sink = first 4 tokens), composition of their slot
+caches in a seeded order into an 8192-slot cache covering 32768 original
+positions, a 64-token question prefill, and 256 decode steps with random
+query vectors (batch 1).  Inputs are synthetic N(0, 1) tensors resident in
+HBM before timing starts.
+
+The metric is the decode attention's KV read rate (GB/s, algorithmic bytes)
+together with the extraction's masked-attention TFLOP/s (visible cells only).
+The 256 decode launches of a step are replayed from one HIP graph.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def visible_cells(n: int, k: int) -> int:
+    """Visible cells of one document's structured mask with sink = k:
+    n(n+1)/2 doc->doc, (m-1)k + n slot->doc (n >= k), m(m+1)/2 slot->slot."""
+    m = (n + k - 1) // k
+    sd = (m - 1) * k + n if n >= k else n
+    return n * (n + 1) // 2 + sd + m * (m + 1) // 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-decode-steps", type=int, default=8)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, M, P, tq, nsteps):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    `nsteps` decode steps over the full composed cache (M slots + question),
+    and the extraction of one document (all 32 heads)."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    d, hq, hkv = w.head_dim, w.hq, w.hkv
+    L0 = M + tq
+    ck = W.normal((L0, hkv, d), w.dtype, 90, W.P_K).float().numpy()
+    cv = W.normal((L0, hkv, d), w.dtype, 90, W.P_V).float().numpy()
+    t0 = time.perf_counter()
+    nbytes = 0
+    for s in range(nsteps):
+        q = W.normal((hq, d), w.dtype, 90, W.P_DEC_Q, salt=s).float().numpy()
+        kn = W.normal((hkv, d), w.dtype, 90, W.P_NEW_KV, salt=s).float().numpy()
+        vn = W.normal((hkv, d), w.dtype, 90, W.P_NEW_KV, salt=1000 + s).float().numpy()
+        _, _, ck, cv = O.decode_step(q, kn, vn, ck, cv, P + tq + s, w.rope_theta, "bf16")
+        nbytes += ck.shape[0] * hkv * d * 2 * 2
+    dec_s = time.perf_counter() - t0
+    n, k = w.doc_lens[0], w.ratio_k
+    rows = n + O.num_slots(n, k)
+    q = W.normal((rows, hq, d), w.dtype, 91, W.P_Q).float().numpy()
+    kk = W.normal((rows, hkv, d), w.dtype, 91, W.P_K).float().numpy()
+    v = W.normal((rows, hkv, d), w.dtype, 91, W.P_V).float().numpy()
+    t0 = time.perf_counter()
+    O.extract_attn(q, kk, v, [n], k, w.sink_len, w.rope_theta)
+    ext_s = time.perf_counter() - t0
+    ext_flops = hq * 4 * d * visible_cells(n, k)
+    return {
+        "value": nbytes / dec_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"{nsteps} decode steps over the full {L0}-row composed cache (32/8 heads, d=128), "
+                  f"plus extraction of 1 of the 8 documents (all 32 heads)",
+        "decode_seconds": dec_s, "extraction_tflops": ext_flops / ext_s / 1e12, "extraction_seconds": ext_s,
+        "host_cores": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this path does not shard "
+              f"across GPUs).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = W.LLAMA
+    d, hq, hkv, k, theta, dt = w.head_dim, w.hq, w.hkv, w.ratio_k, w.rope_theta, w.dtype
+    lens = list(w.doc_lens)
+    rows = c2kv.packed_rows(lens, k)
+    q = W.device_normal((rows, hq, d), dt, w.wid, W.P_Q, dev)
+    kk = W.device_normal((rows, hkv, d), dt, w.wid, W.P_K, dev)
+    v = W.device_normal((rows, hkv, d), dt, w.wid, W.P_V, dev)
+    o_ext = torch.empty_like(q)
+    order = W.llama_doc_order(w)
+    views = c2kv.slot_views(kk, v, lens, k)
+    requests = [[views[t] for t in order]]
+    M = sum(c2kv.num_slots(n, k) for n in lens)
+    P = sum(lens)
+    tq, S = w.tq, w.decode_steps
+    cap = M + tq + S
+    ck = torch.zeros((1, hkv, cap, d), dtype=dt, device=dev)
+    cv = torch.zeros_like(ck)
+    qp = W.device_normal((1, tq, hq, d), dt, w.wid, W.P_PREFILL, dev)
+    kp = W.device_normal((1, tq, hkv, d), dt, w.wid, W.P_NEW_KV, dev)
+    vp = W.device_normal((1, tq, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=1)
+    qd = W.device_normal((S, 1, hq, d), dt, w.wid, W.P_DEC_Q, dev)
+    kd = W.device_normal((S, 1, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=2)
+    vd = W.device_normal((S, 1, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=3)
+    ws_ext = torch.empty(c2kv.workspace_size_extract(lens, k, hkv, d, dt), dtype=torch.uint8, device=dev)
+    ws_pre = torch.empty(c2kv.workspace_size_prefill([M], tq, hq, hkv, d, dt), dtype=torch.uint8, device=dev)
+    ws_dec = torch.empty(max(c2kv.workspace_size_decode([M + tq + s], hq, hkv, d, dt) for s in range(S)),
+                         dtype=torch.uint8, device=dev)
+
+    def extract():
+        c2kv.extract_attn(q, kk, v, lens, k, w.sink_len, theta, out=o_ext, workspace=ws_ext)
+
+    def compose():
+        c2kv.compose(requests, k, theta, ck, cv)
+
+    def prefill():
+        c2kv.attn_prefill(qp, kp, vp, ck, cv, [M], [P], theta, workspace=ws_pre)
+
+    def decode_loop():
+        for s in range(S):
+            c2kv.attn_decode(qd[s], kd[s], vd[s], ck, cv, [M + tq + s], [P + tq + s], theta, workspace=ws_dec)
+
+    # eager pass (also the reference for the graph), then capture the decode loop
+    extract(); compose(); prefill(); decode_loop()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode_loop()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_loop()
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        extract()
+        if ev: ev[1].record()
+        compose()
+        if ev: ev[2].record()
+        prefill()
+        if ev: ev[3].record()
+        graph.replay()
+        if ev: ev[4].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(a.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    ph = [0.0] * 4
+    for e in evs:
+        for j in range(4):
+            ph[j] += e[j].elapsed_time(e[j + 1])
+    ph = [x / a.steps for x in ph]   # ms per step
+    ms_step = total_ms / a.steps
+
+    es = 2
+    ext_flops = hq * 4 * d * sum(visible_cells(n, k) for n in lens)
+    comp_bytes = 4 * M * hkv * d * es
+    pre_flops = 4 * d * hq * tq * (M + (tq + 1) / 2)
+    dec_bytes = sum((M + tq + s + 1) * hkv * d * es * 2 + (2 * hq + 2 * hkv) * d * es for s in range(S))
+    ext_tflops = ext_flops / (ph[0] * 1e-3) / 1e12
+    dec_gbs = dec_bytes / (ph[3] * 1e-3) / 1e9
+    comp_gbs = comp_bytes / (ph[1] * 1e-3) / 1e9
+
+    # dominant kernel of the step: the phase with the largest share of the step
+    if ph[0] >= ph[3]:
+        roof = {"bound": "mfma", "kernel": "extract_attn_kernel<bf16,128>", "achieved": ext_tflops,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ext_tflops / BF16_PEAK_TFLOPS,
+                "traffic": None, "per_launch_ms": ph[0], "algorithmic_per_launch": ext_flops}
+    else:
+        per_launch_ms = ph[3] / S
+        roof = {"bound": "hbm", "kernel": "decode step (append_kernel + cache_attn_kernel<bf16,128>)",
+                "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                "traffic": None, "per_launch_ms": per_launch_ms, "algorithmic_per_launch": dec_bytes / S}
+
+    line = {
+        "metric": "C2KV decode-attn KV GB/s (% HBM peak) + extraction masked-attn TFLOP/s",
+        "value": dec_gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) Q/K/V of the workload's shapes, resident in HBM",
+        "config": {"workload": "llama31_8b_1layer: extract 8 docs x 4096 tok (k=4, sink 4), compose 8192 slots "
+                               "(32768 positions), prefill 64, 256 decode steps, batch 1",
+                   "hq": hq, "hkv": hkv, "head_dim": d, "rope_theta": theta, "decode_graph": True},
+        "hbm_frac": dec_gbs / HBM_PEAK_GBS,
+        "extraction_tflops": ext_tflops,
+        "extraction_frac": ext_tflops / BF16_PEAK_TFLOPS,
+        "phase_ms": {"extract": ph[0], "compose": ph[1], "prefill": ph[2], "decode_256": ph[3]},
+        "compose_gbs": comp_gbs,
+        "prefill_tflops": pre_flops / (ph[2] * 1e-3) / 1e12,
+        "wall_s": t_wall,
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, M, P, tq, a.cpu_decode_steps)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

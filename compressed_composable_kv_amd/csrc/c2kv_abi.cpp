@@ -1,0 +1,561 @@
+// Host side of the C2KV C ABI: argument validation (always before the first
+// HIP call), workspace planning, kernel-argument tables and launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "c2kv.h"
+#include "c2kv_launch.hpp"
+
+using namespace c2kv;
+
+namespace {
+
+thread_local std::string g_err;
+
+c2kv_status fail(c2kv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+c2kv_status ok() {
+  g_err.clear();
+  return C2KV_OK;
+}
+
+c2kv_status hip_fail(hipError_t e, const char* what) {
+  return fail(C2KV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t elem_bytes(c2kv_dtype dt) { return dt == C2KV_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+c2kv_status check_heads(int32_t hq, int32_t hkv, int32_t head_dim, c2kv_dtype dt) {
+  if (dt != C2KV_BF16 && dt != C2KV_F32) return fail(C2KV_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (hq < 1 || hkv < 1) return fail(C2KV_ERR_INVALID_ARG, "hq=%d hkv=%d must be >= 1", hq, hkv);
+  if (hq % hkv != 0) return fail(C2KV_ERR_INVALID_ARG, "hq=%d is not a multiple of hkv=%d", hq, hkv);
+  if (hq / hkv > 16) return fail(C2KV_ERR_UNSUPPORTED, "hq/hkv=%d exceeds 16", hq / hkv);
+  if (head_dim != 64 && head_dim != 128) return fail(C2KV_ERR_UNSUPPORTED, "head_dim=%d (64 or 128 supported)", head_dim);
+  return C2KV_OK;
+}
+
+c2kv_status check_theta(float theta) {
+  if (!(theta > 1.0f) || !std::isfinite(theta)) return fail(C2KV_ERR_INVALID_ARG, "rope_theta=%g must be finite and > 1", (double)theta);
+  return C2KV_OK;
+}
+
+RopeFreqs make_freqs(int head_dim, float theta) {
+  RopeFreqs f;
+  std::memset(&f, 0, sizeof(f));
+  for (int i = 0; i < head_dim / 2; ++i)
+    f.f[i] = (float)std::pow((double)theta, -2.0 * (double)i / (double)head_dim);
+  return f;
+}
+
+float scale_log2(int head_dim) {
+  return (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+}
+
+int32_t num_slots_i(int32_t n, int32_t k) { return (n + k - 1) / k; }
+
+// ------------------------------------------------------------- extraction
+struct ExtractLayout {
+  int64_t rows = 0;
+  int32_t max_n = 0;
+  size_t krot_off = 0, table_off = 0, total = 0;
+};
+
+c2kv_status extract_layout(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t hkv,
+                           int32_t head_dim, c2kv_dtype dt, ExtractLayout& L) {
+  if (!doc_lens) return fail(C2KV_ERR_INVALID_ARG, "doc_lens is NULL");
+  if (num_docs < 1) return fail(C2KV_ERR_INVALID_ARG, "num_docs=%d must be >= 1", num_docs);
+  if (ratio_k < 1) return fail(C2KV_ERR_INVALID_ARG, "ratio_k=%d must be >= 1", ratio_k);
+  L.rows = 0;
+  L.max_n = 0;
+  for (int32_t b = 0; b < num_docs; ++b) {
+    const int32_t n = doc_lens[b];
+    if (n < 1) return fail(C2KV_ERR_INVALID_ARG, "doc_lens[%d]=%d must be >= 1", b, n);
+    if (n > (1 << 24)) return fail(C2KV_ERR_CAPACITY, "doc_lens[%d]=%d exceeds 2^24 positions", b, n);
+    L.rows += n + num_slots_i(n, ratio_k);
+    L.max_n = std::max(L.max_n, n);
+  }
+  if (L.rows >= ((int64_t)1 << 31)) return fail(C2KV_ERR_CAPACITY, "%lld packed rows exceed 2^31-1", (long long)L.rows);
+  L.krot_off = 0;
+  L.table_off = align_up((size_t)L.rows * hkv * head_dim * elem_bytes(dt));
+  L.total = L.table_off + align_up((size_t)L.max_n * (head_dim / 2) * sizeof(float2));
+  return C2KV_OK;
+}
+
+// Fill the per-launch document tables; returns the number of docs consumed.
+int fill_extract_chunk(const int32_t* doc_lens, int32_t first, int32_t num_docs, int32_t ratio_k,
+                       int32_t G, int32_t hkv, int64_t row0, ExtractParams& p, RotateParams& rp) {
+  const int cnt = std::min<int>(C2KV_MAX_BATCH, num_docs - first);
+  int64_t wg = 0, row = row0;
+  for (int i = 0; i < cnt; ++i) {
+    const int32_t n = doc_lens[first + i];
+    const int32_t m = num_slots_i(n, ratio_k);
+    ExtractDoc& d = p.docs[i];
+    d.row0 = row;
+    d.n = n;
+    d.m = m;
+    d.wg0 = (int32_t)wg;
+    d.nwg_doc = (int32_t)ceil_div(ceil_div(n, kQW) * G, kWaves);
+    d.nwg_slot = (int32_t)ceil_div(ceil_div(m, kQW) * G, kWaves);
+    d.pad = 0;
+    wg += (int64_t)hkv * (d.nwg_doc + d.nwg_slot);
+    rp.docs[i].row0 = row;
+    rp.docs[i].n = n;
+    rp.docs[i].m = m;
+    row += n + m;
+  }
+  p.num_docs = cnt;
+  p.total_wg = (int32_t)wg;
+  p.grid_wg = (int32_t)((wg + 7) / 8 * 8);
+  rp.num_docs = cnt;
+  rp.row_begin = row0;
+  rp.row_end = row;
+  return cnt;
+}
+
+// ------------------------------------------------------ prefill / decode
+// Split plan shared by the size query and the call.  Keys of a request are
+// cut into `chunk`-key pieces processed by separate workgroups; chunk is a
+// multiple of the kernel's key step and sized so that a launch fills the
+// chip (about four workgroups per CU for decode, one for prefill), with at
+// most C2KV_MAX_SPLITS pieces per request.
+struct CachePlan {
+  bool decode = false;
+  int32_t nug = 0, nblk_q = 0, chunk = 0;
+  std::vector<int32_t> nsplit;
+  size_t qrot_off = 0, part_off = 0, total = 0;
+};
+
+c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, int32_t hq, int32_t hkv,
+                       int32_t head_dim, c2kv_dtype dt, int64_t cap_or_neg, bool decode, CachePlan& P) {
+  if (!cache_len) return fail(C2KV_ERR_INVALID_ARG, "cache_len is NULL");
+  if (num_reqs < 1) return fail(C2KV_ERR_INVALID_ARG, "num_reqs=%d must be >= 1", num_reqs);
+  if (tq < 1) return fail(C2KV_ERR_INVALID_ARG, "tq=%d must be >= 1", tq);
+  const int32_t G = hq / hkv;
+  P.decode = decode;
+  P.nblk_q = (int32_t)ceil_div(tq, kQW);
+  P.nug = decode ? 1 : (int32_t)ceil_div((int64_t)P.nblk_q * G, kWaves);
+  int64_t total_keys = 0, max_len = 0;
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    const int64_t c = cache_len[r];
+    if (c < 0) return fail(C2KV_ERR_INVALID_ARG, "cache_len[%d]=%lld is negative", r, (long long)c);
+    if (cap_or_neg >= 0 && c + tq > cap_or_neg)
+      return fail(C2KV_ERR_CAPACITY, "cache_len[%d]=%lld + %d new rows exceed cap=%lld", r, (long long)c, tq,
+                  (long long)cap_or_neg);
+    if (c + tq >= ((int64_t)1 << 30)) return fail(C2KV_ERR_CAPACITY, "request %d has too many rows", r);
+    total_keys += c + tq;
+    max_len = std::max(max_len, c + tq);
+  }
+  const int64_t step = decode ? 4 * 32 : kBN;        // keys per workgroup step
+  const int64_t target_wg = decode ? 1024 : 256;
+  int64_t chunk = ceil_div(total_keys * hkv * P.nug, target_wg);
+  chunk = std::max<int64_t>(step, ceil_div(chunk, step) * step);
+  chunk = std::max<int64_t>(chunk, ceil_div(ceil_div(max_len, C2KV_MAX_SPLITS), step) * step);
+  P.chunk = (int32_t)chunk;
+  P.nsplit.resize(num_reqs);
+  size_t max_part = 0;
+  for (int32_t r0 = 0; r0 < num_reqs; r0 += C2KV_MAX_BATCH) {
+    const int32_t r1 = std::min(num_reqs, r0 + C2KV_MAX_BATCH);
+    int32_t stride = 0;
+    for (int32_t r = r0; r < r1; ++r) {
+      P.nsplit[r] = (int32_t)ceil_div(cache_len[r] + tq, chunk);
+      stride = std::max(stride, P.nsplit[r]);
+    }
+    if (stride > 1)
+      max_part = std::max(max_part, (size_t)(r1 - r0) * hq * tq * stride * (head_dim + 4) * sizeof(float));
+  }
+  P.qrot_off = 0;
+  P.part_off = decode ? 0 : align_up((size_t)num_reqs * tq * hq * head_dim * elem_bytes(dt));
+  P.total = P.part_off + align_up(max_part);
+  return C2KV_OK;
+}
+
+c2kv_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return C2KV_OK;
+  if (!ws) return fail(C2KV_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned256(ws)) return fail(C2KV_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < need) return fail(C2KV_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return C2KV_OK;
+}
+
+c2kv_status check_dev(const void* p, const char* name) {
+  if (!p) return fail(C2KV_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(C2KV_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return C2KV_OK;
+}
+
+c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new, void* cache_k, void* cache_v,
+                            int64_t cap, const int32_t* cache_len, const int32_t* q_pos0, int32_t num_reqs,
+                            int32_t tq, bool decode, int32_t hq, int32_t hkv, int32_t head_dim, float rope_theta,
+                            void* o, float* lse, c2kv_dtype dt, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  c2kv_status s;
+  if ((s = check_heads(hq, hkv, head_dim, dt))) return s;
+  if ((s = check_theta(rope_theta))) return s;
+  if ((s = check_dev(q, "q")) || (s = check_dev(k_new, "k_new")) || (s = check_dev(v_new, "v_new")) ||
+      (s = check_dev(cache_k, "cache_k")) || (s = check_dev(cache_v, "cache_v")) || (s = check_dev(o, "o")))
+    return s;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(C2KV_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  if (!q_pos0) return fail(C2KV_ERR_INVALID_ARG, "q_pos is NULL");
+  if (cap < 1) return fail(C2KV_ERR_INVALID_ARG, "cap=%lld must be >= 1", (long long)cap);
+  CachePlan P;
+  if ((s = cache_plan(cache_len, num_reqs, tq, hq, hkv, head_dim, dt, cap, decode, P))) return s;
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    if (q_pos0[r] < 0 || (int64_t)q_pos0[r] + tq > (1 << 24))
+      return fail(C2KV_ERR_CAPACITY, "q_pos[%d]=%d + %d tokens outside [0, 2^24]", r, q_pos0[r], tq);
+  }
+  if ((s = check_ws(workspace, ws_bytes, P.total))) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + P.part_off);
+  const RopeFreqs freqs = make_freqs(head_dim, rope_theta);
+  const int32_t G = hq / hkv;
+  for (int32_t r0 = 0; r0 < num_reqs; r0 += C2KV_MAX_BATCH) {
+    const int32_t cnt = std::min<int32_t>(C2KV_MAX_BATCH, num_reqs - r0);
+    int32_t stride = 0;
+    for (int32_t i = 0; i < cnt; ++i) stride = std::max(stride, P.nsplit[r0 + i]);
+    hipError_t e;
+    if (decode) {
+      DecodeParams dp;
+      std::memset(&dp, 0, sizeof(dp));
+      dp.q = q; dp.k_new = k_new; dp.v_new = v_new; dp.kc = cache_k; dp.vc = cache_v; dp.o = o; dp.lse = lse;
+      dp.part = part; dp.cap = cap; dp.req0 = r0; dp.num_reqs = cnt; dp.hq = hq; dp.hkv = hkv; dp.G = G;
+      dp.chunk = P.chunk; dp.nsplit_stride = stride; dp.scale_log2 = scale_log2(head_dim); dp.freqs = freqs;
+      int64_t wg = 0;
+      for (int32_t i = 0; i < cnt; ++i) {
+        dp.reqs[i].wg0 = (int32_t)wg;
+        dp.reqs[i].cache_len = cache_len[r0 + i];
+        dp.reqs[i].pos = q_pos0[r0 + i];
+        dp.reqs[i].nsplit = P.nsplit[r0 + i];
+        wg += (int64_t)hkv * P.nsplit[r0 + i];
+      }
+      dp.total_wg = (int32_t)wg;
+      e = launch_decode_attn(dp, dt, head_dim, stream);
+      if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    } else {
+      AppendParams ap;
+      std::memset(&ap, 0, sizeof(ap));
+      ap.q = q; ap.k_new = k_new; ap.v_new = v_new;
+      ap.qrot = ws + P.qrot_off;
+      ap.cache_k = cache_k; ap.cache_v = cache_v; ap.cap = cap;
+      ap.req0 = r0; ap.num_reqs = cnt; ap.tq = tq; ap.hq = hq; ap.hkv = hkv;
+      ap.freqs = freqs;
+      for (int32_t i = 0; i < cnt; ++i) { ap.reqs[i].cache_len = cache_len[r0 + i]; ap.reqs[i].pos0 = q_pos0[r0 + i]; }
+      e = launch_append(ap, dt, head_dim, stream);
+      if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+      CacheParams cp;
+      std::memset(&cp, 0, sizeof(cp));
+      cp.qrot = ws + P.qrot_off;
+      cp.kc = cache_k; cp.vc = cache_v; cp.o = o; cp.lse = lse; cp.part = part;
+      cp.cap = cap; cp.req0 = r0; cp.num_reqs = cnt; cp.tq = tq; cp.hq = hq; cp.hkv = hkv; cp.G = G;
+      cp.nblk_q = P.nblk_q; cp.nug = P.nug; cp.chunk = P.chunk; cp.nsplit_stride = stride;
+      cp.scale_log2 = scale_log2(head_dim);
+      int64_t wg = 0;
+      for (int32_t i = 0; i < cnt; ++i) {
+        cp.reqs[i].wg0 = (int32_t)wg;
+        cp.reqs[i].cache_len = cache_len[r0 + i];
+        cp.reqs[i].nsplit = P.nsplit[r0 + i];
+        wg += (int64_t)hkv * P.nsplit[r0 + i] * P.nug;
+      }
+      cp.total_wg = (int32_t)wg;
+      cp.grid_wg = (int32_t)((wg + 7) / 8 * 8);
+      e = launch_cache_attn(cp, dt, head_dim, stream);
+      if (e != hipSuccess) return hip_fail(e, "cache attention kernel launch");
+    }
+    if (stride > 1) {
+      MergeParams mp;
+      std::memset(&mp, 0, sizeof(mp));
+      mp.part = part; mp.o = o; mp.lse = lse; mp.req0 = r0; mp.num_rows = cnt * hq * tq; mp.hq = hq; mp.tq = tq;
+      mp.nsplit_stride = stride;
+      for (int32_t i = 0; i < cnt; ++i) mp.nsplit[i] = P.nsplit[r0 + i];
+      e = launch_merge(mp, dt, head_dim, stream);
+      if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    }
+  }
+  return ok();
+}
+
+}  // namespace
+
+// ========================================================================
+extern "C" {
+
+const char* c2kv_version(void) { return "c2kv-mi355x 0.1.0 (gfx950)"; }
+
+const char* c2kv_status_string(c2kv_status s) {
+  switch (s) {
+    case C2KV_OK: return "ok";
+    case C2KV_ERR_INVALID_ARG: return "invalid argument";
+    case C2KV_ERR_UNSUPPORTED: return "unsupported";
+    case C2KV_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case C2KV_ERR_CAPACITY: return "capacity exceeded";
+    case C2KV_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* c2kv_last_error(void) { return g_err.c_str(); }
+
+int32_t c2kv_num_slots(int32_t n, int32_t k) {
+  if (n < 0 || k < 1) return -1;
+  return (int32_t)(((int64_t)n + k - 1) / k);
+}
+
+int32_t c2kv_slot_position(int32_t n, int32_t k, int32_t j) {
+  const int32_t m = c2kv_num_slots(n, k);
+  if (m < 0 || j < 0 || j >= m) return -1;
+  return (int32_t)std::min<int64_t>((int64_t)j * k + k - 1, (int64_t)n - 1);
+}
+
+c2kv_status c2kv_rope_inv_freq(int32_t head_dim, float rope_theta, float* out) {
+  if (!out) return fail(C2KV_ERR_INVALID_ARG, "out is NULL");
+  if (head_dim < 2 || head_dim % 2 || head_dim > 2 * kMaxHalfDim)
+    return fail(C2KV_ERR_INVALID_ARG, "head_dim=%d must be even and <= %d", head_dim, 2 * kMaxHalfDim);
+  c2kv_status s;
+  if ((s = check_theta(rope_theta))) return s;
+  const RopeFreqs f = make_freqs(head_dim, rope_theta);
+  std::memcpy(out, f.f, sizeof(float) * (head_dim / 2));
+  return ok();
+}
+
+// ------------------------------------------------------------- extraction
+size_t c2kv_workspace_size_extract(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t hkv,
+                                   int32_t head_dim, c2kv_dtype dt) {
+  ExtractLayout L;
+  if (hkv < 1 || (head_dim != 64 && head_dim != 128)) return 0;
+  if (extract_layout(doc_lens, num_docs, ratio_k, hkv, head_dim, dt, L)) return 0;
+  return L.total;
+}
+
+c2kv_status c2kv_extract_attn(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t sink_len,
+                              int32_t hq, int32_t hkv, int32_t head_dim, float rope_theta, c2kv_dtype dt,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  c2kv_status s;
+  if ((s = check_heads(hq, hkv, head_dim, dt))) return s;
+  if ((s = check_theta(rope_theta))) return s;
+  if ((s = check_dev(q, "q")) || (s = check_dev(k, "k")) || (s = check_dev(v, "v")) || (s = check_dev(o, "o")))
+    return s;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(C2KV_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  if (sink_len < 0) return fail(C2KV_ERR_INVALID_ARG, "sink_len=%d must be >= 0", sink_len);
+  ExtractLayout L;
+  if ((s = extract_layout(doc_lens, num_docs, ratio_k, hkv, head_dim, dt, L))) return s;
+  if ((s = check_ws(workspace, ws_bytes, L.total))) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  float2* table = reinterpret_cast<float2*>(ws + L.table_off);
+  const RopeFreqs freqs = make_freqs(head_dim, rope_theta);
+  hipError_t e = launch_rope_table(table, L.max_n, head_dim, freqs, stream);
+  if (e != hipSuccess) return hip_fail(e, "rope table kernel launch");
+
+  ExtractParams p;
+  RotateParams rp;
+  std::memset(&p, 0, sizeof(p));
+  std::memset(&rp, 0, sizeof(rp));
+  p.q = q; p.krot = ws + L.krot_off; p.v = v; p.o = o; p.lse = lse; p.rope = table;
+  p.total_rows = L.rows;
+  p.hq = hq; p.hkv = hkv; p.G = hq / hkv; p.ratio_k = ratio_k; p.sink_len = sink_len;
+  p.scale_log2 = scale_log2(head_dim);
+  rp.k = k; rp.krot = ws + L.krot_off; rp.rope = table; rp.hkv = hkv; rp.ratio_k = ratio_k;
+  int64_t row = 0;
+  for (int32_t b = 0; b < num_docs;) {
+    const int cnt = fill_extract_chunk(doc_lens, b, num_docs, ratio_k, p.G, hkv, row, p, rp);
+    e = launch_rotate_k(rp, dt, head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "key rotation kernel launch");
+    e = launch_extract_attn(p, dt, head_dim, false, stream);
+    if (e != hipSuccess) return hip_fail(e, "extraction attention kernel launch");
+    row = rp.row_end;
+    b += cnt;
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------ composition
+size_t c2kv_workspace_size_compose(int32_t num_segs) {
+  (void)num_segs;
+  return 0;
+}
+
+c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32_t* req_seg_ptr, int32_t num_reqs,
+                         const int32_t* pos_base, int32_t ratio_k, int32_t hkv, int32_t head_dim, float rope_theta,
+                         void* cache_k, void* cache_v, int64_t cap, int32_t* pos_out, int32_t* cache_len_out,
+                         int32_t* next_pos_out, c2kv_dtype dt, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  c2kv_status s;
+  if ((s = check_heads(hkv, hkv, head_dim, dt))) return s;
+  if ((s = check_theta(rope_theta))) return s;
+  if (ratio_k < 1) return fail(C2KV_ERR_INVALID_ARG, "ratio_k=%d must be >= 1", ratio_k);
+  if (!segs || num_segs < 1) return fail(C2KV_ERR_INVALID_ARG, "segs is NULL or num_segs=%d < 1", num_segs);
+  if (!req_seg_ptr || num_reqs < 1) return fail(C2KV_ERR_INVALID_ARG, "req_seg_ptr is NULL or num_reqs < 1");
+  if (!cache_len_out) return fail(C2KV_ERR_INVALID_ARG, "cache_len_out is NULL");
+  if ((s = check_dev(cache_k, "cache_k")) || (s = check_dev(cache_v, "cache_v"))) return s;
+  if (pos_out && (reinterpret_cast<uintptr_t>(pos_out) & 3u)) return fail(C2KV_ERR_INVALID_ARG, "pos_out misaligned");
+  if (cap < 1) return fail(C2KV_ERR_INVALID_ARG, "cap=%lld must be >= 1", (long long)cap);
+  if (req_seg_ptr[0] != 0 || req_seg_ptr[num_reqs] != num_segs)
+    return fail(C2KV_ERR_INVALID_ARG, "req_seg_ptr must start at 0 and end at num_segs");
+  const int64_t row_elems = (int64_t)hkv * head_dim;
+  std::vector<int32_t> lens(num_reqs), nexts(num_reqs);
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    if (req_seg_ptr[r + 1] < req_seg_ptr[r]) return fail(C2KV_ERR_INVALID_ARG, "req_seg_ptr is not monotone at %d", r);
+    int64_t rows = 0, pos = pos_base ? pos_base[r] : 0;
+    if (pos < 0) return fail(C2KV_ERR_INVALID_ARG, "pos_base[%d] is negative", r);
+    for (int32_t t = req_seg_ptr[r]; t < req_seg_ptr[r + 1]; ++t) {
+      const c2kv_segment& g = segs[t];
+      if ((s = check_dev(g.k, "segs[].k")) || (s = check_dev(g.v, "segs[].v"))) return s;
+      if (g.doc_len < 1) return fail(C2KV_ERR_INVALID_ARG, "segs[%d].doc_len=%d must be >= 1", t, g.doc_len);
+      if (g.reserved != 0) return fail(C2KV_ERR_INVALID_ARG, "segs[%d].reserved must be 0", t);
+      if (g.row_stride < row_elems || g.row_stride >= ((int64_t)1 << 31) || (g.row_stride * (int64_t)elem_bytes(dt)) % 16)
+        return fail(C2KV_ERR_INVALID_ARG, "segs[%d].row_stride=%lld invalid (>= hkv*head_dim, 16-byte multiple)", t,
+                    (long long)g.row_stride);
+      rows += num_slots_i(g.doc_len, ratio_k);
+      pos += g.doc_len;
+    }
+    if (rows > cap) return fail(C2KV_ERR_CAPACITY, "request %d composes %lld rows > cap=%lld", r, (long long)rows, (long long)cap);
+    if (pos > (1 << 24)) return fail(C2KV_ERR_CAPACITY, "request %d reaches position %lld > 2^24", r, (long long)pos);
+    lens[r] = (int32_t)rows;
+    nexts[r] = (int32_t)pos;
+  }
+
+  ComposeParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.cache_k = cache_k; p.cache_v = cache_v; p.pos_out = pos_out; p.cap = cap;
+  p.hkv = hkv; p.ratio_k = ratio_k; p.freqs = make_freqs(head_dim, rope_theta);
+  int cnt = 0;
+  int32_t rows = 0;
+  auto flush = [&]() -> hipError_t {
+    if (cnt == 0) return hipSuccess;
+    p.num_segs = cnt;
+    p.total_rows = rows;
+    hipError_t e = launch_compose(p, dt, head_dim, stream);
+    cnt = 0;
+    rows = 0;
+    return e;
+  };
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    int32_t out_row = 0;
+    int64_t pos = pos_base ? pos_base[r] : 0;
+    for (int32_t t = req_seg_ptr[r]; t < req_seg_ptr[r + 1]; ++t) {
+      const c2kv_segment& g = segs[t];
+      const int32_t m = num_slots_i(g.doc_len, ratio_k);
+      if (cnt == kComposeSegs || (int64_t)rows + m >= ((int64_t)1 << 30)) {
+        hipError_t e = flush();
+        if (e != hipSuccess) return hip_fail(e, "compose kernel launch");
+      }
+      ComposeSeg& d = p.segs[cnt++];
+      d.k = g.k; d.v = g.v; d.stride = (int32_t)g.row_stride; d.n = g.doc_len;
+      d.req = r; d.out_row = out_row; d.pos_off = (int32_t)pos; d.row_prefix = rows;
+      rows += m;
+      out_row += m;
+      pos += g.doc_len;
+    }
+  }
+  hipError_t e = flush();
+  if (e != hipSuccess) return hip_fail(e, "compose kernel launch");
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    cache_len_out[r] = lens[r];
+    if (next_pos_out) next_pos_out[r] = nexts[r];
+  }
+  return ok();
+}
+
+// ------------------------------------------------------ prefill / decode
+size_t c2kv_workspace_size_prefill(const int32_t* cache_len, int32_t num_reqs, int32_t tq, int32_t hq, int32_t hkv,
+                                   int32_t head_dim, c2kv_dtype dt) {
+  if (hq < 1 || hkv < 1 || hq % hkv) return 0;
+  CachePlan P;
+  if (cache_plan(cache_len, num_reqs, tq, hq, hkv, head_dim, dt, -1, false, P)) return 0;
+  return std::max<size_t>(P.total, kAlign);
+}
+
+size_t c2kv_workspace_size_decode(const int32_t* cache_len, int32_t num_reqs, int32_t hq, int32_t hkv,
+                                  int32_t head_dim, c2kv_dtype dt) {
+  if (hq < 1 || hkv < 1 || hq % hkv) return 0;
+  CachePlan P;
+  if (cache_plan(cache_len, num_reqs, 1, hq, hkv, head_dim, dt, -1, true, P)) return 0;
+  return std::max<size_t>(P.total, kAlign);
+}
+
+c2kv_status c2kv_attn_prefill(const void* q, const void* k_new, const void* v_new, void* cache_k, void* cache_v,
+                              int64_t cap, const int32_t* cache_len, const int32_t* q_pos0, int32_t num_reqs,
+                              int32_t tq, int32_t hq, int32_t hkv, int32_t head_dim, float rope_theta, void* o,
+                              float* lse, c2kv_dtype dt, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return cache_attention(q, k_new, v_new, cache_k, cache_v, cap, cache_len, q_pos0, num_reqs, tq, false, hq, hkv,
+                         head_dim, rope_theta, o, lse, dt, workspace, ws_bytes, stream);
+}
+
+c2kv_status c2kv_attn_decode(const void* q, const void* k_new, const void* v_new, void* cache_k, void* cache_v,
+                             int64_t cap, const int32_t* cache_len, const int32_t* q_pos, int32_t num_reqs,
+                             int32_t hq, int32_t hkv, int32_t head_dim, float rope_theta, void* o, float* lse,
+                             c2kv_dtype dt, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return cache_attention(q, k_new, v_new, cache_k, cache_v, cap, cache_len, q_pos, num_reqs, 1, true, hq, hkv,
+                         head_dim, rope_theta, o, lse, dt, workspace, ws_bytes, stream);
+}
+
+c2kv_status c2kv_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (ws_bytes == 0) return ok();
+  if (!workspace || !aligned256(workspace)) return fail(C2KV_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
+  if (ws_bytes % 4) return fail(C2KV_ERR_INVALID_ARG, "ws_bytes=%zu is not a multiple of 4", ws_bytes);
+  hipError_t e = launch_fill_zero(workspace, ws_bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "fill kernel launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------- testing
+size_t c2kv_workspace_size_mask_cells(void) { return 256; }
+
+c2kv_status c2kv_mask_cells(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t sink_len,
+                            uint64_t* counts_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  c2kv_status s;
+  if (!counts_out) return fail(C2KV_ERR_INVALID_ARG, "counts_out is NULL");
+  if (sink_len < 0) return fail(C2KV_ERR_INVALID_ARG, "sink_len=%d must be >= 0", sink_len);
+  ExtractLayout L;
+  if ((s = extract_layout(doc_lens, num_docs, ratio_k, 1, 64, C2KV_F32, L))) return s;
+  if ((s = check_ws(workspace, ws_bytes, c2kv_workspace_size_mask_cells()))) return s;
+  uint64_t* counts = static_cast<uint64_t*>(workspace);
+  hipError_t e = launch_fill_zero(counts, 64, stream);
+  if (e != hipSuccess) return hip_fail(e, "fill kernel launch");
+  ExtractParams p;
+  RotateParams rp;
+  std::memset(&p, 0, sizeof(p));
+  std::memset(&rp, 0, sizeof(rp));
+  p.hq = 1; p.hkv = 1; p.G = 1; p.ratio_k = ratio_k; p.sink_len = sink_len; p.counts = counts;
+  p.total_rows = L.rows;
+  int64_t row = 0;
+  for (int32_t b = 0; b < num_docs;) {
+    const int cnt = fill_extract_chunk(doc_lens, b, num_docs, ratio_k, 1, 1, row, p, rp);
+    e = launch_extract_attn(p, C2KV_F32, 64, true, stream);
+    if (e != hipSuccess) return hip_fail(e, "mask count kernel launch");
+    row = rp.row_end;
+    b += cnt;
+  }
+  uint64_t host[5];
+  e = hipMemcpyAsync(host, counts, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  std::memcpy(counts_out, host, sizeof(host));
+  return ok();
+}
+
+}  // extern "C"

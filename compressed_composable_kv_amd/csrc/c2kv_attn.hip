@@ -1,0 +1,629 @@
+// MFMA flash-attention kernels of the C2KV hot path for gfx950:
+//   * extraction attention under the structured-flow mask (the C2KV
+//     explainer's "structured information flow" section: documents causal and
+//     blind to slots; slot j sees the sink block, its own k-token block and
+//     the slots up to itself), enumerating only tiles that hold a visible
+//     cell for some wave of the workgroup;
+//   * the same enumeration in a counting mode (test support);
+//   * split-K attention of question tokens over a composed cache (the
+//     explainer's "overall flow" section), writing final rows when a request
+//     has one key chunk and log-sum-exp partials for merge_kernel otherwise.
+//
+// Tile shapes.  A workgroup is 4 waves; each wave owns one "unit" = 32 query
+// rows of one query head, and all units of a workgroup share one KV head, so
+// the K/V tiles staged in LDS (64 keys, double buffered) serve every wave.
+// S^T = K Q^T is computed with v_mfma_f32_16x16x32_bf16 (keys on the M side,
+// queries on the N side), so each lane's accumulators belong to ONE query:
+// softmax row statistics need two cross-lane steps and the O^T rescale is a
+// per-lane scalar.  P^T goes straight from the S^T accumulators into the B
+// operand of O^T += V^T P^T; V is stored transposed in LDS for that product.
+#include "c2kv_device.hpp"
+#include "c2kv_launch.hpp"
+
+namespace c2kv {
+
+// ------------------------------------------------------------------ LDS
+template <typename T, int D>
+struct Smem {
+  static constexpr int kKRow = D + 16 / (int)sizeof(T);   // padded K row
+  static constexpr int kVRow = kBN + kVPad;               // padded V^T row
+  static constexpr int kKElems = kBN * kKRow;
+  static constexpr int kVElems = D * kVRow;
+  static constexpr int kStage = kKElems + kVElems;
+};
+
+// Two workgroups per CU (two waves per SIMD) fit the 160 KB LDS except for
+// fp32 with head_dim 128, whose double-buffered tiles need 141 KB.
+template <typename T, int D>
+constexpr int kMinWaves = (2 * Smem<T, D>::kStage * (int)sizeof(T) * 2 <= 160 * 1024) ? 2 : 1;
+
+// V^T rows hold 16 groups of 4 keys; the group index is XOR-swizzled with
+// (d >> 3) so that both the transposing writes and the MFMA operand reads
+// are free of LDS bank conflicts.
+__device__ __forceinline__ int vt_group(int d, int kg) { return kg ^ ((d >> 3) & 15); }
+
+template <typename T>
+__device__ __forceinline__ uint32_t half_of(const uint4& x, int e);
+
+// ---------------------------------------------------------- tile loader
+// Global -> registers -> LDS staging of one 64-key K/V tile.  Every thread
+// owns KPT 16-byte chunks of K (row-major, coalesced) and VPT groups of 4
+// keys x one 16-byte chunk of V, which it writes transposed.
+template <typename T, int D>
+struct KVStage {
+  static constexpr int CE = ElemTraits<T>::kChunk;
+  static constexpr int CPR = D / CE;
+  static constexpr int KPT = kBN * CPR / kThreads;
+  static constexpr int VTASKS = (kBN / 4) * CPR;
+  static constexpr int VPT = (VTASKS + kThreads - 1) / kThreads;
+  static_assert(KPT >= 1 && (kBN * CPR) % kThreads == 0, "tile/thread mismatch");
+
+  uint4 kr[KPT];
+  uint4 vr[VPT][4];
+
+  // kb/vb: wave-uniform base of the tile; stride: elements between key rows
+  // (< 2^31 / 64, so per-thread offsets stay 32-bit).
+  __device__ __forceinline__ void load(const T* __restrict__ kb, const T* __restrict__ vb,
+                                       int stride, int nvalid, int tid) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * kThreads;
+      const int row = c / CPR, col = c % CPR;
+      const int off = row * stride + col * CE;
+      kr[i] = row < nvalid ? *reinterpret_cast<const uint4*>(kb + off) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int task = tid + i * kThreads;
+      const int kg = task / CPR, dc = task % CPR;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * kg + r;
+        const int off = row * stride + dc * CE;
+        vr[i][r] = (task < VTASKS && row < nvalid) ? *reinterpret_cast<const uint4*>(vb + off)
+                                                   : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(T* ks, T* vt, int tid) const {
+    using S = Smem<T, D>;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * kThreads;
+      const int row = c / CPR, col = c % CPR;
+      *reinterpret_cast<uint4*>(ks + row * S::kKRow + col * CE) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int task = tid + i * kThreads;
+      if (task >= VTASKS) break;
+      const int kg = task / CPR, dc = task % CPR;
+#pragma unroll
+      for (int e = 0; e < CE; ++e) {
+        const int d = dc * CE + e;
+        T* dst = vt + d * S::kVRow + vt_group(d, kg) * 4;
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t h0 = half_of<T>(vr[i][0], e), h1 = half_of<T>(vr[i][1], e);
+          const uint32_t h2 = half_of<T>(vr[i][2], e), h3 = half_of<T>(vr[i][3], e);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        } else {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(half_of<T>(vr[i][0], e), half_of<T>(vr[i][1], e),
+                                                      half_of<T>(vr[i][2], e), half_of<T>(vr[i][3], e));
+        }
+      }
+    }
+  }
+};
+
+template <>
+__device__ __forceinline__ uint32_t half_of<bf16>(const uint4& x, int e) {
+  const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+template <>
+__device__ __forceinline__ uint32_t half_of<float>(const uint4& x, int e) {
+  return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
+}
+
+// ------------------------------------------------------ visibility rules
+// kind 0: document row q, document key c:  c <= q            (causal)
+// kind 1: slot j, document key c:          c < sink or c in [j k, j k + k)
+// kind 2: slot j, slot key j':             j' <= j           (causal)
+// kind 3: cache query t, cache row c:      c < cache_len + t + 1
+// plus c < kmax (the keys that exist in this region).
+struct Pred {
+  int kind, kmax, a, b;   // kind 1: a = sink, b = k;  kind 3: a = cache_len
+  __device__ __forceinline__ bool operator()(int q, int c) const {
+    if (c >= kmax) return false;
+    switch (kind) {
+      case 0: case 2: return c <= q;
+      case 1: return c < a || (c >= q * b && c < q * b + b);
+      default: return c <= a + q;
+    }
+  }
+};
+
+// ------------------------------------------------------ wave tile engine
+template <typename T, int D>
+struct WaveAttn {
+  using V8 = typename ElemTraits<T>::v8;
+  using V4 = typename ElemTraits<T>::v4;
+  static constexpr int KS = D / 32;   // 32-wide k steps of QK^T
+  static constexpr int DB = D / 16;   // 16-row blocks of O^T
+
+  V8 qB[2][KS];
+  f32x4 o[DB][2];
+  float m[2], l[2];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[0] = m[1] = -INFINITY;
+    l[0] = l[1] = 0.f;
+  }
+
+  // One 64-key tile: S^T = K Q^T, optional mask, online softmax, O^T += V^T P^T.
+  template <bool kMasked>
+  __device__ __forceinline__ void tile(const T* ks, const T* vt, int lane, float scale_log2,
+                                       const Pred& pred, int q0, int key0) {
+    using S = Smem<T, D>;
+    const int r16 = lane & 15, g = lane >> 4;
+    f32x4 s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const V8 a = *reinterpret_cast<const V8*>(ks + (16 * kb + r16) * S::kKRow + 32 * k + 8 * g);
+        s[kb][0] = mma16(a, qB[0][k], s[kb][0]);
+        s[kb][1] = mma16(a, qB[1][k], s[kb][1]);
+      }
+    }
+    V8 pB[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float x[4][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = s[kb][qb][i] * scale_log2;
+          if constexpr (kMasked) {
+            if (!pred(q0 + 16 * qb + r16, key0 + 16 * kb + 4 * g + i)) v = -INFINITY;
+          }
+          x[kb][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = wave_max_16_32(mx);
+      const float mnew = fmaxf(m[qb], mx);
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(m[qb] - muse);
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(x[kb][i] - muse);
+          x[kb][i] = p;
+          rs += p;
+        }
+      l[qb] = l[qb] * alpha + rs;
+      m[qb] = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pB[c][qb][i] = from_f32<T>(x[2 * c][i]);
+          pB[c][qb][4 + i] = from_f32<T>(x[2 * c + 1][i]);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = 16 * db + r16;
+        const T* row = vt + d * S::kVRow;
+        const V4 lo = *reinterpret_cast<const V4*>(row + vt_group(d, 8 * c + g) * 4);
+        const V4 hi = *reinterpret_cast<const V4*>(row + vt_group(d, 8 * c + 4 + g) * 4);
+        V8 a;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { a[i] = lo[i]; a[4 + i] = hi[i]; }
+        o[db][0] = mma16(a, pB[c][0], o[db][0]);
+        o[db][1] = mma16(a, pB[c][1], o[db][1]);
+      }
+    }
+  }
+};
+
+// Load 8 elements (one lane's k-group) of a row as fp32.
+template <typename T>
+__device__ __forceinline__ void load8_f32(const T* p, float* out);
+template <>
+__device__ __forceinline__ void load8_f32<bf16>(const bf16* p, float* out) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = static_cast<float>(v[e]);
+}
+template <>
+__device__ __forceinline__ void load8_f32<float>(const float* p, float* out) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { out[e] = a[e]; out[4 + e] = b[e]; }
+}
+
+// ===================================================== extraction kernel
+struct ExtractPlan {
+  int doc, kvh, slot_region, wvalid, head, q0, qend;
+  int nA0, nA1, nB0, nB1, nS;        // doc tiles [nA0,nA1) u [nB0,nB1), slot tiles [0,nS)
+  int64_t row0;
+  int n, m, ratio_k, sink;
+};
+
+__device__ __forceinline__ ExtractPlan extract_plan(const ExtractParams& p, int L, int wave) {
+  ExtractPlan P;
+  int b = 0;
+  while (b + 1 < p.num_docs && p.docs[b + 1].wg0 <= L) ++b;
+  const ExtractDoc& dc = p.docs[b];
+  P.doc = b;
+  P.row0 = dc.row0;
+  P.n = dc.n;
+  P.m = dc.m;
+  P.ratio_k = p.ratio_k;
+  P.sink = min(p.sink_len, dc.n);
+  const int per = dc.nwg_doc + dc.nwg_slot;
+  const int local = L - dc.wg0;
+  P.kvh = local / per;
+  int w = local % per;
+  P.slot_region = w >= dc.nwg_doc;
+  if (P.slot_region) w -= dc.nwg_doc;
+  const int G = p.G;
+  const int nrows = P.slot_region ? P.m : P.n;
+  const int nblk = (nrows + kQW - 1) / kQW;
+  const int nunits = nblk * G;
+  auto unit_rows = [&](int u, int& q0, int& q1) {
+    const int blk = P.slot_region ? u / G : nblk - 1 - u / G;
+    q0 = blk * kQW;
+    q1 = min(nrows, q0 + kQW);
+  };
+  const int u = w * kWaves + wave;
+  P.wvalid = u < nunits;
+  P.head = P.kvh * G + (u % G);
+  P.q0 = 0;
+  P.qend = 0;
+  if (P.wvalid) unit_rows(u, P.q0, P.qend);
+  // union of the waves' tile needs (identical in every wave)
+  int tmax = 0, j0 = 1 << 30, j1 = 0;
+  for (int ww = 0; ww < kWaves; ++ww) {
+    const int uu = w * kWaves + ww;
+    if (uu >= nunits) break;
+    int a0, a1;
+    unit_rows(uu, a0, a1);
+    tmax = max(tmax, (a1 + kBN - 1) / kBN);
+    j0 = min(j0, a0);
+    j1 = max(j1, a1);
+  }
+  if (!P.slot_region) {
+    P.nA0 = 0; P.nA1 = tmax; P.nB0 = 0; P.nB1 = 0; P.nS = 0;
+  } else {
+    const int ts = (P.sink + kBN - 1) / kBN;
+    const int blo = (j0 * P.ratio_k) / kBN;
+    const int bhi = (min(P.n, j1 * P.ratio_k) + kBN - 1) / kBN;
+    P.nA0 = 0; P.nA1 = ts;
+    P.nB0 = max(ts, blo); P.nB1 = max(P.nB0, bhi);
+    P.nS = tmax;
+  }
+  return P;
+}
+
+// Tile `it` of the plan: whether it holds a document or slot key range,
+// its index, and the visibility predicate / activity of the calling wave.
+struct TileSel {
+  int is_slot, t, key0, nvalid, active, masked;
+  Pred pred;
+};
+
+__device__ __forceinline__ TileSel extract_tile(const ExtractPlan& P, int it) {
+  TileSel s;
+  const int na = P.nA1 - P.nA0, nb = P.nB1 - P.nB0;
+  s.is_slot = it >= na + nb;
+  s.t = it < na ? P.nA0 + it : (it < na + nb ? P.nB0 + (it - na) : it - na - nb);
+  s.key0 = s.t * kBN;
+  const int nkeys = s.is_slot ? P.m : P.n;
+  s.nvalid = min(kBN, nkeys - s.key0);
+  if (!P.slot_region) {
+    s.active = P.wvalid && s.key0 < P.qend;
+    s.masked = (s.key0 + kBN - 1 > P.q0) || (s.key0 + kBN > P.n);
+    s.pred = Pred{0, P.n, 0, 0};
+  } else if (!s.is_slot) {
+    const int ts = (P.sink + kBN - 1) / kBN;
+    const int blo = (P.q0 * P.ratio_k) / kBN;
+    const int bhi = (min(P.n, P.qend * P.ratio_k) + kBN - 1) / kBN;
+    s.active = P.wvalid && (s.t < ts || (s.t >= blo && s.t < bhi));
+    s.masked = 1;
+    s.pred = Pred{1, P.n, P.sink, P.ratio_k};
+  } else {
+    s.active = P.wvalid && s.key0 < P.qend;
+    s.masked = (s.key0 + kBN - 1 > P.q0) || (s.key0 + kBN > P.m);
+    s.pred = Pred{2, P.m, 0, 0};
+  }
+  return s;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, (kMinWaves<T, D>)) void extract_attn_kernel(const ExtractParams p) {
+  using S = Smem<T, D>;
+  __shared__ __attribute__((aligned(16))) T smem[2 * S::kStage];
+  const int L = xcd_logical(blockIdx.x, p.grid_wg);
+  if (L >= p.total_wg) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const ExtractPlan P = extract_plan(p, L, wave);
+  const int hq = p.hq, hkv = p.hkv;
+  const int64_t kv_stride = (int64_t)hkv * D;
+  const T* kbase = reinterpret_cast<const T*>(p.krot) + P.row0 * kv_stride + (int64_t)P.kvh * D;
+  const T* vbase = reinterpret_cast<const T*>(p.v) + P.row0 * kv_stride + (int64_t)P.kvh * D;
+  const int64_t qrow_off = P.slot_region ? P.n : 0;
+
+  WaveAttn<T, D> W;
+  W.init();
+  // ---- queries: load, rotate at the extraction positions, keep as B operand
+  {
+    const int r16 = lane & 15, g = lane >> 4;
+    constexpr int H = D / 2;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int ql = P.q0 + 16 * qb + r16;
+      const bool ok = P.wvalid && ql < P.qend;
+      const int pos = P.slot_region ? min(ql * P.ratio_k + P.ratio_k - 1, P.n - 1) : ql;
+      const T* qrow = reinterpret_cast<const T*>(p.q) + ((P.row0 + qrow_off + ql) * hq + P.head) * (int64_t)D;
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) {
+        float lo[8], hi[8];
+        if (ok) {
+          load8_f32<T>(qrow + 32 * k + 8 * g, lo);
+          load8_f32<T>(qrow + H + 32 * k + 8 * g, hi);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lo[e] = hi[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 cs = ok ? p.rope[(int64_t)pos * H + 32 * k + 8 * g + e] : make_float2(1.f, 0.f);
+          float y0, y1;
+          rope_pair(lo[e], hi[e], cs.x, cs.y, y0, y1);
+          W.qB[qb][k][e] = from_f32<T>(y0);
+          W.qB[qb][k + D / 64][e] = from_f32<T>(y1);
+        }
+      }
+    }
+  }
+
+  const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
+  KVStage<T, D> ld;
+  auto issue = [&](int it) {
+    const TileSel ts = extract_tile(P, it);
+    const int64_t r = ts.is_slot ? (int64_t)P.n + ts.key0 : ts.key0;
+    ld.load(kbase + r * kv_stride, vbase + r * kv_stride, (int)kv_stride, ts.nvalid, tid);
+  };
+  if (ntiles > 0) issue(0);
+  for (int it = 0; it < ntiles; ++it) {
+    T* ks = smem + (it & 1) * S::kStage;
+    T* vt = ks + S::kKElems;
+    ld.store(ks, vt, tid);
+    __syncthreads();
+    if (it + 1 < ntiles) issue(it + 1);
+    const TileSel ts = extract_tile(P, it);
+    if (ts.active) {
+      const int qsel = P.q0;
+      if (ts.masked)
+        W.template tile<true>(ks, vt, lane, p.scale_log2, ts.pred, qsel, ts.key0);
+      else
+        W.template tile<false>(ks, vt, lane, p.scale_log2, ts.pred, qsel, ts.key0);
+    }
+  }
+
+  // ---- normalise and write rows
+  if (!P.wvalid) return;
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = wave_sum_16_32(W.l[qb]);
+    const float inv = 1.f / lt;
+    const int ql = P.q0 + 16 * qb + r16;
+    if (ql < P.qend) {
+      const int64_t prow = P.row0 + qrow_off + ql;
+      T* orow = reinterpret_cast<T*>(p.o) + (prow * hq + P.head) * (int64_t)D;
+#pragma unroll
+      for (int db = 0; db < WaveAttn<T, D>::DB; ++db) {
+        typename ElemTraits<T>::v4 outv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) outv[i] = from_f32<T>(W.o[db][qb][i] * inv);
+        *reinterpret_cast<typename ElemTraits<T>::v4*>(orow + 16 * db + 4 * g) = outv;
+      }
+      if (g == 0 && p.lse) p.lse[(int64_t)P.head * p.total_rows + prow] = (W.m[qb] + __log2f(lt)) * 0.69314718055994531f;
+    }
+  }
+}
+
+// Counting twin of the extraction kernel: the same plan, tile enumeration and
+// predicate, but each active (wave, tile) pair counts its visible cells.
+__global__ __launch_bounds__(kThreads) void mask_count_kernel(const ExtractParams p) {
+  const int L = xcd_logical(blockIdx.x, p.grid_wg);
+  if (L >= p.total_wg) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const ExtractPlan P = extract_plan(p, L, wave);
+  const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
+  unsigned long long c_dd = 0, c_sd = 0, c_ss = 0, c_empty = 0, c_tiles = 0;
+  for (int it = 0; it < ntiles; ++it) {
+    const TileSel ts = extract_tile(P, it);
+    if (!ts.active) continue;
+    // lane -> query row (lane % 32), keys [32*(lane/32), +32)
+    const int q = P.q0 + (lane & 31);
+    int cnt = 0;
+    if (q < P.qend) {
+      for (int kk = 0; kk < 32; ++kk) {
+        const int c = ts.key0 + 32 * (lane >> 5) + kk;
+        cnt += ts.pred(q, c) ? 1 : 0;
+      }
+    }
+    int tot = cnt;
+    for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off);
+    c_tiles += 1;
+    if (tot == 0) c_empty += 1;
+    if (!P.slot_region) c_dd += tot;
+    else if (!ts.is_slot) c_sd += tot;
+    else c_ss += tot;
+  }
+  // one query head per KV group is counted (the mask does not depend on the head)
+  if (lane == 0 && P.wvalid && (P.head % p.G) == 0) {
+    atomicAdd(reinterpret_cast<unsigned long long*>(p.counts + 0), c_dd);
+    atomicAdd(reinterpret_cast<unsigned long long*>(p.counts + 1), c_sd);
+    atomicAdd(reinterpret_cast<unsigned long long*>(p.counts + 2), c_ss);
+    atomicAdd(reinterpret_cast<unsigned long long*>(p.counts + 3), c_empty);
+    atomicAdd(reinterpret_cast<unsigned long long*>(p.counts + 4), c_tiles);
+  }
+}
+
+// ============================================== attention over the cache
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, (kMinWaves<T, D>)) void cache_attn_kernel(const CacheParams p) {
+  using S = Smem<T, D>;
+  __shared__ __attribute__((aligned(16))) T smem[2 * S::kStage];
+  const int L = xcd_logical(blockIdx.x, p.grid_wg);
+  if (L >= p.total_wg) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int ri = 0;
+  while (ri + 1 < p.num_reqs && p.reqs[ri + 1].wg0 <= L) ++ri;
+  const CacheReq rq = p.reqs[ri];
+  const int r = p.req0 + ri;
+  const int per_kvh = rq.nsplit * p.nug;
+  const int local = L - rq.wg0;
+  const int kvh = local / per_kvh;
+  const int rem = local % per_kvh;
+  const int split = rem / p.nug, ug = rem % p.nug;
+  const int G = p.G;
+  const int u = ug * kWaves + wave;
+  const int nunits = p.nblk_q * G;
+  const bool wvalid = u < nunits;
+  const int blk = u / G, head = kvh * G + (u % G);
+  const int t0 = blk * kQW, t1 = wvalid ? min(p.tq, t0 + kQW) : 0;
+  const int Lr = rq.cache_len + p.tq;
+  const int ks0 = split * p.chunk, ks1 = min(Lr, ks0 + p.chunk);
+  constexpr int stride = D;
+  const int64_t head_base = ((int64_t)r * p.hkv + kvh) * p.cap;
+  const T* kbase = reinterpret_cast<const T*>(p.kc) + (head_base + ks0) * D;
+  const T* vbase = reinterpret_cast<const T*>(p.vc) + (head_base + ks0) * D;
+
+  WaveAttn<T, D> W;
+  W.init();
+  {
+    const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int t = t0 + 16 * qb + r16;
+      const bool ok = wvalid && t < t1;
+      const T* qrow = reinterpret_cast<const T*>(p.qrot) + (((int64_t)r * p.tq + t) * p.hq + head) * D;
+#pragma unroll
+      for (int k = 0; k < D / 32; ++k) {
+        float x[8];
+        if (ok) load8_f32<T>(qrow + 32 * k + 8 * g, x);
+        else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) W.qB[qb][k][e] = from_f32<T>(x[e]);
+      }
+    }
+  }
+  const int ntiles = (ks1 - ks0 + kBN - 1) / kBN;
+  KVStage<T, D> ld;
+  const Pred pred{3, ks1, rq.cache_len, 0};
+  if (ntiles > 0) ld.load(kbase, vbase, stride, min(kBN, ks1 - ks0), tid);
+  for (int it = 0; it < ntiles; ++it) {
+    T* ks = smem + (it & 1) * S::kStage;
+    T* vt = ks + S::kKElems;
+    ld.store(ks, vt, tid);
+    __syncthreads();
+    if (it + 1 < ntiles) {
+      const int k0 = (it + 1) * kBN;
+      ld.load(kbase + (int64_t)k0 * stride, vbase + (int64_t)k0 * stride, stride, min(kBN, ks1 - ks0 - k0), tid);
+    }
+    const int key0 = ks0 + it * kBN;
+    const bool active = wvalid && key0 < rq.cache_len + t1;
+    if (active) {
+      const bool masked = (key0 + kBN > rq.cache_len + t0 + 1) || (key0 + kBN > ks1);
+      if (masked) W.template tile<true>(ks, vt, lane, p.scale_log2, pred, t0, key0);
+      else W.template tile<false>(ks, vt, lane, p.scale_log2, pred, t0, key0);
+    }
+  }
+
+  // ---- final rows (one key chunk) or split partials [o(D) | m | l | pad]
+  if (!wvalid) return;
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = wave_sum_16_32(W.l[qb]);
+    const int t = t0 + 16 * qb + r16;
+    if (t >= t1) continue;
+    if (rq.nsplit == 1) {
+      const float inv = 1.f / lt;
+      T* orow = reinterpret_cast<T*>(p.o) + (((int64_t)r * p.tq + t) * p.hq + head) * D;
+#pragma unroll
+      for (int db = 0; db < WaveAttn<T, D>::DB; ++db) {
+        typename ElemTraits<T>::v4 outv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) outv[i] = from_f32<T>(W.o[db][qb][i] * inv);
+        *reinterpret_cast<typename ElemTraits<T>::v4*>(orow + 16 * db + 4 * g) = outv;
+      }
+      if (g == 0 && p.lse)
+        p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (W.m[qb] + __log2f(lt)) * 0.69314718055994531f;
+    } else {
+      float* prow = p.part + ((((int64_t)ri * p.hq + head) * p.tq + t) * p.nsplit_stride + split) * (D + 4);
+      if (g == 0) { prow[D] = W.m[qb]; prow[D + 1] = lt; }
+#pragma unroll
+      for (int db = 0; db < WaveAttn<T, D>::DB; ++db)
+        *reinterpret_cast<f32x4*>(prow + 16 * db + 4 * g) = W.o[db][qb];
+    }
+  }
+}
+
+// ------------------------------------------------------------ launchers
+template <typename T, int D>
+static hipError_t launch_extract_t(const ExtractParams& p, bool count, hipStream_t st) {
+  if (count) {
+    hipLaunchKernelGGL(mask_count_kernel, dim3(p.grid_wg), dim3(kThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((extract_attn_kernel<T, D>), dim3(p.grid_wg), dim3(kThreads), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_extract_attn(const ExtractParams& p, int dtype, int head_dim, bool count, hipStream_t st) {
+  if (dtype == C2KV_BF16) {
+    return head_dim == 128 ? launch_extract_t<bf16, 128>(p, count, st) : launch_extract_t<bf16, 64>(p, count, st);
+  }
+  return head_dim == 128 ? launch_extract_t<float, 128>(p, count, st) : launch_extract_t<float, 64>(p, count, st);
+}
+
+template <typename T, int D>
+static hipError_t launch_cache_t(const CacheParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((cache_attn_kernel<T, D>), dim3(p.grid_wg), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_attn(const CacheParams& p, int dtype, int head_dim, hipStream_t st) {
+  if (dtype == C2KV_BF16) {
+    return head_dim == 128 ? launch_cache_t<bf16, 128>(p, st) : launch_cache_t<bf16, 64>(p, st);
+  }
+  return head_dim == 128 ? launch_cache_t<float, 128>(p, st) : launch_cache_t<float, 64>(p, st);
+}
+
+}  // namespace c2kv

@@ -1,0 +1,265 @@
+// Bandwidth-bound kernels of the C2KV hot path for gfx950:
+//   * RoPE cos/sin table and key pre-rotation for extraction,
+//   * compose: realigned RoPE of the stored pre-RoPE slot keys fused with the
+//     scatter of keys and values into the contiguous per-request cache (the
+//     C2KV explainer's positions section: every document keeps its original
+//     length in positions, later documents are offset by the lengths before
+//     them, slot j sits at its block's last token),
+//   * append: rotation of question/decode queries and keys, with the new keys
+//     and values written into the cache,
+//   * a zero-fill kernel for workspaces.
+//
+// Every RoPE'd element pair (x_i, x_{i+d/2}) is handled by one thread that
+// reads both halves with 16-byte loads, so rotation needs no data exchange;
+// a thread covers one 16-byte chunk of each half.
+#include "c2kv_device.hpp"
+#include "c2kv_launch.hpp"
+
+namespace c2kv {
+
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16> {
+  static constexpr int CE = 8;
+  __device__ static void unpack(const uint4& u, float* f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static uint4 pack(const float* f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16 a = static_cast<bf16>(f[2 * i]);
+      const bf16 b = static_cast<bf16>(f[2 * i + 1]);
+      w[i] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct Chunk<float> {
+  static constexpr int CE = 4;
+  __device__ static void unpack(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+};
+
+// Rotate one chunk pair (lo = elements [i0, i0+CE), hi = the same + d/2)
+// with per-element (cos, sin).
+template <typename T>
+__device__ __forceinline__ void rotate_chunk(uint4& lo, uint4& hi, const float* c, const float* s) {
+  constexpr int CE = Chunk<T>::CE;
+  float a[CE], b[CE], y0[CE], y1[CE];
+  Chunk<T>::unpack(lo, a);
+  Chunk<T>::unpack(hi, b);
+#pragma unroll
+  for (int e = 0; e < CE; ++e) rope_pair(a[e], b[e], c[e], s[e], y0[e], y1[e]);
+  lo = Chunk<T>::pack(y0);
+  hi = Chunk<T>::pack(y1);
+}
+
+// ------------------------------------------------------------ RoPE table
+__global__ void rope_table_kernel(float2* table, int npos, int half, const RopeFreqs f) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)npos * half) return;
+  const int pos = (int)(idx / half), i = (int)(idx % half);
+  float c, s;
+  rope_cs(pos, f.f[i], c, s);
+  table[idx] = make_float2(c, s);
+}
+
+hipError_t launch_rope_table(float2* table, int npos, int head_dim, const RopeFreqs& f, hipStream_t st) {
+  const int half = head_dim / 2;
+  const int64_t n = (int64_t)npos * half;
+  const int blocks = (int)((n + 255) / 256);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, st, table, npos, half, f);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------ extraction key rotation
+template <typename T, int D>
+__global__ void rotate_k_kernel(const RotateParams p) {
+  constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = (int64_t)p.hkv * TPH;
+  const int64_t row = p.row_begin + idx / per_row;
+  if (row >= p.row_end) return;
+  const int h = (int)((idx % per_row) / TPH), c = (int)(idx % TPH);
+  int b = 0;
+  while (b + 1 < p.num_docs && p.docs[b + 1].row0 <= row) ++b;
+  const int local = (int)(row - p.docs[b].row0);
+  const int n = p.docs[b].n;
+  const int pos = local < n ? local : min((local - n) * p.ratio_k + p.ratio_k - 1, n - 1);
+  const int64_t off = (row * p.hkv + h) * D + c * CE;
+  const T* src = reinterpret_cast<const T*>(p.k) + off;
+  T* dst = reinterpret_cast<T*>(p.krot) + off;
+  uint4 lo = *reinterpret_cast<const uint4*>(src);
+  uint4 hi = *reinterpret_cast<const uint4*>(src + H);
+  float cs[CE], sn[CE];
+#pragma unroll
+  for (int e = 0; e < CE; ++e) {
+    const float2 t = p.rope[(int64_t)pos * H + c * CE + e];
+    cs[e] = t.x;
+    sn[e] = t.y;
+  }
+  rotate_chunk<T>(lo, hi, cs, sn);
+  *reinterpret_cast<uint4*>(dst) = lo;
+  *reinterpret_cast<uint4*>(dst + H) = hi;
+}
+
+template <typename T, int D>
+static hipError_t launch_rotate_k_t(const RotateParams& p, hipStream_t st) {
+  constexpr int TPH = D / 2 / Chunk<T>::CE;
+  const int64_t n = (p.row_end - p.row_begin) * p.hkv * TPH;
+  const int blocks = (int)((n + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((rotate_k_kernel<T, D>), dim3(blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipStream_t st) {
+  if (dtype == C2KV_BF16) return head_dim == 128 ? launch_rotate_k_t<bf16, 128>(p, st) : launch_rotate_k_t<bf16, 64>(p, st);
+  return head_dim == 128 ? launch_rotate_k_t<float, 128>(p, st) : launch_rotate_k_t<float, 64>(p, st);
+}
+
+// ---------------------------------------------------------------- compose
+// One thread per (composed slot row, KV head, 16-byte chunk of the low
+// half).  The row's segment is found by binary search in the launch's
+// segment table; its realigned position is the document offset plus the
+// slot's extraction position.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void compose_kernel(const ComposeParams p) {
+  constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = (int64_t)p.hkv * TPH;
+  const int64_t grow = idx / per_row;
+  if (grow >= p.total_rows) return;
+  const int h = (int)((idx % per_row) / TPH), c = (int)(idx % TPH);
+  int lo_s = 0, hi_s = p.num_segs - 1;
+  while (lo_s < hi_s) {
+    const int mid = (lo_s + hi_s + 1) >> 1;
+    if (p.segs[mid].row_prefix <= grow) lo_s = mid; else hi_s = mid - 1;
+  }
+  const ComposeSeg sg = p.segs[lo_s];
+  const int j = (int)(grow - sg.row_prefix);
+  const int cpos = sg.pos_off + min(j * p.ratio_k + p.ratio_k - 1, sg.n - 1);
+  const int64_t src_off = (int64_t)j * sg.stride + (int64_t)h * D + c * CE;
+  const int64_t dst_off = (((int64_t)sg.req * p.hkv + h) * p.cap + sg.out_row + j) * D + c * CE;
+  const T* ks = reinterpret_cast<const T*>(sg.k) + src_off;
+  const T* vs = reinterpret_cast<const T*>(sg.v) + src_off;
+  uint4 klo = *reinterpret_cast<const uint4*>(ks);
+  uint4 khi = *reinterpret_cast<const uint4*>(ks + H);
+  const uint4 vlo = *reinterpret_cast<const uint4*>(vs);
+  const uint4 vhi = *reinterpret_cast<const uint4*>(vs + H);
+  float cs[CE], sn[CE];
+#pragma unroll
+  for (int e = 0; e < CE; ++e) rope_cs(cpos, p.freqs.f[c * CE + e], cs[e], sn[e]);
+  rotate_chunk<T>(klo, khi, cs, sn);
+  T* kd = reinterpret_cast<T*>(p.cache_k) + dst_off;
+  T* vd = reinterpret_cast<T*>(p.cache_v) + dst_off;
+  *reinterpret_cast<uint4*>(kd) = klo;
+  *reinterpret_cast<uint4*>(kd + H) = khi;
+  *reinterpret_cast<uint4*>(vd) = vlo;
+  *reinterpret_cast<uint4*>(vd + H) = vhi;
+  if (p.pos_out && h == 0 && c == 0) p.pos_out[(int64_t)sg.req * p.cap + sg.out_row + j] = cpos;
+}
+
+template <typename T, int D>
+static hipError_t launch_compose_t(const ComposeParams& p, hipStream_t st) {
+  constexpr int TPH = D / 2 / Chunk<T>::CE;
+  const int64_t n = (int64_t)p.total_rows * p.hkv * TPH;
+  const int blocks = (int)((n + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((compose_kernel<T, D>), dim3(blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_compose(const ComposeParams& p, int dtype, int head_dim, hipStream_t st) {
+  if (dtype == C2KV_BF16) return head_dim == 128 ? launch_compose_t<bf16, 128>(p, st) : launch_compose_t<bf16, 64>(p, st);
+  return head_dim == 128 ? launch_compose_t<float, 128>(p, st) : launch_compose_t<float, 64>(p, st);
+}
+
+// ----------------------------------------------------------------- append
+// One thread per (request, token, head, chunk); heads [0, hq) are query
+// heads (rotated into the workspace), heads [hq, hq+hkv) are new keys
+// (rotated into the cache) together with their values (copied).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
+  constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int nh = p.hq + p.hkv;
+  const int64_t per_tok = (int64_t)nh * TPH;
+  const int64_t tok = idx / per_tok;
+  if (tok >= (int64_t)p.num_reqs * p.tq) return;
+  const int ri = (int)(tok / p.tq), t = (int)(tok % p.tq);
+  const int h = (int)((idx % per_tok) / TPH), c = (int)(idx % TPH);
+  const int r = p.req0 + ri;
+  const AppendReq rq = p.reqs[ri];
+  const int pos = rq.pos0 + t;
+  float cs[CE], sn[CE];
+#pragma unroll
+  for (int e = 0; e < CE; ++e) rope_cs(pos, p.freqs.f[c * CE + e], cs[e], sn[e]);
+  if (h < p.hq) {
+    const int64_t off = (((int64_t)r * p.tq + t) * p.hq + h) * D + c * CE;
+    const T* src = reinterpret_cast<const T*>(p.q) + off;
+    T* dst = reinterpret_cast<T*>(p.qrot) + off;
+    uint4 lo = *reinterpret_cast<const uint4*>(src);
+    uint4 hi = *reinterpret_cast<const uint4*>(src + H);
+    rotate_chunk<T>(lo, hi, cs, sn);
+    *reinterpret_cast<uint4*>(dst) = lo;
+    *reinterpret_cast<uint4*>(dst + H) = hi;
+  } else {
+    const int kvh = h - p.hq;
+    const int64_t soff = (((int64_t)r * p.tq + t) * p.hkv + kvh) * D + c * CE;
+    const int64_t doff = (((int64_t)r * p.hkv + kvh) * p.cap + rq.cache_len + t) * D + c * CE;
+    const T* ks = reinterpret_cast<const T*>(p.k_new) + soff;
+    const T* vs = reinterpret_cast<const T*>(p.v_new) + soff;
+    uint4 lo = *reinterpret_cast<const uint4*>(ks);
+    uint4 hi = *reinterpret_cast<const uint4*>(ks + H);
+    rotate_chunk<T>(lo, hi, cs, sn);
+    T* kd = reinterpret_cast<T*>(p.cache_k) + doff;
+    T* vd = reinterpret_cast<T*>(p.cache_v) + doff;
+    *reinterpret_cast<uint4*>(kd) = lo;
+    *reinterpret_cast<uint4*>(kd + H) = hi;
+    *reinterpret_cast<uint4*>(vd) = *reinterpret_cast<const uint4*>(vs);
+    *reinterpret_cast<uint4*>(vd + H) = *reinterpret_cast<const uint4*>(vs + H);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_append_t(const AppendParams& p, hipStream_t st) {
+  constexpr int TPH = D / 2 / Chunk<T>::CE;
+  const int64_t n = (int64_t)p.num_reqs * p.tq * (p.hq + p.hkv) * TPH;
+  const int blocks = (int)((n + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((append_kernel<T, D>), dim3(blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendParams& p, int dtype, int head_dim, hipStream_t st) {
+  if (dtype == C2KV_BF16) return head_dim == 128 ? launch_append_t<bf16, 128>(p, st) : launch_append_t<bf16, 64>(p, st);
+  return head_dim == 128 ? launch_append_t<float, 128>(p, st) : launch_append_t<float, 64>(p, st);
+}
+
+// --------------------------------------------------------------- zero fill
+__global__ void fill_zero_kernel(uint32_t* p, int64_t nwords) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) p[i] = 0u;
+}
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t st) {
+  const int64_t nwords = (int64_t)(bytes / 4);
+  if (nwords == 0) return hipSuccess;
+  const int64_t want = (nwords + 255) / 256;
+  const int blocks = (int)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, st, reinterpret_cast<uint32_t*>(ptr), nwords);
+  return hipGetLastError();
+}
+
+}  // namespace c2kv

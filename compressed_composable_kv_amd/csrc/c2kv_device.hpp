@@ -1,0 +1,186 @@
+// Device-side building blocks of the C2KV kernels for gfx950 (CDNA4):
+// element traits, MFMA wrappers, RoPE rotation, wave reductions, and the
+// kernel parameter blocks shared with the host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "c2kv.h"
+
+namespace c2kv {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- tiling
+constexpr int kBN = 64;        // keys per K/V tile
+constexpr int kQW = 32;        // query rows per wave (two 16-row MFMA blocks)
+constexpr int kWaves = 4;      // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kVPad = 8;       // elements of padding per V^T row in LDS
+constexpr int kMaxHalfDim = 64;
+
+template <typename T> struct ElemTraits;
+template <> struct ElemTraits<bf16> {
+  using v8 = bf16x8;
+  using v4 = bf16x4;
+  static constexpr int kChunk = 8;     // elements per 16-byte chunk
+};
+template <> struct ElemTraits<float> {
+  using v8 = f32x8;
+  using v4 = f32x4;
+  static constexpr int kChunk = 4;
+};
+
+// D[16x16] += A[16x32] * B[32x16].  Lane l supplies A row l%16 and B column
+// l%16, each with 8 consecutive k-elements of group l/16; the same (group,
+// element) -> k assignment holds for A and B, so any k order the hardware
+// uses gives the same sum.  Result lane l holds D rows 4*(l/16)+i, column l%16.
+__device__ __forceinline__ f32x4 mma16(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// fp32 operands: eight 16x16x4 steps, step e taking element e of each lane's
+// 8-element group as that lane's single k value.
+__device__ __forceinline__ f32x4 mma16(const f32x8& a, const f32x8& b, f32x4 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// ---------------------------------------------------------------- RoPE
+// Rotation of one half-split pair (x_i, x_{i+d/2}) by (c, s) with each
+// product and sum rounded to fp32 separately (no contraction).
+__device__ __forceinline__ void rope_pair(float x0, float x1, float c, float s,
+                                          float& y0, float& y1) {
+#pragma clang fp contract(off)
+  const float a = x0 * c;
+  const float b = x1 * s;
+  const float e = x1 * c;
+  const float f = x0 * s;
+  y0 = a - b;
+  y1 = e + f;
+}
+
+// cos/sin of the fp32 angle fp32(pos) * inv_freq (one rounded multiply).
+__device__ __forceinline__ void rope_cs(int32_t pos, float inv_freq, float& c, float& s) {
+#pragma clang fp contract(off)
+  const float ang = static_cast<float>(pos) * inv_freq;
+  sincosf(ang, &s, &c);
+}
+
+struct RopeFreqs {
+  float f[kMaxHalfDim];
+};
+
+// ---------------------------------------------------------------- waves
+__device__ __forceinline__ float wave_max_16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_16_32(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Physical workgroup -> logical workgroup so that each XCD (8 per MI355X,
+// dispatched round robin) runs a contiguous slice of the logical order; the
+// workgroups that share K/V tiles then share one XCD's L2.
+__device__ __forceinline__ int xcd_logical(int p, int grid) {
+  const int per = grid >> 3;  // grid is a multiple of 8
+  return (p & 7) * per + (p >> 3);
+}
+
+// ---------------------------------------------------------------- params
+struct ExtractDoc {
+  int64_t row0;      // first packed row of the document in the batch
+  int32_t n, m;      // document tokens, slots
+  int32_t wg0;       // first logical workgroup of the document
+  int32_t nwg_doc;   // workgroups per KV head over document rows
+  int32_t nwg_slot;  // workgroups per KV head over slot rows
+  int32_t pad;
+};
+
+struct ExtractParams {
+  const void* q;        // [rows][hq][D]   pre-RoPE
+  const void* krot;     // [rows][hkv][D]  rotated keys (workspace)
+  const void* v;        // [rows][hkv][D]
+  void* o;              // [rows][hq][D]
+  float* lse;           // [hq][rows] or null
+  const float2* rope;   // [max_n][D/2] (cos, sin)
+  uint64_t* counts;     // mask-count mode: 5 counters
+  int64_t total_rows;
+  int32_t num_docs, hq, hkv, G, ratio_k, sink_len;
+  int32_t total_wg, grid_wg;
+  float scale_log2;
+  ExtractDoc docs[C2KV_MAX_BATCH];
+};
+
+struct CacheReq {
+  int32_t wg0;       // first logical workgroup of the request
+  int32_t cache_len; // rows before the appended question
+  int32_t nsplit;    // key chunks
+  int32_t pad;
+};
+
+// Split partial rows are laid out [request of launch][head][token][split]
+// with (D + 4) floats each: o (unnormalised, D), running max m (log2
+// domain), sum l, two pad words.
+struct CacheParams {
+  const void* qrot;     // [R][tq][hq][D] rotated queries (workspace)
+  const void* kc;       // [R][hkv][cap][D]
+  const void* vc;
+  void* o;              // [R][tq][hq][D]
+  float* lse;           // [R][hq][tq] or null
+  float* part;          // split partials
+  int64_t cap;
+  int32_t req0;         // first request of this launch (global index)
+  int32_t num_reqs, tq, hq, hkv, G, nblk_q, nug, chunk, nsplit_stride;
+  int32_t total_wg, grid_wg;
+  float scale_log2;
+  CacheReq reqs[C2KV_MAX_BATCH];
+};
+
+struct DecodeReq {
+  int32_t wg0;       // first workgroup of the request
+  int32_t cache_len; // rows before the new token (its row)
+  int32_t pos;       // position of the new token
+  int32_t nsplit;
+};
+
+struct DecodeParams {
+  const void* q;        // [R][hq][D] pre-RoPE
+  const void* k_new;    // [R][hkv][D] pre-RoPE
+  const void* v_new;
+  void* kc;             // [R][hkv][cap][D]
+  void* vc;
+  void* o;              // [R][hq][D]
+  float* lse;           // [R][hq] or null
+  float* part;          // split partials (see CacheParams)
+  int64_t cap;
+  int32_t req0, num_reqs, hq, hkv, G, chunk, nsplit_stride, total_wg;
+  float scale_log2;
+  RopeFreqs freqs;
+  DecodeReq reqs[C2KV_MAX_BATCH];
+};
+
+struct MergeParams {
+  const float* part;
+  void* o;              // [R][tq][hq][D]
+  float* lse;           // [R][hq][tq] or null
+  int32_t req0, num_rows, hq, tq, nsplit_stride, pad;
+  int32_t nsplit[C2KV_MAX_BATCH];
+};
+
+}  // namespace c2kv

@@ -1,0 +1,264 @@
+"""Python binding of the C2KV C ABI: the same entry points, taking torch
+tensors.  Argument marshalling only -- every step runs in libc2kv.so's HIP
+kernels; torch provides device memory and the current stream.  Raises
+ImportError when the library is missing and C2KVError on any failure status.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import C2KVError, Segment, check, load
+
+_DT = {torch.bfloat16: 0, torch.float32: 1}
+
+
+def _arr_i32(vals: Sequence[int]):
+    a = (ctypes.c_int32 * max(1, len(vals)))(*[int(v) for v in vals])
+    return a
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype=None) -> None:
+    _need(isinstance(t, torch.Tensor) and t.is_cuda, f"{name} must be a CUDA tensor")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}")
+
+
+class _Workspaces:
+    """Per-device scratch buffers, grown on demand (the library ignores
+    their contents on entry)."""
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, key, nbytes: int, device: torch.device, zero: bool) -> torch.Tensor:
+        k = (key, device.index)
+        buf = self._bufs.get(k)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(256, (nbytes + 255) // 256 * 256), dtype=torch.uint8, device=device)
+            if zero:
+                check(load().c2kv_workspace_init(_ptr(buf), buf.numel(), _stream(device)))
+            self._bufs[k] = buf
+        return buf
+
+
+WORKSPACES = _Workspaces()
+
+
+def _workspace(given: Optional[torch.Tensor], key: str, nbytes: int, device: torch.device) -> torch.Tensor:
+    if given is None:
+        return WORKSPACES.get(key, nbytes, device, zero=False)
+    _dev_tensor(given, "workspace", torch.uint8)
+    _need(given.numel() >= nbytes, f"workspace has {given.numel()} bytes, {nbytes} needed")
+    return given
+
+
+def workspace_size_extract(doc_lens: Sequence[int], ratio_k: int, hkv: int, head_dim: int, dtype) -> int:
+    return int(load().c2kv_workspace_size_extract(_arr_i32(doc_lens), len(doc_lens), ratio_k, hkv, head_dim,
+                                                  _DT[dtype]))
+
+
+def workspace_size_prefill(cache_len: Sequence[int], tq: int, hq: int, hkv: int, head_dim: int, dtype) -> int:
+    return int(load().c2kv_workspace_size_prefill(_arr_i32(cache_len), len(cache_len), tq, hq, hkv, head_dim,
+                                                  _DT[dtype]))
+
+
+def workspace_size_decode(cache_len: Sequence[int], hq: int, hkv: int, head_dim: int, dtype) -> int:
+    return int(load().c2kv_workspace_size_decode(_arr_i32(cache_len), len(cache_len), hq, hkv, head_dim,
+                                                 _DT[dtype]))
+
+
+# ------------------------------------------------------------ closed forms
+
+def version() -> str:
+    return load().c2kv_version().decode()
+
+
+def num_slots(n: int, k: int) -> int:
+    return int(load().c2kv_num_slots(n, k))
+
+
+def slot_position(n: int, k: int, j: int) -> int:
+    return int(load().c2kv_slot_position(n, k, j))
+
+
+def rope_inv_freq(head_dim: int, rope_theta: float) -> List[float]:
+    out = (ctypes.c_float * (head_dim // 2))()
+    check(load().c2kv_rope_inv_freq(head_dim, rope_theta, out))
+    return list(out)
+
+
+def packed_rows(doc_lens: Sequence[int], ratio_k: int) -> int:
+    return sum(int(n) + num_slots(int(n), ratio_k) for n in doc_lens)
+
+
+# -------------------------------------------------------------- extraction
+
+def extract_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_lens: Sequence[int],
+                 ratio_k: int, sink_len: Optional[int] = None, rope_theta: float = 10000.0,
+                 return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None
+                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Structured-flow extraction attention (c2kv_extract_attn).
+
+    q [sum_T][hq][d], k/v [sum_T][hkv][d], rows packed per document as
+    [n doc | ceil(n/k) slots].  Returns (o [sum_T][hq][d], lse [hq][sum_T] or None).
+    """
+    lib = load()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_tensor(t, nm, q.dtype)
+    _need(q.dtype in _DT, "dtype must be bfloat16 or float32")
+    rows, hq, d = q.shape
+    _need(k.shape == v.shape and k.shape[0] == rows and k.shape[2] == d, "k/v shape mismatch")
+    hkv = k.shape[1]
+    _need(rows == packed_rows(doc_lens, ratio_k), "q rows != packed rows of doc_lens")
+    if sink_len is None:
+        sink_len = ratio_k
+    o = out if out is not None else torch.empty_like(q)
+    _dev_tensor(o, "out", q.dtype)
+    lse = torch.empty((hq, rows), dtype=torch.float32, device=q.device) if return_lse else None
+    lens = _arr_i32(doc_lens)
+    dt = _DT[q.dtype]
+    nbytes = lib.c2kv_workspace_size_extract(lens, len(doc_lens), ratio_k, hkv, d, dt)
+    _need(nbytes > 0, "invalid extraction arguments")
+    ws = _workspace(workspace, "extract", nbytes, q.device)
+    check(lib.c2kv_extract_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), lens, len(doc_lens),
+                                ratio_k, sink_len, hq, hkv, d, float(rope_theta), dt,
+                                _ptr(ws), ws.numel(), _stream(q.device)))
+    return o, lse
+
+
+def slot_views(k: torch.Tensor, v: torch.Tensor, doc_lens: Sequence[int], ratio_k: int
+               ) -> List[Tuple[torch.Tensor, torch.Tensor, int]]:
+    """The stored C2KV of each document: views of its slot rows in the packed
+    extraction K/V (pre-RoPE), as (k [m][hkv][d], v [m][hkv][d], n)."""
+    segs, row = [], 0
+    for n in doc_lens:
+        m = num_slots(int(n), ratio_k)
+        segs.append((k[row + n: row + n + m], v[row + n: row + n + m], int(n)))
+        row += n + m
+    return segs
+
+
+# ------------------------------------------------------------- composition
+
+def compose(requests: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int]]], ratio_k: int,
+            rope_theta: float, cache_k: torch.Tensor, cache_v: torch.Tensor,
+            pos_base: Optional[Sequence[int]] = None, pos_out: Optional[torch.Tensor] = None
+            ) -> Tuple[List[int], List[int]]:
+    """Compose per-request lists of (slot_k, slot_v, doc_len) into
+    cache_k/cache_v [R][hkv][cap][d] (c2kv_compose).  Returns
+    (cache_len per request, next position per request)."""
+    lib = load()
+    _dev_tensor(cache_k, "cache_k")
+    _dev_tensor(cache_v, "cache_v", cache_k.dtype)
+    R, hkv, cap, d = cache_k.shape
+    _need(len(requests) == R, "one segment list per request")
+    segs, ptr, keep = [], [0], []
+    for req in requests:
+        for sk, sv, n in req:
+            _need(sk.is_cuda and sv.is_cuda and sk.dtype == cache_k.dtype and sv.dtype == cache_k.dtype,
+                  "segments must be CUDA tensors of the cache dtype")
+            _need(sk.dim() == 3 and sk.shape[1:] == (hkv, d) and sv.shape == sk.shape, "segment shape")
+            _need(sk.stride(2) == 1 and sk.stride(1) == d and sv.stride() == sk.stride(), "segment layout")
+            segs.append(Segment(sk.data_ptr(), sv.data_ptr(), sk.stride(0), int(n), 0))
+            keep.append((sk, sv))
+        ptr.append(len(segs))
+    arr = (Segment * len(segs))(*segs)
+    lens = (ctypes.c_int32 * R)()
+    nxt = (ctypes.c_int32 * R)()
+    if pos_out is not None:
+        _dev_tensor(pos_out, "pos_out", torch.int32)
+        _need(pos_out.shape == (R, cap), "pos_out must be [R][cap]")
+    base = _arr_i32(pos_base) if pos_base is not None else None
+    check(lib.c2kv_compose(arr, len(segs), _arr_i32(ptr), R, base, ratio_k, hkv, d, float(rope_theta),
+                           _ptr(cache_k), _ptr(cache_v), cap, _ptr(pos_out), lens, nxt,
+                           _DT[cache_k.dtype], None, 0, _stream(cache_k.device)))
+    return list(lens), list(nxt)
+
+
+# ------------------------------------------------ attention over the cache
+
+def _cache_call(fn_name, q, k_new, v_new, cache_k, cache_v, cache_len, q_pos, rope_theta, return_lse, tq,
+                workspace=None):
+    lib = load()
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (cache_k, "cache_k"), (cache_v, "cache_v")):
+        _dev_tensor(t, nm, cache_k.dtype)
+    R, hkv, cap, d = cache_k.shape
+    hq = q.shape[-2]
+    _need(len(cache_len) == R and len(q_pos) == R, "cache_len/q_pos need one entry per request")
+    lens = _arr_i32(cache_len)
+    pos = _arr_i32(q_pos)
+    dt = _DT[cache_k.dtype]
+    o = torch.empty_like(q)
+    if tq is None:
+        _need(q.shape == (R, hq, d) and k_new.shape == (R, hkv, d) and v_new.shape == k_new.shape, "decode shapes")
+        lse = torch.empty((R, hq), dtype=torch.float32, device=q.device) if return_lse else None
+        nbytes = lib.c2kv_workspace_size_decode(lens, R, hq, hkv, d, dt)
+        _need(nbytes > 0, "invalid decode arguments")
+        ws = _workspace(workspace, "cache", nbytes, q.device)
+        check(lib.c2kv_attn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cache_k), _ptr(cache_v), cap,
+                                   lens, pos, R, hq, hkv, d, float(rope_theta), _ptr(o), _ptr(lse), dt,
+                                   _ptr(ws), ws.numel(), _stream(q.device)))
+    else:
+        _need(q.shape == (R, tq, hq, d) and k_new.shape == (R, tq, hkv, d) and v_new.shape == k_new.shape,
+              "prefill shapes")
+        lse = torch.empty((R, hq, tq), dtype=torch.float32, device=q.device) if return_lse else None
+        nbytes = lib.c2kv_workspace_size_prefill(lens, R, tq, hq, hkv, d, dt)
+        _need(nbytes > 0, "invalid prefill arguments")
+        ws = _workspace(workspace, "cache", nbytes, q.device)
+        check(lib.c2kv_attn_prefill(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cache_k), _ptr(cache_v), cap,
+                                    lens, pos, R, tq, hq, hkv, d, float(rope_theta), _ptr(o), _ptr(lse), dt,
+                                    _ptr(ws), ws.numel(), _stream(q.device)))
+    return o, lse
+
+
+def attn_prefill(q, k_new, v_new, cache_k, cache_v, cache_len, q_pos0, rope_theta, return_lse=False,
+                 workspace=None):
+    """Question prefill over composed caches (c2kv_attn_prefill).
+    q [R][tq][hq][d], k_new/v_new [R][tq][hkv][d]; appends to the caches."""
+    return _cache_call("prefill", q, k_new, v_new, cache_k, cache_v, cache_len, q_pos0, rope_theta,
+                       return_lse, q.shape[1], workspace)
+
+
+def attn_decode(q, k_new, v_new, cache_k, cache_v, cache_len, q_pos, rope_theta, return_lse=False,
+                workspace=None):
+    """One decode step over composed caches (c2kv_attn_decode).
+    q [R][hq][d], k_new/v_new [R][hkv][d]; appends one row per request."""
+    return _cache_call("decode", q, k_new, v_new, cache_k, cache_v, cache_len, q_pos, rope_theta,
+                       return_lse, None, workspace)
+
+
+# ----------------------------------------------------------------- testing
+
+def mask_cells(doc_lens: Sequence[int], ratio_k: int, sink_len: Optional[int] = None,
+               device: Optional[torch.device] = None) -> Tuple[int, int, int, int, int]:
+    """GPU count of visible cells (doc->doc, slot->doc, slot->slot), active
+    tiles without a visible cell, and active tiles, from the extraction
+    kernel's own tile enumeration (c2kv_mask_cells)."""
+    lib = load()
+    dev = device or torch.device("cuda", torch.cuda.current_device())
+    if sink_len is None:
+        sink_len = ratio_k
+    ws = WORKSPACES.get("mask", lib.c2kv_workspace_size_mask_cells(), dev, zero=False)
+    out = (ctypes.c_uint64 * 5)()
+    check(lib.c2kv_mask_cells(_arr_i32(doc_lens), len(doc_lens), ratio_k, sink_len, out,
+                              _ptr(ws), ws.numel(), _stream(dev)))
+    return tuple(int(x) for x in out)

@@ -1,0 +1,262 @@
+/*
+ * c2kv.h -- C ABI of the C2KV hot path on AMD Instinct MI355X (gfx950).
+ *
+ * C2KV (compressed, composable KV-cache reuse) has three data-parallel steps
+ * on its hot path, each exported here:
+ *
+ *   c2kv_extract_attn   structured-flow attention of the extractor over one
+ *                       batch of documents (doc tokens + C2 slot tokens)
+ *   c2kv_compose        RoPE-realigned concatenation of pre-RoPE slot K/V of
+ *                       several documents into one contiguous cache
+ *   c2kv_attn_prefill   question prefill over a composed cache (GQA)
+ *   c2kv_attn_decode    one decode step over a composed cache (GQA, split-K)
+ *
+ * Sources, cited by page and section:
+ *   [Explainer] "C2KV: Compressed and Composable KV Cache Reuse for Efficient
+ *               LLM Inference", paper-daily.com explainer page.
+ *   [Abstract]  arXiv 2607.17715 abstract page (arxivdaily.com).
+ *   [KV-size]   "LLM inference optimisation: KV cache compression schemes"
+ *               (feinterview.poetries.top), Llama 3 / GQA paragraph.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every function returns c2kv_status.  On failure c2kv_last_error()
+ *   returns a thread-local message describing the first problem found.
+ * - All arguments are validated on the host BEFORE any HIP call, so a bad
+ *   argument never reaches the GPU (and can be tested on a machine without
+ *   one).  Device pointers are checked for NULL and 16-byte alignment only.
+ * - Device tensors are dense, row-major, in the element type `dt`
+ *   (C2KV_BF16 or C2KV_F32).  head_dim must be 64 or 128; hq % hkv == 0;
+ *   hq / hkv <= 16.
+ * - Ownership: the caller owns every buffer (tensors, caches, workspace).
+ *   The library allocates no memory and keeps no state between calls beyond
+ *   the thread-local error string.  Host arrays are read during the call
+ *   and may be released when it returns.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *   the legacy default stream).  Results are valid once the stream has
+ *   reached the work.  Calls are reentrant; two calls that are in flight at
+ *   the same time must not share a workspace.
+ * - workspace: device memory, 256-byte aligned, of at least the size the
+ *   matching c2kv_workspace_size_* function returns for the same arguments.
+ *   Its contents on entry are ignored (prefill/decode zero their own split-K
+ *   arrival counters in their first kernel) and are undefined on return.
+ * - Per-call tables (documents, requests) are passed to the GPU as kernel
+ *   arguments in chunks of at most C2KV_MAX_BATCH entries per launch, so
+ *   extract/prefill/decode perform no host-to-device copies and may be
+ *   captured in a HIP graph.  Compose passes its segment table the same way
+ *   (at most 48 segments per launch) and needs no workspace.
+ */
+#ifndef C2KV_H_
+#define C2KV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum c2kv_status {
+  C2KV_OK = 0,
+  C2KV_ERR_INVALID_ARG = 1,   /* NULL pointer, bad shape, dtype, k < 1, ... */
+  C2KV_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. head_dim 96) */
+  C2KV_ERR_WORKSPACE = 3,     /* workspace too small or misaligned */
+  C2KV_ERR_CAPACITY = 4,      /* cache rows would exceed `cap`, or an index overflows */
+  C2KV_ERR_HIP = 5            /* a HIP launch or runtime call failed */
+} c2kv_status;
+
+typedef enum c2kv_dtype {
+  C2KV_BF16 = 0,              /* bfloat16 storage, fp32 accumulation */
+  C2KV_F32 = 1                /* fp32 storage and accumulation */
+} c2kv_dtype;
+
+#define C2KV_MAX_BATCH 64     /* documents / requests per kernel launch */
+#define C2KV_MAX_SPLITS 512   /* split-K chunks per (request, KV head) */
+
+/* ---- library information ------------------------------------------------ */
+
+const char* c2kv_version(void);
+const char* c2kv_status_string(c2kv_status s);
+/* Message of the last failure on the calling thread ("" if none). */
+const char* c2kv_last_error(void);
+
+/* ---- closed forms (host only, no GPU) ----------------------------------- */
+
+/* Number of C2 slots of an n-token document at compression ratio k:
+ * ceil(n / k).  [Explainer] "C2 token" section: one slot per k document
+ * tokens; a trailing partial block also gets a slot.  Returns -1 when
+ * n < 0 or k < 1. */
+int32_t c2kv_num_slots(int32_t n, int32_t k);
+
+/* Extraction-time position of slot j: the position of the last token of
+ * the block it summarises, min(j*k + k - 1, n - 1).  [Explainer] section on
+ * positions at concatenation (3, 7, ... at k = 4).  Returns -1 for
+ * arguments outside 0 <= j < c2kv_num_slots(n, k). */
+int32_t c2kv_slot_position(int32_t n, int32_t k, int32_t j);
+
+/* RoPE inverse frequencies theta^(-2i/d), i < head_dim/2, computed in
+ * double and rounded once to float, written to out[head_dim/2] (host).
+ * Every kernel rotates with exactly these values: angle = fp32(pos * f_i),
+ * x'_i = x_i c - x_{i+d/2} s, x'_{i+d/2} = x_{i+d/2} c + x_i s with each
+ * product and sum rounded to fp32 (no fused multiply-add). */
+c2kv_status c2kv_rope_inv_freq(int32_t head_dim, float rope_theta, float* out);
+
+/* ---- extraction: structured-flow attention ------------------------------- */
+
+/* Workspace bytes for c2kv_extract_attn with the same arguments. */
+size_t c2kv_workspace_size_extract(const int32_t* doc_lens, int32_t num_docs,
+                                   int32_t ratio_k, int32_t hkv, int32_t head_dim,
+                                   c2kv_dtype dt);
+
+/* Attention of the C2 extractor over a batch of independently extracted
+ * documents.  [Explainer] "structured information flow" section and its mask
+ * figure; "C2 token" section; positions section.  [Abstract]: structured
+ * attention flow of the sidecar extractor.
+ *
+ * Rows of document b are packed as [n_b document tokens | m_b slots],
+ * m_b = c2kv_num_slots(n_b, ratio_k), documents back to back.
+ *   q      device [sum_T][hq][head_dim]   pre-RoPE queries
+ *   k, v   device [sum_T][hkv][head_dim]  pre-RoPE keys, values
+ *   o      device [sum_T][hq][head_dim]   output (may not alias q/k/v)
+ *   lse    device [hq][sum_T] float or NULL: natural-log sum-exp of the
+ *          scaled scores of each row
+ *   doc_lens  host [num_docs], each >= 1; num_docs >= 1
+ * Queries and keys are rotated at the extraction positions (document token
+ * i at i, slot j at c2kv_slot_position(n, k, j)); V is not rotated.  Row
+ * visibility (rows = queries, columns = keys):
+ *   doc i  -> doc c  iff c <= i;  doc -> slot never;
+ *   slot j -> doc c  iff c < min(sink_len, n) or c / k == j;
+ *   slot j -> slot j' iff j' <= j.
+ * The sink is the document's first min(sink_len, n) tokens; the pages fix
+ * sink_len = ratio_k.  Query head h reads KV head h / (hq / hkv).  Scale is
+ * 1/sqrt(head_dim).  Key/value tiles with no visible cell are never loaded.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, CAPACITY (sum_T >= 2^31
+ * rows), HIP. */
+c2kv_status c2kv_extract_attn(const void* q, const void* k, const void* v,
+                              void* o, float* lse,
+                              const int32_t* doc_lens, int32_t num_docs,
+                              int32_t ratio_k, int32_t sink_len,
+                              int32_t hq, int32_t hkv, int32_t head_dim,
+                              float rope_theta, c2kv_dtype dt,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- composition --------------------------------------------------------- */
+
+/* One document's stored slot cache: `doc_len` is the document's ORIGINAL
+ * token count n (its slots number c2kv_num_slots(n, ratio_k)).  k and v
+ * point at slot 0's row; row j of head h is at element offset
+ * j*row_stride + h*head_dim.  Pre-RoPE keys. */
+typedef struct c2kv_segment {
+  const void* k;
+  const void* v;
+  int64_t row_stride;   /* elements between consecutive slot rows (>= hkv*head_dim) */
+  int32_t doc_len;      /* original document length n >= 1 */
+  int32_t reserved;     /* must be 0 */
+} c2kv_segment;
+
+size_t c2kv_workspace_size_compose(int32_t num_segs);
+
+/* Compose the slot caches of several documents, per request, in the given
+ * order.  [Explainer] "overall flow" section (fetch the stored caches,
+ * re-apply positions, concatenate, no patching) and the positions section
+ * (each document keeps its original length in positions: document t starts
+ * at pos_base + sum of the earlier documents' lengths; its slot j sits at
+ * that offset + c2kv_slot_position(n_t, k, j)).
+ *   segs          host [num_segs], grouped per request in composition order
+ *   req_seg_ptr   host [num_reqs+1], CSR: request r owns segs[ptr[r]..ptr[r+1])
+ *   pos_base      host [num_reqs] or NULL (all 0)
+ *   cache_k/v     device [num_reqs][hkv][cap][head_dim]: row i of request r
+ *                 receives composed slot i; K rotated (fp32, rounded once to
+ *                 dt), V copied bit for bit.  Rows >= cache_len are untouched.
+ *   pos_out       device [num_reqs][cap] int32 or NULL: composed positions
+ *   cache_len_out host [num_reqs]: number of composed rows per request
+ *   next_pos_out  host [num_reqs] or NULL: pos_base + sum of the request's
+ *                 document lengths (where the question starts)
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, CAPACITY (a request needs more
+ * than cap rows, or a position exceeds 2^24), HIP. */
+c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs,
+                         const int32_t* req_seg_ptr, int32_t num_reqs,
+                         const int32_t* pos_base,
+                         int32_t ratio_k, int32_t hkv, int32_t head_dim, float rope_theta,
+                         void* cache_k, void* cache_v, int64_t cap,
+                         int32_t* pos_out, int32_t* cache_len_out, int32_t* next_pos_out,
+                         c2kv_dtype dt, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- attention over the composed cache ----------------------------------- */
+
+size_t c2kv_workspace_size_prefill(const int32_t* cache_len, int32_t num_reqs, int32_t tq,
+                                   int32_t hq, int32_t hkv, int32_t head_dim, c2kv_dtype dt);
+
+/* Question prefill over composed caches.  [Explainer] "overall flow" section:
+ * after concatenation the question is appended and generation starts, with
+ * nothing in the reused cache patched; positions section for where the
+ * question starts.
+ *   q             device [num_reqs][tq][hq][head_dim]  pre-RoPE
+ *   k_new, v_new  device [num_reqs][tq][hkv][head_dim] pre-RoPE
+ *   cache_k/v     device [num_reqs][hkv][cap][head_dim]
+ *   cache_len     host [num_reqs]: rows already in each cache
+ *   q_pos0        host [num_reqs]: position of the first question token
+ *   o             device [num_reqs][tq][hq][head_dim]
+ *   lse           device [num_reqs][hq][tq] float or NULL
+ * Token t of request r is rotated at q_pos0[r] + t; its key (rounded to dt)
+ * and value are written to row cache_len[r] + t.  Token t attends to every
+ * row < cache_len[r] and to question rows <= t.  GQA as for extraction.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, CAPACITY (cache_len + tq > cap),
+ * HIP. */
+c2kv_status c2kv_attn_prefill(const void* q, const void* k_new, const void* v_new,
+                              void* cache_k, void* cache_v, int64_t cap,
+                              const int32_t* cache_len, const int32_t* q_pos0,
+                              int32_t num_reqs, int32_t tq, int32_t hq, int32_t hkv,
+                              int32_t head_dim, float rope_theta,
+                              void* o, float* lse, c2kv_dtype dt,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
+
+size_t c2kv_workspace_size_decode(const int32_t* cache_len, int32_t num_reqs,
+                                  int32_t hq, int32_t hkv, int32_t head_dim, c2kv_dtype dt);
+
+/* One decode step over composed caches ([Explainer] experimental-results
+ * section: every generated token reads the whole compressed cache).  Same
+ * contract as c2kv_attn_prefill with tq = 1:
+ *   q [num_reqs][hq][head_dim], k_new/v_new [num_reqs][hkv][head_dim],
+ *   o [num_reqs][hq][head_dim], lse [num_reqs][hq] or NULL,
+ *   cache_len[r] rows before the append; the new token goes to that row and
+ *   is rotated at q_pos[r].
+ * The sequence is split into chunks processed in parallel and merged by
+ * log-sum-exp; the result does not depend on the number of chunks beyond
+ * fp32 rounding. */
+c2kv_status c2kv_attn_decode(const void* q, const void* k_new, const void* v_new,
+                             void* cache_k, void* cache_v, int64_t cap,
+                             const int32_t* cache_len, const int32_t* q_pos,
+                             int32_t num_reqs, int32_t hq, int32_t hkv,
+                             int32_t head_dim, float rope_theta,
+                             void* o, float* lse, c2kv_dtype dt,
+                             void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Zero `ws_bytes` (a multiple of 4) bytes of device memory with a fill
+ * kernel on `stream` (no hipMemset, so it may be captured in a graph).  No
+ * entry point requires a zeroed workspace; this is a convenience. */
+c2kv_status c2kv_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- test support ------------------------------------------------------- */
+
+/* Count visible cells of the extraction mask ON THE GPU with the same tile
+ * enumeration and visibility predicate the extraction kernel uses, for
+ * doc_lens[num_docs] at ratio k and sink length.  counts_out (host) receives
+ * [0] doc->doc, [1] slot->doc, [2] slot->slot visible cells, [3] tiles that
+ * were enumerated for a wave but hold no visible cell for it (0 when the
+ * enumeration is tight), [4] tiles enumerated in total.  Counts are summed
+ * over documents (one query head).  Synchronises `stream`.
+ * [Explainer] mask figure: 4 + 8 + 8 = 20 slot->doc cells for a 12-token
+ * document at k = 4. */
+size_t c2kv_workspace_size_mask_cells(void);
+c2kv_status c2kv_mask_cells(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k,
+                            int32_t sink_len, uint64_t* counts_out,
+                            void* workspace, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* C2KV_H_ */

@@ -1,0 +1,155 @@
+"""The C ABI library on a machine without a GPU: it loads, exports every
+function include/c2kv.h declares, its closed forms agree with the oracle,
+and invalid arguments are rejected with the documented status before any
+HIP call is made."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library shares)
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "c2kv.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, CAPACITY = 0, 1, 2, 3, 4
+FAKE = 0x10000   # an aligned non-null address; never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from compressed_composable_kv_amd import _lib
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(c2kv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in c2kv.h but not exported"
+    from compressed_composable_kv_amd import _lib
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_version_and_status_strings(lib):
+    assert b"gfx950" in lib.c2kv_version()
+    for s in range(6):
+        assert lib.c2kv_status_string(s)
+
+
+def test_closed_forms_match_oracle(lib):
+    for n in list(range(0, 70)) + [400, 4000, 4096, 8191, 8192]:
+        for k in (1, 2, 3, 4, 8, 16):
+            m = lib.c2kv_num_slots(n, k)
+            assert m == O.num_slots(n, k)
+            for j in range(m):
+                assert lib.c2kv_slot_position(n, k, j) == O.slot_position(n, k, j)
+            assert lib.c2kv_slot_position(n, k, m) == -1
+    assert lib.c2kv_num_slots(5, 0) == -1 and lib.c2kv_num_slots(-1, 4) == -1
+
+
+@pytest.mark.parametrize("d,theta", [(64, 1e4), (128, 5e5), (128, 1e6), (64, 1e6)])
+def test_inv_freq_bit_identical_to_oracle(lib, d, theta):
+    out = (ctypes.c_float * (d // 2))()
+    assert lib.c2kv_rope_inv_freq(d, theta, out) == OK
+    got = np.array(out[:], dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), O.rope_inv_freq(d, theta).view(np.uint32))
+
+
+def _arr(vals):
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def _extract(lib, q=FAKE, hq=4, hkv=2, d=128, dt=0, lens=(16, 9), k=4, sink=4, theta=1e4, ws=FAKE, wsb=1 << 30):
+    L = _arr(list(lens))
+    return lib.c2kv_extract_attn(q, FAKE, FAKE, FAKE, None, L, len(lens), k, sink, hq, hkv, d, theta, dt,
+                                 ws, wsb, None)
+
+
+def test_extract_validation(lib):
+    assert _extract(lib, q=None) == INVALID
+    assert b"q" in lib.c2kv_last_error()
+    assert _extract(lib, q=FAKE + 4) == INVALID          # misaligned
+    assert _extract(lib, hq=6, hkv=4) == INVALID
+    assert _extract(lib, hq=34, hkv=2) == UNSUPPORTED    # group of 17
+    assert _extract(lib, d=96) == UNSUPPORTED
+    assert _extract(lib, dt=7) == INVALID
+    assert _extract(lib, lens=(16, 0)) == INVALID
+    assert _extract(lib, k=0) == INVALID
+    assert _extract(lib, sink=-1) == INVALID
+    assert _extract(lib, theta=0.5) == INVALID
+    assert _extract(lib, theta=float("nan")) == INVALID
+    assert _extract(lib, wsb=10) == WORKSPACE
+    assert _extract(lib, ws=None) == WORKSPACE
+    assert _extract(lib, ws=FAKE + 16) == WORKSPACE
+    assert _extract(lib, lens=(1 << 25,)) == CAPACITY
+
+
+def test_workspace_sizes(lib):
+    L = _arr([4096] * 8)
+    ext = lib.c2kv_workspace_size_extract(L, 8, 4, 8, 128, 0)
+    rows = 8 * (4096 + 1024)
+    assert ext >= rows * 8 * 128 * 2 + 4096 * 64 * 8
+    assert lib.c2kv_workspace_size_extract(L, 8, 0, 8, 128, 0) == 0
+    c = _arr([8192])
+    assert lib.c2kv_workspace_size_decode(c, 1, 32, 8, 128, 0) > 0
+    assert lib.c2kv_workspace_size_decode(c, 1, 30, 8, 128, 0) == 0
+    assert lib.c2kv_workspace_size_prefill(c, 1, 64, 32, 8, 128, 0) > lib.c2kv_workspace_size_decode(c, 1, 32, 8, 128, 0)
+    assert lib.c2kv_workspace_size_compose(100) == 0
+
+
+def _compose(lib, segs, ptr, cap=100, k=4, d=128, hkv=2, theta=1e6, base=None):
+    from compressed_composable_kv_amd._lib import Segment
+    arr = (Segment * len(segs))(*[Segment(*s) for s in segs])
+    lens = (ctypes.c_int32 * (len(ptr) - 1))()
+    return lib.c2kv_compose(arr, len(segs), _arr(ptr), len(ptr) - 1, _arr(base) if base else None, k, hkv, d,
+                            theta, FAKE, FAKE, cap, None, lens, None, 0, None, 0, None)
+
+
+def test_compose_validation(lib):
+    good = (FAKE, FAKE, 256, 40, 0)
+    assert _compose(lib, [good], [0, 1], cap=9) == CAPACITY           # 10 slots > cap 9
+    assert _compose(lib, [(FAKE, FAKE, 256, 40, 1)], [0, 1]) == INVALID      # reserved
+    assert _compose(lib, [(FAKE, FAKE, 100, 40, 0)], [0, 1]) == INVALID      # stride < hkv*d
+    assert _compose(lib, [(FAKE, FAKE, 256, 0, 0)], [0, 1]) == INVALID       # empty document
+    assert _compose(lib, [(None, FAKE, 256, 4, 0)], [0, 1]) == INVALID
+    assert _compose(lib, [good, good], [0, 1]) == INVALID                     # CSR does not cover segs
+    assert _compose(lib, [good, good], [0, 2, 1]) == INVALID                  # not monotone
+    assert _compose(lib, [good], [0, 1], base=[(1 << 24) - 10]) == CAPACITY   # position overflow
+    assert _compose(lib, [good], [0, 1], k=0) == INVALID
+
+
+def _decode(lib, lens, pos, cap=100, hq=8, hkv=2, d=128, ws=FAKE, wsb=1 << 30):
+    return lib.c2kv_attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, cap, _arr(lens), _arr(pos), len(lens), hq, hkv, d,
+                                1e6, FAKE, None, 0, ws, wsb, None)
+
+
+def test_decode_and_prefill_validation(lib):
+    assert _decode(lib, [100], [5]) == CAPACITY          # no room for the new row
+    assert _decode(lib, [-1], [5]) == INVALID
+    assert _decode(lib, [10], [-3]) == CAPACITY
+    assert _decode(lib, [10], [5], hq=3) == INVALID
+    assert _decode(lib, [5000], [5], cap=6000, wsb=16) == WORKSPACE     # split-K partials need room
+    assert _decode(lib, [10], [5], cap=0) == INVALID
+    r = lib.c2kv_attn_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, 100, _arr([90]), _arr([0]), 1, 11, 8, 2, 128, 1e6,
+                              FAKE, None, 0, FAKE, 1 << 30, None)
+    assert r == CAPACITY
+    r = lib.c2kv_attn_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, 100, _arr([90]), _arr([0]), 1, 0, 8, 2, 128, 1e6,
+                              FAKE, None, 0, FAKE, 1 << 30, None)
+    assert r == INVALID
+
+
+def test_mask_cells_validation(lib):
+    out = (ctypes.c_uint64 * 5)()
+    assert lib.c2kv_mask_cells(_arr([12]), 1, 4, 4, None, FAKE, 256, None) == INVALID
+    assert lib.c2kv_mask_cells(_arr([12]), 1, 4, 4, out, FAKE, 8, None) == WORKSPACE
+    assert lib.c2kv_mask_cells(_arr([12]), 1, 0, 4, out, FAKE, 256, None) == INVALID

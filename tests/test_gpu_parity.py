@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: positions, offsets, cache lengths, composed V, mask cell counts.
+Composed/appended K: within 1 bf16 ulp (fp32: 2^-21 relative bound).
+Attention outputs: 2e-2 max-abs for bf16 (1e-5 for fp32) plus a per-row
+relative bound of 1e-2 (1e-5).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from parity_util import (assert_close, assert_lse_close, assert_rotated_close, np32,
+                         oracle_extract_rows)
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+
+
+@pytest.fixture(scope="module")
+def c2kv():
+    import compressed_composable_kv_amd as m
+    return m
+
+
+def dtname(dt):
+    return "bf16" if dt == torch.bfloat16 else "f32"
+
+
+def packed_inputs(wid, doc_lens, ratio_k, hq, hkv, d, dt, c2kv, salt=0):
+    rows = c2kv.packed_rows(doc_lens, ratio_k)
+    assert rows == O.doc_row_offsets(doc_lens, ratio_k)[-1]
+    q = W.normal((rows, hq, d), dt, wid, W.P_Q, salt)
+    k = W.normal((rows, hkv, d), dt, wid, W.P_K, salt)
+    v = W.normal((rows, hkv, d), dt, wid, W.P_V, salt)
+    return q, k, v
+
+
+# ------------------------------------------------------------------ extraction
+
+EXTRACT_CASES = [
+    # (doc_lens, k, sink, hq, hkv, d, dtype)
+    ((64, 40), 4, 4, 1, 1, 64, torch.float32),                  # tiny workload
+    ((300, 129, 7, 1000), 4, 4, 8, 2, 128, torch.bfloat16),    # ragged, several tiles
+    ((513, 65, 3), 8, 8, 5, 1, 128, torch.bfloat16),            # G = 5, k not dividing n
+    ((250, 97), 16, 16, 7, 1, 128, torch.bfloat16),             # G = 7, partial blocks
+    ((1, 2, 5, 33), 4, 4, 2, 2, 64, torch.float32),             # n < k, single token
+    ((200, 131), 4, 2, 4, 2, 64, torch.bfloat16),               # sink shorter than k
+    ((180,), 4, 0, 2, 1, 128, torch.float32),                   # no sink
+    ((96, 70), 4, 9, 4, 4, 64, torch.float32),                  # sink longer than k
+]
+
+
+@pytest.mark.parametrize("case", EXTRACT_CASES, ids=lambda c: f"n{'-'.join(map(str, c[0]))}_k{c[1]}_s{c[2]}_G{c[3]//c[4]}_d{c[5]}_{dtname(c[6])}")
+def test_extract_parity(c2kv, case):
+    doc_lens, k, sink, hq, hkv, d, dt = case
+    theta = 1e4 if dt == torch.float32 else 5e5
+    q, kk, v = packed_inputs(11, doc_lens, k, hq, hkv, d, dt, c2kv, salt=EXTRACT_CASES.index(case))
+    print(f"extract case {case}", flush=True)
+    o, lse = c2kv.extract_attn(q.to(DEV), kk.to(DEV), v.to(DEV), doc_lens, k, sink, theta, return_lse=True)
+    torch.cuda.synchronize()
+    ref = O.extract_attn(q.float().numpy(), kk.float().numpy(), v.float().numpy(), doc_lens, k, sink, theta)
+    offs = O.doc_row_offsets(doc_lens, k)
+    og, lg = np32(o), np32(lse)
+    for b in range(len(doc_lens)):
+        ro, rl = ref[b]
+        assert_close(og[offs[b]:offs[b + 1]], ro, dtname(dt), f"doc {b} output")
+        assert_lse_close(lg[:, offs[b]:offs[b + 1]], rl, dtname(dt), f"doc {b}")
+
+
+def test_extract_doc_rows_independent_of_slots(c2kv):
+    """Document rows never see slots: changing every slot row's K/V leaves
+    the document rows' outputs bitwise unchanged."""
+    doc_lens, k, hq, hkv, d = (200, 77), 4, 4, 2, 128
+    q, kk, v = packed_inputs(12, doc_lens, k, hq, hkv, d, torch.bfloat16, c2kv)
+    o1, _ = c2kv.extract_attn(q.to(DEV), kk.to(DEV), v.to(DEV), doc_lens, k, k, 5e5)
+    offs = O.doc_row_offsets(doc_lens, k)
+    k2, v2 = kk.clone(), v.clone()
+    for b, n in enumerate(doc_lens):
+        k2[offs[b] + n: offs[b + 1]] *= -3
+        v2[offs[b] + n: offs[b + 1]] += 1
+    o2, _ = c2kv.extract_attn(q.to(DEV), k2.to(DEV), v2.to(DEV), doc_lens, k, k, 5e5)
+    for b, n in enumerate(doc_lens):
+        assert torch.equal(o1[offs[b]:offs[b] + n], o2[offs[b]:offs[b] + n])
+        assert not torch.equal(o1[offs[b] + n:offs[b + 1]], o2[offs[b] + n:offs[b + 1]])
+
+
+@pytest.mark.parametrize("doc_lens,k,sink", [((12,), 4, 4), ((64, 40), 4, 4), ((4096,) * 8, 4, 4),
+                                             ((1023, 1, 7, 4097), 16, 16), ((8192,) * 3, 8, 8),
+                                             ((300, 5), 4, 2), ((70,), 4, 0), ((33, 9), 3, 5)])
+def test_mask_cells_bit_exact(c2kv, doc_lens, k, sink):
+    got = c2kv.mask_cells(doc_lens, k, sink)
+    dd = sd = ss = 0
+    for n in doc_lens:
+        a, b, c = O.mask_cell_counts(n, k, sink)
+        dd, sd, ss = dd + a, sd + b, ss + c
+    assert got[:3] == (dd, sd, ss)
+    assert got[3] == 0, "an enumerated tile holds no visible cell"
+
+
+def test_mask_cells_worked_example(c2kv):
+    # the 12-token, k=4 figure: 4 + 8 + 8 = 20 slot->doc cells
+    assert c2kv.mask_cells([12], 4, 4)[1] == 20
+
+
+# ---------------------------------------------------------------- composition
+
+def _compose_check(c2kv, reqs_docs, pool_k, pool_v, pool_n, ratio_k, theta, dt, pos_base=None, cap_extra=0):
+    R = len(reqs_docs)
+    hkv, d = pool_k[0].shape[1], pool_k[0].shape[2]
+    Ms = [sum(O.num_slots(pool_n[t], ratio_k) for t in docs) for docs in reqs_docs]
+    cap = max(Ms) + cap_extra
+    ck = torch.zeros((R, hkv, cap, d), dtype=dt, device=DEV)
+    cv = torch.zeros_like(ck)
+    pos = torch.full((R, cap), -1, dtype=torch.int32, device=DEV)
+    dk = [x.to(DEV) for x in pool_k]
+    dv = [x.to(DEV) for x in pool_v]
+    requests = [[(dk[t], dv[t], pool_n[t]) for t in docs] for docs in reqs_docs]
+    lens, nxt = c2kv.compose(requests, ratio_k, theta, ck, cv, pos_base=pos_base, pos_out=pos)
+    torch.cuda.synchronize()
+    assert lens == Ms
+    for r, docs in enumerate(reqs_docs):
+        base = pos_base[r] if pos_base else 0
+        rk, rv, rpos, rnext = O.compose([pool_k[t].float().numpy() for t in docs],
+                                        [pool_v[t].float().numpy() for t in docs],
+                                        [pool_n[t] for t in docs], ratio_k, theta, dtname(dt), base)
+        assert nxt[r] == rnext
+        assert np.array_equal(pos[r, :Ms[r]].cpu().numpy(), rpos)
+        gk = np32(ck[r, :, :Ms[r]]).transpose(1, 0, 2)
+        gv = cv[r, :, :Ms[r]].transpose(0, 1).contiguous()
+        assert torch.equal(gv.cpu(), torch.cat([pool_v[t] for t in docs]))
+        pre = np.concatenate([pool_k[t].float().numpy() for t in docs])
+        assert_rotated_close(gk, rk, pre, dtname(dt), f"request {r} keys")
+        assert (pos[r, Ms[r]:] == -1).all()
+    return ck, cv, lens, nxt
+
+
+def test_compose_tiny(c2kv):
+    w = W.TINY
+    q, kk, v = packed_inputs(w.wid, w.doc_lens, w.ratio_k, w.hq, w.hkv, w.head_dim, w.dtype, c2kv)
+    views = c2kv.slot_views(kk, v, w.doc_lens, w.ratio_k)
+    ck, cv, lens, nxt = _compose_check(c2kv, [[0, 1]], [s[0] for s in views], [s[1] for s in views],
+                                       list(w.doc_lens), w.ratio_k, w.rope_theta, w.dtype, cap_extra=24)
+    assert lens == [26] and nxt == [104]
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_compose_multi_request_ragged(c2kv, dt):
+    g = torch.Generator().manual_seed(5)
+    pool_n = [int(x) for x in torch.randint(1, 700, (20,), generator=g)] + [1, 16, 17]
+    k = 16 if dt == torch.bfloat16 else 4
+    pool_k = [W.normal((O.num_slots(n, k), 3, 128), dt, 13, W.P_K, salt=i) for i, n in enumerate(pool_n)]
+    pool_v = [W.normal((O.num_slots(n, k), 3, 128), dt, 13, W.P_V, salt=i) for i, n in enumerate(pool_n)]
+    reqs = [[3, 1, 4, 15, 9, 2, 6], [22, 21, 20], [0], list(range(23))[::-1], [7, 7, 8]]
+    _compose_check(c2kv, reqs, pool_k, pool_v, pool_n, k, 1e6, dt, pos_base=[0, 5, 100000, 3, 0], cap_extra=3)
+
+
+# ------------------------------------------------- prefill / decode parity
+
+def _oracle_cache(slot_k, slot_v, lens, k, theta, dt, base=0):
+    return O.compose([x.float().numpy() for x in slot_k], [x.float().numpy() for x in slot_v], lens, k,
+                     theta, dtname(dt), base)
+
+
+def test_tiny_end_to_end(c2kv):
+    """Tiny workload: extraction, compose (positions 3..63, 67..103),
+    8-token prefill at 104..111, 16 decode steps at 112..127."""
+    w = W.TINY
+    q, kk, v = packed_inputs(w.wid, w.doc_lens, w.ratio_k, w.hq, w.hkv, w.head_dim, w.dtype, c2kv)
+    qd, kd, vd = q.to(DEV), kk.to(DEV), v.to(DEV)
+    o, _ = c2kv.extract_attn(qd, kd, vd, w.doc_lens, w.ratio_k, w.sink_len, w.rope_theta)
+    views = c2kv.slot_views(kd, vd, w.doc_lens, w.ratio_k)
+    cap = 26 + w.tq + w.decode_steps
+    ck = torch.zeros((1, 1, cap, 64), dtype=w.dtype, device=DEV)
+    cv = torch.zeros_like(ck)
+    pos = torch.zeros((1, cap), dtype=torch.int32, device=DEV)
+    lens, nxt = c2kv.compose([[(s[0], s[1], s[2]) for s in views]], w.ratio_k, w.rope_theta, ck, cv, pos_out=pos)
+    assert lens == [26] and nxt == [104]
+    assert pos[0, :26].tolist() == list(range(3, 64, 4)) + list(range(67, 104, 4))
+    hviews = c2kv.slot_views(kk, v, w.doc_lens, w.ratio_k)
+    rk, rv, _, P = _oracle_cache([s[0] for s in hviews], [s[1] for s in hviews], list(w.doc_lens),
+                                 w.ratio_k, w.rope_theta, w.dtype)
+    qp = W.normal((1, w.tq, 1, 64), w.dtype, w.wid, W.P_PREFILL)
+    kp = W.normal((1, w.tq, 1, 64), w.dtype, w.wid, W.P_NEW_KV)
+    vp = W.normal((1, w.tq, 1, 64), w.dtype, w.wid, W.P_NEW_KV, salt=1)
+    op, lp = c2kv.attn_prefill(qp.to(DEV), kp.to(DEV), vp.to(DEV), ck, cv, lens, [P], w.rope_theta, return_lse=True)
+    ro, rl, rk, rv = O.append_and_attend(qp[0].numpy(), kp[0].numpy(), vp[0].numpy(), rk, rv, P, w.rope_theta, "f32")
+    assert_close(np32(op[0]), ro, "f32", "prefill output")
+    assert_lse_close(np32(lp[0]), rl, "f32", "prefill")
+    L = 26 + w.tq
+    for s in range(w.decode_steps):
+        qs = W.normal((1, 1, 64), w.dtype, w.wid, W.P_DEC_Q, salt=s)
+        ks = W.normal((1, 1, 64), w.dtype, w.wid, W.P_NEW_KV, salt=100 + s)
+        vs = W.normal((1, 1, 64), w.dtype, w.wid, W.P_NEW_KV, salt=200 + s)
+        od, ld = c2kv.attn_decode(qs.to(DEV), ks.to(DEV), vs.to(DEV), ck, cv, [L], [P + w.tq + s], w.rope_theta,
+                                  return_lse=True)
+        ro, rl, rk, rv = O.decode_step(qs[0].numpy(), ks[0].numpy(), vs[0].numpy(), rk, rv, P + w.tq + s,
+                                       w.rope_theta, "f32")
+        assert_close(np32(od[0]), ro, "f32", f"decode step {s}")
+        assert_lse_close(np32(ld[0]), rl, "f32", f"decode step {s}")
+        L += 1
+    gk = np32(ck[0, :, :L]).transpose(1, 0, 2)
+    assert torch.equal(cv[0, :, :L].transpose(0, 1).cpu(), torch.from_numpy(rv).to(w.dtype))
+    assert np.abs(gk - rk).max() <= 1e-5
+
+
+@pytest.mark.parametrize("tq,hq,hkv,dt", [(1, 4, 1, torch.bfloat16), (5, 8, 2, torch.bfloat16),
+                                          (33, 7, 1, torch.bfloat16), (70, 4, 4, torch.float32),
+                                          (64, 32, 8, torch.bfloat16)])
+def test_prefill_parity_ragged(c2kv, tq, hq, hkv, dt):
+    d = 128 if dt == torch.bfloat16 else 64
+    theta = 5e5
+    lens = [700, 1, 2500, 64]
+    R = len(lens)
+    cap = max(lens) + tq + 3
+    ck = W.normal((R, hkv, cap, d), dt, 14, W.P_K)
+    cv = W.normal((R, hkv, cap, d), dt, 14, W.P_V)
+    q = W.normal((R, tq, hq, d), dt, 14, W.P_PREFILL)
+    kn = W.normal((R, tq, hkv, d), dt, 14, W.P_NEW_KV)
+    vn = W.normal((R, tq, hkv, d), dt, 14, W.P_NEW_KV, salt=1)
+    qpos = [lens[r] * 3 + 17 for r in range(R)]
+    ckd, cvd = ck.to(DEV), cv.to(DEV)
+    o, lse = c2kv.attn_prefill(q.to(DEV), kn.to(DEV), vn.to(DEV), ckd, cvd, lens, qpos, theta, return_lse=True)
+    for r in range(R):
+        rk = ck[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        rv = cv[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        ro, rl, rk2, rv2 = O.append_and_attend(q[r].float().numpy(), kn[r].float().numpy(), vn[r].float().numpy(),
+                                                rk, rv, qpos[r], theta, dtname(dt))
+        assert_close(np32(o[r]), ro, dtname(dt), f"request {r}")
+        assert_lse_close(np32(lse[r]), rl, dtname(dt), f"request {r}")
+        gk = np32(ckd[r, :, :lens[r] + tq]).transpose(1, 0, 2)
+        assert_rotated_close(gk[lens[r]:], rk2[lens[r]:], kn[r].float().numpy(), dtname(dt), f"appended keys {r}")
+        assert torch.equal(cvd[r, :, lens[r]:lens[r] + tq].transpose(0, 1).cpu(), vn[r])
+        # rows outside [cache_len, cache_len + tq) untouched
+        assert torch.equal(ckd[r, :, :lens[r]].cpu(), ck[r, :, :lens[r]])
+        assert torch.equal(ckd[r, :, lens[r] + tq:].cpu(), ck[r, :, lens[r] + tq:])
+
+
+@pytest.mark.parametrize("hq,hkv,d,dt", [(32, 8, 128, torch.bfloat16), (28, 4, 128, torch.bfloat16),
+                                         (40, 8, 128, torch.bfloat16), (3, 3, 64, torch.float32)])
+def test_decode_parity_varlen(c2kv, hq, hkv, d, dt):
+    theta = 1e6
+    lens = [9000, 1, 130, 4096, 64, 2047]
+    R = len(lens)
+    cap = max(lens) + 2
+    ck = W.normal((R, hkv, cap, d), dt, 15, W.P_K)
+    cv = W.normal((R, hkv, cap, d), dt, 15, W.P_V)
+    q = W.normal((R, hq, d), dt, 15, W.P_DEC_Q)
+    kn = W.normal((R, hkv, d), dt, 15, W.P_NEW_KV)
+    vn = W.normal((R, hkv, d), dt, 15, W.P_NEW_KV, salt=1)
+    qpos = [200000 + 7 * r for r in range(R)]
+    ckd, cvd = ck.to(DEV), cv.to(DEV)
+    o, lse = c2kv.attn_decode(q.to(DEV), kn.to(DEV), vn.to(DEV), ckd, cvd, lens, qpos, theta, return_lse=True)
+    for r in range(R):
+        rk = ck[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        rv = cv[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        ro, rl, _, _ = O.decode_step(q[r].float().numpy(), kn[r].float().numpy(), vn[r].float().numpy(),
+                                     rk, rv, qpos[r], theta, dtname(dt))
+        assert_close(np32(o[r]), ro, dtname(dt), f"request {r}")
+        assert_lse_close(np32(lse[r]), rl, dtname(dt), f"request {r}")
+
+
+def test_decode_split_invariance(c2kv):
+    """The split-K merge does not change the result beyond fp32 rounding:
+    the same decode over a cache split into many chunks (long cache) and the
+    same rows at the front of a request whose chunking differs."""
+    d, hq, hkv, dt = 128, 8, 2, torch.bfloat16
+    L = 5000
+    ck = W.normal((2, hkv, L + 1, d), dt, 16, W.P_K)
+    cv = W.normal((2, hkv, L + 1, d), dt, 16, W.P_V)
+    ck[1] = ck[0]
+    cv[1] = cv[0]
+    q = W.normal((1, hq, d), dt, 16, W.P_DEC_Q).repeat(2, 1, 1)
+    kn = W.normal((1, hkv, d), dt, 16, W.P_NEW_KV).repeat(2, 1, 1)
+    vn = W.normal((1, hkv, d), dt, 16, W.P_NEW_KV, salt=1).repeat(2, 1, 1)
+    # request 1 shares the cache; a third long request changes the chunk size
+    big = 60000
+    ck3 = torch.zeros((3, hkv, big + 1, d), dtype=dt)
+    cv3 = torch.zeros_like(ck3)
+    ck3[:2, :, :L + 1] = ck
+    cv3[:2, :, :L + 1] = cv
+    o_a, _ = c2kv.attn_decode(q.to(DEV), kn.to(DEV), vn.to(DEV), ck.to(DEV), cv.to(DEV), [L, L], [L, L], 1e6)
+    q3 = torch.cat([q, q[:1]])
+    kn3 = torch.cat([kn, kn[:1]])
+    vn3 = torch.cat([vn, vn[:1]])
+    o_b, _ = c2kv.attn_decode(q3.to(DEV), kn3.to(DEV), vn3.to(DEV), ck3.to(DEV), cv3.to(DEV), [L, L, big],
+                              [L, L, big], 1e6)
+    assert torch.equal(o_a[0], o_a[1])
+    diff = (o_a[0].float() - o_b[0].float()).abs().max().item()
+    assert diff <= 2e-3

@@ -137,3 +137,15 @@ def sink_biased(q: torch.Tensor, k: torch.Tensor, sink_rows: int, sigma: float =
     dirs = dirs / dirs.norm(dim=-1, keepdim=True).clamp_min(1e-6)
     kf[:sink_rows] += sigma * dirs.unsqueeze(0) * (k.shape[-1] ** 0.5) / 4.0
     return kf.to(k.dtype)
+
+
+def device_normal(shape: Sequence[int], dtype: torch.dtype, workload_id: int, purpose: int,
+                  device: torch.device, salt: int = 0) -> torch.Tensor:
+    """Bulk N(0, 1) inputs drawn by torch's device generator (for full-size
+    timing runs, where the values do not matter for speed).  Seeded like
+    ``normal``; a parity check reads back only the slices it compares."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(workload_id, purpose, salt))
+    x = torch.empty(tuple(int(s) for s in shape), dtype=torch.float32, device=device)
+    x.normal_(generator=g)
+    return x.to(dtype)
