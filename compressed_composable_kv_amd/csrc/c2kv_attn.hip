@@ -127,22 +127,23 @@ __device__ __forceinline__ uint32_t half_of<float>(const uint4& x, int e) {
 }
 
 // ------------------------------------------------------ visibility rules
-// kind 0: document row q, document key c:  c <= q            (causal)
-// kind 1: slot j, document key c:          c < sink or c in [j k, j k + k)
-// kind 2: slot j, slot key j':             j' <= j           (causal)
-// kind 3: cache query t, cache row c:      c < cache_len + t + 1
-// plus c < kmax (the keys that exist in this region).
+// One branch-free formula covers every rule on this path:
+//   visible(q, c) = c < kmax && (c <= q + a || (b > 0 && q b <= c < q b + b) || c < sink)
+//   document row q, document key c:  a = 0                      (causal)
+//   slot j, document key c:          a = -2^30, b = k, sink     (sink block + own block)
+//   slot j, slot key j':             a = 0                      (causal)
+//   cache query t, cache row c:      a = cache_len              (all cached rows + causal new rows)
 struct Pred {
-  int kind, kmax, a, b;   // kind 1: a = sink, b = k;  kind 3: a = cache_len
+  int kmax, a, b, sink;
   __device__ __forceinline__ bool operator()(int q, int c) const {
-    if (c >= kmax) return false;
-    switch (kind) {
-      case 0: case 2: return c <= q;
-      case 1: return c < a || (c >= q * b && c < q * b + b);
-      default: return c <= a + q;
-    }
+    const int qb = q * b;
+    const bool causal = c <= q + a;
+    const bool own = (c >= qb) & (c < qb + b);
+    return (c < kmax) & (causal | own | (c < sink));
   }
 };
+__host__ __device__ constexpr Pred pred_causal(int kmax, int offset) { return Pred{kmax, offset, 0, 0}; }
+__host__ __device__ constexpr Pred pred_slot_doc(int n, int k, int sink) { return Pred{n, -(1 << 30), k, sink}; }
 
 // ------------------------------------------------------ wave tile engine
 template <typename T, int D>
@@ -193,9 +194,7 @@ struct WaveAttn {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = s[kb][qb][i] * scale_log2;
-          if constexpr (kMasked) {
-            if (!pred(q0 + 16 * qb + r16, key0 + 16 * kb + 4 * g + i)) v = -INFINITY;
-          }
+          if constexpr (kMasked) v = pred(q0 + 16 * qb + r16, key0 + 16 * kb + 4 * g + i) ? v : -INFINITY;
           x[kb][i] = v;
           mx = fmaxf(mx, v);
         }
@@ -341,37 +340,232 @@ __device__ __forceinline__ TileSel extract_tile(const ExtractPlan& P, int it) {
   if (!P.slot_region) {
     s.active = P.wvalid && s.key0 < P.qend;
     s.masked = (s.key0 + kBN - 1 > P.q0) || (s.key0 + kBN > P.n);
-    s.pred = Pred{0, P.n, 0, 0};
+    s.pred = pred_causal(P.n, 0);
   } else if (!s.is_slot) {
     const int ts = (P.sink + kBN - 1) / kBN;
     const int blo = (P.q0 * P.ratio_k) / kBN;
     const int bhi = (min(P.n, P.qend * P.ratio_k) + kBN - 1) / kBN;
     s.active = P.wvalid && (s.t < ts || (s.t >= blo && s.t < bhi));
     s.masked = 1;
-    s.pred = Pred{1, P.n, P.sink, P.ratio_k};
+    s.pred = pred_slot_doc(P.n, P.ratio_k, P.sink);
   } else {
     s.active = P.wvalid && s.key0 < P.qend;
     s.masked = (s.key0 + kBN - 1 > P.q0) || (s.key0 + kBN > P.m);
-    s.pred = Pred{2, P.m, 0, 0};
+    s.pred = pred_causal(P.m, 0);
   }
   return s;
 }
 
+// ------------------------------------------------ extraction tile layout
+// A stage holds one 64-key tile: K [64 keys][D] and V^T [D][64 keys], both
+// filled by buffer_load ... lds (16 bytes per lane, consecutive lanes to
+// consecutive LDS slots) from the rotated-K and transposed-V workspaces.
+// Bank conflicts are avoided by XOR-swizzling 16-byte chunks: a lane that
+// fills LDS slot (row, pc) loads logical chunk pc ^ swz(row).
+//
+// S^T blocks use a permuted key order: in block kb, MFMA row r reads key
+// 32(kb/2) + 8(r/4) + 4(kb%2) + r%4.  Then a lane's 8 scores of a 32-key
+// half are 8 consecutive keys, which is exactly one 16-byte V^T read for the
+// A operand of O^T += V^T P^T.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, (kMinWaves<T, D>)) void extract_attn_kernel(const ExtractParams p) {
-  using S = Smem<T, D>;
-  __shared__ __attribute__((aligned(16))) T smem[2 * S::kStage];
+struct XTile {
+  static constexpr int ES = sizeof(T);
+  static constexpr int RB = D * ES;            // bytes of one K row
+  static constexpr int CPR = RB / 16;          // 16-byte chunks per K row
+  static constexpr int KBYTES = kBN * RB;
+  static constexpr int VB = kBN * ES;          // bytes of one V^T row
+  static constexpr int VC = VB / 16;
+  static constexpr int VBYTES = D * VB;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int KBLK = KBYTES / 1024;   // 1 KB DMA blocks per stage
+  static constexpr int VBLK = VBYTES / 1024;
+  static_assert(KBLK % kWaves == 0 && VBLK % kWaves == 0, "DMA blocks must split over the waves");
+};
+
+template <int CPR>
+__device__ __forceinline__ int k_swz(int row) { return ((row & 3) | (((row >> 3) & 3) << 2)) & (CPR - 1); }
+template <int VC>
+__device__ __forceinline__ int vt_swz(int d) { return VC == 8 ? ((d >> 1) & 7) : (d & (VC - 1)); }
+
+__device__ __forceinline__ int s_key_row(int kb, int r) {
+  return 32 * (kb >> 1) + 8 * (r >> 2) + 4 * (kb & 1) + (r & 3);
+}
+
+// Wait for this wave's outstanding vector-memory operations (the LDS DMA).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <typename T, int D>
+__device__ __forceinline__ void dma_tile(char* stage, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                         int krow0, int hkv, int vcol0, int vt_cols, int wave, int lane) {
+  using X = XTile<T, D>;
+#pragma unroll
+  for (int j = 0; j < X::KBLK / kWaves; ++j) {
+    const int b = wave * (X::KBLK / kWaves) + j;
+    const int byte = b * 1024 + lane * 16;
+    const int row = byte / X::RB, pc = (byte % X::RB) / 16;
+    const int c = pc ^ k_swz<X::CPR>(row);
+    const int voff = ((krow0 + row) * hkv) * X::RB + c * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(stage + b * 1024), 16, voff, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < X::VBLK / kWaves; ++j) {
+    const int b = wave * (X::VBLK / kWaves) + j;
+    const int byte = b * 1024 + lane * 16;
+    const int d = byte / X::VB, pc = (byte % X::VB) / 16;
+    const int c = pc ^ vt_swz<X::VC>(d);
+    const int voff = (d * vt_cols + vcol0) * X::ES + c * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(stage + X::KBYTES + b * 1024), 16, voff, 0, 0, 0);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ typename ElemTraits<T>::v8 lds_v8(const char* base, int chunk0, int swz, int nchunks);
+template <>
+__device__ __forceinline__ bf16x8 lds_v8<bf16>(const char* base, int chunk0, int swz, int nchunks) {
+  return *reinterpret_cast<const bf16x8*>(base + ((chunk0 ^ swz) & (nchunks - 1)) * 16);
+}
+template <>
+__device__ __forceinline__ f32x8 lds_v8<float>(const char* base, int chunk0, int swz, int nchunks) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(base + ((chunk0 ^ swz) & (nchunks - 1)) * 16);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(base + (((chunk0 + 1) ^ swz) & (nchunks - 1)) * 16);
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { r[e] = a[e]; r[4 + e] = b[e]; }
+  return r;
+}
+
+// One wave's 32 query rows against one staged tile.
+template <typename T, int D>
+struct XAttn {
+  using V8 = typename ElemTraits<T>::v8;
+  using X = XTile<T, D>;
+  static constexpr int KS = D / 32, DB = D / 16;
+  static constexpr int CPE = 16 / (int)sizeof(T) == 8 ? 1 : 2;   // 16-byte chunks per 8 elements
+
+  V8 qB[2][KS];
+  f32x4 o[DB][2];
+  float m[2], l[2];   // running max of the raw scores, running sum
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db][0] = o[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[0] = m[1] = -INFINITY;
+    l[0] = l[1] = 0.f;
+  }
+
+  template <bool kMasked>
+  __device__ __forceinline__ void tile(const char* stage, int lane, float sl2, const Pred& pred, int q0, int key0) {
+    const int r16 = lane & 15, g = lane >> 4;
+    const char* ks = stage;
+    const char* vt = stage + X::KBYTES;
+    f32x4 s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int row = s_key_row(kb, r16);
+        const V8 a = lds_v8<T>(ks + row * X::RB, (4 * k + g) * CPE, k_swz<X::CPR>(row), X::CPR);
+        s[kb][0] = mma16(a, qB[0][k], s[kb][0]);
+        s[kb][1] = mma16(a, qB[1][k], s[kb][1]);
+      }
+    }
+    V8 pB[2][2];
+    float alpha[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float x[4][4];
+      float mx = -INFINITY;
+      const int q = q0 + 16 * qb + r16;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = s[kb][qb][i];
+          if constexpr (kMasked) {
+            const int key = key0 + 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + i;
+            v = pred(q, key) ? v : -INFINITY;
+          }
+          x[kb][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = wave_max_16_32(mx);
+      const float mnew = fmaxf(m[qb], mx);
+      const float mneg = mnew == -INFINITY ? 0.f : -mnew * sl2;
+      alpha[qb] = __builtin_amdgcn_exp2f(__builtin_fmaf(m[qb], sl2, mneg));
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][i], sl2, mneg));
+          rs += pv;
+          pB[kb >> 1][qb][4 * (kb & 1) + i] = from_f32<T>(pv);
+        }
+      l[qb] = l[qb] * alpha[qb] + rs;
+      m[qb] = mnew;
+    }
+    // rescale O only when some lane's running max moved
+    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        o[db][0] *= alpha[0];
+        o[db][1] *= alpha[1];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = 16 * db + r16;
+        const V8 a = lds_v8<T>(vt + d * X::VB, (4 * c + g) * CPE, vt_swz<X::VC>(d), X::VC);
+        o[db][0] = mma16(a, pB[c][0], o[db][0]);
+        o[db][1] = mma16(a, pB[c][1], o[db][1]);
+      }
+    }
+  }
+};
+
+template <typename T, int D>
+constexpr int kXMinWaves = (2 * XTile<T, D>::STAGE * 2 <= 160 * 1024) ? 2 : 1;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void extract_attn_kernel(const ExtractParams p) {
+  using X = XTile<T, D>;
+  __shared__ __attribute__((aligned(1024))) char stage0[X::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[X::STAGE];
+  // The stages are written only by buffer_load ... lds; escape them so the
+  // compiler does not treat them as never-stored memory.
+  asm volatile("" : : "r"(stage0), "r"(stage1) : "memory");
   const int L = xcd_logical(blockIdx.x, p.grid_wg);
   if (L >= p.total_wg) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const ExtractPlan P = extract_plan(p, L, wave);
+  const ExtractDoc& dc = p.docs[P.doc];
   const int hq = p.hq, hkv = p.hkv;
-  const int64_t kv_stride = (int64_t)hkv * D;
-  const T* kbase = reinterpret_cast<const T*>(p.krot) + P.row0 * kv_stride + (int64_t)P.kvh * D;
-  const T* vbase = reinterpret_cast<const T*>(p.v) + P.row0 * kv_stride + (int64_t)P.kvh * D;
   const int64_t qrow_off = P.slot_region ? P.n : 0;
+  // buffer resources: this document's rotated keys of KV head kvh, and the
+  // V^T rows of kvh; reads past the end return zeros
+  const int64_t doc_rows = (int64_t)P.n + P.m;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(p.krot) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
+      (int)(doc_rows * hkv * X::RB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(p.vt) + (int64_t)P.kvh * D * p.vt_cols * X::ES), 0,
+      (int)((int64_t)D * p.vt_cols * X::ES), 0x00020000);
+  auto issue = [&](int it, char* stage) {
+    const TileSel ts = extract_tile(P, it);
+    const int krow0 = (ts.is_slot ? P.n : 0) + ts.key0;
+    const int vcol0 = (ts.is_slot ? dc.vt_slot : dc.vt_doc) + ts.key0;
+    dma_tile<T, D>(stage, krs, vrs, krow0, hkv, vcol0, p.vt_cols, wave, lane);
+  };
+  const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
+  if (ntiles > 0) issue(0, stage0);
 
-  WaveAttn<T, D> W;
+  XAttn<T, D> W;
   W.init();
   // ---- queries: load, rotate at the extraction positions, keep as B operand
   {
@@ -405,28 +599,22 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<T, D>)) void extract_attn_kern
     }
   }
 
-  const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
-  KVStage<T, D> ld;
-  auto issue = [&](int it) {
+  auto compute = [&](int it, const char* stage) {
     const TileSel ts = extract_tile(P, it);
-    const int64_t r = ts.is_slot ? (int64_t)P.n + ts.key0 : ts.key0;
-    ld.load(kbase + r * kv_stride, vbase + r * kv_stride, (int)kv_stride, ts.nvalid, tid);
+    if (!ts.active) return;
+    if (ts.masked) W.template tile<true>(stage, lane, p.scale_log2, ts.pred, P.q0, ts.key0);
+    else W.template tile<false>(stage, lane, p.scale_log2, ts.pred, P.q0, ts.key0);
   };
-  if (ntiles > 0) issue(0);
-  for (int it = 0; it < ntiles; ++it) {
-    T* ks = smem + (it & 1) * S::kStage;
-    T* vt = ks + S::kKElems;
-    ld.store(ks, vt, tid);
+  for (int it = 0; it < ntiles; it += 2) {
+    wait_vmem();
     __syncthreads();
-    if (it + 1 < ntiles) issue(it + 1);
-    const TileSel ts = extract_tile(P, it);
-    if (ts.active) {
-      const int qsel = P.q0;
-      if (ts.masked)
-        W.template tile<true>(ks, vt, lane, p.scale_log2, ts.pred, qsel, ts.key0);
-      else
-        W.template tile<false>(ks, vt, lane, p.scale_log2, ts.pred, qsel, ts.key0);
-    }
+    if (it + 1 < ntiles) issue(it + 1, stage1);
+    compute(it, stage0);
+    if (it + 1 >= ntiles) break;
+    wait_vmem();
+    __syncthreads();
+    if (it + 2 < ntiles) issue(it + 2, stage0);
+    compute(it + 1, stage1);
   }
 
   // ---- normalise and write rows
@@ -441,13 +629,15 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<T, D>)) void extract_attn_kern
       const int64_t prow = P.row0 + qrow_off + ql;
       T* orow = reinterpret_cast<T*>(p.o) + (prow * hq + P.head) * (int64_t)D;
 #pragma unroll
-      for (int db = 0; db < WaveAttn<T, D>::DB; ++db) {
+      for (int db = 0; db < XAttn<T, D>::DB; ++db) {
         typename ElemTraits<T>::v4 outv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) outv[i] = from_f32<T>(W.o[db][qb][i] * inv);
         *reinterpret_cast<typename ElemTraits<T>::v4*>(orow + 16 * db + 4 * g) = outv;
       }
-      if (g == 0 && p.lse) p.lse[(int64_t)P.head * p.total_rows + prow] = (W.m[qb] + __log2f(lt)) * 0.69314718055994531f;
+      if (g == 0 && p.lse)
+        p.lse[(int64_t)P.head * p.total_rows + prow] =
+            (W.m[qb] * p.scale_log2 + __log2f(lt)) * 0.69314718055994531f;
     }
   }
 }
@@ -545,7 +735,7 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<T, D>)) void cache_attn_kernel
   }
   const int ntiles = (ks1 - ks0 + kBN - 1) / kBN;
   KVStage<T, D> ld;
-  const Pred pred{3, ks1, rq.cache_len, 0};
+  const Pred pred = pred_causal(ks1, rq.cache_len);
   if (ntiles > 0) ld.load(kbase, vbase, stride, min(kBN, ks1 - ks0), tid);
   for (int it = 0; it < ntiles; ++it) {
     T* ks = smem + (it & 1) * S::kStage;
