@@ -242,6 +242,10 @@ c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new,
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(C2KV_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   if (!q_pos0) return fail(C2KV_ERR_INVALID_ARG, "q_pos is NULL");
   if (cap < 1) return fail(C2KV_ERR_INVALID_ARG, "cap=%lld must be >= 1", (long long)cap);
+  // per-head byte offsets (plus one workgroup step of 128 keys) are 32-bit
+  // in the kernels
+  if ((cap + 128) * head_dim * elem_bytes(dt) >= ((int64_t)1 << 31))
+    return fail(C2KV_ERR_CAPACITY, "cap=%lld rows of one head exceed 2 GiB", (long long)cap);
   CachePlan P;
   if ((s = cache_plan(cache_len, num_reqs, tq, hq, hkv, head_dim, dt, cap, decode, P))) return s;
   for (int32_t r = 0; r < num_reqs; ++r) {

@@ -396,27 +396,42 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Per-lane part of the DMA byte offsets (loop invariant); the tile's own
+// offset is wave-uniform and goes into the instructions' SGPR offset.
+template <typename T, int D>
+struct DmaLanes {
+  using X = XTile<T, D>;
+  int k[X::KBLK / kWaves];
+  int v[X::VBLK / kWaves];
+  __device__ __forceinline__ void init(int hkv, int vt_cols, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < X::KBLK / kWaves; ++j) {
+      const int byte = (wave * (X::KBLK / kWaves) + j) * 1024 + lane * 16;
+      const int row = byte / X::RB, pc = (byte % X::RB) / 16;
+      k[j] = row * hkv * X::RB + (pc ^ k_swz<X::CPR>(row)) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < X::VBLK / kWaves; ++j) {
+      const int byte = (wave * (X::VBLK / kWaves) + j) * 1024 + lane * 16;
+      const int d = byte / X::VB, pc = (byte % X::VB) / 16;
+      v[j] = d * vt_cols * X::ES + (pc ^ vt_swz<X::VC>(d)) * 16;
+    }
+  }
+};
+
 template <typename T, int D>
 __device__ __forceinline__ void dma_tile(char* stage, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                         int krow0, int hkv, int vcol0, int vt_cols, int wave, int lane) {
+                                         const DmaLanes<T, D>& ln, int ksoff, int vsoff, int wave) {
   using X = XTile<T, D>;
 #pragma unroll
   for (int j = 0; j < X::KBLK / kWaves; ++j) {
     const int b = wave * (X::KBLK / kWaves) + j;
-    const int byte = b * 1024 + lane * 16;
-    const int row = byte / X::RB, pc = (byte % X::RB) / 16;
-    const int c = pc ^ k_swz<X::CPR>(row);
-    const int voff = ((krow0 + row) * hkv) * X::RB + c * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(stage + b * 1024), 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(stage + b * 1024), 16, ln.k[j], ksoff, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < X::VBLK / kWaves; ++j) {
     const int b = wave * (X::VBLK / kWaves) + j;
-    const int byte = b * 1024 + lane * 16;
-    const int d = byte / X::VB, pc = (byte % X::VB) / 16;
-    const int c = pc ^ vt_swz<X::VC>(d);
-    const int voff = (d * vt_cols + vcol0) * X::ES + c * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(stage + X::KBYTES + b * 1024), 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(stage + X::KBYTES + b * 1024), 16, ln.v[j], vsoff, 0, 0);
   }
 }
 
@@ -556,11 +571,13 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void extract_attn_ker
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(reinterpret_cast<const char*>(p.vt) + (int64_t)P.kvh * D * p.vt_cols * X::ES), 0,
       (int)((int64_t)D * p.vt_cols * X::ES), 0x00020000);
+  DmaLanes<T, D> lanes;
+  lanes.init(hkv, p.vt_cols, wave, lane);
   auto issue = [&](int it, char* stage) {
     const TileSel ts = extract_tile(P, it);
     const int krow0 = (ts.is_slot ? P.n : 0) + ts.key0;
     const int vcol0 = (ts.is_slot ? dc.vt_slot : dc.vt_doc) + ts.key0;
-    dma_tile<T, D>(stage, krs, vrs, krow0, hkv, vcol0, p.vt_cols, wave, lane);
+    dma_tile<T, D>(stage, krs, vrs, lanes, krow0 * hkv * X::RB, vcol0 * X::ES, wave);
   };
   const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
   if (ntiles > 0) issue(0, stage0);

@@ -5,14 +5,18 @@
 // cache once.  A workgroup owns one (request, KV head, key chunk); ALL query
 // heads of the group sit in the 16 columns of one wave's MFMA tiles, and the
 // four waves stream disjoint 32-key steps of the chunk, so every K/V byte is
-// read from HBM exactly once and never shared through LDS:
+// read from HBM exactly once:
 //   * K goes straight from global memory into MFMA A-operand registers
 //     (S^T = K Q^T, keys on the M side, heads on N);
-//   * V is transposed through a small wave-private LDS tile for the
-//     O^T += V^T P^T product;
+//   * V goes from global memory into a wave-private LDS tile by
+//     buffer_load ... lds (row-major, 16-byte chunks XOR-swizzled), and the
+//     V^T operand of O^T += V^T P^T is read back transposed with
+//     ds_read_b64_tr_b16 (bf16) or element reads (fp32);
+//   * the first step's loads are issued before the query prologue, so the
+//     RoPE table and query rotation overlap the memory latency;
 //   * the new token's key is rotated (RoPE at the decode position) in the
-//     registers that would have loaded it, used as is, and written to the
-//     cache together with its value -- no separate append launch;
+//     registers that would have loaded it, its value is patched into the LDS
+//     tile, and both are written to the cache -- no separate append launch;
 //   * the four waves' (max, sum, O) are combined in LDS; with one chunk per
 //     (request, KV head) the workgroup writes the final output, otherwise a
 //     partial row that merge_kernel combines by log-sum-exp.
@@ -20,12 +24,6 @@
 #include "c2kv_launch.hpp"
 
 namespace c2kv {
-
-constexpr int kDecVPad = 8;                    // elements of padding per V^T row
-constexpr int kDecVRow = 32 + kDecVPad;
-
-// 4-key group swizzle of the 32-key V^T rows (conflict-free operand reads).
-__device__ __forceinline__ int dvt_group(int d, int kg) { return kg ^ ((d >> 3) & 7); }
 
 // Order this wave's own LDS writes before its reads of other lanes' data
 // (and the reads of one step before the next step's writes).
@@ -35,36 +33,151 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename T> __device__ __forceinline__ uint32_t elem_bits(const uint4& x, int e);
-template <> __device__ __forceinline__ uint32_t elem_bits<bf16>(const uint4& x, int e) {
-  const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-template <> __device__ __forceinline__ uint32_t elem_bits<float>(const uint4& x, int e) {
-  return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
-}
+// Wait for this wave's outstanding vector-memory operations (incl. LDS DMA).
+__device__ __forceinline__ void dec_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef __attribute__((address_space(3))) void dec_lds_void;
+typedef short dec_s4 __attribute__((ext_vector_type(4)));
 
 template <typename T> __device__ __forceinline__ void v8_to_f32(const typename ElemTraits<T>::v8& v, float* f) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] = to_f32(v[e]);
 }
 
+// One wave's V tile: 32 keys x D, row-major, 16-byte chunks swizzled.
 template <typename T, int D>
-constexpr int kDecMinWaves = (kWaves * D * kDecVRow * (int)sizeof(T) * 2 <= 160 * 1024) ? 2 : 1;
+struct DecTile {
+  static constexpr int ES = sizeof(T);
+  static constexpr int RB = D * ES;              // bytes per key row
+  static constexpr int CPR = RB / 16;            // chunks per row
+  static constexpr int BYTES = 32 * RB;
+  static constexpr int NDMA = BYTES / 1024;      // 1 KB DMA instructions per step
+  static_assert(BYTES % 1024 == 0, "tile must be whole DMA blocks");
+};
+
+// Physical chunk of logical chunk c in tile row `row` is c ^ dv_swz(row).
+// bf16: the transposed reads of a 32-lane half touch 8 rows x 32 bytes,
+// spread over all 64 banks by XOR-ing the 32-byte pair index with the row.
+// fp32: the element reads of the four lane groups hit 4 rows, offset by 4
+// chunks each.
+template <typename T, int D>
+__device__ __forceinline__ int dv_swz(int row) {
+  constexpr int CPR = DecTile<T, D>::CPR;
+  if constexpr (sizeof(T) == 2) return CPR >= 16 ? 2 * (row & 7) : 2 * ((row >> 1) & 3);
+  else return (4 * ((row >> 2) & 3)) & (CPR - 1);
+}
+
+// buffer_load ... lds of one V tile: instruction j fills LDS bytes
+// [1024 j, 1024 j + 1024) of the tile, lane i taking 16 bytes from byte
+// offset row_off + off[j] of the resource (zeros past its end).
+template <int NDMA>
+__device__ __forceinline__ void dma_v_tile(__amdgpu_buffer_rsrc_t rs, char* tile, const int* off, int row_off) {
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (dec_lds_void*)(tile + j * 1024), 16, row_off + off[j], 0, 0, 0);
+}
+
+// K A-operand of one 32-key step through a buffer resource (rows past its
+// end read as zeros): lane (r16, g) takes, for each 16-key block kb, the 8
+// elements 32 ks + 8 g .. +7 of key key0 + 16 kb + r16.
+template <typename T, int D>
+__device__ __forceinline__ void dec_load_k(typename ElemTraits<T>::v8 (&ka)[2][D / 32], __amdgpu_buffer_rsrc_t rs,
+                                           int key0, int r16, int g) {
+  using V8 = typename ElemTraits<T>::v8;
+  constexpr int ES = sizeof(T), RB = D * ES;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = (key0 + 16 * kb + r16) * RB;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const int off = row + (32 * ks + 8 * g) * ES;
+      if constexpr (ES == 2) {
+        const auto u = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        ka[kb][ks] = __builtin_bit_cast(V8, u);
+      } else {
+        const auto u0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        const auto u1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+        typedef unsigned int u8v __attribute__((ext_vector_type(8)));
+        const u8v w = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+        ka[kb][ks] = __builtin_bit_cast(V8, w);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+constexpr int kDecLdsBytes = (kWaves * DecTile<T, D>::BYTES > kWaves * 16 * (D + 2) * 4)
+                                 ? kWaves * DecTile<T, D>::BYTES : kWaves * 16 * (D + 2) * 4;
+
+template <typename T, int D>
+constexpr int kDecMinWaves = (kDecLdsBytes<T, D> * 3 <= 160 * 1024) ? 3 : 1;
+
+// V^T A operand for dims 16 db .. 16 db + 15: lane (r16, g) gets dim
+// 16 db + r16 of keys 4g + a (elements a = 0..3) and 16 + 4g + a (4..7),
+// the key order of the P^T operand built from the S^T accumulators.
+template <typename T, int D>
+__device__ __forceinline__ typename ElemTraits<T>::v8 vt_operand(const char* vt, int db, int r16, int g);
+
+template <>
+__device__ __forceinline__ bf16x8 vt_operand<bf16, 128>(const char* vt, int db, int r16, int g) {
+  // ds_read_b64_tr_b16: within each 16 lanes, output lane j element a is
+  // element (j % 4) of the 4 values addressed by source lane 4a + j / 4.
+  // Source lane i therefore addresses row 16h + 4g + i/4, dims
+  // 16 db + 4 (i % 4) .. +3.
+  dec_s4 x[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 16 * h + 4 * g + (r16 >> 2);
+    const int off = row * 256 + 32 * (db ^ (row & 7)) + 8 * (r16 & 3);
+    x[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) dec_s4*)(vt + off));
+  }
+  typedef short s8 __attribute__((ext_vector_type(8)));
+  const s8 v = {x[0][0], x[0][1], x[0][2], x[0][3], x[1][0], x[1][1], x[1][2], x[1][3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+template <>
+__device__ __forceinline__ bf16x8 vt_operand<bf16, 64>(const char* vt, int db, int r16, int g) {
+  dec_s4 x[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 16 * h + 4 * g + (r16 >> 2);
+    const int off = row * 128 + 32 * (db ^ ((row >> 1) & 3)) + 8 * (r16 & 3);
+    x[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) dec_s4*)(vt + off));
+  }
+  typedef short s8 __attribute__((ext_vector_type(8)));
+  const s8 v = {x[0][0], x[0][1], x[0][2], x[0][3], x[1][0], x[1][1], x[1][2], x[1][3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+template <int D>
+__device__ __forceinline__ f32x8 vt_operand_f32(const char* vt, int db, int r16, int g) {
+  constexpr int RB = D * 4;
+  f32x8 a;
+  const int col = 16 * db + r16;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = 16 * (e >> 2) + 4 * g + (e & 3);
+    const int off = row * RB + (((col >> 2) ^ dv_swz<float, D>(row)) << 4) + 4 * (col & 3);
+    a[e] = *reinterpret_cast<const float*>(vt + off);
+  }
+  return a;
+}
+template <>
+__device__ __forceinline__ f32x8 vt_operand<float, 128>(const char* vt, int db, int r16, int g) {
+  return vt_operand_f32<128>(vt, db, r16, g);
+}
+template <>
+__device__ __forceinline__ f32x8 vt_operand<float, 64>(const char* vt, int db, int r16, int g) {
+  return vt_operand_f32<64>(vt, db, r16, g);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_kernel(const DecodeParams p) {
   using V8 = typename ElemTraits<T>::v8;
-  using V4 = typename ElemTraits<T>::v4;
+  using Tile = DecTile<T, D>;
   constexpr int KS = D / 32, DB = D / 16, H = D / 2;
-  constexpr int CE = ElemTraits<T>::kChunk, CPR = D / CE;
-  constexpr int VTASK = 8 * CPR;                       // (4 keys x 1 chunk) tasks per step
-  constexpr int VPT = (VTASK + 63) / 64;
-  constexpr int kVtElems = D * kDecVRow;
-  __shared__ float2 s_cs[H];
-  __shared__ __attribute__((aligned(16))) T s_vt[kWaves * kVtElems];
-  static_assert(kWaves * 16 * (D + 2) * sizeof(float) <= sizeof(T) * kWaves * kVtElems,
-                "wave-combine scratch must fit in the V^T tiles");
+  constexpr int RB = Tile::RB, CPR = Tile::CPR, NDMA = Tile::NDMA;
+  __shared__ float2 s_cs[kWaves * H];
+  __shared__ __attribute__((aligned(1024))) char s_raw[kDecLdsBytes<T, D>];
 
   const int L = blockIdx.x;
   if (L >= p.total_wg) return;
@@ -79,106 +192,112 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
   const int G = p.G;
   const int newk = rq.cache_len;                       // row of the new token
   const int k0 = split * p.chunk, k1 = min(newk + 1, k0 + p.chunk);
+  const int nsteps = (k1 - k0 + 31) / 32;
 
-  // cos/sin of the decode position, shared by the query and the new key
-  if (tid < H) {
-    float c, s;
-    rope_cs(rq.pos, p.freqs.f[tid], c, s);
-    s_cs[tid] = make_float2(c, s);
+  const int64_t head_base = ((int64_t)r * p.hkv + kvh) * p.cap;
+  const T* knew = reinterpret_cast<const T*>(p.k_new) + ((int64_t)r * p.hkv + kvh) * D;
+  const T* vnew = reinterpret_cast<const T*>(p.v_new) + ((int64_t)r * p.hkv + kvh) * D;
+  char* vt = s_raw + wave * Tile::BYTES;
+  // K and V rows of this head: rows at or past min(k1, newk) read as zeros
+  // (the new token's key is loaded from k_new, its value patched in LDS)
+  const int nrec = min(k1, newk) * RB;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(p.kc) + head_base * RB), 0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(p.vc) + head_base * RB), 0, nrec, 0x00020000);
+  int voff[NDMA];
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) {
+    const int byte = j * 1024 + lane * 16;
+    const int row = byte / RB, pc = (byte % RB) / 16;
+    voff[j] = row * RB + ((pc ^ dv_swz<T, D>(row)) << 4);
   }
-  __syncthreads();
 
-  // ---- queries of the group's heads as the B operand (column = head)
-  V8 qB[KS];
+  V8 ka[2][KS];
+
+  // ---- loads in the order they are consumed (the vector-memory counter
+  // retires in order): RoPE frequency, query, then the first step's K and V
+  const float freq = p.freqs.f[lane];                 // 64 entries, zero past H
+  V8 qraw[KS];
   {
     const bool ok = r16 < G;
     const T* qrow = reinterpret_cast<const T*>(p.q) + ((int64_t)r * p.hq + kvh * G + (ok ? r16 : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS / 2; ++ks) {
-      float lo[8], hi[8];
-      if (ok) {
-        v8_to_f32<T>(*reinterpret_cast<const V8*>(qrow + 32 * ks + 8 * g), lo);
-        v8_to_f32<T>(*reinterpret_cast<const V8*>(qrow + H + 32 * ks + 8 * g), hi);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lo[e] = hi[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 cs = s_cs[32 * ks + 8 * g + e];
-        float y0, y1;
-        rope_pair(lo[e], hi[e], cs.x, cs.y, y0, y1);
-        qB[ks][e] = from_f32<T>(y0);
-        qB[ks + KS / 2][e] = from_f32<T>(y1);
-      }
+      qraw[ks] = *reinterpret_cast<const V8*>(qrow + 32 * ks + 8 * g);
+      qraw[ks + KS / 2] = *reinterpret_cast<const V8*>(qrow + H + 32 * ks + 8 * g);
     }
   }
+  // (unconditional: a wave without a step reads past the resource, i.e.
+  // zeros, so the counter waits below stay exact)
+  dec_load_k<T, D>(ka, krs, k0 + 32 * wave, r16, g);
+  dma_v_tile<NDMA>(vrs, vt, voff, (k0 + 32 * wave) * RB);
 
-  const int64_t head_base = ((int64_t)r * p.hkv + kvh) * p.cap;
-  const T* kc = reinterpret_cast<const T*>(p.kc) + head_base * D;
-  const T* vc = reinterpret_cast<const T*>(p.vc) + head_base * D;
-  const T* knew = reinterpret_cast<const T*>(p.k_new) + ((int64_t)r * p.hkv + kvh) * D;
-  const T* vnew = reinterpret_cast<const T*>(p.v_new) + ((int64_t)r * p.hkv + kvh) * D;
-  T* vt = s_vt + wave * kVtElems;
+  // cos/sin of the decode position (shared by the query and the new key),
+  // one table per wave so no workgroup barrier waits on the loads above
+  float2* cs_tab = s_cs + wave * H;
+  if (lane < H) {
+    float c, s;
+    rope_cs(rq.pos, freq, c, s);
+    cs_tab[lane] = make_float2(c, s);
+  }
+  wave_lds_sync();
+
+  // ---- queries of the group's heads as the B operand (column = head);
+  // heads past G give zero columns
+  V8 qB[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS / 2; ++ks) {
+    float lo[8], hi[8];
+    v8_to_f32<T>(qraw[ks], lo);
+    v8_to_f32<T>(qraw[ks + KS / 2], hi);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 cs = cs_tab[32 * ks + 8 * g + e];
+      float y0, y1;
+      rope_pair(lo[e], hi[e], cs.x, cs.y, y0, y1);
+      qB[ks][e] = from_f32<T>(r16 < G ? y0 : 0.f);
+      qB[ks + KS / 2][e] = from_f32<T>(r16 < G ? y1 : 0.f);
+    }
+  }
 
   f32x4 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
-  const int nsteps = (k1 - k0 + 31) / 32;
 
   for (int st = wave; st < nsteps; st += kWaves) {
     const int key0 = k0 + 32 * st;
-    // ---- K: A operand rows key0 + 16 kb + r16, k-group g
-    V8 ka[2][KS];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = key0 + 16 * kb + r16;
-      if (key < k1 && key != newk) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ka[kb][ks] = *reinterpret_cast<const V8*>(kc + (int64_t)key * D + 32 * ks + 8 * g);
-      } else if (key == newk && key < k1) {
-        // the new token: rotate its key here and append key and value
-        T* kdst = reinterpret_cast<T*>(p.kc) + (head_base + key) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS / 2; ++ks) {
-          float lo[8], hi[8];
-          v8_to_f32<T>(*reinterpret_cast<const V8*>(knew + 32 * ks + 8 * g), lo);
-          v8_to_f32<T>(*reinterpret_cast<const V8*>(knew + H + 32 * ks + 8 * g), hi);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float2 cs = s_cs[32 * ks + 8 * g + e];
-            float y0, y1;
-            rope_pair(lo[e], hi[e], cs.x, cs.y, y0, y1);
-            ka[kb][ks][e] = from_f32<T>(y0);
-            ka[kb][ks + KS / 2][e] = from_f32<T>(y1);
-          }
-          *reinterpret_cast<V8*>(kdst + 32 * ks + 8 * g) = ka[kb][ks];
-          *reinterpret_cast<V8*>(kdst + H + 32 * ks + 8 * g) = ka[kb][ks + KS / 2];
-        }
-        T* vdst = reinterpret_cast<T*>(p.vc) + (head_base + key) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          *reinterpret_cast<V8*>(vdst + 32 * ks + 8 * g) = *reinterpret_cast<const V8*>(vnew + 32 * ks + 8 * g);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ka[kb][ks][e] = from_f32<T>(0.f);
-      }
+    if (st != wave) {
+      wave_lds_sync();   // previous step's V^T reads are done before the DMA refills the tile
+      dec_load_k<T, D>(ka, krs, key0, r16, g);
+      dma_v_tile<NDMA>(vrs, vt, voff, key0 * RB);
     }
-    // ---- V: 4 keys x one 16-byte chunk per task, transposed into LDS
-    uint4 vr[VPT][4];
+    const bool has_new = newk >= key0 && newk < key0 + 32;   // wave-uniform
+    // the new token: rotate its key in place and append key and value
+    if (has_new) {
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int t = lane + 64 * i;
-      const int kg = t / CPR, dc = t % CPR;
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = key0 + 16 * kb + r16;
+        if (key == newk) {
+          T* kdst = reinterpret_cast<T*>(p.kc) + (head_base + key) * D;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = key0 + 4 * kg + rr;
-        const T* src = key == newk ? vnew + dc * CE : vc + (int64_t)key * D + dc * CE;
-        vr[i][rr] = (t < VTASK && key < k1) ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+          for (int ks = 0; ks < KS / 2; ++ks) {
+            float lo[8], hi[8];
+            v8_to_f32<T>(*reinterpret_cast<const V8*>(knew + 32 * ks + 8 * g), lo);
+            v8_to_f32<T>(*reinterpret_cast<const V8*>(knew + H + 32 * ks + 8 * g), hi);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float2 cs = cs_tab[32 * ks + 8 * g + e];
+              float y0, y1;
+              rope_pair(lo[e], hi[e], cs.x, cs.y, y0, y1);
+              ka[kb][ks][e] = from_f32<T>(y0);
+              ka[kb][ks + KS / 2][e] = from_f32<T>(y1);
+            }
+            *reinterpret_cast<V8*>(kdst + 32 * ks + 8 * g) = ka[kb][ks];
+            *reinterpret_cast<V8*>(kdst + H + 32 * ks + 8 * g) = ka[kb][ks + KS / 2];
+          }
+        }
       }
     }
     // ---- S^T = K Q^T over the 32 keys of the step
@@ -187,26 +306,6 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
     for (int ks = 0; ks < KS; ++ks) {
       s[0] = mma16(ka[0][ks], qB[ks], s[0]);
       s[1] = mma16(ka[1][ks], qB[ks], s[1]);
-    }
-    wave_lds_sync();   // previous step's V^T reads are done
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int t = lane + 64 * i;
-      if (t >= VTASK) break;
-      const int kg = t / CPR, dc = t % CPR;
-#pragma unroll
-      for (int e = 0; e < CE; ++e) {
-        const int d = dc * CE + e;
-        T* dst = vt + d * kDecVRow + dvt_group(d, kg) * 4;
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t h0 = elem_bits<T>(vr[i][0], e), h1 = elem_bits<T>(vr[i][1], e);
-          const uint32_t h2 = elem_bits<T>(vr[i][2], e), h3 = elem_bits<T>(vr[i][3], e);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        } else {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(elem_bits<T>(vr[i][0], e), elem_bits<T>(vr[i][1], e),
-                                                      elem_bits<T>(vr[i][2], e), elem_bits<T>(vr[i][3], e));
-        }
-      }
     }
     // ---- online softmax over the step (column = head, 8 keys per lane)
     float x[2][4];
@@ -237,24 +336,26 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
     m = mnew;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    wave_lds_sync();   // this step's V^T writes are visible to the wave
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = 16 * db + r16;
-      const T* row = vt + d * kDecVRow;
-      const V4 lo = *reinterpret_cast<const V4*>(row + dvt_group(d, g) * 4);
-      const V4 hi = *reinterpret_cast<const V4*>(row + dvt_group(d, 4 + g) * 4);
-      V8 a;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = lo[i]; a[4 + i] = hi[i]; }
-      o[db] = mma16(a, pB, o[db]);
+    dec_wait_vmem();   // the V tile has landed in LDS
+    if (has_new) {
+      // patch the new token's value row (zeros from the DMA) and append it
+      const int row = newk - key0;
+      if (lane < CPR) {
+        const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(vnew) + lane * 16);
+        *reinterpret_cast<uint4*>(vt + row * RB + ((lane ^ dv_swz<T, D>(row)) << 4)) = vv;
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.vc) + (head_base + newk) * RB + lane * 16) = vv;
+      }
     }
+    wave_lds_sync();
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = mma16(vt_operand<T, D>(vt, db, r16, g), pB, o[db]);
   }
 
   // ---- combine the four waves (LDS reused), then write output or partial
   const float lt = wave_sum_16_32(l);
+  dec_wait_vmem();   // no DMA into the tiles is still in flight
   __syncthreads();
-  float* cmb = reinterpret_cast<float*>(s_vt);          // [kWaves][16][D + 2]
+  float* cmb = reinterpret_cast<float*>(s_raw);          // [kWaves][16][D + 2]
   constexpr int CROW = D + 2;
   if (r16 < G) {
     float* row = cmb + (wave * 16 + r16) * CROW;
@@ -298,9 +399,9 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   constexpr int C4 = D / 4, SG = kThreads / C4;        // split groups
-  __shared__ float s_red[kThreads];
+  constexpr int NB = 16;                               // splits in flight per thread
   __shared__ __attribute__((aligned(16))) float s_acc[SG][D];
-  __shared__ float s_l[SG];
+  __shared__ float s_m[SG], s_l[SG];
   const int row = blockIdx.x;
   if (row >= p.num_rows) return;
   const int tid = threadIdx.x;
@@ -308,41 +409,59 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   const int nsplit = p.nsplit[ri];
   if (nsplit <= 1) return;        // single-chunk requests were written directly
   const float* base = p.part + (int64_t)row * p.nsplit_stride * (D + 4);
-  // max over splits
-  float M = -INFINITY;
-  for (int s = tid; s < nsplit; s += kThreads) M = fmaxf(M, base[(int64_t)s * (D + 4) + D]);
-  s_red[tid] = M;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
-    __syncthreads();
-  }
-  M = s_red[0];
-  // weighted sums: thread (split group sg, 4-wide chunk d4)
+  // thread (split group sg, 4-wide chunk d4): splits sg, sg + SG, ... in
+  // batches of NB whose loads are all issued before any arithmetic
   const int sg = tid / C4, d4 = tid % C4;
+  float M = -INFINITY, ls = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ls = 0.f;
-#pragma unroll 4
-  for (int s = sg; s < nsplit; s += SG) {
-    const float* pr = base + (int64_t)s * (D + 4);
-    const float ms = pr[D];
-    const float wt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    acc += *reinterpret_cast<const f32x4*>(pr + 4 * d4) * wt;
-    ls += pr[D + 1] * wt;
+  for (int s0 = sg; s0 < nsplit; s0 += SG * NB) {
+    float ms[NB], lp[NB];
+    f32x4 os[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      // unconditional loads (clamped split) so that all of them are in flight
+      const int s = s0 + SG * i;
+      const float* pr = base + (int64_t)min(s, nsplit - 1) * (D + 4);
+      const float mv = pr[D];
+      lp[i] = pr[D + 1];
+      os[i] = *reinterpret_cast<const f32x4*>(pr + 4 * d4);
+      ms[i] = s < nsplit ? mv : -INFINITY;
+    }
+    float mx = M;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) mx = fmaxf(mx, ms[i]);
+    if (mx == -INFINITY) continue;
+    const float a = __builtin_amdgcn_exp2f(M - mx);
+    acc *= a;
+    ls *= a;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const float w = ms[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[i] - mx);
+      acc += os[i] * w;
+      ls += lp[i] * w;
+    }
+    M = mx;
   }
   *reinterpret_cast<f32x4*>(&s_acc[sg][4 * d4]) = acc;
-  if (d4 == 0) s_l[sg] = ls;
+  if (d4 == 0) { s_m[sg] = M; s_l[sg] = ls; }
   __syncthreads();
   if (tid < D) {
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < SG; ++j) Mx = fmaxf(Mx, s_m[j]);
     float a = 0.f, lsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < SG; ++j) { a += s_acc[j][tid]; lsum += s_l[j]; }
+    for (int j = 0; j < SG; ++j) {
+      const float wt = s_m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[j] - Mx);
+      a += s_acc[j][tid] * wt;
+      lsum += s_l[j] * wt;
+    }
     const int rem = row % (p.hq * p.tq);
     const int head = rem / p.tq, t = rem % p.tq;
     const int r = p.req0 + ri;
     T* orow = reinterpret_cast<T*>(p.o) + (((int64_t)r * p.tq + t) * p.hq + head) * D;
     orow[tid] = from_f32<T>(a / lsum);
-    if (tid == 0 && p.lse) p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (M + __log2f(lsum)) * 0.69314718055994531f;
+    if (tid == 0 && p.lse) p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (Mx + __log2f(lsum)) * 0.69314718055994531f;
   }
 }
 

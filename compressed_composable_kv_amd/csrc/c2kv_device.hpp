@@ -83,15 +83,21 @@ struct RopeFreqs {
 };
 
 // ---------------------------------------------------------------- waves
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48) with gfx950's VALU lane swaps instead of LDS permutes: with both
+// operands equal to x, v_permlane16_swap returns {x[l], x[l^16]} and
+// v_permlane32_swap returns {x[l], x[l^32]} across its two results.
 __device__ __forceinline__ float wave_max_16_32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wave_sum_16_32(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Physical workgroup -> logical workgroup so that each XCD (8 per MI355X,

@@ -203,8 +203,8 @@ size_t c2kv_workspace_size_prefill(const int32_t* cache_len, int32_t num_reqs, i
  * Token t of request r is rotated at q_pos0[r] + t; its key (rounded to dt)
  * and value are written to row cache_len[r] + t.  Token t attends to every
  * row < cache_len[r] and to question rows <= t.  GQA as for extraction.
- * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, CAPACITY (cache_len + tq > cap),
- * HIP. */
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, CAPACITY (cache_len + tq > cap,
+ * or (cap + 128) rows of one KV head reach 2 GiB), HIP. */
 c2kv_status c2kv_attn_prefill(const void* q, const void* k_new, const void* v_new,
                               void* cache_k, void* cache_v, int64_t cap,
                               const int32_t* cache_len, const int32_t* q_pos0,
