@@ -393,75 +393,80 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
 }
 
 // ---------------------------------------------------------------- merge
-// One workgroup per output row (request of the launch, head, token): the
-// split partials [o(D) | m | l] of that row are combined by log-sum-exp.
-// Rows of requests with a single key chunk already hold their output.
+// One workgroup per (output row, 32-dim slice): the split partials
+// [o(D) | m | l] of that row (request of the launch, head, token) are
+// combined by log-sum-exp.  The (m, l) pairs are staged in LDS with one
+// load per split, the o slices are loaded in batches of kMergeNB splits per
+// thread with every load in flight before the arithmetic.  Rows of
+// requests with a single key chunk already hold their output.
+constexpr int kMergeDims = 32;                         // dims per workgroup
+constexpr int kMergeSG = kThreads / (kMergeDims / 4);  // split groups (32)
+constexpr int kMergeNB = 4;
+
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return wave_max_16_32(x);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
-  constexpr int C4 = D / 4, SG = kThreads / C4;        // split groups
-  constexpr int NB = 16;                               // splits in flight per thread
-  __shared__ __attribute__((aligned(16))) float s_acc[SG][D];
-  __shared__ float s_m[SG], s_l[SG];
-  const int row = blockIdx.x;
+  constexpr int DQ = D / kMergeDims, SG = kMergeSG, NB = kMergeNB;
+  __shared__ float s_m[C2KV_MAX_SPLITS], s_l[C2KV_MAX_SPLITS];
+  __shared__ __attribute__((aligned(16))) float s_acc[SG][kMergeDims];
+  __shared__ float s_ls[SG];
+  const int row = blockIdx.x / DQ, dq = blockIdx.x % DQ;
   if (row >= p.num_rows) return;
   const int tid = threadIdx.x;
   const int ri = row / (p.hq * p.tq);
   const int nsplit = p.nsplit[ri];
   if (nsplit <= 1) return;        // single-chunk requests were written directly
   const float* base = p.part + (int64_t)row * p.nsplit_stride * (D + 4);
-  // thread (split group sg, 4-wide chunk d4): splits sg, sg + SG, ... in
-  // batches of NB whose loads are all issued before any arithmetic
-  const int sg = tid / C4, d4 = tid % C4;
-  float M = -INFINITY, ls = 0.f;
+  const int sg = tid >> 3, d4 = tid & 7;
+  const int col = dq * kMergeDims + 4 * d4;
+  for (int s = tid; s < nsplit; s += kThreads) {
+    const float* pr = base + (int64_t)s * (D + 4);
+    s_m[s] = pr[D];
+    s_l[s] = pr[D + 1];
+  }
+  // first batch of o slices in flight while the maxima are reduced
+  f32x4 os[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    os[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(sg + SG * i, nsplit - 1) * (D + 4) + col);
+  __syncthreads();
+  float M = -INFINITY;
+  for (int s = tid & 63; s < nsplit; s += 64) M = fmaxf(M, s_m[s]);
+  M = wave_max64(M);              // every wave holds the row maximum
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = sg; s0 < nsplit; s0 += SG * NB) {
-    float ms[NB], lp[NB];
-    f32x4 os[NB];
+  float ls = 0.f;
+  for (int s0 = sg;; s0 += SG * NB) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      // unconditional loads (clamped split) so that all of them are in flight
       const int s = s0 + SG * i;
-      const float* pr = base + (int64_t)min(s, nsplit - 1) * (D + 4);
-      const float mv = pr[D];
-      lp[i] = pr[D + 1];
-      os[i] = *reinterpret_cast<const f32x4*>(pr + 4 * d4);
-      ms[i] = s < nsplit ? mv : -INFINITY;
-    }
-    float mx = M;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) mx = fmaxf(mx, ms[i]);
-    if (mx == -INFINITY) continue;
-    const float a = __builtin_amdgcn_exp2f(M - mx);
-    acc *= a;
-    ls *= a;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const float w = ms[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[i] - mx);
+      const float w = (s < nsplit && s_m[s] != -INFINITY) ? __builtin_amdgcn_exp2f(s_m[s] - M) : 0.f;
       acc += os[i] * w;
-      ls += lp[i] * w;
+      if (s < nsplit) ls += s_l[s] * w;
     }
-    M = mx;
+    if (s0 + SG * NB >= nsplit) break;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      os[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(s0 + SG * (NB + i), nsplit - 1) * (D + 4) + col);
   }
   *reinterpret_cast<f32x4*>(&s_acc[sg][4 * d4]) = acc;
-  if (d4 == 0) { s_m[sg] = M; s_l[sg] = ls; }
+  if (d4 == 0) s_ls[sg] = ls;
   __syncthreads();
-  if (tid < D) {
-    float Mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < SG; ++j) Mx = fmaxf(Mx, s_m[j]);
+  if (tid < kMergeDims) {
     float a = 0.f, lsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < SG; ++j) {
-      const float wt = s_m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[j] - Mx);
-      a += s_acc[j][tid] * wt;
-      lsum += s_l[j] * wt;
-    }
+    for (int j = 0; j < SG; ++j) { a += s_acc[j][tid]; lsum += s_ls[j]; }
     const int rem = row % (p.hq * p.tq);
     const int head = rem / p.tq, t = rem % p.tq;
     const int r = p.req0 + ri;
     T* orow = reinterpret_cast<T*>(p.o) + (((int64_t)r * p.tq + t) * p.hq + head) * D;
-    orow[tid] = from_f32<T>(a / lsum);
-    if (tid == 0 && p.lse) p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (Mx + __log2f(lsum)) * 0.69314718055994531f;
+    orow[dq * kMergeDims + tid] = from_f32<T>(a / lsum);
+    if (dq == 0 && tid == 0 && p.lse)
+      p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (M + __log2f(lsum)) * 0.69314718055994531f;
   }
 }
 
@@ -479,7 +484,7 @@ hipError_t launch_decode_attn(const DecodeParams& p, int dtype, int head_dim, hi
 
 template <typename T, int D>
 static hipError_t launch_merge_t(const MergeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(p.num_rows), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(p.num_rows * (D / kMergeDims)), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
