@@ -16,7 +16,18 @@ The 256 decode launches of a step are replayed from one HIP graph.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
-Prints one JSON line.
+Prints one JSON line.  Besides the step, it reports the decode rate with the
+256 steps spread over 16 replicas of the cache (a working set of about
+0.6 GB, above the 256 MB last-level cache), and, when a counter summary
+for the current decode sources is committed under profiles/, the HBM
+traffic the hardware counters measured for one decode call.
+
+Profiling helpers (no GPU work):
+    python bench.py --summarize DIR [DIR2] --out FILE --cmd "COMMAND"
+summarises rocprofv3 output directories into a short text file: a
+kernel-trace table, or (for --pmc runs, FETCH_SIZE and WRITE_SIZE passes)
+per-kernel counter averages scaled by a device copy of known size that
+`--calibration-copy-mib N` adds to a run.
 """
 from __future__ import annotations
 
@@ -33,6 +44,108 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
+# sources that define the decode call's kernels and launch shapes; a counter
+# summary applies to the build whose sources hash to the recorded value
+DECODE_SOURCES = ("compressed_composable_kv_amd/csrc/c2kv_decode.hip",
+                  "compressed_composable_kv_amd/csrc/c2kv_device.hpp",
+                  "compressed_composable_kv_amd/csrc/c2kv_launch.hpp",
+                  "compressed_composable_kv_amd/csrc/c2kv_abi.cpp")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_decode_llama31_8b_1layer.txt")
+CALIB_KERNEL = "neg_kernel"    # torch.neg over int32: reads and writes N MiB
+
+
+def sources_sha(paths=DECODE_SOURCES) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for pth in paths:
+        with open(os.path.join(ROOT, pth), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _db(d):
+    import glob
+    import sqlite3
+    dbs = glob.glob(os.path.join(d, "**", "*.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    return sqlite3.connect(dbs[0])
+
+
+def summarize(dirs, out, cmd, calib_mib):
+    """Short text summary of rocprofv3 output (see the module docstring)."""
+    lines = []
+    con = _db(dirs[0])
+    has_pmc = con.execute("select count(*) from sqlite_master where name='counters_collection'").fetchone()[0] and \
+        con.execute("select count(*) from counters_collection").fetchone()[0] > 0
+    if not has_pmc:
+        rows = con.execute("select name, count(*), avg(end-start), sum(end-start), min(end-start), max(end-start) "
+                           "from kernels group by name order by sum(end-start) desc").fetchall()
+        tot = sum(r[3] for r in rows)
+        lines.append("# rocprofv3 kernel-trace summary (durations from the kernel dispatch records)")
+        lines.append(f"# command: {cmd}")
+        lines.append("# calls    avg_us      min_us      max_us    total_ms   share  kernel")
+        for r in rows:
+            lines.append(f"{r[1]:7d} {r[2] / 1e3:9.2f} {r[4] / 1e3:11.2f} {r[5] / 1e3:11.2f} {r[3] / 1e6:11.3f} "
+                         f"{100 * r[3] / tot:6.1f}%  {r[0][:110]}")
+    else:
+        avg = {}
+        for d in dirs:
+            c = _db(d)
+            q = ("select kernel_name, counter_name, avg(v), count(*) from (select dispatch_id, kernel_name, "
+                 "counter_name, sum(value) as v from counters_collection group by dispatch_id, counter_name) "
+                 "group by kernel_name, counter_name")
+            for kname, cname, v, n in c.execute(q).fetchall():
+                avg.setdefault(kname, {})[cname] = (v, n)
+        calib = [k for k in avg if CALIB_KERNEL in k]
+        if not calib:
+            raise SystemExit("no calibration copy in the counter runs (use --calibration-copy-mib)")
+        cal = avg[calib[0]]
+        known_kib = calib_mib * 1024.0
+        fs = known_kib / cal["FETCH_SIZE"][0]
+        ws = known_kib / cal["WRITE_SIZE"][0]
+        lines.append("# rocprofv3 --pmc summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged),")
+        lines.append("# each pass a run of its own; scale factors from a device copy of known size")
+        lines.append(f"# command: {cmd}")
+        lines.append(f"# calibration: {calib_mib} MiB read + {calib_mib} MiB written by {CALIB_KERNEL}: "
+                     f"FETCH_SIZE {cal['FETCH_SIZE'][0]:.0f} KiB, WRITE_SIZE {cal['WRITE_SIZE'][0]:.0f} KiB "
+                     f"-> scale {fs:.4f} / {ws:.4f}")
+        lines.append("# dispatches  FETCH_KiB  WRITE_KiB  traffic_MB(scaled)  kernel")
+        traffic = {}
+        for kname, cs in sorted(avg.items()):
+            if "c2kv" not in kname or "FETCH_SIZE" not in cs or "WRITE_SIZE" not in cs:
+                continue
+            t = (cs["FETCH_SIZE"][0] * fs + cs["WRITE_SIZE"][0] * ws) * 1024.0
+            short = kname.split("(")[0][:80]
+            traffic[short] = t
+            lines.append(f"{cs['FETCH_SIZE'][1]:11d} {cs['FETCH_SIZE'][0]:10.1f} {cs['WRITE_SIZE'][0]:10.1f} "
+                         f"{t / 1e6:18.3f}  {short}")
+        lines.append("# json: " + json.dumps({"sources_sha": sources_sha(), "fetch_scale": fs, "write_scale": ws,
+                                              "traffic_bytes": traffic}))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def committed_traffic(kernel_keys):
+    """HBM bytes per decode call from the committed counter summary, or
+    None when there is none or the decode sources changed since."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            js = [l for l in f if l.startswith("# json: ")]
+        info = json.loads(js[-1][len("# json: "):])
+    except (OSError, IndexError, ValueError):
+        return None
+    if info.get("sources_sha") != sources_sha():
+        return None
+    tot = 0.0
+    for key in kernel_keys:
+        hits = [v for k, v in info["traffic_bytes"].items() if key in k]
+        if len(hits) != 1:
+            return None
+        tot += hits[0]
+    return tot
+
 
 def visible_cells(n: int, k: int) -> int:
     """Visible cells of one document's structured mask with sink = k:
@@ -48,7 +161,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-decode-steps", type=int, default=8)
+    ap.add_argument("--cpu-decode-steps", type=int, default=24)
+    ap.add_argument("--cold-replicas", type=int, default=16)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0)
+    ap.add_argument("--summarize", nargs="+", metavar="DIR")
+    ap.add_argument("--out")
+    ap.add_argument("--cmd", default="")
     return ap.parse_args()
 
 
@@ -97,6 +215,9 @@ def cpu_baseline(w, M, P, tq, nsteps):
 
 def main():
     a = parse()
+    if a.summarize:
+        summarize(a.summarize, a.out, a.cmd, a.calibration_copy_mib)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this path does not shard "
               f"across GPUs).", file=sys.stderr)
@@ -173,6 +294,12 @@ def main():
         graph.replay()
         if ev: ev[4].record()
 
+    if a.calibration_copy_mib:
+        src = torch.ones(a.calibration_copy_mib * 262144, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -187,6 +314,29 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
+
+    # decode with the steps spread over replicas of the cache (working set
+    # above the last-level cache); not part of the step
+    cold_gbs = None
+    if a.cold_replicas > 1:
+        reps = [(ck.clone(), cv.clone()) for _ in range(a.cold_replicas)]
+        torch.cuda.synchronize()
+        gcold = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gcold):
+            for s in range(S):
+                rk_, rv_ = reps[s % a.cold_replicas]
+                c2kv.attn_decode(qd[s], kd[s], vd[s], rk_, rv_, [M + tq + s], [P + tq + s], theta, workspace=ws_dec)
+        gcold.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            gcold.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        cold_ms = e0.elapsed_time(e1) / 3
+        del gcold, reps
+        torch.cuda.empty_cache()
     ph = [0.0] * 4
     for e in evs:
         for j in range(4):
@@ -201,6 +351,8 @@ def main():
     dec_bytes = sum((M + tq + s + 1) * hkv * d * es * 2 + (2 * hq + 2 * hkv) * d * es for s in range(S))
     ext_tflops = ext_flops / (ph[0] * 1e-3) / 1e12
     dec_gbs = dec_bytes / (ph[3] * 1e-3) / 1e9
+    if a.cold_replicas > 1:
+        cold_gbs = dec_bytes / (cold_ms * 1e-3) / 1e9
     comp_gbs = comp_bytes / (ph[1] * 1e-3) / 1e9
 
     # dominant kernel of the step: the phase with the largest share of the step
@@ -209,10 +361,13 @@ def main():
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ext_tflops / BF16_PEAK_TFLOPS,
                 "traffic": None, "per_launch_ms": ph[0], "algorithmic_per_launch": ext_flops}
     else:
+        # one launch = one c2kv_attn_decode call: decode_attn_kernel plus
+        # merge_kernel, timed per call from the graph replay
         per_launch_ms = ph[3] / S
-        roof = {"bound": "hbm", "kernel": "decode step (append_kernel + cache_attn_kernel<bf16,128>)",
+        traffic = committed_traffic(("decode_attn_kernel", "merge_kernel"))
+        roof = {"bound": "hbm", "kernel": "c2kv_attn_decode (decode_attn_kernel<bf16,128> + merge_kernel<bf16,128>)",
                 "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
-                "traffic": None, "per_launch_ms": per_launch_ms, "algorithmic_per_launch": dec_bytes / S}
+                "traffic": traffic, "per_launch_ms": per_launch_ms, "algorithmic_per_launch": dec_bytes / S}
 
     line = {
         "metric": "C2KV decode-attn KV GB/s (% HBM peak) + extraction masked-attn TFLOP/s",
@@ -235,6 +390,8 @@ def main():
         "extraction_frac": ext_tflops / BF16_PEAK_TFLOPS,
         "phase_ms": {"extract": ph[0], "compose": ph[1], "prefill": ph[2], "decode_256": ph[3]},
         "compose_gbs": comp_gbs,
+        "decode_gbs_cache_replicas": cold_gbs,
+        "cache_replicas": a.cold_replicas,
         "prefill_tflops": pre_flops / (ph[2] * 1e-3) / 1e12,
         "wall_s": t_wall,
         "roofline": roof,
