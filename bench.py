@@ -22,6 +22,14 @@ Prints one JSON line.  Besides the step, it reports the decode rate with the
 for the current decode sources is committed under profiles/, the HBM
 traffic the hardware counters measured for one decode call.
 
+Decode sweep over the other decode workloads (one JSON line each, not the
+step): the Qwen2.5-7B pool (32 requests composed from 64 ragged documents
+at k = 16) and the long-context sweep (64 requests at 16k..128k original
+tokens at k = 4, with the uncompressed cache of the same original length as
+the comparator), each a graph of decode calls over caches well above the
+last-level cache:
+    python bench.py --decode-sweep
+
 Profiling helpers (no GPU work):
     python bench.py --summarize DIR [DIR2] --out FILE --cmd "COMMAND"
 summarises rocprofv3 output directories into a short text file: a
@@ -165,6 +173,7 @@ def parse():
     ap.add_argument("--cold-replicas", type=int, default=16)
     ap.add_argument("--calibration-copy-mib", type=int, default=0)
     ap.add_argument("--summarize", nargs="+", metavar="DIR")
+    ap.add_argument("--decode-sweep", action="store_true")
     ap.add_argument("--out")
     ap.add_argument("--cmd", default="")
     return ap.parse_args()
@@ -213,10 +222,74 @@ def cpu_baseline(w, M, P, tq, nsteps):
     }
 
 
+def decode_sweep():
+    """Decode rate (algorithmic KV bytes per second) of the other decode
+    workloads; caches are device-generated N(0, 1) rows (decode time does
+    not depend on their values)."""
+    import torch
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def run(name, lens, w, steps, extra):
+        d, hq, hkv, dt = w.head_dim, w.hq, w.hkv, w.dtype
+        R = len(lens)
+        cap = max(lens) + steps
+        ck = W.device_normal((R, hkv, cap, d), dt, w.wid, W.P_K, dev, salt=7)
+        cv = W.device_normal((R, hkv, cap, d), dt, w.wid, W.P_V, dev, salt=7)
+        qd = W.device_normal((steps, R, hq, d), dt, w.wid, W.P_DEC_Q, dev, salt=7)
+        kd = W.device_normal((steps, R, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=7)
+        vd = W.device_normal((steps, R, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=8)
+        ws = torch.empty(max(c2kv.workspace_size_decode([x + s for x in lens], hq, hkv, d, dt)
+                             for s in range(steps)), dtype=torch.uint8, device=dev)
+
+        def loop():
+            for s in range(steps):
+                c2kv.attn_decode(qd[s], kd[s], vd[s], ck, cv, [x + s for x in lens], [4 * x + s for x in lens],
+                                 w.rope_theta, workspace=ws)
+        loop()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            loop()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (3 * steps)
+        nbytes = sum((x + steps / 2 + 1) * hkv * d * 2 * 2 + (2 * hq + 2 * hkv) * d * 2 for x in lens)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        print(json.dumps({"workload": name, "requests": R, "rows_min": min(lens), "rows_max": max(lens),
+                          "us_per_step": us, "kv_bytes_per_step": nbytes, "gbs": gbs,
+                          "hbm_frac": gbs / HBM_PEAK_GBS, **extra}), flush=True)
+        del ck, cv, g
+        torch.cuda.empty_cache()
+
+    w3 = W.QWEN25
+    pool = W.qwen25_pool(w3)
+    lens3 = [sum(c2kv.num_slots(pool[t], w3.ratio_k) for t in r) for r in W.qwen25_requests(w3)]
+    run("qwen25_7b_pool_decode", lens3, w3, 32, {"cache": "composed, k=16"})
+    w4 = W.LONGCTX
+    for nd in W.longctx_doc_counts():
+        L = 4096 * nd
+        run(f"llama31_8b_longctx_{L // 1024}k_c2kv", [nd * c2kv.num_slots(4096, w4.ratio_k)] * w4.num_reqs, w4, 8,
+            {"cache": "composed, k=4", "original_tokens": L})
+        run(f"llama31_8b_longctx_{L // 1024}k_full", [L] * w4.num_reqs, w4, 4,
+            {"cache": "uncompressed comparator", "original_tokens": L})
+
+
 def main():
     a = parse()
     if a.summarize:
         summarize(a.summarize, a.out, a.cmd, a.calibration_copy_mib)
+        return
+    if a.decode_sweep:
+        decode_sweep()
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this path does not shard "
