@@ -290,3 +290,48 @@ def test_decode_split_invariance(c2kv):
     assert torch.equal(o_a[0], o_a[1])
     diff = (o_a[0].float() - o_b[0].float()).abs().max().item()
     assert diff <= 2e-3
+
+
+def test_extract_sink_heavy(c2kv):
+    """Attention mass concentrated on the first tokens (keys of the sink
+    leaning towards the mean query direction): document and slot rows."""
+    doc_lens, k, hq, hkv, d = (700, 129), 4, 8, 2, 128
+    dt = torch.bfloat16
+    q, kk, v = packed_inputs(17, doc_lens, k, hq, hkv, d, dt, c2kv)
+    offs = O.doc_row_offsets(doc_lens, k)
+    for b, n in enumerate(doc_lens):
+        seg = slice(offs[b], offs[b + 1])
+        kk[seg] = W.sink_biased(q[seg], kk[seg], k)
+    o, lse = c2kv.extract_attn(q.to(DEV), kk.to(DEV), v.to(DEV), doc_lens, k, k, 5e5, return_lse=True)
+    ref = O.extract_attn(q.float().numpy(), kk.float().numpy(), v.float().numpy(), doc_lens, k, k, 5e5)
+    og, lg = np32(o), np32(lse)
+    for b in range(len(doc_lens)):
+        ro, rl = ref[b]
+        assert_close(og[offs[b]:offs[b + 1]], ro, "bf16", f"sink-heavy doc {b}")
+        assert_lse_close(lg[:, offs[b]:offs[b + 1]], rl, "bf16", f"sink-heavy doc {b}")
+
+
+def test_decode_sink_heavy(c2kv):
+    """Decode over a cache whose first rows dominate the softmax."""
+    hq, hkv, d, dt, theta = 32, 8, 128, torch.bfloat16, 5e5
+    lens = [3000, 257]
+    R = len(lens)
+    cap = max(lens) + 1
+    ck = W.normal((R, hkv, cap, d), dt, 18, W.P_K)
+    cv = W.normal((R, hkv, cap, d), dt, 18, W.P_V)
+    q = W.normal((R, hq, d), dt, 18, W.P_DEC_Q)
+    kn = W.normal((R, hkv, d), dt, 18, W.P_NEW_KV)
+    vn = W.normal((R, hkv, d), dt, 18, W.P_NEW_KV, salt=1)
+    for r in range(R):
+        rows = ck[r].transpose(0, 1)                                   # [cap][hkv][d]
+        ck[r] = W.sink_biased(q[r:r + 1], rows, 4, sigma=6.0).transpose(0, 1)
+    qpos = [4 * lens[r] for r in range(R)]
+    o, lse = c2kv.attn_decode(q.to(DEV), kn.to(DEV), vn.to(DEV), ck.to(DEV), cv.to(DEV), lens, qpos, theta,
+                              return_lse=True)
+    for r in range(R):
+        rk = ck[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        rv = cv[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        ro, rl, _, _ = O.decode_step(q[r].float().numpy(), kn[r].float().numpy(), vn[r].float().numpy(),
+                                     rk, rv, qpos[r], theta, "bf16")
+        assert_close(np32(o[r]), ro, "bf16", f"sink-heavy request {r}")
+        assert_lse_close(np32(lse[r]), rl, "bf16", f"sink-heavy request {r}")
