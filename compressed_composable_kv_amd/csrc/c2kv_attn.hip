@@ -451,6 +451,9 @@ __device__ __forceinline__ f32x8 lds_v8<float>(const char* base, int chunk0, int
   return r;
 }
 
+// Reference-max slack of the online softmax, in log2 units (see tile()).
+constexpr float kLazyLog2 = 8.f;
+
 // One wave's 32 query rows against one staged tile.
 template <typename T, int D>
 struct XAttn {
@@ -461,7 +464,7 @@ struct XAttn {
 
   V8 qB[2][KS];
   f32x4 o[DB][2];
-  float m[2], l[2];   // running max of the raw scores, running sum
+  float m[2], l[2];   // reference max of the raw scores, running sum
 
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -508,9 +511,13 @@ struct XAttn {
           mx = fmaxf(mx, v);
         }
       mx = wave_max_16_32(mx);
-      const float mnew = fmaxf(m[qb], mx);
+      // Lazy rescaling: the reference max moves only when the tile's max
+      // exceeds it by more than kLazyLog2 (in log2 units), so most tiles
+      // leave O untouched; probabilities stay below 2^kLazyLog2.
+      const bool grow = (mx - m[qb]) * sl2 > kLazyLog2;
+      const float mnew = grow ? mx : m[qb];
       const float mneg = mnew == -INFINITY ? 0.f : -mnew * sl2;
-      alpha[qb] = __builtin_amdgcn_exp2f(__builtin_fmaf(m[qb], sl2, mneg));
+      alpha[qb] = grow ? __builtin_amdgcn_exp2f(__builtin_fmaf(m[qb], sl2, mneg)) : 1.f;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -523,12 +530,15 @@ struct XAttn {
       l[qb] = l[qb] * alpha[qb] + rs;
       m[qb] = mnew;
     }
-    // rescale O only when some lane's running max moved
+    // rescale O only when some lane's reference max moved (the empty asm
+    // keeps the multiplies inside the rarely taken branch)
     if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
+      float a0 = alpha[0], a1 = alpha[1];
+      asm volatile("" : "+v"(a0), "+v"(a1));
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        o[db][0] *= alpha[0];
-        o[db][1] *= alpha[1];
+        o[db][0] *= a0;
+        o[db][1] *= a1;
       }
     }
 #pragma unroll
