@@ -476,15 +476,16 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
   std::memset(&p, 0, sizeof(p));
   p.cache_k = cache_k; p.cache_v = cache_v; p.pos_out = pos_out; p.cap = cap;
   p.hkv = hkv; p.ratio_k = ratio_k; p.freqs = make_freqs(head_dim, rope_theta);
+  const int rpt = compose_rows_per_tile((int)elem_bytes(dt), head_dim);
   int cnt = 0;
-  int32_t rows = 0;
+  int32_t tiles = 0;
   auto flush = [&]() -> hipError_t {
     if (cnt == 0) return hipSuccess;
     p.num_segs = cnt;
-    p.total_rows = rows;
+    p.total_tiles = tiles;
     hipError_t e = launch_compose(p, dt, head_dim, stream);
     cnt = 0;
-    rows = 0;
+    tiles = 0;
     return e;
   };
   for (int32_t r = 0; r < num_reqs; ++r) {
@@ -493,14 +494,15 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
     for (int32_t t = req_seg_ptr[r]; t < req_seg_ptr[r + 1]; ++t) {
       const c2kv_segment& g = segs[t];
       const int32_t m = num_slots_i(g.doc_len, ratio_k);
-      if (cnt == kComposeSegs || (int64_t)rows + m >= ((int64_t)1 << 30)) {
+      const int32_t mt = (m + rpt - 1) / rpt;
+      if (cnt == kComposeSegs || (int64_t)tiles + mt >= ((int64_t)1 << 24)) {
         hipError_t e = flush();
         if (e != hipSuccess) return hip_fail(e, "compose kernel launch");
       }
       ComposeSeg& d = p.segs[cnt++];
       d.k = g.k; d.v = g.v; d.stride = (int32_t)g.row_stride; d.n = g.doc_len;
-      d.req = r; d.out_row = out_row; d.pos_off = (int32_t)pos; d.row_prefix = rows;
-      rows += m;
+      d.req = r; d.out_row = out_row; d.pos_off = (int32_t)pos; d.tile0 = tiles;
+      tiles += mt;
       out_row += m;
       pos += g.doc_len;
     }

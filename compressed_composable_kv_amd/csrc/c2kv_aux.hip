@@ -185,53 +185,102 @@ hipError_t launch_transpose_v(const RotateParams& p, int dtype, int head_dim, hi
 }
 
 // ---------------------------------------------------------------- compose
-// One thread per (composed slot row, KV head, 16-byte chunk of the low
-// half).  The row's segment is found by binary search in the launch's
-// segment table; its realigned position is the document offset plus the
-// slot's extraction position.
+// Work unit = (row tile of ONE segment, group of two KV heads); a thread owns
+// one 16-byte chunk of the low half of a row (and the matching chunk of the
+// high half) and rotates it for both heads with one set of cos/sin.  The
+// unit's segment is found by a uniform search of the segment table; its
+// realigned position is the document offset plus the slot's extraction
+// position.  Workgroups loop over units with the next unit's loads issued
+// before the current unit's rotation and stores, so reads and writes of
+// the cache stream overlap.
+template <typename T, int D>
+struct ComposeUnit {
+  static constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE, RPT = 256 / TPH;
+  uint4 kl0, kh0, vl0, vh0, kl1, kh1, vl1, vh1;
+  float fr[CE];
+  int seg, j, c, h0, cpos;
+  bool live;
+
+  __device__ __forceinline__ void load(const ComposeParams& p, int u, int ngroups) {
+    const int tile = u / ngroups, hgrp = u % ngroups;
+    int lo_s = 0, hi_s = p.num_segs - 1;
+    while (lo_s < hi_s) {
+      const int mid = (lo_s + hi_s + 1) >> 1;
+      if (p.segs[mid].tile0 <= tile) lo_s = mid; else hi_s = mid - 1;
+    }
+    seg = lo_s;
+    const ComposeSeg& sg = p.segs[seg];
+    const int m = (sg.n + p.ratio_k - 1) / p.ratio_k;
+    j = (tile - sg.tile0) * RPT + (int)threadIdx.x / TPH;
+    c = (int)threadIdx.x % TPH;
+    live = j < m;
+    const int jj = live ? j : m - 1;     // dead lanes load a valid row
+    cpos = sg.pos_off + min(jj * p.ratio_k + p.ratio_k - 1, sg.n - 1);
+#pragma unroll
+    for (int e = 0; e < CE; e += 4) {
+      const f32x4 f4 = *reinterpret_cast<const f32x4*>(&p.freqs.f[c * CE + e]);
+      fr[e] = f4[0]; fr[e + 1] = f4[1]; fr[e + 2] = f4[2]; fr[e + 3] = f4[3];
+    }
+    const T* ksrc = reinterpret_cast<const T*>(sg.k) + (int64_t)jj * sg.stride + c * CE;
+    const T* vsrc = reinterpret_cast<const T*>(sg.v) + (int64_t)jj * sg.stride + c * CE;
+    h0 = hgrp * 2;
+    const int h1 = min(h0 + 1, p.hkv - 1);
+    kl0 = *reinterpret_cast<const uint4*>(ksrc + h0 * D);
+    kh0 = *reinterpret_cast<const uint4*>(ksrc + h0 * D + H);
+    vl0 = *reinterpret_cast<const uint4*>(vsrc + h0 * D);
+    vh0 = *reinterpret_cast<const uint4*>(vsrc + h0 * D + H);
+    kl1 = *reinterpret_cast<const uint4*>(ksrc + h1 * D);
+    kh1 = *reinterpret_cast<const uint4*>(ksrc + h1 * D + H);
+    vl1 = *reinterpret_cast<const uint4*>(vsrc + h1 * D);
+    vh1 = *reinterpret_cast<const uint4*>(vsrc + h1 * D + H);
+  }
+
+  __device__ __forceinline__ void store(const ComposeParams& p) {
+    if (!live) return;
+    const ComposeSeg& sg = p.segs[seg];
+    float cs[CE], sn[CE];
+#pragma unroll
+    for (int e = 0; e < CE; ++e) rope_cs(cpos, fr[e], cs[e], sn[e]);
+    auto put = [&](int h, uint4 kl, uint4 kh, const uint4& vl, const uint4& vh) {
+      rotate_chunk<T>(kl, kh, cs, sn);
+      const int64_t dst = (((int64_t)sg.req * p.hkv + h) * p.cap + sg.out_row + j) * D + c * CE;
+      T* kd = reinterpret_cast<T*>(p.cache_k) + dst;
+      T* vd = reinterpret_cast<T*>(p.cache_v) + dst;
+      *reinterpret_cast<uint4*>(kd) = kl;
+      *reinterpret_cast<uint4*>(kd + H) = kh;
+      *reinterpret_cast<uint4*>(vd) = vl;
+      *reinterpret_cast<uint4*>(vd + H) = vh;
+    };
+    put(h0, kl0, kh0, vl0, vh0);
+    if (h0 + 1 < p.hkv) put(h0 + 1, kl1, kh1, vl1, vh1);
+    if (p.pos_out && h0 == 0 && c == 0) p.pos_out[(int64_t)sg.req * p.cap + sg.out_row + j] = cpos;
+  }
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void compose_kernel(const ComposeParams p) {
-  constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per_row = (int64_t)p.hkv * TPH;
-  const int64_t grow = idx / per_row;
-  if (grow >= p.total_rows) return;
-  const int h = (int)((idx % per_row) / TPH), c = (int)(idx % TPH);
-  int lo_s = 0, hi_s = p.num_segs - 1;
-  while (lo_s < hi_s) {
-    const int mid = (lo_s + hi_s + 1) >> 1;
-    if (p.segs[mid].row_prefix <= grow) lo_s = mid; else hi_s = mid - 1;
+  static_assert(kComposeHPT == 2, "two heads per thread");
+  const int ngroups = (p.hkv + 1) / 2;
+  const int total = p.total_tiles * ngroups;
+  int u = blockIdx.x;
+  if (u >= total) return;
+  ComposeUnit<T, D> cur, nxt;
+  cur.load(p, u, ngroups);
+  for (; u < total; u += gridDim.x) {
+    const bool more = u + (int)gridDim.x < total;
+    if (more) nxt.load(p, u + gridDim.x, ngroups);
+    cur.store(p);
+    if (!more) break;
+    cur = nxt;
   }
-  const ComposeSeg sg = p.segs[lo_s];
-  const int j = (int)(grow - sg.row_prefix);
-  const int cpos = sg.pos_off + min(j * p.ratio_k + p.ratio_k - 1, sg.n - 1);
-  const int64_t src_off = (int64_t)j * sg.stride + (int64_t)h * D + c * CE;
-  const int64_t dst_off = (((int64_t)sg.req * p.hkv + h) * p.cap + sg.out_row + j) * D + c * CE;
-  const T* ks = reinterpret_cast<const T*>(sg.k) + src_off;
-  const T* vs = reinterpret_cast<const T*>(sg.v) + src_off;
-  uint4 klo = *reinterpret_cast<const uint4*>(ks);
-  uint4 khi = *reinterpret_cast<const uint4*>(ks + H);
-  const uint4 vlo = *reinterpret_cast<const uint4*>(vs);
-  const uint4 vhi = *reinterpret_cast<const uint4*>(vs + H);
-  float cs[CE], sn[CE];
-#pragma unroll
-  for (int e = 0; e < CE; ++e) rope_cs(cpos, p.freqs.f[c * CE + e], cs[e], sn[e]);
-  rotate_chunk<T>(klo, khi, cs, sn);
-  T* kd = reinterpret_cast<T*>(p.cache_k) + dst_off;
-  T* vd = reinterpret_cast<T*>(p.cache_v) + dst_off;
-  *reinterpret_cast<uint4*>(kd) = klo;
-  *reinterpret_cast<uint4*>(kd + H) = khi;
-  *reinterpret_cast<uint4*>(vd) = vlo;
-  *reinterpret_cast<uint4*>(vd + H) = vhi;
-  if (p.pos_out && h == 0 && c == 0) p.pos_out[(int64_t)sg.req * p.cap + sg.out_row + j] = cpos;
 }
 
 template <typename T, int D>
 static hipError_t launch_compose_t(const ComposeParams& p, hipStream_t st) {
-  constexpr int TPH = D / 2 / Chunk<T>::CE;
-  const int64_t n = (int64_t)p.total_rows * p.hkv * TPH;
-  const int blocks = (int)((n + 255) / 256);
-  if (blocks == 0) return hipSuccess;
+  const int units = p.total_tiles * ((p.hkv + kComposeHPT - 1) / kComposeHPT);
+  if (units == 0) return hipSuccess;
+  // about two units per workgroup, at most four workgroups per CU
+  const int blocks = units < 2048 ? (units + 1) / 2 : min(units, 1024);
   hipLaunchKernelGGL((compose_kernel<T, D>), dim3(blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }

@@ -35,19 +35,27 @@ struct ComposeSeg {
   int32_t req;         // request index
   int32_t out_row;     // first cache row of this segment
   int32_t pos_off;     // position offset of the document
-  int32_t row_prefix;  // index of this segment's first slot row within the launch
+  int32_t tile0;       // first row tile of this segment within the launch
 };
-constexpr int kComposeSegs = 48;   // segments per launch (kernel-argument table)
+constexpr int kComposeSegs = 64;   // segments per launch (kernel-argument table)
+constexpr int kComposeHPT = 2;     // KV heads per thread
 
 struct ComposeParams {
   void* cache_k;
   void* cache_v;
   int32_t* pos_out;
   int64_t cap;
-  int32_t num_segs, hkv, ratio_k, total_rows;
+  int32_t num_segs, hkv, ratio_k, total_tiles;
   RopeFreqs freqs;
   ComposeSeg segs[kComposeSegs];
 };
+static_assert(sizeof(ComposeParams) <= 4096, "compose table must fit the kernel arguments");
+
+// Composed rows per row tile of compose_kernel (one workgroup of 256 threads
+// covers a tile of rows, each thread one 16-byte chunk of a half row).
+inline int compose_rows_per_tile(int dtype_bytes, int head_dim) {
+  return 256 / (head_dim / 2 * dtype_bytes / 16);
+}
 
 struct AppendReq {
   int32_t cache_len, pos0;

@@ -44,7 +44,7 @@
  *   arguments in chunks of at most C2KV_MAX_BATCH entries per launch, so
  *   extract/prefill/decode perform no host-to-device copies and may be
  *   captured in a HIP graph.  Compose passes its segment table the same way
- *   (at most 48 segments per launch) and needs no workspace.
+ *   (at most 64 segments per launch) and needs no workspace.
  */
 #ifndef C2KV_H_
 #define C2KV_H_
