@@ -16,115 +16,13 @@
 // queries on the N side), so each lane's accumulators belong to ONE query:
 // softmax row statistics need two cross-lane steps and the O^T rescale is a
 // per-lane scalar.  P^T goes straight from the S^T accumulators into the B
-// operand of O^T += V^T P^T; V is stored transposed in LDS for that product.
+// operand of O^T += V^T P^T.  Tiles arrive by LDS DMA; extraction stages V^T
+// tiles from a transposed workspace, prefill stages row-major V tiles of the
+// cache and reads the V^T operand with transposing LDS reads.
 #include "c2kv_device.hpp"
 #include "c2kv_launch.hpp"
 
 namespace c2kv {
-
-// ------------------------------------------------------------------ LDS
-template <typename T, int D>
-struct Smem {
-  static constexpr int kKRow = D + 16 / (int)sizeof(T);   // padded K row
-  static constexpr int kVRow = kBN + kVPad;               // padded V^T row
-  static constexpr int kKElems = kBN * kKRow;
-  static constexpr int kVElems = D * kVRow;
-  static constexpr int kStage = kKElems + kVElems;
-};
-
-// Two workgroups per CU (two waves per SIMD) fit the 160 KB LDS except for
-// fp32 with head_dim 128, whose double-buffered tiles need 141 KB.
-template <typename T, int D>
-constexpr int kMinWaves = (2 * Smem<T, D>::kStage * (int)sizeof(T) * 2 <= 160 * 1024) ? 2 : 1;
-
-// V^T rows hold 16 groups of 4 keys; the group index is XOR-swizzled with
-// (d >> 3) so that both the transposing writes and the MFMA operand reads
-// are free of LDS bank conflicts.
-__device__ __forceinline__ int vt_group(int d, int kg) { return kg ^ ((d >> 3) & 15); }
-
-template <typename T>
-__device__ __forceinline__ uint32_t half_of(const uint4& x, int e);
-
-// ---------------------------------------------------------- tile loader
-// Global -> registers -> LDS staging of one 64-key K/V tile.  Every thread
-// owns KPT 16-byte chunks of K (row-major, coalesced) and VPT groups of 4
-// keys x one 16-byte chunk of V, which it writes transposed.
-template <typename T, int D>
-struct KVStage {
-  static constexpr int CE = ElemTraits<T>::kChunk;
-  static constexpr int CPR = D / CE;
-  static constexpr int KPT = kBN * CPR / kThreads;
-  static constexpr int VTASKS = (kBN / 4) * CPR;
-  static constexpr int VPT = (VTASKS + kThreads - 1) / kThreads;
-  static_assert(KPT >= 1 && (kBN * CPR) % kThreads == 0, "tile/thread mismatch");
-
-  uint4 kr[KPT];
-  uint4 vr[VPT][4];
-
-  // kb/vb: wave-uniform base of the tile; stride: elements between key rows
-  // (< 2^31 / 64, so per-thread offsets stay 32-bit).
-  __device__ __forceinline__ void load(const T* __restrict__ kb, const T* __restrict__ vb,
-                                       int stride, int nvalid, int tid) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / CPR, col = c % CPR;
-      const int off = row * stride + col * CE;
-      kr[i] = row < nvalid ? *reinterpret_cast<const uint4*>(kb + off) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int task = tid + i * kThreads;
-      const int kg = task / CPR, dc = task % CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * kg + r;
-        const int off = row * stride + dc * CE;
-        vr[i][r] = (task < VTASKS && row < nvalid) ? *reinterpret_cast<const uint4*>(vb + off)
-                                                   : make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(T* ks, T* vt, int tid) const {
-    using S = Smem<T, D>;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / CPR, col = c % CPR;
-      *reinterpret_cast<uint4*>(ks + row * S::kKRow + col * CE) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int task = tid + i * kThreads;
-      if (task >= VTASKS) break;
-      const int kg = task / CPR, dc = task % CPR;
-#pragma unroll
-      for (int e = 0; e < CE; ++e) {
-        const int d = dc * CE + e;
-        T* dst = vt + d * S::kVRow + vt_group(d, kg) * 4;
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t h0 = half_of<T>(vr[i][0], e), h1 = half_of<T>(vr[i][1], e);
-          const uint32_t h2 = half_of<T>(vr[i][2], e), h3 = half_of<T>(vr[i][3], e);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        } else {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(half_of<T>(vr[i][0], e), half_of<T>(vr[i][1], e),
-                                                      half_of<T>(vr[i][2], e), half_of<T>(vr[i][3], e));
-        }
-      }
-    }
-  }
-};
-
-template <>
-__device__ __forceinline__ uint32_t half_of<bf16>(const uint4& x, int e) {
-  const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-template <>
-__device__ __forceinline__ uint32_t half_of<float>(const uint4& x, int e) {
-  return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
-}
 
 // ------------------------------------------------------ visibility rules
 // One branch-free formula covers every rule on this path:
@@ -144,102 +42,6 @@ struct Pred {
 };
 __host__ __device__ constexpr Pred pred_causal(int kmax, int offset) { return Pred{kmax, offset, 0, 0}; }
 __host__ __device__ constexpr Pred pred_slot_doc(int n, int k, int sink) { return Pred{n, -(1 << 30), k, sink}; }
-
-// ------------------------------------------------------ wave tile engine
-template <typename T, int D>
-struct WaveAttn {
-  using V8 = typename ElemTraits<T>::v8;
-  using V4 = typename ElemTraits<T>::v4;
-  static constexpr int KS = D / 32;   // 32-wide k steps of QK^T
-  static constexpr int DB = D / 16;   // 16-row blocks of O^T
-
-  V8 qB[2][KS];
-  f32x4 o[DB][2];
-  float m[2], l[2];
-
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[0] = m[1] = -INFINITY;
-    l[0] = l[1] = 0.f;
-  }
-
-  // One 64-key tile: S^T = K Q^T, optional mask, online softmax, O^T += V^T P^T.
-  template <bool kMasked>
-  __device__ __forceinline__ void tile(const T* ks, const T* vt, int lane, float scale_log2,
-                                       const Pred& pred, int q0, int key0) {
-    using S = Smem<T, D>;
-    const int r16 = lane & 15, g = lane >> 4;
-    f32x4 s[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const V8 a = *reinterpret_cast<const V8*>(ks + (16 * kb + r16) * S::kKRow + 32 * k + 8 * g);
-        s[kb][0] = mma16(a, qB[0][k], s[kb][0]);
-        s[kb][1] = mma16(a, qB[1][k], s[kb][1]);
-      }
-    }
-    V8 pB[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float x[4][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[kb][qb][i] * scale_log2;
-          if constexpr (kMasked) v = pred(q0 + 16 * qb + r16, key0 + 16 * kb + 4 * g + i) ? v : -INFINITY;
-          x[kb][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = wave_max_16_32(mx);
-      const float mnew = fmaxf(m[qb], mx);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - muse);
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(x[kb][i] - muse);
-          x[kb][i] = p;
-          rs += p;
-        }
-      l[qb] = l[qb] * alpha + rs;
-      m[qb] = mnew;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pB[c][qb][i] = from_f32<T>(x[2 * c][i]);
-          pB[c][qb][4 + i] = from_f32<T>(x[2 * c + 1][i]);
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = 16 * db + r16;
-        const T* row = vt + d * S::kVRow;
-        const V4 lo = *reinterpret_cast<const V4*>(row + vt_group(d, 8 * c + g) * 4);
-        const V4 hi = *reinterpret_cast<const V4*>(row + vt_group(d, 8 * c + 4 + g) * 4);
-        V8 a;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { a[i] = lo[i]; a[4 + i] = hi[i]; }
-        o[db][0] = mma16(a, pB[c][0], o[db][0]);
-        o[db][1] = mma16(a, pB[c][1], o[db][1]);
-      }
-    }
-  }
-};
 
 // Load 8 elements (one lane's k-group) of a row as fp32.
 template <typename T>
@@ -451,6 +253,49 @@ __device__ __forceinline__ f32x8 lds_v8<float>(const char* base, int chunk0, int
   return r;
 }
 
+// ------------------------------------------ row-major V tiles (prefill)
+// A V tile of 64 keys x D, row-major, filled by LDS DMA.  32-byte pairs of
+// a row are XOR-swizzled with vr_swz(row) so that the transposed operand
+// reads of a half wave (8 rows x 32 bytes) hit distinct banks.
+template <int RB>
+__device__ __forceinline__ int vr_swz(int row) {
+  if constexpr (RB >= 256) return (row & 3) | (((row >> 3) & 1) << 2);
+  else return ((row >> 1) & 1) | (((row >> 3) & 1) << 1);
+}
+
+typedef short pf_s4 __attribute__((ext_vector_type(4)));
+
+// V^T operand of O^T += V^T P^T for half c and dims 16 db .. +15: lane
+// (r16, g) gets dim 16 db + r16 of keys 32 c + 8 g + e, e = 0..7 (the key
+// order of the P^T operand).  bf16: ds_read_b64_tr_b16, where within each
+// 16 lanes output lane j element a is element j % 4 of the 4 values
+// addressed by source lane 4a + j / 4; fp32: element reads.
+template <typename T, int D>
+__device__ __forceinline__ typename ElemTraits<T>::v8 vrow_operand(const char* vt, int c, int db, int r16, int g) {
+  constexpr int RB = D * (int)sizeof(T);
+  if constexpr (sizeof(T) == 2) {
+    pf_s4 x[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 32 * c + 8 * g + 4 * h + (r16 >> 2);
+      const int off = row * RB + 32 * (db ^ vr_swz<RB>(row)) + 8 * (r16 & 3);
+      x[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) pf_s4*)(vt + off));
+    }
+    typedef short s8 __attribute__((ext_vector_type(8)));
+    const s8 v = {x[0][0], x[0][1], x[0][2], x[0][3], x[1][0], x[1][1], x[1][2], x[1][3]};
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    f32x8 a;
+    const int d = 16 * db + r16;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = 32 * c + 8 * g + e;
+      a[e] = *reinterpret_cast<const float*>(vt + row * RB + (((d >> 2) ^ (2 * vr_swz<256>(row))) << 4) + 4 * (d & 3));
+    }
+    return a;
+  }
+}
+
 // Reference-max slack of the online softmax, in log2 units (see tile()).
 constexpr float kLazyLog2 = 8.f;
 
@@ -473,7 +318,9 @@ struct XAttn {
     l[0] = l[1] = 0.f;
   }
 
-  template <bool kMasked>
+  // kVRow: the stage holds V row-major ([64 keys][D], pair-swizzled) instead
+  // of V^T, and the V^T operand is read transposed from it.
+  template <bool kMasked, bool kVRow = false>
   __device__ __forceinline__ void tile(const char* stage, int lane, float sl2, const Pred& pred, int q0, int key0) {
     const int r16 = lane & 15, g = lane >> 4;
     const char* ks = stage;
@@ -546,7 +393,9 @@ struct XAttn {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int d = 16 * db + r16;
-        const V8 a = lds_v8<T>(vt + d * X::VB, (4 * c + g) * CPE, vt_swz<X::VC>(d), X::VC);
+        V8 a;
+        if constexpr (kVRow) a = vrow_operand<T, D>(vt, c, db, r16, g);
+        else a = lds_v8<T>(vt + d * X::VB, (4 * c + g) * CPE, vt_swz<X::VC>(d), X::VC);
         o[db][0] = mma16(a, pB[c][0], o[db][0]);
         o[db][1] = mma16(a, pB[c][1], o[db][1]);
       }
@@ -709,10 +558,33 @@ __global__ __launch_bounds__(kThreads) void mask_count_kernel(const ExtractParam
 }
 
 // ============================================== attention over the cache
+// LDS DMA of one K tile and one row-major V tile (KB bytes each) of cache
+// rows; this wave fills 1 KB blocks wave*NDMA .. +NDMA-1 of each.
+template <int NDMA, int KB>
+__device__ __forceinline__ void kv_rows_dma(char* stage, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                            const int* koff, const int* voff, int soff, int wave) {
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) {
+    const int b = wave * NDMA + j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(stage + b * 1024), 16, koff[j], soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(stage + KB + b * 1024), 16, voff[j], soff, 0, 0);
+  }
+}
+
+// Question prefill over a composed cache, split-K over the keys.  A
+// workgroup owns (request, KV head, key chunk, group of 4 units); a unit is
+// 32 question rows of one query head.  K and V tiles of 64 keys come from
+// the cache by LDS DMA (double buffered, rows past the chunk read as zeros)
+// and feed the same tile code as extraction; V stays row-major and its
+// transposed operand is read with ds_read_b64_tr_b16.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, (kMinWaves<T, D>)) void cache_attn_kernel(const CacheParams p) {
-  using S = Smem<T, D>;
-  __shared__ __attribute__((aligned(16))) T smem[2 * S::kStage];
+__global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void cache_attn_kernel(const CacheParams p) {
+  using X = XTile<T, D>;
+  constexpr int RB = X::RB, CPR = X::CPR, KB = X::KBYTES;     // V tile is KB bytes too
+  constexpr int NDMA = KB / 1024 / kWaves;                    // per wave, per tensor
+  __shared__ __attribute__((aligned(1024))) char stage0[2 * KB];
+  __shared__ __attribute__((aligned(1024))) char stage1[2 * KB];
+  asm volatile("" : : "r"(stage0), "r"(stage1) : "memory");
   const int L = xcd_logical(blockIdx.x, p.grid_wg);
   if (L >= p.total_wg) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -733,12 +605,26 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<T, D>)) void cache_attn_kernel
   const int t0 = blk * kQW, t1 = wvalid ? min(p.tq, t0 + kQW) : 0;
   const int Lr = rq.cache_len + p.tq;
   const int ks0 = split * p.chunk, ks1 = min(Lr, ks0 + p.chunk);
-  constexpr int stride = D;
   const int64_t head_base = ((int64_t)r * p.hkv + kvh) * p.cap;
-  const T* kbase = reinterpret_cast<const T*>(p.kc) + (head_base + ks0) * D;
-  const T* vbase = reinterpret_cast<const T*>(p.vc) + (head_base + ks0) * D;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(p.kc) + head_base * RB), 0, ks1 * RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(p.vc) + head_base * RB), 0, ks1 * RB, 0x00020000);
+  int koff[NDMA], voff[NDMA];
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) {
+    const int byte = (wave * NDMA + j) * 1024 + lane * 16;
+    const int row = byte / RB, pc = (byte % RB) / 16;
+    koff[j] = row * RB + ((pc ^ k_swz<CPR>(row)) << 4);
+    voff[j] = row * RB + ((pc ^ (2 * vr_swz<RB>(row))) << 4);
+  }
+  auto issue = [&](int it, char* stage) {
+    kv_rows_dma<NDMA, KB>(stage, krs, vrs, koff, voff, (ks0 + it * kBN) * RB, wave);
+  };
+  const int ntiles = (ks1 - ks0 + kBN - 1) / kBN;
+  if (ntiles > 0) issue(0, stage0);
 
-  WaveAttn<T, D> W;
+  XAttn<T, D> W;
   W.init();
   {
     const int r16 = lane & 15, g = lane >> 4;
@@ -746,67 +632,64 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<T, D>)) void cache_attn_kernel
     for (int qb = 0; qb < 2; ++qb) {
       const int t = t0 + 16 * qb + r16;
       const bool ok = wvalid && t < t1;
-      const T* qrow = reinterpret_cast<const T*>(p.qrot) + (((int64_t)r * p.tq + t) * p.hq + head) * D;
+      const T* qrow = reinterpret_cast<const T*>(p.qrot) + (((int64_t)r * p.tq + (ok ? t : 0)) * p.hq + head) * D;
 #pragma unroll
       for (int k = 0; k < D / 32; ++k) {
         float x[8];
-        if (ok) load8_f32<T>(qrow + 32 * k + 8 * g, x);
-        else {
+        load8_f32<T>(qrow + 32 * k + 8 * g, x);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) W.qB[qb][k][e] = from_f32<T>(x[e]);
+        for (int e = 0; e < 8; ++e) W.qB[qb][k][e] = from_f32<T>(ok ? x[e] : 0.f);
       }
     }
   }
-  const int ntiles = (ks1 - ks0 + kBN - 1) / kBN;
-  KVStage<T, D> ld;
   const Pred pred = pred_causal(ks1, rq.cache_len);
-  if (ntiles > 0) ld.load(kbase, vbase, stride, min(kBN, ks1 - ks0), tid);
-  for (int it = 0; it < ntiles; ++it) {
-    T* ks = smem + (it & 1) * S::kStage;
-    T* vt = ks + S::kKElems;
-    ld.store(ks, vt, tid);
-    __syncthreads();
-    if (it + 1 < ntiles) {
-      const int k0 = (it + 1) * kBN;
-      ld.load(kbase + (int64_t)k0 * stride, vbase + (int64_t)k0 * stride, stride, min(kBN, ks1 - ks0 - k0), tid);
-    }
+  auto compute = [&](int it, const char* stage) {
     const int key0 = ks0 + it * kBN;
-    const bool active = wvalid && key0 < rq.cache_len + t1;
-    if (active) {
-      const bool masked = (key0 + kBN > rq.cache_len + t0 + 1) || (key0 + kBN > ks1);
-      if (masked) W.template tile<true>(ks, vt, lane, p.scale_log2, pred, t0, key0);
-      else W.template tile<false>(ks, vt, lane, p.scale_log2, pred, t0, key0);
-    }
+    if (!(wvalid && key0 < rq.cache_len + t1)) return;
+    if ((key0 + kBN - 1 > rq.cache_len + t0) || (key0 + kBN > ks1))
+      W.template tile<true, true>(stage, lane, p.scale_log2, pred, t0, key0);
+    else
+      W.template tile<false, true>(stage, lane, p.scale_log2, pred, t0, key0);
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 < ntiles) issue(it + 1, stage1);
+    compute(it, stage0);
+    if (it + 1 >= ntiles) break;
+    wait_vmem();
+    __syncthreads();
+    if (it + 2 < ntiles) issue(it + 2, stage0);
+    compute(it + 1, stage1);
   }
 
-  // ---- final rows (one key chunk) or split partials [o(D) | m | l | pad]
+  // ---- final rows (one key chunk) or split partials [o(D) | m | l | pad],
+  // m in log2 units
   if (!wvalid) return;
   const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lt = wave_sum_16_32(W.l[qb]);
+    const float m2 = W.m[qb] * p.scale_log2;
     const int t = t0 + 16 * qb + r16;
     if (t >= t1) continue;
     if (rq.nsplit == 1) {
       const float inv = 1.f / lt;
       T* orow = reinterpret_cast<T*>(p.o) + (((int64_t)r * p.tq + t) * p.hq + head) * D;
 #pragma unroll
-      for (int db = 0; db < WaveAttn<T, D>::DB; ++db) {
+      for (int db = 0; db < XAttn<T, D>::DB; ++db) {
         typename ElemTraits<T>::v4 outv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) outv[i] = from_f32<T>(W.o[db][qb][i] * inv);
         *reinterpret_cast<typename ElemTraits<T>::v4*>(orow + 16 * db + 4 * g) = outv;
       }
       if (g == 0 && p.lse)
-        p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (W.m[qb] + __log2f(lt)) * 0.69314718055994531f;
+        p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (m2 + __log2f(lt)) * 0.69314718055994531f;
     } else {
       float* prow = p.part + ((((int64_t)ri * p.hq + head) * p.tq + t) * p.nsplit_stride + split) * (D + 4);
-      if (g == 0) { prow[D] = W.m[qb]; prow[D + 1] = lt; }
+      if (g == 0) { prow[D] = W.m[qb] == -INFINITY ? -INFINITY : m2; prow[D + 1] = lt; }
 #pragma unroll
-      for (int db = 0; db < WaveAttn<T, D>::DB; ++db)
+      for (int db = 0; db < XAttn<T, D>::DB; ++db)
         *reinterpret_cast<f32x4*>(prow + 16 * db + 4 * g) = W.o[db][qb];
     }
   }

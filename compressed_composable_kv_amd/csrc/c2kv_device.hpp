@@ -21,7 +21,6 @@ constexpr int kBN = 64;        // keys per K/V tile
 constexpr int kQW = 32;        // query rows per wave (two 16-row MFMA blocks)
 constexpr int kWaves = 4;      // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kVPad = 8;       // elements of padding per V^T row in LDS
 constexpr int kMaxHalfDim = 64;
 
 template <typename T> struct ElemTraits;
