@@ -74,16 +74,13 @@ float scale_log2(int head_dim) {
 int32_t num_slots_i(int32_t n, int32_t k) { return (n + k - 1) / k; }
 
 // ------------------------------------------------------------- extraction
-// Workspace: rotated keys [rows][hkv][D], transposed values [hkv][D][vt_cols]
-// (each document's tokens and slots start at 64-aligned columns), and the
-// RoPE cos/sin table [max_n][D/2].
+// Workspace: rotated keys [rows][hkv][D] and the RoPE cos/sin table
+// [max_n][D/2].  Values are read in place.
 struct ExtractLayout {
-  int64_t rows = 0, vt_cols = 0;
+  int64_t rows = 0;
   int32_t max_n = 0;
-  size_t krot_off = 0, vt_off = 0, table_off = 0, total = 0;
+  size_t krot_off = 0, table_off = 0, total = 0;
 };
-
-int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 
 c2kv_status extract_layout(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t hkv,
                            int32_t head_dim, c2kv_dtype dt, ExtractLayout& L) {
@@ -92,36 +89,31 @@ c2kv_status extract_layout(const int32_t* doc_lens, int32_t num_docs, int32_t ra
   if (ratio_k < 1) return fail(C2KV_ERR_INVALID_ARG, "ratio_k=%d must be >= 1", ratio_k);
   const int64_t rb = (int64_t)head_dim * elem_bytes(dt);
   L.rows = 0;
-  L.vt_cols = 0;
   L.max_n = 0;
   for (int32_t b = 0; b < num_docs; ++b) {
     const int32_t n = doc_lens[b];
     if (n < 1) return fail(C2KV_ERR_INVALID_ARG, "doc_lens[%d]=%d must be >= 1", b, n);
     if (n > (1 << 24)) return fail(C2KV_ERR_CAPACITY, "doc_lens[%d]=%d exceeds 2^24 positions", b, n);
     const int64_t m = num_slots_i(n, ratio_k);
-    if ((n + m) * hkv * rb >= ((int64_t)1 << 31))
+    // a document's rows (plus one 64-key tile) are addressed with 32-bit offsets
+    if ((n + m + 64) * hkv * rb >= ((int64_t)1 << 31))
       return fail(C2KV_ERR_CAPACITY, "document %d: %lld rows x %d KV heads exceed the 2 GiB tile window", b,
                   (long long)(n + m), hkv);
     L.rows += n + m;
-    L.vt_cols += round64(n) + round64(m);
     L.max_n = std::max(L.max_n, n);
   }
   if (L.rows >= ((int64_t)1 << 31)) return fail(C2KV_ERR_CAPACITY, "%lld packed rows exceed 2^31-1", (long long)L.rows);
-  if (L.vt_cols * head_dim * (int64_t)elem_bytes(dt) >= ((int64_t)1 << 31))
-    return fail(C2KV_ERR_CAPACITY, "the batch's transposed values exceed 2 GiB per KV head; split the batch");
   L.krot_off = 0;
-  L.vt_off = align_up((size_t)L.rows * hkv * head_dim * elem_bytes(dt));
-  L.table_off = L.vt_off + align_up((size_t)hkv * head_dim * L.vt_cols * elem_bytes(dt));
+  L.table_off = align_up((size_t)L.rows * hkv * head_dim * elem_bytes(dt));
   L.total = L.table_off + align_up((size_t)L.max_n * (head_dim / 2) * sizeof(float2));
   return C2KV_OK;
 }
 
 // Fill the per-launch document tables; returns the number of docs consumed.
 int fill_extract_chunk(const int32_t* doc_lens, int32_t first, int32_t num_docs, int32_t ratio_k,
-                       int32_t G, int32_t hkv, int64_t row0, int64_t vcol0, ExtractParams& p, RotateParams& rp,
-                       int64_t* vcol_end) {
+                       int32_t G, int32_t hkv, int64_t row0, ExtractParams& p, RotateParams& rp) {
   const int cnt = std::min<int>(C2KV_MAX_BATCH, num_docs - first);
-  int64_t wg = 0, row = row0, vcol = vcol0, tiles = 0;
+  int64_t wg = 0, row = row0;
   for (int i = 0; i < cnt; ++i) {
     const int32_t n = doc_lens[first + i];
     const int32_t m = num_slots_i(n, ratio_k);
@@ -132,19 +124,12 @@ int fill_extract_chunk(const int32_t* doc_lens, int32_t first, int32_t num_docs,
     d.wg0 = (int32_t)wg;
     d.nwg_doc = (int32_t)ceil_div(ceil_div(n, kQW) * G, kWaves);
     d.nwg_slot = (int32_t)ceil_div(ceil_div(m, kQW) * G, kWaves);
-    d.vt_doc = (int32_t)vcol;
-    d.vt_slot = (int32_t)(vcol + round64(n));
     d.pad = 0;
     wg += (int64_t)hkv * (d.nwg_doc + d.nwg_slot);
     rp.docs[i].row0 = row;
     rp.docs[i].n = n;
     rp.docs[i].m = m;
-    rp.docs[i].tile0 = (int32_t)tiles;
-    rp.docs[i].vt_doc = d.vt_doc;
-    rp.docs[i].vt_slot = d.vt_slot;
-    tiles += ceil_div(n, 64) + ceil_div(m, 64);
     row += n + m;
-    vcol += round64(n) + round64(m);
   }
   p.num_docs = cnt;
   p.total_wg = (int32_t)wg;
@@ -152,8 +137,6 @@ int fill_extract_chunk(const int32_t* doc_lens, int32_t first, int32_t num_docs,
   rp.num_docs = cnt;
   rp.row_begin = row0;
   rp.row_end = row;
-  rp.total_tiles = (int32_t)tiles;
-  *vcol_end = vcol;
   return cnt;
 }
 
@@ -400,25 +383,20 @@ c2kv_status c2kv_extract_attn(const void* q, const void* k, const void* v, void*
   RotateParams rp;
   std::memset(&p, 0, sizeof(p));
   std::memset(&rp, 0, sizeof(rp));
-  p.q = q; p.krot = ws + L.krot_off; p.vt = ws + L.vt_off; p.o = o; p.lse = lse; p.rope = table;
+  p.q = q; p.krot = ws + L.krot_off; p.v = v; p.o = o; p.lse = lse; p.rope = table;
   p.total_rows = L.rows;
-  p.vt_cols = (int32_t)L.vt_cols;
   p.hq = hq; p.hkv = hkv; p.G = hq / hkv; p.ratio_k = ratio_k; p.sink_len = sink_len;
   p.scale_log2 = scale_log2(head_dim);
-  rp.k = k; rp.krot = ws + L.krot_off; rp.v = v; rp.vt = ws + L.vt_off; rp.rope = table;
-  rp.hkv = hkv; rp.ratio_k = ratio_k; rp.vt_cols = (int32_t)L.vt_cols;
-  int64_t row = 0, vcol = 0;
+  rp.k = k; rp.krot = ws + L.krot_off; rp.rope = table;
+  rp.hkv = hkv; rp.ratio_k = ratio_k;
+  int64_t row = 0;
   for (int32_t b = 0; b < num_docs;) {
-    int64_t vcol_end = 0;
-    const int cnt = fill_extract_chunk(doc_lens, b, num_docs, ratio_k, p.G, hkv, row, vcol, p, rp, &vcol_end);
+    const int cnt = fill_extract_chunk(doc_lens, b, num_docs, ratio_k, p.G, hkv, row, p, rp);
     e = launch_rotate_k(rp, dt, head_dim, stream);
     if (e != hipSuccess) return hip_fail(e, "key rotation kernel launch");
-    e = launch_transpose_v(rp, dt, head_dim, stream);
-    if (e != hipSuccess) return hip_fail(e, "value transpose kernel launch");
     e = launch_extract_attn(p, dt, head_dim, false, stream);
     if (e != hipSuccess) return hip_fail(e, "extraction attention kernel launch");
     row = rp.row_end;
-    vcol = vcol_end;
     b += cnt;
   }
   return ok();
@@ -578,11 +556,9 @@ c2kv_status c2kv_mask_cells(const int32_t* doc_lens, int32_t num_docs, int32_t r
   std::memset(&rp, 0, sizeof(rp));
   p.hq = 1; p.hkv = 1; p.G = 1; p.ratio_k = ratio_k; p.sink_len = sink_len; p.counts = counts;
   p.total_rows = L.rows;
-  int64_t row = 0, vcol = 0;
+  int64_t row = 0;
   for (int32_t b = 0; b < num_docs;) {
-    int64_t vcol_end = 0;
-    const int cnt = fill_extract_chunk(doc_lens, b, num_docs, ratio_k, 1, 1, row, vcol, p, rp, &vcol_end);
-    vcol = vcol_end;
+    const int cnt = fill_extract_chunk(doc_lens, b, num_docs, ratio_k, 1, 1, row, p, rp);
     e = launch_extract_attn(p, C2KV_F32, 64, true, stream);
     if (e != hipSuccess) return hip_fail(e, "mask count kernel launch");
     row = rp.row_end;

@@ -158,102 +158,7 @@ __device__ __forceinline__ TileSel extract_tile(const ExtractPlan& P, int it) {
   return s;
 }
 
-// ------------------------------------------------ extraction tile layout
-// A stage holds one 64-key tile: K [64 keys][D] and V^T [D][64 keys], both
-// filled by buffer_load ... lds (16 bytes per lane, consecutive lanes to
-// consecutive LDS slots) from the rotated-K and transposed-V workspaces.
-// Bank conflicts are avoided by XOR-swizzling 16-byte chunks: a lane that
-// fills LDS slot (row, pc) loads logical chunk pc ^ swz(row).
-//
-// S^T blocks use a permuted key order: in block kb, MFMA row r reads key
-// 32(kb/2) + 8(r/4) + 4(kb%2) + r%4.  Then a lane's 8 scores of a 32-key
-// half are 8 consecutive keys, which is exactly one 16-byte V^T read for the
-// A operand of O^T += V^T P^T.
-template <typename T, int D>
-struct XTile {
-  static constexpr int ES = sizeof(T);
-  static constexpr int RB = D * ES;            // bytes of one K row
-  static constexpr int CPR = RB / 16;          // 16-byte chunks per K row
-  static constexpr int KBYTES = kBN * RB;
-  static constexpr int VB = kBN * ES;          // bytes of one V^T row
-  static constexpr int VC = VB / 16;
-  static constexpr int VBYTES = D * VB;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KBLK = KBYTES / 1024;   // 1 KB DMA blocks per stage
-  static constexpr int VBLK = VBYTES / 1024;
-  static_assert(KBLK % kWaves == 0 && VBLK % kWaves == 0, "DMA blocks must split over the waves");
-};
-
-template <int CPR>
-__device__ __forceinline__ int k_swz(int row) { return ((row & 3) | (((row >> 3) & 3) << 2)) & (CPR - 1); }
-template <int VC>
-__device__ __forceinline__ int vt_swz(int d) { return VC == 8 ? ((d >> 1) & 7) : (d & (VC - 1)); }
-
-__device__ __forceinline__ int s_key_row(int kb, int r) {
-  return 32 * (kb >> 1) + 8 * (r >> 2) + 4 * (kb & 1) + (r & 3);
-}
-
-// Wait for this wave's outstanding vector-memory operations (the LDS DMA).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Per-lane part of the DMA byte offsets (loop invariant); the tile's own
-// offset is wave-uniform and goes into the instructions' SGPR offset.
-template <typename T, int D>
-struct DmaLanes {
-  using X = XTile<T, D>;
-  int k[X::KBLK / kWaves];
-  int v[X::VBLK / kWaves];
-  __device__ __forceinline__ void init(int hkv, int vt_cols, int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < X::KBLK / kWaves; ++j) {
-      const int byte = (wave * (X::KBLK / kWaves) + j) * 1024 + lane * 16;
-      const int row = byte / X::RB, pc = (byte % X::RB) / 16;
-      k[j] = row * hkv * X::RB + (pc ^ k_swz<X::CPR>(row)) * 16;
-    }
-#pragma unroll
-    for (int j = 0; j < X::VBLK / kWaves; ++j) {
-      const int byte = (wave * (X::VBLK / kWaves) + j) * 1024 + lane * 16;
-      const int d = byte / X::VB, pc = (byte % X::VB) / 16;
-      v[j] = d * vt_cols * X::ES + (pc ^ vt_swz<X::VC>(d)) * 16;
-    }
-  }
-};
-
-template <typename T, int D>
-__device__ __forceinline__ void dma_tile(char* stage, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                         const DmaLanes<T, D>& ln, int ksoff, int vsoff, int wave) {
-  using X = XTile<T, D>;
-#pragma unroll
-  for (int j = 0; j < X::KBLK / kWaves; ++j) {
-    const int b = wave * (X::KBLK / kWaves) + j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(stage + b * 1024), 16, ln.k[j], ksoff, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < X::VBLK / kWaves; ++j) {
-    const int b = wave * (X::VBLK / kWaves) + j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(stage + X::KBYTES + b * 1024), 16, ln.v[j], vsoff, 0, 0);
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ typename ElemTraits<T>::v8 lds_v8(const char* base, int chunk0, int swz, int nchunks);
-template <>
-__device__ __forceinline__ bf16x8 lds_v8<bf16>(const char* base, int chunk0, int swz, int nchunks) {
-  return *reinterpret_cast<const bf16x8*>(base + ((chunk0 ^ swz) & (nchunks - 1)) * 16);
-}
-template <>
-__device__ __forceinline__ f32x8 lds_v8<float>(const char* base, int chunk0, int swz, int nchunks) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(base + ((chunk0 ^ swz) & (nchunks - 1)) * 16);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(base + (((chunk0 + 1) ^ swz) & (nchunks - 1)) * 16);
-  f32x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { r[e] = a[e]; r[4 + e] = b[e]; }
-  return r;
-}
-
-// ------------------------------------------ row-major V tiles (prefill)
+// ------------------------------------------------- row-major V tiles
 // A V tile of 64 keys x D, row-major, filled by LDS DMA.  32-byte pairs of
 // a row are XOR-swizzled with vr_swz(row) so that the transposed operand
 // reads of a half wave (8 rows x 32 bytes) hit distinct banks.
@@ -296,6 +201,95 @@ __device__ __forceinline__ typename ElemTraits<T>::v8 vrow_operand(const char* v
   }
 }
 
+// ------------------------------------------------------- tile layout
+// A stage holds one 64-key tile: K [64 keys][D] and V [64 keys][D], both
+// row-major and filled by buffer_load ... lds (16 bytes per lane,
+// consecutive lanes to consecutive LDS slots).  Bank conflicts are avoided
+// by XOR-swizzling: a lane that fills K slot (row, pc) loads logical chunk
+// pc ^ k_swz(row); V rows swizzle 32-byte pairs with vr_swz(row).
+//
+// S^T blocks use a permuted key order: in block kb, MFMA row r reads key
+// 32(kb/2) + 8(r/4) + 4(kb%2) + r%4.  Then a lane's 8 scores of a 32-key
+// half are 8 consecutive keys, the k-order of the V^T operand read
+// transposed from the V rows for O^T += V^T P^T.
+template <typename T, int D>
+struct XTile {
+  static constexpr int ES = sizeof(T);
+  static constexpr int RB = D * ES;            // bytes of one K or V row
+  static constexpr int CPR = RB / 16;          // 16-byte chunks per row
+  static constexpr int KBYTES = kBN * RB;      // one K (or V) tile
+  static constexpr int STAGE = 2 * KBYTES;
+  static constexpr int KBLK = KBYTES / 1024;   // 1 KB DMA blocks per tile
+  static_assert(KBLK % kWaves == 0, "DMA blocks must split over the waves");
+};
+
+template <int CPR>
+__device__ __forceinline__ int k_swz(int row) { return ((row & 3) | (((row >> 3) & 3) << 2)) & (CPR - 1); }
+
+__device__ __forceinline__ int s_key_row(int kb, int r) {
+  return 32 * (kb >> 1) + 8 * (r >> 2) + 4 * (kb & 1) + (r & 3);
+}
+
+// Wait for this wave's outstanding vector-memory operations (the LDS DMA).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Per-lane part of the DMA byte offsets (loop invariant); the tile's own
+// offset is wave-uniform and goes into the instructions' SGPR offset.
+template <typename T, int D>
+struct DmaLanes {
+  using X = XTile<T, D>;
+  int k[X::KBLK / kWaves];
+  int v[X::KBLK / kWaves];
+  __device__ __forceinline__ void init(int hkv, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < X::KBLK / kWaves; ++j) {
+      const int byte = (wave * (X::KBLK / kWaves) + j) * 1024 + lane * 16;
+      const int row = byte / X::RB, pc = (byte % X::RB) / 16;
+      k[j] = row * hkv * X::RB + (pc ^ k_swz<X::CPR>(row)) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < X::KBLK / kWaves; ++j) {
+      const int byte = (wave * (X::KBLK / kWaves) + j) * 1024 + lane * 16;
+      const int row = byte / X::RB, pc = (byte % X::RB) / 16;
+      v[j] = row * hkv * X::RB + ((pc ^ (2 * vr_swz<X::RB>(row))) << 4);
+    }
+  }
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void dma_tile(char* stage, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                         const DmaLanes<T, D>& ln, int ksoff, int vsoff, int wave) {
+  using X = XTile<T, D>;
+#pragma unroll
+  for (int j = 0; j < X::KBLK / kWaves; ++j) {
+    const int b = wave * (X::KBLK / kWaves) + j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(stage + b * 1024), 16, ln.k[j], ksoff, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < X::KBLK / kWaves; ++j) {
+    const int b = wave * (X::KBLK / kWaves) + j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(stage + X::KBYTES + b * 1024), 16, ln.v[j], vsoff, 0, 0);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ typename ElemTraits<T>::v8 lds_v8(const char* base, int chunk0, int swz, int nchunks);
+template <>
+__device__ __forceinline__ bf16x8 lds_v8<bf16>(const char* base, int chunk0, int swz, int nchunks) {
+  return *reinterpret_cast<const bf16x8*>(base + ((chunk0 ^ swz) & (nchunks - 1)) * 16);
+}
+template <>
+__device__ __forceinline__ f32x8 lds_v8<float>(const char* base, int chunk0, int swz, int nchunks) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(base + ((chunk0 ^ swz) & (nchunks - 1)) * 16);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(base + (((chunk0 + 1) ^ swz) & (nchunks - 1)) * 16);
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { r[e] = a[e]; r[4 + e] = b[e]; }
+  return r;
+}
+
 // Reference-max slack of the online softmax, in log2 units (see tile()).
 constexpr float kLazyLog2 = 8.f;
 
@@ -318,9 +312,7 @@ struct XAttn {
     l[0] = l[1] = 0.f;
   }
 
-  // kVRow: the stage holds V row-major ([64 keys][D], pair-swizzled) instead
-  // of V^T, and the V^T operand is read transposed from it.
-  template <bool kMasked, bool kVRow = false>
+  template <bool kMasked>
   __device__ __forceinline__ void tile(const char* stage, int lane, float sl2, const Pred& pred, int q0, int key0) {
     const int r16 = lane & 15, g = lane >> 4;
     const char* ks = stage;
@@ -392,10 +384,7 @@ struct XAttn {
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d = 16 * db + r16;
-        V8 a;
-        if constexpr (kVRow) a = vrow_operand<T, D>(vt, c, db, r16, g);
-        else a = lds_v8<T>(vt + d * X::VB, (4 * c + g) * CPE, vt_swz<X::VC>(d), X::VC);
+        const V8 a = vrow_operand<T, D>(vt, c, db, r16, g);
         o[db][0] = mma16(a, pB[c][0], o[db][0]);
         o[db][1] = mma16(a, pB[c][1], o[db][1]);
       }
@@ -418,25 +407,23 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void extract_attn_ker
   if (L >= p.total_wg) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const ExtractPlan P = extract_plan(p, L, wave);
-  const ExtractDoc& dc = p.docs[P.doc];
   const int hq = p.hq, hkv = p.hkv;
   const int64_t qrow_off = P.slot_region ? P.n : 0;
-  // buffer resources: this document's rotated keys of KV head kvh, and the
-  // V^T rows of kvh; reads past the end return zeros
+  // buffer resources: this document's rotated keys and its values, KV head
+  // kvh; reads past the document's rows return zeros
   const int64_t doc_rows = (int64_t)P.n + P.m;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(reinterpret_cast<const char*>(p.krot) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
       (int)(doc_rows * hkv * X::RB), 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const char*>(p.vt) + (int64_t)P.kvh * D * p.vt_cols * X::ES), 0,
-      (int)((int64_t)D * p.vt_cols * X::ES), 0x00020000);
+      (void*)(reinterpret_cast<const char*>(p.v) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
+      (int)(doc_rows * hkv * X::RB), 0x00020000);
   DmaLanes<T, D> lanes;
-  lanes.init(hkv, p.vt_cols, wave, lane);
+  lanes.init(hkv, wave, lane);
   auto issue = [&](int it, char* stage) {
     const TileSel ts = extract_tile(P, it);
     const int krow0 = (ts.is_slot ? P.n : 0) + ts.key0;
-    const int vcol0 = (ts.is_slot ? dc.vt_slot : dc.vt_doc) + ts.key0;
-    dma_tile<T, D>(stage, krs, vrs, lanes, krow0 * hkv * X::RB, vcol0 * X::ES, wave);
+    dma_tile<T, D>(stage, krs, vrs, lanes, krow0 * hkv * X::RB, krow0 * hkv * X::RB, wave);
   };
   const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
   if (ntiles > 0) issue(0, stage0);
@@ -647,9 +634,9 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void cache_attn_kerne
     const int key0 = ks0 + it * kBN;
     if (!(wvalid && key0 < rq.cache_len + t1)) return;
     if ((key0 + kBN - 1 > rq.cache_len + t0) || (key0 + kBN > ks1))
-      W.template tile<true, true>(stage, lane, p.scale_log2, pred, t0, key0);
+      W.template tile<true>(stage, lane, p.scale_log2, pred, t0, key0);
     else
-      W.template tile<false, true>(stage, lane, p.scale_log2, pred, t0, key0);
+      W.template tile<false>(stage, lane, p.scale_log2, pred, t0, key0);
   };
   for (int it = 0; it < ntiles; it += 2) {
     wait_vmem();

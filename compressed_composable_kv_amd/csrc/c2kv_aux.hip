@@ -128,62 +128,6 @@ hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipSt
   return head_dim == 128 ? launch_rotate_k_t<float, 128>(p, st) : launch_rotate_k_t<float, 64>(p, st);
 }
 
-// ---------------------------------------------------- extraction V^T
-// V of every KV head transposed to [hkv][D][vt_cols]: each document's
-// tokens start at a 64-aligned column, its slots at the next 64-aligned
-// column, so the extraction kernel copies V^T tiles (64 keys of one d) as
-// whole aligned rows.  Padding columns are written with zeros.  One
-// workgroup transposes 64 rows x D of one KV head through LDS.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void transpose_v_kernel(const RotateParams p) {
-  constexpr int CE = Chunk<T>::CE, CPR = D / CE;           // 16-byte chunks per V row
-  constexpr int RP = D + CE;                                // padded LDS row (elements)
-  __shared__ __attribute__((aligned(16))) T tile[64 * RP];
-  const int tix = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
-  if (tix >= p.total_tiles) return;
-  int b = 0;
-  while (b + 1 < p.num_docs && p.docs[b + 1].tile0 <= tix) ++b;
-  const RotDoc dc = p.docs[b];
-  const int lt = tix - dc.tile0;
-  const int tn = (dc.n + 63) / 64;
-  const bool slot = lt >= tn;
-  const int t = slot ? lt - tn : lt;
-  const int count = slot ? dc.m : dc.n;
-  const int64_t row_start = dc.row0 + (slot ? dc.n : 0) + 64 * t;
-  const int col0 = (slot ? dc.vt_slot : dc.vt_doc) + 64 * t;
-  const int valid = min(64, count - 64 * t);
-  for (int c = tid; c < 64 * CPR; c += 256) {
-    const int row = c / CPR, ch = c % CPR;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (row < valid)
-      x = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(p.v) + ((row_start + row) * p.hkv + kvh) * D + ch * CE);
-    *reinterpret_cast<uint4*>(tile + row * RP + ch * CE) = x;
-  }
-  __syncthreads();
-  // out: V^T row d, keys [8j, 8j+8) (bf16) / [4j, 4j+4) (fp32) as one 16-byte store
-  constexpr int OC = 64 / CE;                                // output chunks per V^T row
-  T* vt = reinterpret_cast<T*>(p.vt) + ((int64_t)kvh * D) * p.vt_cols + col0;
-  for (int c = tid; c < D * OC; c += 256) {
-    const int d = c / OC, j = c % OC;
-    T vals[CE];
-#pragma unroll
-    for (int e = 0; e < CE; ++e) vals[e] = tile[(j * CE + e) * RP + d];
-    *reinterpret_cast<uint4*>(vt + (int64_t)d * p.vt_cols + j * CE) = *reinterpret_cast<const uint4*>(vals);
-  }
-}
-
-template <typename T, int D>
-static hipError_t launch_transpose_v_t(const RotateParams& p, hipStream_t st) {
-  if (p.total_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((transpose_v_kernel<T, D>), dim3(p.total_tiles, p.hkv), dim3(256), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_v(const RotateParams& p, int dtype, int head_dim, hipStream_t st) {
-  if (dtype == C2KV_BF16) return head_dim == 128 ? launch_transpose_v_t<bf16, 128>(p, st) : launch_transpose_v_t<bf16, 64>(p, st);
-  return head_dim == 128 ? launch_transpose_v_t<float, 128>(p, st) : launch_transpose_v_t<float, 64>(p, st);
-}
-
 // ---------------------------------------------------------------- compose
 // Work unit = (row tile of ONE segment, group of two KV heads); a thread owns
 // one 16-byte chunk of the low half of a row (and the matching chunk of the

@@ -114,21 +114,18 @@ struct ExtractDoc {
   int32_t wg0;       // first logical workgroup of the document
   int32_t nwg_doc;   // workgroups per KV head over document rows
   int32_t nwg_slot;  // workgroups per KV head over slot rows
-  int32_t vt_doc;    // V^T column of the document's first token (multiple of 64)
-  int32_t vt_slot;   // V^T column of its first slot (multiple of 64)
   int32_t pad;
 };
 
 struct ExtractParams {
   const void* q;        // [rows][hq][D]   pre-RoPE
   const void* krot;     // [rows][hkv][D]  rotated keys (workspace)
-  const void* vt;       // [hkv][D][vt_cols] transposed values (workspace)
+  const void* v;        // [rows][hkv][D] values (input)
   void* o;              // [rows][hq][D]
   float* lse;           // [hq][rows] or null
   const float2* rope;   // [max_n][D/2] (cos, sin)
   uint64_t* counts;     // mask-count mode: 5 counters
   int64_t total_rows;
-  int32_t vt_cols;      // columns of each V^T row
   int32_t num_docs, hq, hkv, G, ratio_k, sink_len;
   int32_t total_wg, grid_wg;
   float scale_log2;

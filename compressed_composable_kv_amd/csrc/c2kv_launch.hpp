@@ -12,17 +12,13 @@ namespace c2kv {
 struct RotDoc {
   int64_t row0;
   int32_t n, m;
-  int32_t tile0;     // first 64-row transpose tile of the document
-  int32_t vt_doc, vt_slot, pad;
 };
 struct RotateParams {
   const void* k;
   void* krot;
-  const void* v;
-  void* vt;                     // [hkv][D][vt_cols]
   const float2* rope;
   int64_t row_begin, row_end;   // packed rows covered by this launch
-  int32_t num_docs, hkv, ratio_k, vt_cols, total_tiles, pad;
+  int32_t num_docs, hkv, ratio_k, pad;
   RotDoc docs[C2KV_MAX_BATCH];
 };
 
@@ -75,7 +71,6 @@ struct AppendParams {
 
 hipError_t launch_rope_table(float2* table, int npos, int head_dim, const RopeFreqs& f, hipStream_t st);
 hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipStream_t st);
-hipError_t launch_transpose_v(const RotateParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_extract_attn(const ExtractParams& p, int dtype, int head_dim, bool count, hipStream_t st);
 hipError_t launch_cache_attn(const CacheParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_decode_attn(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);

@@ -132,8 +132,10 @@ size_t c2kv_workspace_size_extract(const int32_t* doc_lens, int32_t num_docs,
  * The sink is the document's first min(sink_len, n) tokens; the pages fix
  * sink_len = ratio_k.  Query head h reads KV head h / (hq / hkv).  Scale is
  * 1/sqrt(head_dim).  Key/value tiles with no visible cell are never loaded.
+ * The workspace holds the rotated keys and the cos/sin table; q, k and v
+ * are read in place.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, CAPACITY (sum_T >= 2^31
- * rows), HIP. */
+ * rows, or one document's rows of all KV heads reach 2 GiB), HIP. */
 c2kv_status c2kv_extract_attn(const void* q, const void* k, const void* v,
                               void* o, float* lse,
                               const int32_t* doc_lens, int32_t num_docs,
