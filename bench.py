@@ -105,6 +105,20 @@ def summarize(dirs, out, cmd, calib_mib):
                  "group by kernel_name, counter_name")
             for kname, cname, v, n in c.execute(q).fetchall():
                 avg.setdefault(kname, {})[cname] = (v, n)
+        names = sorted({c for cs in avg.values() for c in cs})
+        if "FETCH_SIZE" not in names or "WRITE_SIZE" not in names:
+            lines.append("# rocprofv3 --pmc summary: counter values per dispatch, averaged over dispatches")
+            lines.append(f"# command: {cmd}")
+            for kname, cs in sorted(avg.items()):
+                if "c2kv" not in kname:
+                    continue
+                lines.append(f"{kname.split('(')[0][:80]}  (dispatches {max(v[1] for v in cs.values())})")
+                for cname in sorted(cs):
+                    lines.append(f"    {cname:32s} {cs[cname][0]:20.1f}")
+            with open(out, "w") as f:
+                f.write("\n".join(lines) + "\n")
+            print("\n".join(lines))
+            return
         calib = [k for k in avg if CALIB_KERNEL in k]
         if not calib:
             raise SystemExit("no calibration copy in the counter runs (use --calibration-copy-mib)")
