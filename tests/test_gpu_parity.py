@@ -335,3 +335,116 @@ def test_decode_sink_heavy(c2kv):
                                      rk, rv, qpos[r], theta, "bf16")
         assert_close(np32(o[r]), ro, "bf16", f"sink-heavy request {r}")
         assert_lse_close(np32(lse[r]), rl, "bf16", f"sink-heavy request {r}")
+
+
+# ------------------------------------------------------------- edge cases
+
+def test_decode_and_prefill_on_empty_cache(c2kv):
+    """cache_len = 0: the step sees only its own (new) rows."""
+    hq, hkv, d, dt, theta = 8, 2, 128, torch.bfloat16, 1e6
+    R, tq = 3, 5
+    ck = torch.zeros((R, hkv, tq + 1, d), dtype=dt)
+    cv = torch.zeros_like(ck)
+    q = W.normal((R, tq, hq, d), dt, 19, W.P_PREFILL)
+    kn = W.normal((R, tq, hkv, d), dt, 19, W.P_NEW_KV)
+    vn = W.normal((R, tq, hkv, d), dt, 19, W.P_NEW_KV, salt=1)
+    ckd, cvd = ck.to(DEV), cv.to(DEV)
+    o, lse = c2kv.attn_prefill(q.to(DEV), kn.to(DEV), vn.to(DEV), ckd, cvd, [0] * R, [0, 7, 100000], theta,
+                               return_lse=True)
+    empty = np.zeros((0, hkv, d), np.float32)
+    for r, p0 in enumerate([0, 7, 100000]):
+        ro, rl, _, _ = O.append_and_attend(q[r].float().numpy(), kn[r].float().numpy(), vn[r].float().numpy(),
+                                           empty, empty, p0, theta, "bf16")
+        assert_close(np32(o[r]), ro, "bf16", f"prefill request {r}")
+        assert_lse_close(np32(lse[r]), rl, "bf16", f"prefill request {r}")
+    # a single decode token over an empty cache: o = v_new exactly (up to bf16)
+    ck2 = torch.zeros((R, hkv, 1, d), dtype=dt, device=DEV)
+    cv2 = torch.zeros_like(ck2)
+    od, ld = c2kv.attn_decode(q[:, 0].to(DEV), kn[:, 0].to(DEV), vn[:, 0].to(DEV), ck2, cv2, [0] * R, [3] * R, theta,
+                              return_lse=True)
+    G = hq // hkv
+    for r in range(R):
+        ro, rl, _, _ = O.decode_step(q[r, 0].float().numpy(), kn[r, 0].float().numpy(), vn[r, 0].float().numpy(),
+                                     empty, empty, 3, theta, "bf16")
+        assert_close(np32(od[r]), ro, "bf16", f"decode request {r}")
+        for h in range(hq):
+            assert torch.equal(od[r, h].cpu(), vn[r, 0, h // G])
+
+
+def test_extract_more_documents_than_one_launch(c2kv):
+    """70 short documents (the kernel-argument table holds 64 per launch)."""
+    g = torch.Generator().manual_seed(21)
+    doc_lens = [int(x) for x in torch.randint(1, 90, (70,), generator=g)]
+    k, hq, hkv, d, dt = 4, 4, 2, 64, torch.bfloat16
+    q, kk, v = packed_inputs(20, doc_lens, k, hq, hkv, d, dt, c2kv)
+    o, lse = c2kv.extract_attn(q.to(DEV), kk.to(DEV), v.to(DEV), doc_lens, k, k, 5e5, return_lse=True)
+    ref = O.extract_attn(q.float().numpy(), kk.float().numpy(), v.float().numpy(), doc_lens, k, k, 5e5)
+    offs = O.doc_row_offsets(doc_lens, k)
+    og, lg = np32(o), np32(lse)
+    for b in range(len(doc_lens)):
+        ro, rl = ref[b]
+        assert_close(og[offs[b]:offs[b + 1]], ro, "bf16", f"doc {b}")
+        assert_lse_close(lg[:, offs[b]:offs[b + 1]], rl, "bf16", f"doc {b}")
+    got = c2kv.mask_cells(doc_lens, k, k)
+    tot = [sum(O.mask_cell_counts(n, k, k)[i] for n in doc_lens) for i in range(3)]
+    assert list(got[:3]) == tot and got[3] == 0
+
+
+@pytest.mark.parametrize("hq,hkv,d,dt", [(16, 1, 128, torch.bfloat16), (32, 2, 64, torch.bfloat16)])
+def test_decode_more_requests_than_one_launch(c2kv, hq, hkv, d, dt):
+    """70 requests (64 per launch), G up to 16, head_dim 64 in bf16."""
+    g = torch.Generator().manual_seed(22)
+    lens = [int(x) for x in torch.randint(0, 700, (70,), generator=g)]
+    R = len(lens)
+    cap = max(lens) + 1
+    ck = W.normal((R, hkv, cap, d), dt, 23, W.P_K)
+    cv = W.normal((R, hkv, cap, d), dt, 23, W.P_V)
+    q = W.normal((R, hq, d), dt, 23, W.P_DEC_Q)
+    kn = W.normal((R, hkv, d), dt, 23, W.P_NEW_KV)
+    vn = W.normal((R, hkv, d), dt, 23, W.P_NEW_KV, salt=1)
+    qpos = [3 * x + 11 for x in lens]
+    o, lse = c2kv.attn_decode(q.to(DEV), kn.to(DEV), vn.to(DEV), ck.to(DEV), cv.to(DEV), lens, qpos, 5e5,
+                              return_lse=True)
+    og, lg = np32(o), np32(lse)
+    for r in range(R):
+        rk = ck[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        rv = cv[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        ro, rl, _, _ = O.decode_step(q[r].float().numpy(), kn[r].float().numpy(), vn[r].float().numpy(),
+                                     rk, rv, qpos[r], 5e5, dtname(dt))
+        assert_close(og[r], ro, dtname(dt), f"request {r}")
+        assert_lse_close(lg[r], rl, dtname(dt), f"request {r}")
+
+
+def test_prefill_more_requests_than_one_launch(c2kv):
+    hq, hkv, d, dt, tq = 8, 8, 64, torch.bfloat16, 3
+    g = torch.Generator().manual_seed(24)
+    lens = [int(x) for x in torch.randint(0, 300, (66,), generator=g)]
+    R = len(lens)
+    cap = max(lens) + tq
+    ck = W.normal((R, hkv, cap, d), dt, 25, W.P_K)
+    cv = W.normal((R, hkv, cap, d), dt, 25, W.P_V)
+    q = W.normal((R, tq, hq, d), dt, 25, W.P_PREFILL)
+    kn = W.normal((R, tq, hkv, d), dt, 25, W.P_NEW_KV)
+    vn = W.normal((R, tq, hkv, d), dt, 25, W.P_NEW_KV, salt=1)
+    qpos = [x + 1 for x in lens]
+    o, lse = c2kv.attn_prefill(q.to(DEV), kn.to(DEV), vn.to(DEV), ck.to(DEV), cv.to(DEV), lens, qpos, 1e4,
+                               return_lse=True)
+    og, lg = np32(o), np32(lse)
+    for r in range(R):
+        rk = ck[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        rv = cv[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        ro, rl, _, _ = O.append_and_attend(q[r].float().numpy(), kn[r].float().numpy(), vn[r].float().numpy(),
+                                           rk, rv, qpos[r], 1e4, "bf16")
+        assert_close(og[r], ro, "bf16", f"request {r}")
+        assert_lse_close(lg[r], rl, "bf16", f"request {r}")
+
+
+def test_compose_single_token_documents_and_k1(c2kv):
+    """Documents of one token (one slot at position offset + 0) and k = 1
+    (every token is a slot): degenerate compression ratios."""
+    for k in (4, 1):
+        pool_n = [1, 1, 2, 5, 1] if k == 4 else [3, 1, 7]
+        pool_k = [W.normal((O.num_slots(n, k), 2, 64), torch.bfloat16, 26, W.P_K, salt=i) for i, n in enumerate(pool_n)]
+        pool_v = [W.normal((O.num_slots(n, k), 2, 64), torch.bfloat16, 26, W.P_V, salt=i) for i, n in enumerate(pool_n)]
+        reqs = [list(range(len(pool_n))), list(range(len(pool_n)))[::-1]]
+        _compose_check(c2kv, reqs, pool_k, pool_v, pool_n, k, 5e5, torch.bfloat16, pos_base=[0, 9], cap_extra=2)
