@@ -38,8 +38,7 @@
  *   the same time must not share a workspace.
  * - workspace: device memory, 256-byte aligned, of at least the size the
  *   matching c2kv_workspace_size_* function returns for the same arguments.
- *   Its contents on entry are ignored (prefill/decode zero their own split-K
- *   arrival counters in their first kernel) and are undefined on return.
+ *   Its contents on entry are ignored and are undefined on return.
  * - Per-call tables (documents, requests) are passed to the GPU as kernel
  *   arguments in chunks of at most C2KV_MAX_BATCH entries per launch, so
  *   extract/prefill/decode perform no host-to-device copies and may be
