@@ -223,8 +223,10 @@ template <typename T, int D>
 static hipError_t launch_compose_t(const ComposeParams& p, hipStream_t st) {
   const int units = p.total_tiles * ((p.hkv + kComposeHPT - 1) / kComposeHPT);
   if (units == 0) return hipSuccess;
-  // about two units per workgroup, at most four workgroups per CU
-  const int blocks = units < 2048 ? (units + 1) / 2 : min(units, 1024);
+  // three workgroups per CU (12 waves) is the measured optimum for 1k-2k
+  // units: fewer leaves HBM idle, more adds dispatch without more bytes
+  // in flight (the loop already prefetches one unit ahead)
+  const int blocks = min(units, 3 * 256);
   hipLaunchKernelGGL((compose_kernel<T, D>), dim3(blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
