@@ -426,40 +426,54 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void extract_attn_ker
     dma_tile<T, D>(stage, krs, vrs, lanes, krow0 * hkv * X::RB, krow0 * hkv * X::RB, wave);
   };
   const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
-  if (ntiles > 0) issue(0, stage0);
 
   XAttn<T, D> W;
   W.init();
-  // ---- queries: load, rotate at the extraction positions, keep as B operand
+  // ---- queries: load, rotate at the extraction positions, keep as B operand.
+  // Every query and cos/sin load is issued before the first tile's DMA, and
+  // unconditionally (a row outside the wave's range reads the wave's first
+  // row, or the region's row 0, and is zeroed afterwards): the vector-memory
+  // counter retires in order, so one wait then covers all of them while the
+  // tile is still in flight.
   {
+    constexpr int H = D / 2, QK = D / 64;
     const int r16 = lane & 15, g = lane >> 4;
-    constexpr int H = D / 2;
+    float lo[2][QK][8], hi[2][QK][8];
+    f32x4 cs4[2][QK][4];
+    bool ok[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int ql = P.q0 + 16 * qb + r16;
-      const bool ok = P.wvalid && ql < P.qend;
-      const int pos = P.slot_region ? min(ql * P.ratio_k + P.ratio_k - 1, P.n - 1) : ql;
-      const T* qrow = reinterpret_cast<const T*>(p.q) + ((P.row0 + qrow_off + ql) * hq + P.head) * (int64_t)D;
+      ok[qb] = P.wvalid && ql < P.qend;
+      const int qc = ok[qb] ? ql : P.q0;
+      const int pos = P.slot_region ? min(qc * P.ratio_k + P.ratio_k - 1, P.n - 1) : qc;
+      const T* qrow = reinterpret_cast<const T*>(p.q) + ((P.row0 + qrow_off + qc) * hq + P.head) * (int64_t)D;
+      const f32x4* crow = reinterpret_cast<const f32x4*>(p.rope + (int64_t)pos * H);
 #pragma unroll
-      for (int k = 0; k < D / 64; ++k) {
-        float lo[8], hi[8];
-        if (ok) {
-          load8_f32<T>(qrow + 32 * k + 8 * g, lo);
-          load8_f32<T>(qrow + H + 32 * k + 8 * g, hi);
-        } else {
+      for (int k = 0; k < QK; ++k) {
+        load8_f32<T>(qrow + 32 * k + 8 * g, lo[qb][k]);
+        load8_f32<T>(qrow + H + 32 * k + 8 * g, hi[qb][k]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) lo[e] = hi[e] = 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float2 cs = ok ? p.rope[(int64_t)pos * H + 32 * k + 8 * g + e] : make_float2(1.f, 0.f);
-          float y0, y1;
-          rope_pair(lo[e], hi[e], cs.x, cs.y, y0, y1);
-          W.qB[qb][k][e] = from_f32<T>(y0);
-          W.qB[qb][k + D / 64][e] = from_f32<T>(y1);
-        }
+        for (int j = 0; j < 4; ++j) cs4[qb][k][j] = crow[16 * k + 4 * g + j];
       }
     }
+    // unconditional, so the wait below is not widened by a branch: a launched
+    // workgroup always has a tile (its wave 0 owns rows), and a DMA past the
+    // document's rows reads zeros through the buffer range check
+    issue(0, stage0);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int k = 0; k < QK; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const f32x4 c = cs4[qb][k][e >> 1];
+          const float cc = ok[qb] ? c[2 * (e & 1)] : 1.f, sn = ok[qb] ? c[2 * (e & 1) + 1] : 0.f;
+          float y0, y1;
+          rope_pair(ok[qb] ? lo[qb][k][e] : 0.f, ok[qb] ? hi[qb][k][e] : 0.f, cc, sn, y0, y1);
+          W.qB[qb][k][e] = from_f32<T>(y0);
+          W.qB[qb][k + QK][e] = from_f32<T>(y1);
+        }
   }
 
   auto compute = [&](int it, const char* stage) {
