@@ -20,7 +20,11 @@ Prints one JSON line.  Besides the step, it reports the decode rate with the
 256 steps spread over 16 replicas of the cache (a working set of about
 0.6 GB, above the 256 MB last-level cache), and, when a counter summary
 for the current decode sources is committed under profiles/, the HBM
-traffic the hardware counters measured for one decode call.
+traffic the hardware counters measured for one decode call.  It also
+measures, live, the rates this GPU sustains (dense bf16 MFMA from the probe
+library, HBM from a 1 GiB device copy) and reports each kernel against them
+as well as against the published peaks, and times compose from a graph of
+20 back-to-back calls.
 
 Decode sweep over the other decode workloads (one JSON line each, not the
 step): the Qwen2.5-7B pool (32 requests composed from 64 ragged documents
@@ -297,6 +301,43 @@ def decode_sweep():
             {"cache": "uncompressed comparator", "original_tokens": L})
 
 
+def achievable_peaks(torch, dev):
+    """Rates this GPU sustains, measured live: dense bf16 MFMA from the probe
+    library (independent MFMA chains on register operands, 4 waves per SIMD),
+    and HBM from a 1 GiB device-to-device copy (read + write bytes).  They
+    sit below the published peaks because the chip holds a lower clock under
+    sustained load than its nominal 2.4 GHz."""
+    import ctypes
+    from compressed_composable_kv_amd import build_lib
+    mfma = None
+    if os.path.exists(build_lib.PROBE_LIB):
+        lib = ctypes.CDLL(build_lib.PROBE_LIB)
+        lib.c2kv_probe_mfma_bf16.restype = ctypes.c_double
+        lib.c2kv_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+        ms = ctypes.c_float()
+        rates = [lib.c2kv_probe_mfma_bf16(512, 512, 4000, ctypes.byref(ms)) for _ in range(3)]
+        mfma = max(rates) if max(rates) > 0 else None
+    n = 1 << 29                                   # 1 GiB of bf16
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        best = t if best is None else min(best, t)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": mfma, "hbm_copy_gbs": 2 * 2 * n / (best * 1e-3) / 1e9,
+            "how": "MFMA: probe/mfma_peak.hip, 512 workgroups x 8 waves, 16 independent chains per wave; "
+                   "HBM: torch copy of 1 GiB, read + write bytes over the best of 3"}
+
+
 def main():
     a = parse()
     if a.summarize:
@@ -424,6 +465,24 @@ def main():
         cold_ms = e0.elapsed_time(e1) / 3
         del gcold, reps
         torch.cuda.empty_cache()
+    # compose on its own: 20 back-to-back calls from a graph, per-call time
+    # without the launch gap of a single eager call; not part of the step
+    gcomp = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gcomp):
+        for _ in range(20):
+            compose()
+    gcomp.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        gcomp.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    comp_graph_ms = e0.elapsed_time(e1) / 100
+    del gcomp
+    ach = achievable_peaks(torch, dev)
+
     ph = [0.0] * 4
     for e in evs:
         for j in range(4):
@@ -477,6 +536,11 @@ def main():
         "extraction_frac": ext_tflops / BF16_PEAK_TFLOPS,
         "phase_ms": {"extract": ph[0], "compose": ph[1], "prefill": ph[2], "decode_256": ph[3]},
         "compose_gbs": comp_gbs,
+        "compose_gbs_graph": comp_bytes / (comp_graph_ms * 1e-3) / 1e9,
+        "achievable": ach,
+        "extraction_frac_of_achievable": ext_tflops / ach["mfma_bf16_tflops"] if ach["mfma_bf16_tflops"] else None,
+        "decode_frac_of_achievable": dec_gbs / ach["hbm_copy_gbs"],
+        "compose_graph_frac_of_achievable": comp_bytes / (comp_graph_ms * 1e-3) / 1e9 / ach["hbm_copy_gbs"],
         "decode_gbs_cache_replicas": cold_gbs,
         "cache_replicas": a.cold_replicas,
         "prefill_tflops": pre_flops / (ph[2] * 1e-3) / 1e12,

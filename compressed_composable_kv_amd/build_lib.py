@@ -3,7 +3,9 @@
     python -m compressed_composable_kv_amd.build_lib [--jobs N]
 
 Compiles every source under csrc/ for --offload-arch=gfx950 and links the
-shared library next to this file.  Always rebuilds.
+shared library next to this file.  Also builds libc2kv_probe.so from probe/,
+a measurement tool the benchmark loads (the achievable MFMA rate); the
+library does not use it.  Always rebuilds.
 """
 from __future__ import annotations
 
@@ -21,6 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libc2kv.so")
+PROBE_SRC = os.path.join(PKG, "probe", "mfma_peak.hip")
+PROBE_LIB = os.path.join(PKG, "libc2kv_probe.so")
 
 SOURCES = ["c2kv_attn.hip", "c2kv_decode.hip", "c2kv_aux.hip", "c2kv_abi.cpp"]
 
@@ -71,7 +75,19 @@ def build(jobs: int = 4) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe() -> str:
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *[f for f in CFLAGS if not f.startswith("-I")], "-shared", "-o", tmp, PROBE_SRC,
+           "-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def main() -> None:
