@@ -34,6 +34,9 @@ the comparator), each a graph of decode calls over caches well above the
 last-level cache:
     python bench.py --decode-sweep
 
+One phase alone, for counter runs under rocprofv3:
+    python bench.py --profile-phase extract --calls 2
+
 Profiling helpers (no GPU work):
     python bench.py --summarize DIR [DIR2] --out FILE --cmd "COMMAND"
 summarises rocprofv3 output directories into a short text file: a
@@ -192,6 +195,9 @@ def parse():
     ap.add_argument("--calibration-copy-mib", type=int, default=0)
     ap.add_argument("--summarize", nargs="+", metavar="DIR")
     ap.add_argument("--decode-sweep", action="store_true")
+    ap.add_argument("--profile-phase", choices=("extract", "compose", "prefill", "decode"),
+                    help="run only this phase of the step --calls times (for counter runs), print nothing else")
+    ap.add_argument("--calls", type=int, default=2)
     ap.add_argument("--out")
     ap.add_argument("--cmd", default="")
     return ap.parse_args()
@@ -396,6 +402,18 @@ def main():
     def decode_loop():
         for s in range(S):
             c2kv.attn_decode(qd[s], kd[s], vd[s], ck, cv, [M + tq + s], [P + tq + s], theta, workspace=ws_dec)
+
+    if a.profile_phase:
+        fn = {"extract": extract, "compose": compose, "prefill": prefill,
+              "decode": lambda: c2kv.attn_decode(qd[0], kd[0], vd[0], ck, cv, [M + tq], [P + tq], theta,
+                                                 workspace=ws_dec)}[a.profile_phase]
+        if a.profile_phase in ("prefill", "decode"):
+            compose()
+        for _ in range(a.calls):
+            fn()
+        torch.cuda.synchronize()
+        print(f"{a.profile_phase}: {a.calls} calls done", flush=True)
+        return
 
     # eager pass (also the reference for the graph), then capture the decode loop
     extract(); compose(); prefill(); decode_loop()

@@ -293,6 +293,14 @@ __device__ __forceinline__ f32x8 lds_v8<float>(const char* base, int chunk0, int
 // Reference-max slack of the online softmax, in log2 units (see tile()).
 constexpr float kLazyLog2 = 8.f;
 
+template <typename T>
+__device__ __forceinline__ typename ElemTraits<T>::v8 ones_v8() {
+  typename ElemTraits<T>::v8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = from_f32<T>(1.f);
+  return r;
+}
+
 // One wave's 32 query rows against one staged tile.
 template <typename T, int D>
 struct XAttn {
@@ -303,13 +311,14 @@ struct XAttn {
 
   V8 qB[2][KS];
   f32x4 o[DB][2];
-  float m[2], l[2];   // reference max of the raw scores, running sum
+  f32x4 ls[2];        // running sums, from a ones row in the PV product
+  float m[2];         // reference max of the raw scores
 
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db][0] = o[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[0] = m[1] = -INFINITY;
-    l[0] = l[1] = 0.f;
+    ls[0] = ls[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   template <bool kMasked>
@@ -357,16 +366,11 @@ struct XAttn {
       const float mnew = grow ? mx : m[qb];
       const float mneg = mnew == -INFINITY ? 0.f : -mnew * sl2;
       alpha[qb] = grow ? __builtin_amdgcn_exp2f(__builtin_fmaf(m[qb], sl2, mneg)) : 1.f;
-      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][i], sl2, mneg));
-          rs += pv;
-          pB[kb >> 1][qb][4 * (kb & 1) + i] = from_f32<T>(pv);
-        }
-      l[qb] = l[qb] * alpha[qb] + rs;
+        for (int i = 0; i < 4; ++i)
+          pB[kb >> 1][qb][4 * (kb & 1) + i] = from_f32<T>(__builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][i], sl2, mneg)));
       m[qb] = mnew;
     }
     // rescale O only when some lane's reference max moved (the empty asm
@@ -379,6 +383,8 @@ struct XAttn {
         o[db][0] *= a0;
         o[db][1] *= a1;
       }
+      ls[0] *= a0;
+      ls[1] *= a1;
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -388,6 +394,10 @@ struct XAttn {
         o[db][0] = mma16(a, pB[c][0], o[db][0]);
         o[db][1] = mma16(a, pB[c][1], o[db][1]);
       }
+      // row sums of the probabilities as the MFMAs see them: a ones row
+      // as the A operand sums P^T over the half's 32 keys per column
+      ls[0] = mma16(ones_v8<T>(), pB[c][0], ls[0]);
+      ls[1] = mma16(ones_v8<T>(), pB[c][1], ls[1]);
     }
   }
 };
@@ -499,7 +509,7 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void extract_attn_ker
   const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lt = wave_sum_16_32(W.l[qb]);
+    const float lt = W.ls[qb][0];   // every lane of a column holds its sum
     const float inv = 1.f / lt;
     const int ql = P.q0 + 16 * qb + r16;
     if (ql < P.qend) {
@@ -670,7 +680,7 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void cache_attn_kerne
   const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lt = wave_sum_16_32(W.l[qb]);
+    const float lt = W.ls[qb][0];   // every lane of a column holds its sum
     const float m2 = W.m[qb] * p.scale_log2;
     const int t = t0 + 16 * qb + r16;
     if (t >= t1) continue;
