@@ -142,14 +142,20 @@ int fill_extract_chunk(const int32_t* doc_lens, int32_t first, int32_t num_docs,
 
 // ------------------------------------------------------ prefill / decode
 // Split plan shared by the size query and the call.  Keys of a request are
-// cut into `chunk`-key pieces processed by separate workgroups; chunk is a
-// multiple of the kernel's key step and sized so that a launch fills the
-// chip (about four workgroups per CU for decode, one for prefill), with at
-// most C2KV_MAX_SPLITS pieces per request.
+// cut into pieces processed by separate workgroups, at most C2KV_MAX_SPLITS
+// per request.
+//  * prefill: one `chunk` for all requests, a multiple of the kernel's key
+//    tile, sized so that a launch has about one workgroup per CU;
+//  * decode: the launch is sized to one round of the workgroups the chip
+//    holds at once (kDecodeSlots), and each request's keys are cut into
+//    pieces of nearly equal length (chunk_r, a multiple of one wave's 32-key
+//    step), so every workgroup streams about the same number of bytes and
+//    no second, partly filled round trails the first.
+constexpr int64_t kDecodeSlots = 3 * 256;   // decode workgroups resident at once on a 256-CU MI355X
 struct CachePlan {
   bool decode = false;
   int32_t nug = 0, nblk_q = 0, chunk = 0;
-  std::vector<int32_t> nsplit;
+  std::vector<int32_t> nsplit, chunk_r;
   size_t qrot_off = 0, part_off = 0, total = 0;
 };
 
@@ -173,21 +179,49 @@ c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, i
     total_keys += c + tq;
     max_len = std::max(max_len, c + tq);
   }
-  const int64_t step = decode ? 4 * 32 : kBN;        // keys per workgroup step
-  const int64_t target_wg = decode ? 1024 : 256;
-  int64_t chunk = ceil_div(total_keys * hkv * P.nug, target_wg);
-  chunk = std::max<int64_t>(step, ceil_div(chunk, step) * step);
-  chunk = std::max<int64_t>(chunk, ceil_div(ceil_div(max_len, C2KV_MAX_SPLITS), step) * step);
-  P.chunk = (int32_t)chunk;
+  const int64_t step = decode ? 4 * 32 : kBN;        // keys per workgroup step (all waves)
   P.nsplit.resize(num_reqs);
+  P.chunk_r.resize(num_reqs);
+  if (!decode) {
+    int64_t chunk = ceil_div(total_keys * hkv * P.nug, 256);
+    chunk = std::max<int64_t>(step, ceil_div(chunk, step) * step);
+    chunk = std::max<int64_t>(chunk, ceil_div(ceil_div(max_len, C2KV_MAX_SPLITS), step) * step);
+    P.chunk = (int32_t)chunk;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+      P.nsplit[r] = (int32_t)ceil_div(cache_len[r] + tq, chunk);
+      P.chunk_r[r] = (int32_t)chunk;
+    }
+  } else {
+    // per-workgroup key budget w: the smallest multiple of the step whose
+    // pieces fit the resident slots of every launch of C2KV_MAX_BATCH
+    // requests (or one piece per request and head, if even that does not fit)
+    int64_t w = std::max<int64_t>(step, ceil_div(ceil_div(total_keys * hkv, kDecodeSlots), step) * step);
+    w = std::max<int64_t>(w, ceil_div(ceil_div(max_len, C2KV_MAX_SPLITS), step) * step);
+    const int64_t wmax = std::max<int64_t>(step, ceil_div(max_len, step) * step);
+    for (; w < wmax; w += step) {
+      bool fits = true;
+      for (int32_t r0 = 0; r0 < num_reqs && fits; r0 += C2KV_MAX_BATCH) {
+        int64_t wgs = 0;
+        for (int32_t r = r0; r < std::min(num_reqs, r0 + C2KV_MAX_BATCH); ++r)
+          wgs += ceil_div(cache_len[r] + tq, w) * hkv;
+        fits = wgs <= kDecodeSlots;
+      }
+      if (fits) break;
+    }
+    P.chunk = (int32_t)w;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+      const int64_t len = cache_len[r] + tq;
+      const int64_t n = ceil_div(len, w);
+      const int64_t c = ceil_div(ceil_div(len, n), 32) * 32;   // equal pieces, whole 32-key steps
+      P.chunk_r[r] = (int32_t)c;
+      P.nsplit[r] = (int32_t)ceil_div(len, c);
+    }
+  }
   size_t max_part = 0;
   for (int32_t r0 = 0; r0 < num_reqs; r0 += C2KV_MAX_BATCH) {
     const int32_t r1 = std::min(num_reqs, r0 + C2KV_MAX_BATCH);
     int32_t stride = 0;
-    for (int32_t r = r0; r < r1; ++r) {
-      P.nsplit[r] = (int32_t)ceil_div(cache_len[r] + tq, chunk);
-      stride = std::max(stride, P.nsplit[r]);
-    }
+    for (int32_t r = r0; r < r1; ++r) stride = std::max(stride, P.nsplit[r]);
     if (stride > 1)
       max_part = std::max(max_part, (size_t)(r1 - r0) * hq * tq * stride * (head_dim + 4) * sizeof(float));
   }
@@ -251,13 +285,14 @@ c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new,
       std::memset(&dp, 0, sizeof(dp));
       dp.q = q; dp.k_new = k_new; dp.v_new = v_new; dp.kc = cache_k; dp.vc = cache_v; dp.o = o; dp.lse = lse;
       dp.part = part; dp.cap = cap; dp.req0 = r0; dp.num_reqs = cnt; dp.hq = hq; dp.hkv = hkv; dp.G = G;
-      dp.chunk = P.chunk; dp.nsplit_stride = stride; dp.scale_log2 = scale_log2(head_dim); dp.freqs = freqs;
+      dp.nsplit_stride = stride; dp.scale_log2 = scale_log2(head_dim); dp.freqs = freqs;
       int64_t wg = 0;
       for (int32_t i = 0; i < cnt; ++i) {
         dp.reqs[i].wg0 = (int32_t)wg;
         dp.reqs[i].cache_len = cache_len[r0 + i];
         dp.reqs[i].pos = q_pos0[r0 + i];
         dp.reqs[i].nsplit = P.nsplit[r0 + i];
+        dp.reqs[i].chunk = P.chunk_r[r0 + i];
         wg += (int64_t)hkv * P.nsplit[r0 + i];
       }
       dp.total_wg = (int32_t)wg;

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
   const int kvh = local / rq.nsplit, split = local % rq.nsplit;
   const int G = p.G;
   const int newk = rq.cache_len;                       // row of the new token
-  const int k0 = split * p.chunk, k1 = min(newk + 1, k0 + p.chunk);
+  const int k0 = split * rq.chunk, k1 = min(newk + 1, k0 + rq.chunk);
   const int nsteps = (k1 - k0 + 31) / 32;
 
   const int64_t head_base = ((int64_t)r * p.hkv + kvh) * p.cap;

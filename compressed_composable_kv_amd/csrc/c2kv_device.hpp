@@ -161,7 +161,8 @@ struct DecodeReq {
   int32_t wg0;       // first workgroup of the request
   int32_t cache_len; // rows before the new token (its row)
   int32_t pos;       // position of the new token
-  int32_t nsplit;
+  int32_t nsplit;    // key pieces of the request
+  int32_t chunk;     // keys per piece (a multiple of 32)
 };
 
 struct DecodeParams {
@@ -174,7 +175,7 @@ struct DecodeParams {
   float* lse;           // [R][hq] or null
   float* part;          // split partials (see CacheParams)
   int64_t cap;
-  int32_t req0, num_reqs, hq, hkv, G, chunk, nsplit_stride, total_wg;
+  int32_t req0, num_reqs, hq, hkv, G, nsplit_stride, total_wg;
   float scale_log2;
   RopeFreqs freqs;
   DecodeReq reqs[C2KV_MAX_BATCH];
