@@ -33,6 +33,10 @@ tokens at k = 4, with the uncompressed cache of the same original length as
 the comparator), each a graph of decode calls over caches well above the
 last-level cache:
     python bench.py --decode-sweep
+Extraction at the Qwen3-14B shapes (k = 4, 8, 16; 40 layers over two buffer
+sets) and compose of the Qwen2.5-7B pool, one JSON line each:
+    python bench.py --extract-sweep
+    python bench.py --compose-sweep
 
 One phase alone, for counter runs under rocprofv3:
     python bench.py --profile-phase extract --calls 2
@@ -195,6 +199,8 @@ def parse():
     ap.add_argument("--calibration-copy-mib", type=int, default=0)
     ap.add_argument("--summarize", nargs="+", metavar="DIR")
     ap.add_argument("--decode-sweep", action="store_true")
+    ap.add_argument("--extract-sweep", action="store_true")
+    ap.add_argument("--compose-sweep", action="store_true")
     ap.add_argument("--profile-phase", choices=("extract", "compose", "prefill", "decode"),
                     help="run only this phase of the step --calls times (for counter runs), print nothing else")
     ap.add_argument("--calls", type=int, default=2)
@@ -307,6 +313,106 @@ def decode_sweep():
             {"cache": "uncompressed comparator", "original_tokens": L})
 
 
+def extract_sweep():
+    """Extraction throughput at the Qwen3-14B shapes (40 query / 8 KV heads,
+    d = 128, theta 1e6, bf16): 64 documents of 8192 tokens at k = 4, 8, 16
+    (sink = k), 40 attention-only layers whose calls alternate over two
+    input/output buffer sets.  One JSON line per k."""
+    import torch
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = W.QWEN3_14B
+    d, hq, hkv, dt = w.head_dim, w.hq, w.hkv, w.dtype
+    lens = list(w.doc_lens)
+    ach = achievable_peaks(torch, dev)
+    for k in (4, 8, 16):
+        rows = c2kv.packed_rows(lens, k)
+        sets = []
+        for b in range(2):
+            q = W.device_normal((rows, hq, d), dt, w.wid, W.P_Q, dev, salt=10 * k + b)
+            kk = W.device_normal((rows, hkv, d), dt, w.wid, W.P_K, dev, salt=10 * k + b)
+            v = W.device_normal((rows, hkv, d), dt, w.wid, W.P_V, dev, salt=10 * k + b)
+            sets.append((q, kk, v, torch.empty_like(q)))
+        ws = torch.empty(c2kv.workspace_size_extract(lens, k, hkv, d, dt), dtype=torch.uint8, device=dev)
+
+        def layer(i):
+            q, kk, v, o = sets[i % 2]
+            c2kv.extract_attn(q, kk, v, lens, k, k, w.rope_theta, out=o, workspace=ws)
+        layer(0)
+        layer(1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(w.layers):
+            layer(i)
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3
+        flops = w.layers * hq * 4 * d * sum(visible_cells(n, k) for n in lens)
+        tf = flops / sec / 1e12
+        print(json.dumps({"workload": f"qwen3_14b_extract_k{k}", "docs": len(lens), "doc_tokens": lens[0],
+                          "ratio_k": k, "layers": w.layers, "seconds_40_layers": sec, "pflop": flops / 1e15,
+                          "tflops": tf, "frac_of_peak": tf / BF16_PEAK_TFLOPS,
+                          "frac_of_achievable": tf / ach["mfma_bf16_tflops"] if ach["mfma_bf16_tflops"] else None,
+                          "target_seconds_at_half_peak": flops / (0.5 * BF16_PEAK_TFLOPS * 1e12)}), flush=True)
+        del sets, ws
+        torch.cuda.empty_cache()
+
+
+def compose_sweep():
+    """Compose throughput of the Qwen2.5-7B pool workload: 64 pre-extracted
+    documents (k = 16, lengths uniform on 1024..8192, slot K/V N(0, 1)), 32
+    requests each composing a seeded subset of 8..32 documents in seeded
+    order.  Reports algorithmic bytes (read and write every composed row)
+    and minimum traffic (the pool read once plus the writes), per call from
+    a graph of 10 calls."""
+    import torch
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = W.QWEN25
+    d, hkv, dt, k = w.head_dim, w.hkv, w.dtype, w.ratio_k
+    pool = W.qwen25_pool(w)
+    reqs = W.qwen25_requests(w)
+    slots = [c2kv.num_slots(n, k) for n in pool]
+    kv = [(W.device_normal((m, hkv, d), dt, w.wid, W.P_K, dev, salt=100 + i),
+           W.device_normal((m, hkv, d), dt, w.wid, W.P_V, dev, salt=100 + i)) for i, m in enumerate(slots)]
+    requests = [[(kv[t][0], kv[t][1], pool[t]) for t in r] for r in reqs]
+    M = [sum(slots[t] for t in r) for r in reqs]
+    cap = max(M) + 128
+    ck = torch.empty((len(reqs), hkv, cap, d), dtype=dt, device=dev)
+    cv = torch.empty_like(ck)
+    c2kv.compose(requests, k, w.rope_theta, ck, cv)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(10):
+            c2kv.compose(requests, k, w.rope_theta, ck, cv)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 30
+    es = 2
+    alg = 4 * sum(M) * hkv * d * es
+    used = sorted({t for r in reqs for t in r})
+    minimum = 2 * sum(slots[t] for t in used) * hkv * d * es + 2 * sum(M) * hkv * d * es
+    ach = achievable_peaks(torch, dev)
+    print(json.dumps({"workload": "qwen25_7b_pool_compose", "requests": len(reqs), "composed_rows": sum(M),
+                      "us_per_call": us, "algorithmic_bytes": alg, "min_traffic_bytes": minimum,
+                      "gbs_algorithmic": alg / (us * 1e-6) / 1e9, "gbs_min_traffic": minimum / (us * 1e-6) / 1e9,
+                      "frac_of_peak_min_traffic": minimum / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                      "frac_of_achievable_min_traffic": minimum / (us * 1e-6) / 1e9 / ach["hbm_copy_gbs"]}),
+          flush=True)
+
+
 def achievable_peaks(torch, dev):
     """Rates this GPU sustains, measured live: dense bf16 MFMA from the probe
     library (independent MFMA chains on register operands, 4 waves per SIMD),
@@ -351,6 +457,12 @@ def main():
         return
     if a.decode_sweep:
         decode_sweep()
+        return
+    if a.extract_sweep:
+        extract_sweep()
+        return
+    if a.compose_sweep:
+        compose_sweep()
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this path does not shard "
