@@ -390,9 +390,12 @@ def test_extract_more_documents_than_one_launch(c2kv):
     assert list(got[:3]) == tot and got[3] == 0
 
 
-@pytest.mark.parametrize("hq,hkv,d,dt", [(16, 1, 128, torch.bfloat16), (32, 2, 64, torch.bfloat16)])
+@pytest.mark.parametrize("hq,hkv,d,dt", [(16, 1, 128, torch.bfloat16), (32, 2, 64, torch.bfloat16),
+                                         (32, 16, 64, torch.bfloat16)])
 def test_decode_more_requests_than_one_launch(c2kv, hq, hkv, d, dt):
-    """70 requests (64 per launch), G up to 16, head_dim 64 in bf16."""
+    """70 requests (64 per launch), G up to 16, head_dim 64 in bf16.  With 16
+    KV heads the first launch has more (request, head) pairs than the chip
+    holds workgroups at once, so every request takes one key piece."""
     g = torch.Generator().manual_seed(22)
     lens = [int(x) for x in torch.randint(0, 700, (70,), generator=g)]
     R = len(lens)
