@@ -195,19 +195,26 @@ c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, i
     // per-workgroup key budget w: the smallest multiple of the step whose
     // pieces fit the resident slots of every launch of C2KV_MAX_BATCH
     // requests (or one piece per request and head, if even that does not fit)
-    int64_t w = std::max<int64_t>(step, ceil_div(ceil_div(total_keys * hkv, kDecodeSlots), step) * step);
-    w = std::max<int64_t>(w, ceil_div(ceil_div(max_len, C2KV_MAX_SPLITS), step) * step);
-    const int64_t wmax = std::max<int64_t>(step, ceil_div(max_len, step) * step);
-    for (; w < wmax; w += step) {
-      bool fits = true;
-      for (int32_t r0 = 0; r0 < num_reqs && fits; r0 += C2KV_MAX_BATCH) {
+    // (the workgroup count only falls as w grows: binary search over
+    // multiples of the step)
+    auto fits = [&](int64_t w) {
+      for (int32_t r0 = 0; r0 < num_reqs; r0 += C2KV_MAX_BATCH) {
         int64_t wgs = 0;
         for (int32_t r = r0; r < std::min(num_reqs, r0 + C2KV_MAX_BATCH); ++r)
           wgs += ceil_div(cache_len[r] + tq, w) * hkv;
-        fits = wgs <= kDecodeSlots;
+        if (wgs > kDecodeSlots) return false;
       }
-      if (fits) break;
+      return true;
+    };
+    int64_t lo = std::max<int64_t>(1, ceil_div(ceil_div(total_keys * hkv, kDecodeSlots), step));
+    lo = std::max<int64_t>(lo, ceil_div(ceil_div(max_len, C2KV_MAX_SPLITS), step));
+    int64_t hi = std::max<int64_t>(lo, ceil_div(max_len, step));   // one piece per request: the fallback
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (fits(mid * step)) hi = mid;
+      else lo = mid + 1;
     }
+    const int64_t w = lo * step;
     P.chunk = (int32_t)w;
     for (int32_t r = 0; r < num_reqs; ++r) {
       const int64_t len = cache_len[r] + tq;
