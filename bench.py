@@ -18,7 +18,8 @@ The 256 decode launches of a step are replayed from one HIP graph.
 
 Prints one JSON line.  Besides the step, it reports the decode rate with the
 256 steps spread over 16 replicas of the cache (a working set of about
-0.6 GB, above the 256 MB last-level cache), and, when a counter summary
+0.6 GB, above the 256 MB last-level cache) and the compose rate with
+its inputs and caches spread over 16 replicas (about 3 GB), and, when a counter summary
 for the current decode sources is committed under profiles/, the HBM
 traffic the hardware counters measured for one decode call.  It also
 measures, live, the rates this GPU sustains (dense bf16 MFMA from the probe
@@ -595,6 +596,33 @@ def main():
         cold_ms = e0.elapsed_time(e1) / 3
         del gcold, reps
         torch.cuda.empty_cache()
+    # compose with its inputs and caches spread over replicas (each call
+    # reads and writes a different copy: a working set of about 3 GB, far
+    # above the last-level cache); not part of the step
+    comp_cold_gbs = None
+    if a.cold_replicas > 1:
+        creps = []
+        for _ in range(a.cold_replicas):
+            kk_r, v_r = kk.clone(), v.clone()
+            vw = c2kv.slot_views(kk_r, v_r, lens, k)
+            creps.append(([[vw[t] for t in order]], torch.empty_like(ck), torch.empty_like(cv), kk_r, v_r))
+        torch.cuda.synchronize()
+        gcc = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gcc):
+            for req_r, ck_r, cv_r, _, _ in creps:
+                c2kv.compose(req_r, k, theta, ck_r, cv_r)
+        gcc.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            gcc.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        comp_cold_ms = e0.elapsed_time(e1) / (3 * a.cold_replicas)
+        comp_cold_gbs = 4 * M * hkv * d * 2 / (comp_cold_ms * 1e-3) / 1e9
+        del gcc, creps
+        torch.cuda.empty_cache()
     # compose on its own: 20 back-to-back calls from a graph, per-call time
     # without the launch gap of a single eager call; not part of the step
     gcomp = torch.cuda.CUDAGraph()
@@ -667,6 +695,7 @@ def main():
         "phase_ms": {"extract": ph[0], "compose": ph[1], "prefill": ph[2], "decode_256": ph[3]},
         "compose_gbs": comp_gbs,
         "compose_gbs_graph": comp_bytes / (comp_graph_ms * 1e-3) / 1e9,
+        "compose_gbs_cache_replicas": comp_cold_gbs,
         "achievable": ach,
         "extraction_frac_of_achievable": ext_tflops / ach["mfma_bf16_tflops"] if ach["mfma_bf16_tflops"] else None,
         "decode_frac_of_achievable": dec_gbs / ach["hbm_copy_gbs"],

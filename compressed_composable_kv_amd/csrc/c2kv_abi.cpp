@@ -496,7 +496,9 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
   std::memset(&p, 0, sizeof(p));
   p.cache_k = cache_k; p.cache_v = cache_v; p.pos_out = pos_out; p.cap = cap;
   p.hkv = hkv; p.ratio_k = ratio_k; p.freqs = make_freqs(head_dim, rope_theta);
-  const int rpt = compose_rows_per_tile((int)elem_bytes(dt), head_dim);
+  const ComposeTiling tl = compose_tiling((int)elem_bytes(dt), head_dim, hkv);
+  const int rpt = tl.rpt;
+  p.rpt = tl.rpt; p.gpb = tl.gpb; p.nblk = tl.nblk;
   int cnt = 0;
   int32_t tiles = 0;
   auto flush = [&]() -> hipError_t {

@@ -129,9 +129,12 @@ hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipSt
 }
 
 // ---------------------------------------------------------------- compose
-// Work unit = (row tile of ONE segment, group of two KV heads); a thread owns
-// one 16-byte chunk of the low half of a row (and the matching chunk of the
-// high half) and rotates it for both heads with one set of cos/sin.  The
+// Work unit = (row tile of ONE segment, block of gpb pairs of KV heads; see
+// ComposeTiling); a thread owns one 16-byte chunk of the low half of a row
+// (and the matching chunk of the high half) of one head pair and rotates it
+// for both heads with one set of cos/sin.  Consecutive threads take the
+// chunks, then the head pairs, then the rows, so a unit reads whole source
+// rows (all heads of a slot row are contiguous).  The
 // unit's segment is found by a uniform search of the segment table; its
 // realigned position is the document offset plus the slot's extraction
 // position.  Workgroups loop over units with the next unit's loads issued
@@ -139,14 +142,16 @@ hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipSt
 // the cache stream overlap.
 template <typename T, int D>
 struct ComposeUnit {
-  static constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE, RPT = 256 / TPH;
+  static constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE;
   uint4 kl0, kh0, vl0, vh0, kl1, kh1, vl1, vh1;
   float fr[CE];
   int seg, j, c, h0, cpos;
   bool live;
 
-  __device__ __forceinline__ void load(const ComposeParams& p, int u, int ngroups) {
-    const int tile = u / ngroups, hgrp = u % ngroups;
+  __device__ __forceinline__ void load(const ComposeParams& p, int u) {
+    const int tile = u / p.nblk, blk = u % p.nblk;
+    const int t = (int)threadIdx.x;
+    const int hgrp = blk * p.gpb + (t / TPH) % p.gpb;
     int lo_s = 0, hi_s = p.num_segs - 1;
     while (lo_s < hi_s) {
       const int mid = (lo_s + hi_s + 1) >> 1;
@@ -155,9 +160,9 @@ struct ComposeUnit {
     seg = lo_s;
     const ComposeSeg& sg = p.segs[seg];
     const int m = (sg.n + p.ratio_k - 1) / p.ratio_k;
-    j = (tile - sg.tile0) * RPT + (int)threadIdx.x / TPH;
-    c = (int)threadIdx.x % TPH;
-    live = j < m;
+    j = (tile - sg.tile0) * p.rpt + t / (TPH * p.gpb);
+    c = t % TPH;
+    live = j < m && 2 * hgrp < p.hkv;   // padded head pairs load a valid head and store nothing
     const int jj = live ? j : m - 1;     // dead lanes load a valid row
     cpos = sg.pos_off + min(jj * p.ratio_k + p.ratio_k - 1, sg.n - 1);
 #pragma unroll
@@ -167,7 +172,7 @@ struct ComposeUnit {
     }
     const T* ksrc = reinterpret_cast<const T*>(sg.k) + (int64_t)jj * sg.stride + c * CE;
     const T* vsrc = reinterpret_cast<const T*>(sg.v) + (int64_t)jj * sg.stride + c * CE;
-    h0 = hgrp * 2;
+    h0 = min(hgrp * 2, p.hkv - 1);
     const int h1 = min(h0 + 1, p.hkv - 1);
     kl0 = *reinterpret_cast<const uint4*>(ksrc + h0 * D);
     kh0 = *reinterpret_cast<const uint4*>(ksrc + h0 * D + H);
@@ -204,15 +209,14 @@ struct ComposeUnit {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void compose_kernel(const ComposeParams p) {
   static_assert(kComposeHPT == 2, "two heads per thread");
-  const int ngroups = (p.hkv + 1) / 2;
-  const int total = p.total_tiles * ngroups;
+  const int total = p.total_tiles * p.nblk;
   int u = blockIdx.x;
   if (u >= total) return;
   ComposeUnit<T, D> cur, nxt;
-  cur.load(p, u, ngroups);
+  cur.load(p, u);
   for (; u < total; u += gridDim.x) {
     const bool more = u + (int)gridDim.x < total;
-    if (more) nxt.load(p, u + gridDim.x, ngroups);
+    if (more) nxt.load(p, u + gridDim.x);
     cur.store(p);
     if (!more) break;
     cur = nxt;
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(256) void compose_kernel(const ComposeParams p) {
 
 template <typename T, int D>
 static hipError_t launch_compose_t(const ComposeParams& p, hipStream_t st) {
-  const int units = p.total_tiles * ((p.hkv + kComposeHPT - 1) / kComposeHPT);
+  const int units = p.total_tiles * p.nblk;
   if (units == 0) return hipSuccess;
   // three workgroups per CU (12 waves) is the measured optimum for 1k-2k
   // units: fewer leaves HBM idle, more adds dispatch without more bytes

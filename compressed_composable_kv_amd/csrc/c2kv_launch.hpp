@@ -42,15 +42,29 @@ struct ComposeParams {
   int32_t* pos_out;
   int64_t cap;
   int32_t num_segs, hkv, ratio_k, total_tiles;
+  int32_t rpt, gpb, nblk;   // rows per tile, head pairs per unit, units per tile (ComposeTiling)
   RopeFreqs freqs;
   ComposeSeg segs[kComposeSegs];
 };
 static_assert(sizeof(ComposeParams) <= 4096, "compose table must fit the kernel arguments");
 
-// Composed rows per row tile of compose_kernel (one workgroup of 256 threads
-// covers a tile of rows, each thread one 16-byte chunk of a half row).
-inline int compose_rows_per_tile(int dtype_bytes, int head_dim) {
-  return 256 / (head_dim / 2 * dtype_bytes / 16);
+// Tiling of compose_kernel.  A workgroup of 256 threads covers a unit: rpt
+// composed rows times gpb pairs of KV heads, each thread one 16-byte chunk
+// of the low half of a row (and the matching chunk of the high half) for a
+// pair.  gpb is the number of head pairs rounded up to a power of two, capped
+// by the threads, so that a unit reads whole source rows (all heads of a
+// slot are contiguous) where the threads allow; a tile of rows then takes
+// nblk units.
+struct ComposeTiling {
+  int rpt, gpb, nblk;
+};
+inline ComposeTiling compose_tiling(int dtype_bytes, int head_dim, int hkv) {
+  const int tph = head_dim / 2 * dtype_bytes / 16;   // threads per half row
+  const int pairs = (hkv + 1) / 2;
+  int gp = 1;
+  while (gp < pairs) gp <<= 1;
+  const int gpb = gp < 256 / tph ? gp : 256 / tph;
+  return ComposeTiling{256 / tph / gpb, gpb, (pairs + gpb - 1) / gpb};
 }
 
 struct AppendReq {
