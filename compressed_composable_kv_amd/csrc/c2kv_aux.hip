@@ -241,59 +241,69 @@ hipError_t launch_compose(const ComposeParams& p, int dtype, int head_dim, hipSt
 }
 
 // ----------------------------------------------------------------- append
-// One thread per (request, token, head, chunk); heads [0, hq) are query
-// heads (rotated into the workspace), heads [hq, hq+hkv) are new keys
-// (rotated into the cache) together with their values (copied).
+// One workgroup per (request, token): the token's cos/sin are computed once
+// into LDS, then the threads loop over (head, chunk) pairs.  Heads [0, hq)
+// are query heads (rotated and written to the workspace), heads
+// [hq, hq+hkv) are new keys (rotated into the cache) together with their
+// values (copied).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int nh = p.hq + p.hkv;
-  const int64_t per_tok = (int64_t)nh * TPH;
-  const int64_t tok = idx / per_tok;
-  if (tok >= (int64_t)p.num_reqs * p.tq) return;
-  const int ri = (int)(tok / p.tq), t = (int)(tok % p.tq);
-  const int h = (int)((idx % per_tok) / TPH), c = (int)(idx % TPH);
+  __shared__ float2 s_cs[H];
+  const int tok = blockIdx.x;                  // grid = num_reqs * tq
+  const int ri = tok / p.tq, t = tok % p.tq;
   const int r = p.req0 + ri;
   const AppendReq rq = p.reqs[ri];
   const int pos = rq.pos0 + t;
-  float cs[CE], sn[CE];
+  if ((int)threadIdx.x < H) {
+    float c, sn;
+    rope_cs(pos, p.freqs.f[threadIdx.x], c, sn);
+    s_cs[threadIdx.x] = make_float2(c, sn);
+  }
+  __syncthreads();
+  const int nh = p.hq + p.hkv;
+  for (int item = threadIdx.x; item < nh * TPH; item += blockDim.x) {
+    const int h = item / TPH, c = item % TPH;
+    float cs[CE], sn[CE];
 #pragma unroll
-  for (int e = 0; e < CE; ++e) rope_cs(pos, p.freqs.f[c * CE + e], cs[e], sn[e]);
-  if (h < p.hq) {
-    const int64_t off = (((int64_t)r * p.tq + t) * p.hq + h) * D + c * CE;
-    const T* src = reinterpret_cast<const T*>(p.q) + off;
-    T* dst = reinterpret_cast<T*>(p.qrot) + off;
-    uint4 lo = *reinterpret_cast<const uint4*>(src);
-    uint4 hi = *reinterpret_cast<const uint4*>(src + H);
-    rotate_chunk<T>(lo, hi, cs, sn);
-    *reinterpret_cast<uint4*>(dst) = lo;
-    *reinterpret_cast<uint4*>(dst + H) = hi;
-  } else {
-    const int kvh = h - p.hq;
-    const int64_t soff = (((int64_t)r * p.tq + t) * p.hkv + kvh) * D + c * CE;
-    const int64_t doff = (((int64_t)r * p.hkv + kvh) * p.cap + rq.cache_len + t) * D + c * CE;
-    const T* ks = reinterpret_cast<const T*>(p.k_new) + soff;
-    const T* vs = reinterpret_cast<const T*>(p.v_new) + soff;
-    uint4 lo = *reinterpret_cast<const uint4*>(ks);
-    uint4 hi = *reinterpret_cast<const uint4*>(ks + H);
-    rotate_chunk<T>(lo, hi, cs, sn);
-    T* kd = reinterpret_cast<T*>(p.cache_k) + doff;
-    T* vd = reinterpret_cast<T*>(p.cache_v) + doff;
-    *reinterpret_cast<uint4*>(kd) = lo;
-    *reinterpret_cast<uint4*>(kd + H) = hi;
-    *reinterpret_cast<uint4*>(vd) = *reinterpret_cast<const uint4*>(vs);
-    *reinterpret_cast<uint4*>(vd + H) = *reinterpret_cast<const uint4*>(vs + H);
+    for (int e = 0; e < CE; ++e) {
+      const float2 v = s_cs[c * CE + e];
+      cs[e] = v.x;
+      sn[e] = v.y;
+    }
+    if (h < p.hq) {
+      const int64_t off = (((int64_t)r * p.tq + t) * p.hq + h) * D + c * CE;
+      const T* src = reinterpret_cast<const T*>(p.q) + off;
+      T* dst = reinterpret_cast<T*>(p.qrot) + off;
+      uint4 lo = *reinterpret_cast<const uint4*>(src);
+      uint4 hi = *reinterpret_cast<const uint4*>(src + H);
+      rotate_chunk<T>(lo, hi, cs, sn);
+      *reinterpret_cast<uint4*>(dst) = lo;
+      *reinterpret_cast<uint4*>(dst + H) = hi;
+    } else {
+      const int kvh = h - p.hq;
+      const int64_t soff = (((int64_t)r * p.tq + t) * p.hkv + kvh) * D + c * CE;
+      const int64_t doff = (((int64_t)r * p.hkv + kvh) * p.cap + rq.cache_len + t) * D + c * CE;
+      const T* ks = reinterpret_cast<const T*>(p.k_new) + soff;
+      const T* vs = reinterpret_cast<const T*>(p.v_new) + soff;
+      uint4 lo = *reinterpret_cast<const uint4*>(ks);
+      uint4 hi = *reinterpret_cast<const uint4*>(ks + H);
+      rotate_chunk<T>(lo, hi, cs, sn);
+      T* kd = reinterpret_cast<T*>(p.cache_k) + doff;
+      T* vd = reinterpret_cast<T*>(p.cache_v) + doff;
+      *reinterpret_cast<uint4*>(kd) = lo;
+      *reinterpret_cast<uint4*>(kd + H) = hi;
+      *reinterpret_cast<uint4*>(vd) = *reinterpret_cast<const uint4*>(vs);
+      *reinterpret_cast<uint4*>(vd + H) = *reinterpret_cast<const uint4*>(vs + H);
+    }
   }
 }
 
 template <typename T, int D>
 static hipError_t launch_append_t(const AppendParams& p, hipStream_t st) {
-  constexpr int TPH = D / 2 / Chunk<T>::CE;
-  const int64_t n = (int64_t)p.num_reqs * p.tq * (p.hq + p.hkv) * TPH;
-  const int blocks = (int)((n + 255) / 256);
+  const int64_t blocks = (int64_t)p.num_reqs * p.tq;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((append_kernel<T, D>), dim3(blocks), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((append_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
