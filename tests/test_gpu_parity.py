@@ -157,6 +157,20 @@ def test_compose_multi_request_ragged(c2kv, dt):
     _compose_check(c2kv, reqs, pool_k, pool_v, pool_n, k, 1e6, dt, pos_base=[0, 5, 100000, 3, 0], cap_extra=3)
 
 
+@pytest.mark.parametrize("hkv,d,dt", [(5, 64, torch.float32), (6, 128, torch.bfloat16), (80, 128, torch.bfloat16)])
+def test_compose_head_counts(c2kv, hkv, d, dt):
+    """Head counts whose pairs do not fill a power of two (a workgroup's
+    spare pair slots load and store nothing) and more pairs than one
+    workgroup covers (a row tile takes several units)."""
+    g = torch.Generator().manual_seed(27)
+    pool_n = [int(x) for x in torch.randint(1, 300, (6,), generator=g)]
+    k = 4
+    pool_k = [W.normal((O.num_slots(n, k), hkv, d), dt, 27, W.P_K, salt=i) for i, n in enumerate(pool_n)]
+    pool_v = [W.normal((O.num_slots(n, k), hkv, d), dt, 27, W.P_V, salt=i) for i, n in enumerate(pool_n)]
+    reqs = [[0, 1, 2], [5, 4, 3, 2], [1]]
+    _compose_check(c2kv, reqs, pool_k, pool_v, pool_n, k, 1e6, dt, pos_base=[0, 7, 123], cap_extra=1)
+
+
 # ------------------------------------------------- prefill / decode parity
 
 def _oracle_cache(slot_k, slot_v, lens, k, theta, dt, base=0):
