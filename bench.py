@@ -38,6 +38,10 @@ Extraction at the Qwen3-14B shapes (k = 4, 8, 16; 40 layers over two buffer
 sets) and compose of the Qwen2.5-7B pool, one JSON line each:
     python bench.py --extract-sweep
     python bench.py --compose-sweep
+Loading stored caches from pinned host memory (32 layers of the Llama
+shapes): compose reading the slot caches in place across the host link,
+against copying the full caches, one JSON line:
+    python bench.py --host-pool
 
 One phase alone, for counter runs under rocprofv3:
     python bench.py --profile-phase extract --calls 2
@@ -202,6 +206,7 @@ def parse():
     ap.add_argument("--decode-sweep", action="store_true")
     ap.add_argument("--extract-sweep", action="store_true")
     ap.add_argument("--compose-sweep", action="store_true")
+    ap.add_argument("--host-pool", action="store_true")
     ap.add_argument("--profile-phase", choices=("extract", "compose", "prefill", "decode"),
                     help="run only this phase of the step --calls times (for counter runs), print nothing else")
     ap.add_argument("--calls", type=int, default=2)
@@ -414,6 +419,121 @@ def compose_sweep():
           flush=True)
 
 
+PCIE_PEAK_GBS = 64.0           # MI355X host link, PCIe 5.0 x16, one direction, GB/s
+
+
+def host_pool():
+    """Loading stored caches from host memory for one request of the
+    Llama3.1-8B shapes: 8 documents of 4096 tokens, all 32 layers (8 KV
+    heads, d = 128, bf16, theta 5e5), composed in the seeded order.  The
+    stored caches sit in pinned host memory.  Four ways to get them into a
+    realigned device cache, each over the 32 layers:
+      c2kv_zero_copy   compose at k = 4 reading the slot caches in place
+                       across the host link (1024 slot rows per document)
+      c2kv_dma         copy the slot caches to the device, then compose
+      full_zero_copy   compose at k = 1 from the full caches (every token
+                       kept, positions realigned: full-cache reuse)
+      full_dma         copy the full caches to the device (no realignment;
+                       the plain load of an uncompressed cache)
+    The compose loops are replayed from HIP graphs; copies run eagerly.
+    Best of three passes.  Rates count the bytes read from host memory."""
+    import torch
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = W.LLAMA
+    d, hkv, dt, theta = w.head_dim, w.hkv, w.dtype, w.rope_theta
+    L, ndoc, n = 32, len(w.doc_lens), w.doc_lens[0]
+    k = w.ratio_k
+    m = c2kv.num_slots(n, k)
+    order = W.llama_doc_order(w)
+    row_b = hkv * d * 2
+
+    def pool(rows):
+        hk = torch.empty((L, ndoc, rows, hkv, d), dtype=dt, pin_memory=True)
+        hv = torch.empty((L, ndoc, rows, hkv, d), dtype=dt, pin_memory=True)
+        for l in range(L):
+            hk[l].copy_(W.device_normal((ndoc, rows, hkv, d), dt, w.wid, W.P_K, dev, salt=300 + l))
+            hv[l].copy_(W.device_normal((ndoc, rows, hkv, d), dt, w.wid, W.P_V, dev, salt=300 + l))
+        return hk, hv
+
+    t0 = time.time()
+    hk_c, hv_c = pool(m)
+    hk_f, hv_f = pool(n)
+    print(f"host pools ready ({time.time() - t0:.1f} s)", flush=True)
+    ck_c = torch.empty((L, 1, hkv, ndoc * m, d), dtype=dt, device=dev)
+    cv_c = torch.empty_like(ck_c)
+    ck_f = torch.empty((L, 1, hkv, ndoc * n, d), dtype=dt, device=dev)
+    cv_f = torch.empty_like(ck_f)
+    st_k = torch.empty((L, ndoc, m, hkv, d), dtype=dt, device=dev)    # device staging of the slot caches
+    st_v = torch.empty_like(st_k)
+
+    def compose_layers(hk, hv, ck, cv, ratio):
+        for l in range(L):
+            c2kv.compose([[(hk[l, t], hv[l, t], n) for t in order]], ratio, theta, ck[l], cv[l])
+
+    def graph_of(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        # host segments are mapped (a pointer-attribute query) while capturing
+        with torch.cuda.graph(g, capture_error_mode="relaxed"):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def best_ms(fn, reps=3):
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1)
+            best = t if best is None else min(best, t)
+        return best
+
+    g_c = graph_of(lambda: compose_layers(hk_c, hv_c, ck_c, cv_c, k))
+    g_f = graph_of(lambda: compose_layers(hk_f, hv_f, ck_f, cv_f, 1))
+    g_s = graph_of(lambda: compose_layers(st_k, st_v, ck_c, cv_c, k))
+    c2kv_zc = best_ms(g_c.replay)
+    full_zc = best_ms(g_f.replay)
+    print(f"zero-copy compose: c2kv {c2kv_zc:.2f} ms, full {full_zc:.2f} ms", flush=True)
+
+    def full_dma():
+        ck_f.view(L, ndoc, n, hkv, d).copy_(hk_f, non_blocking=True)
+        cv_f.view(L, ndoc, n, hkv, d).copy_(hv_f, non_blocking=True)
+
+    def c2kv_dma():
+        st_k.copy_(hk_c, non_blocking=True)
+        st_v.copy_(hv_c, non_blocking=True)
+        g_s.replay()
+
+    full_dma()
+    torch.cuda.synchronize()
+    full_d = best_ms(full_dma)
+    c2kv_d = best_ms(c2kv_dma)
+    slot_copy = best_ms(lambda: (st_k.copy_(hk_c, non_blocking=True), st_v.copy_(hv_c, non_blocking=True)))
+    dev_compose = best_ms(g_s.replay)
+    print(f"dma: full {full_d:.2f} ms, c2kv {c2kv_d:.2f} ms", flush=True)
+    c_bytes = 2 * L * ndoc * m * row_b
+    f_bytes = 2 * L * ndoc * n * row_b
+    h2d = f_bytes / (full_d * 1e-3) / 1e9
+    zc = c_bytes / (c2kv_zc * 1e-3) / 1e9
+    print(json.dumps({
+        "workload": "llama31_8b_32layer_host_pool_load", "docs": ndoc, "doc_tokens": n, "layers": L,
+        "ratio_k": k, "slot_rows_per_layer": ndoc * m, "host_bytes_c2kv": c_bytes, "host_bytes_full": f_bytes,
+        "c2kv_zero_copy_ms": c2kv_zc, "c2kv_dma_then_compose_ms": c2kv_d, "slot_copy_only_ms": slot_copy,
+        "device_compose_only_ms": dev_compose, "full_zero_copy_k1_ms": full_zc, "full_dma_copy_ms": full_d,
+        "c2kv_zero_copy_gbs": zc, "full_zero_copy_gbs": f_bytes / (full_zc * 1e-3) / 1e9,
+        "h2d_copy_gbs": h2d, "pcie_peak_gbs": PCIE_PEAK_GBS,
+        "c2kv_zero_copy_frac_of_pcie_peak": zc / PCIE_PEAK_GBS, "c2kv_zero_copy_frac_of_h2d_copy": zc / h2d,
+        "speedup_c2kv_zero_copy_vs_full_dma": full_d / c2kv_zc,
+        "speedup_c2kv_best_vs_full_best": min(full_d, full_zc) / min(c2kv_zc, c2kv_d)}), flush=True)
+
+
 def achievable_peaks(torch, dev):
     """Rates this GPU sustains, measured live: dense bf16 MFMA from the probe
     library (independent MFMA chains on register operands, 4 waves per SIMD),
@@ -464,6 +584,9 @@ def main():
         return
     if a.compose_sweep:
         compose_sweep()
+        return
+    if a.host_pool:
+        host_pool()
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this path does not shard "

@@ -48,6 +48,7 @@ SIGNATURES = {
                                c_int32, c_int32, c_int32, c_float,
                                c_void_p, c_void_p, c_int64, c_void_p, P_i32, P_i32,
                                c_int32, c_void_p, c_size_t, c_void_p]),
+    "c2kv_host_device_ptr": (c_int32, [c_void_p, c_size_t, ctypes.POINTER(c_void_p)]),
     "c2kv_workspace_size_prefill": (c_size_t, [P_i32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     "c2kv_attn_prefill": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                     P_i32, P_i32, c_int32, c_int32, c_int32, c_int32, c_int32, c_float,

@@ -580,6 +580,38 @@ c2kv_status c2kv_workspace_init(void* workspace, size_t ws_bytes, hipStream_t st
   return ok();
 }
 
+// ------------------------------------------------- host-resident slot caches
+c2kv_status c2kv_host_device_ptr(const void* host_ptr, size_t bytes, const void** dev_ptr) {
+  if (!host_ptr || !dev_ptr) return fail(C2KV_ERR_INVALID_ARG, "host_ptr or dev_ptr is NULL");
+  if (bytes == 0) return fail(C2KV_ERR_INVALID_ARG, "bytes must be >= 1");
+  const char* first = static_cast<const char*>(host_ptr);
+  const char* last = first + (bytes - 1);
+  if (last < first) return fail(C2KV_ERR_INVALID_ARG, "host range wraps the address space");
+  hipPointerAttribute_t a0, a1;
+  std::memset(&a0, 0, sizeof(a0));
+  std::memset(&a1, 0, sizeof(a1));
+  hipError_t e0 = hipPointerGetAttributes(&a0, first);
+  hipError_t e1 = e0 == hipSuccess ? hipPointerGetAttributes(&a1, last) : hipSuccess;
+  if (e0 != hipSuccess || e1 != hipSuccess) {
+    (void)hipGetLastError();   // the query's own failure is not a launch error
+    return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) is not page-locked host memory (%s)", host_ptr, bytes,
+                hipGetErrorString(e0 != hipSuccess ? e0 : e1));
+  }
+  if (a0.type != hipMemoryTypeHost || a1.type != hipMemoryTypeHost || !a0.devicePointer || !a1.devicePointer ||
+      !a0.hostPointer || !a1.hostPointer)
+    return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) is not page-locked host memory mapped for the device",
+                host_ptr, bytes);
+  // the attributes may describe the queried address or its allocation's
+  // base; the host-side distance to the reported host address maps either
+  const char* d0 = static_cast<const char*>(a0.devicePointer) + (first - static_cast<const char*>(a0.hostPointer));
+  const char* d1 = static_cast<const char*>(a1.devicePointer) + (last - static_cast<const char*>(a1.hostPointer));
+  if (d1 - d0 != last - first)
+    return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) spans more than one page-locked allocation", host_ptr,
+                bytes);
+  *dev_ptr = d0;
+  return ok();
+}
+
 // ---------------------------------------------------------------- testing
 size_t c2kv_workspace_size_mask_cells(void) { return 256; }
 

@@ -164,8 +164,10 @@ def compose(requests: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int]]]
             pos_base: Optional[Sequence[int]] = None, pos_out: Optional[torch.Tensor] = None
             ) -> Tuple[List[int], List[int]]:
     """Compose per-request lists of (slot_k, slot_v, doc_len) into
-    cache_k/cache_v [R][hkv][cap][d] (c2kv_compose).  Returns
-    (cache_len per request, next position per request)."""
+    cache_k/cache_v [R][hkv][cap][d] (c2kv_compose).  A segment's tensors are
+    either on the device or pinned CPU tensors (stored caches kept in host
+    memory, read in place across the host link).  Returns (cache_len per
+    request, next position per request)."""
     lib = load()
     _dev_tensor(cache_k, "cache_k")
     _dev_tensor(cache_v, "cache_v", cache_k.dtype)
@@ -174,11 +176,15 @@ def compose(requests: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int]]]
     segs, ptr, keep = [], [0], []
     for req in requests:
         for sk, sv, n in req:
-            _need(sk.is_cuda and sv.is_cuda and sk.dtype == cache_k.dtype and sv.dtype == cache_k.dtype,
-                  "segments must be CUDA tensors of the cache dtype")
+            _need(sk.dtype == cache_k.dtype and sv.dtype == cache_k.dtype, "segments must have the cache dtype")
             _need(sk.dim() == 3 and sk.shape[1:] == (hkv, d) and sv.shape == sk.shape, "segment shape")
             _need(sk.stride(2) == 1 and sk.stride(1) == d and sv.stride() == sk.stride(), "segment layout")
-            segs.append(Segment(sk.data_ptr(), sv.data_ptr(), sk.stride(0), int(n), 0))
+            if sk.is_cuda and sv.is_cuda:
+                pk, pv = sk.data_ptr(), sv.data_ptr()
+            else:
+                # slot caches kept in host memory: compose reads them in place
+                pk, pv = host_device_ptr(sk), host_device_ptr(sv)
+            segs.append(Segment(pk, pv, sk.stride(0), int(n), 0))
             keep.append((sk, sv))
         ptr.append(len(segs))
     arr = (Segment * len(segs))(*segs)
@@ -192,6 +198,22 @@ def compose(requests: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int]]]
                            _ptr(cache_k), _ptr(cache_v), cap, _ptr(pos_out), lens, nxt,
                            _DT[cache_k.dtype], None, 0, _stream(cache_k.device)))
     return list(lens), list(nxt)
+
+
+# ------------------------------------------------ host-resident slot caches
+
+def host_device_ptr(t: torch.Tensor) -> int:
+    """Device address of a pinned CPU tensor's first element, checked to
+    cover every byte the view spans (c2kv_host_device_ptr).  Segments built
+    from such tensors make c2kv_compose read the slot caches where they
+    live, across the host link."""
+    _need(isinstance(t, torch.Tensor) and t.device.type == "cpu", "host segment must be a CPU tensor")
+    _need(t.is_pinned(), "host segment must be in pinned (page-locked) memory")
+    _need(t.numel() > 0 and all(st >= 0 for st in t.stride()), "host segment must be non-empty with positive strides")
+    span = (sum((sz - 1) * st for sz, st in zip(t.shape, t.stride())) + 1) * t.element_size()
+    out = ctypes.c_void_p()
+    check(load().c2kv_host_device_ptr(ctypes.c_void_p(t.data_ptr()), span, ctypes.byref(out)))
+    return int(out.value)
 
 
 # ------------------------------------------------ attention over the cache

@@ -185,6 +185,29 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs,
                          int32_t* pos_out, int32_t* cache_len_out, int32_t* next_pos_out,
                          c2kv_dtype dt, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ---- host-resident slot caches ------------------------------------------ */
+
+/* Device address of page-locked host memory, so that c2kv_compose can read
+ * stored slot caches where they live.  [Explainer] problem section (Fig. 1):
+ * stored caches sit in host memory and are moved to the GPU when a request
+ * uses them, and that move, not recomputation, dominates time to first
+ * token.  A c2kv_segment whose k/v are addresses returned here makes compose
+ * fetch only the compressed slot rows across the host link and rotate them
+ * on arrival; no staging copy in device memory is made.
+ *   host_ptr  host address inside one allocation made page-locked by
+ *             hipHostMalloc / hipHostAlloc (a pinned PyTorch CPU tensor is one)
+ *   bytes     number of bytes from host_ptr the device may read, >= 1
+ *   dev_ptr   out: the address kernels use for host_ptr; valid while the
+ *             allocation lives.  Host reads and writes stay valid; writes the
+ *             host makes while a kernel reads the memory are a race.
+ * Both host_ptr and host_ptr + bytes - 1 must be page-locked host memory
+ * mapped for the current device, at the same offset from each other on the
+ * device side; pageable memory is rejected, never touched by a kernel.
+ * Synchronous, no device work.  Clears any HIP error state its own queries
+ * raise.
+ * Errors: INVALID_ARG (NULL, bytes == 0, not mapped page-locked memory). */
+c2kv_status c2kv_host_device_ptr(const void* host_ptr, size_t bytes, const void** dev_ptr);
+
 /* ---- attention over the composed cache ----------------------------------- */
 
 size_t c2kv_workspace_size_prefill(const int32_t* cache_len, int32_t num_reqs, int32_t tq,

@@ -153,3 +153,18 @@ def test_mask_cells_validation(lib):
     assert lib.c2kv_mask_cells(_arr([12]), 1, 4, 4, None, FAKE, 256, None) == INVALID
     assert lib.c2kv_mask_cells(_arr([12]), 1, 4, 4, out, FAKE, 8, None) == WORKSPACE
     assert lib.c2kv_mask_cells(_arr([12]), 1, 0, 4, out, FAKE, 256, None) == INVALID
+
+
+def test_host_device_ptr_validation(lib):
+    out = ctypes.c_void_p()
+    assert lib.c2kv_host_device_ptr(None, 16, ctypes.byref(out)) == INVALID
+    assert lib.c2kv_host_device_ptr(FAKE, 16, None) == INVALID
+    assert lib.c2kv_host_device_ptr(FAKE, 0, ctypes.byref(out)) == INVALID
+    assert lib.c2kv_host_device_ptr(ctypes.c_void_p(2 ** 64 - 16), 64, ctypes.byref(out)) == INVALID   # wraps
+
+
+def test_host_segment_needs_pinned_memory():
+    # the binding refuses pageable host tensors before calling the library
+    import compressed_composable_kv_amd as c2kv
+    with pytest.raises(ValueError, match="pinned"):
+        c2kv.host_device_ptr(torch.zeros(4, 2, 64))
