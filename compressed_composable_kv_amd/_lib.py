@@ -25,9 +25,12 @@ P_u64 = ctypes.POINTER(ctypes.c_uint64)
 P_f32 = ctypes.POINTER(ctypes.c_float)
 
 
+SEGMENT_HOST = 1   # C2KV_SEGMENT_HOST
+
+
 class Segment(ctypes.Structure):
     _fields_ = [("k", c_void_p), ("v", c_void_p), ("row_stride", c_int64),
-                ("doc_len", c_int32), ("reserved", c_int32)]
+                ("doc_len", c_int32), ("flags", c_int32)]
 
 
 # name -> (restype, argtypes)
@@ -49,6 +52,12 @@ SIGNATURES = {
                                c_void_p, c_void_p, c_int64, c_void_p, P_i32, P_i32,
                                c_int32, c_void_p, c_size_t, c_void_p]),
     "c2kv_host_device_ptr": (c_int32, [c_void_p, c_size_t, ctypes.POINTER(c_void_p)]),
+    "c2kv_workspace_size_compose_staged": (c_size_t, [ctypes.POINTER(Segment), c_int32, c_int32, c_int32, c_int32,
+                                                      c_int32]),
+    "c2kv_compose_staged": (c_int32, [ctypes.POINTER(Segment), c_int32, P_i32, c_int32, P_i32,
+                                      c_int32, c_int32, c_int32, c_float,
+                                      c_void_p, c_void_p, c_int64, c_void_p, P_i32, P_i32,
+                                      c_int32, c_void_p, c_size_t, c_void_p]),
     "c2kv_workspace_size_prefill": (c_size_t, [P_i32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     "c2kv_attn_prefill": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                     P_i32, P_i32, c_int32, c_int32, c_int32, c_int32, c_int32, c_float,

@@ -450,13 +450,18 @@ size_t c2kv_workspace_size_compose(int32_t num_segs) {
   return 0;
 }
 
-c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32_t* req_seg_ptr, int32_t num_reqs,
+}  // extern "C"
+
+namespace {
+
+// Validation shared by both compose entry points (no HIP call): geometry of
+// every segment, request table, capacity and positions.  Fills the rows and
+// the next position of each request.
+c2kv_status compose_plan(const c2kv_segment* segs, int32_t num_segs, const int32_t* req_seg_ptr, int32_t num_reqs,
                          const int32_t* pos_base, int32_t ratio_k, int32_t hkv, int32_t head_dim, float rope_theta,
-                         void* cache_k, void* cache_v, int64_t cap, int32_t* pos_out, int32_t* cache_len_out,
-                         int32_t* next_pos_out, c2kv_dtype dt, void* workspace, size_t ws_bytes,
-                         hipStream_t stream) {
-  (void)workspace;
-  (void)ws_bytes;
+                         const void* cache_k, const void* cache_v, int64_t cap, const int32_t* pos_out,
+                         const int32_t* cache_len_out, c2kv_dtype dt, std::vector<int32_t>& lens,
+                         std::vector<int32_t>& nexts) {
   c2kv_status s;
   if ((s = check_heads(hkv, hkv, head_dim, dt))) return s;
   if ((s = check_theta(rope_theta))) return s;
@@ -470,7 +475,8 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
   if (req_seg_ptr[0] != 0 || req_seg_ptr[num_reqs] != num_segs)
     return fail(C2KV_ERR_INVALID_ARG, "req_seg_ptr must start at 0 and end at num_segs");
   const int64_t row_elems = (int64_t)hkv * head_dim;
-  std::vector<int32_t> lens(num_reqs), nexts(num_reqs);
+  lens.assign(num_reqs, 0);
+  nexts.assign(num_reqs, 0);
   for (int32_t r = 0; r < num_reqs; ++r) {
     if (req_seg_ptr[r + 1] < req_seg_ptr[r]) return fail(C2KV_ERR_INVALID_ARG, "req_seg_ptr is not monotone at %d", r);
     int64_t rows = 0, pos = pos_base ? pos_base[r] : 0;
@@ -479,7 +485,7 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
       const c2kv_segment& g = segs[t];
       if ((s = check_dev(g.k, "segs[].k")) || (s = check_dev(g.v, "segs[].v"))) return s;
       if (g.doc_len < 1) return fail(C2KV_ERR_INVALID_ARG, "segs[%d].doc_len=%d must be >= 1", t, g.doc_len);
-      if (g.reserved != 0) return fail(C2KV_ERR_INVALID_ARG, "segs[%d].reserved must be 0", t);
+      if (g.flags & ~C2KV_SEGMENT_HOST) return fail(C2KV_ERR_INVALID_ARG, "segs[%d].flags=%d has unknown bits", t, g.flags);
       if (g.row_stride < row_elems || g.row_stride >= ((int64_t)1 << 31) || (g.row_stride * (int64_t)elem_bytes(dt)) % 16)
         return fail(C2KV_ERR_INVALID_ARG, "segs[%d].row_stride=%lld invalid (>= hkv*head_dim, 16-byte multiple)", t,
                     (long long)g.row_stride);
@@ -492,6 +498,58 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
     nexts[r] = (int32_t)pos;
   }
 
+  return C2KV_OK;
+}
+
+// Page-locked host range check; returns the device-side address of `first`.
+c2kv_status map_host_range(const void* host_ptr, size_t bytes, const void** dev_ptr) {
+  if (!host_ptr || !dev_ptr) return fail(C2KV_ERR_INVALID_ARG, "host_ptr or dev_ptr is NULL");
+  if (bytes == 0) return fail(C2KV_ERR_INVALID_ARG, "bytes must be >= 1");
+  const char* first = static_cast<const char*>(host_ptr);
+  const char* last = first + (bytes - 1);
+  if (last < first) return fail(C2KV_ERR_INVALID_ARG, "host range wraps the address space");
+  hipPointerAttribute_t a0, a1;
+  std::memset(&a0, 0, sizeof(a0));
+  std::memset(&a1, 0, sizeof(a1));
+  hipError_t e0 = hipPointerGetAttributes(&a0, first);
+  hipError_t e1 = e0 == hipSuccess ? hipPointerGetAttributes(&a1, last) : hipSuccess;
+  if (e0 != hipSuccess || e1 != hipSuccess) {
+    (void)hipGetLastError();   // the query's own failure is not a launch error
+    return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) is not page-locked host memory (%s)", host_ptr, bytes,
+                hipGetErrorString(e0 != hipSuccess ? e0 : e1));
+  }
+  if (a0.type != hipMemoryTypeHost || a1.type != hipMemoryTypeHost || !a0.devicePointer || !a1.devicePointer ||
+      !a0.hostPointer || !a1.hostPointer)
+    return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) is not page-locked host memory mapped for the device",
+                host_ptr, bytes);
+  // the attributes may describe the queried address or its allocation's
+  // base; the host-side distance to the reported host address maps either
+  const char* d0 = static_cast<const char*>(a0.devicePointer) + (first - static_cast<const char*>(a0.hostPointer));
+  const char* d1 = static_cast<const char*>(a1.devicePointer) + (last - static_cast<const char*>(a1.hostPointer));
+  if (d1 - d0 != last - first)
+    return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) spans more than one page-locked allocation", host_ptr,
+                bytes);
+  *dev_ptr = d0;
+  return C2KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32_t* req_seg_ptr, int32_t num_reqs,
+                         const int32_t* pos_base, int32_t ratio_k, int32_t hkv, int32_t head_dim, float rope_theta,
+                         void* cache_k, void* cache_v, int64_t cap, int32_t* pos_out, int32_t* cache_len_out,
+                         int32_t* next_pos_out, c2kv_dtype dt, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  c2kv_status s;
+  std::vector<int32_t> lens, nexts;
+  if ((s = compose_plan(segs, num_segs, req_seg_ptr, num_reqs, pos_base, ratio_k, hkv, head_dim, rope_theta, cache_k,
+                        cache_v, cap, pos_out, cache_len_out, dt, lens, nexts)))
+    return s;
+
   ComposeParams p;
   std::memset(&p, 0, sizeof(p));
   p.cache_k = cache_k; p.cache_v = cache_v; p.pos_out = pos_out; p.cap = cap;
@@ -501,41 +559,108 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
   p.rpt = tl.rpt; p.gpb = tl.gpb; p.nblk = tl.nblk;
   int cnt = 0;
   int32_t tiles = 0;
+  bool host_pass = false;
   auto flush = [&]() -> hipError_t {
     if (cnt == 0) return hipSuccess;
     p.num_segs = cnt;
     p.total_tiles = tiles;
-    hipError_t e = launch_compose(p, dt, head_dim, stream);
+    hipError_t e = launch_compose(p, dt, head_dim, host_pass, stream);
     cnt = 0;
     tiles = 0;
     return e;
   };
-  for (int32_t r = 0; r < num_reqs; ++r) {
-    int32_t out_row = 0;
-    int64_t pos = pos_base ? pos_base[r] : 0;
-    for (int32_t t = req_seg_ptr[r]; t < req_seg_ptr[r + 1]; ++t) {
-      const c2kv_segment& g = segs[t];
-      const int32_t m = num_slots_i(g.doc_len, ratio_k);
-      const int32_t mt = (m + rpt - 1) / rpt;
-      if (cnt == kComposeSegs || (int64_t)tiles + mt >= ((int64_t)1 << 24)) {
-        hipError_t e = flush();
-        if (e != hipSuccess) return hip_fail(e, "compose kernel launch");
+  // device segments first, then host-resident ones in launches of their own
+  for (int pass = 0; pass < 2; ++pass) {
+    host_pass = pass == 1;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+      int32_t out_row = 0;
+      int64_t pos = pos_base ? pos_base[r] : 0;
+      for (int32_t t = req_seg_ptr[r]; t < req_seg_ptr[r + 1]; ++t) {
+        const c2kv_segment& g = segs[t];
+        const int32_t m = num_slots_i(g.doc_len, ratio_k);
+        const int32_t mt = (m + rpt - 1) / rpt;
+        if (((g.flags & C2KV_SEGMENT_HOST) != 0) == host_pass) {
+          if (cnt == kComposeSegs || (int64_t)tiles + mt >= ((int64_t)1 << 24)) {
+            hipError_t e = flush();
+            if (e != hipSuccess) return hip_fail(e, "compose kernel launch");
+          }
+          ComposeSeg& d = p.segs[cnt++];
+          d.k = g.k; d.v = g.v; d.stride = (int32_t)g.row_stride; d.n = g.doc_len;
+          d.req = r; d.out_row = out_row; d.pos_off = (int32_t)pos; d.tile0 = tiles;
+          tiles += mt;
+        }
+        out_row += m;
+        pos += g.doc_len;
       }
-      ComposeSeg& d = p.segs[cnt++];
-      d.k = g.k; d.v = g.v; d.stride = (int32_t)g.row_stride; d.n = g.doc_len;
-      d.req = r; d.out_row = out_row; d.pos_off = (int32_t)pos; d.tile0 = tiles;
-      tiles += mt;
-      out_row += m;
-      pos += g.doc_len;
     }
+    hipError_t e = flush();
+    if (e != hipSuccess) return hip_fail(e, "compose kernel launch");
   }
-  hipError_t e = flush();
-  if (e != hipSuccess) return hip_fail(e, "compose kernel launch");
   for (int32_t r = 0; r < num_reqs; ++r) {
     cache_len_out[r] = lens[r];
     if (next_pos_out) next_pos_out[r] = nexts[r];
   }
   return ok();
+}
+
+size_t c2kv_workspace_size_compose_staged(const c2kv_segment* segs, int32_t num_segs, int32_t ratio_k, int32_t hkv,
+                                          int32_t head_dim, c2kv_dtype dt) {
+  if (!segs || num_segs < 1 || ratio_k < 1 || hkv < 1 || (head_dim != 64 && head_dim != 128) ||
+      (dt != C2KV_BF16 && dt != C2KV_F32))
+    return 0;
+  size_t total = 0;
+  for (int32_t t = 0; t < num_segs; ++t) {
+    if (segs[t].doc_len < 1) return 0;
+    total += 2 * align_up((size_t)num_slots_i(segs[t].doc_len, ratio_k) * hkv * head_dim * elem_bytes(dt));
+  }
+  return total;
+}
+
+c2kv_status c2kv_compose_staged(const c2kv_segment* segs, int32_t num_segs, const int32_t* req_seg_ptr,
+                                int32_t num_reqs, const int32_t* pos_base, int32_t ratio_k, int32_t hkv,
+                                int32_t head_dim, float rope_theta, void* cache_k, void* cache_v, int64_t cap,
+                                int32_t* pos_out, int32_t* cache_len_out, int32_t* next_pos_out, c2kv_dtype dt,
+                                void* workspace, size_t ws_bytes, hipStream_t stream) {
+  c2kv_status s;
+  std::vector<int32_t> lens, nexts;
+  if ((s = compose_plan(segs, num_segs, req_seg_ptr, num_reqs, pos_base, ratio_k, hkv, head_dim, rope_theta, cache_k,
+                        cache_v, cap, pos_out, cache_len_out, dt, lens, nexts)))
+    return s;
+  if ((s = check_ws(workspace, ws_bytes, c2kv_workspace_size_compose_staged(segs, num_segs, ratio_k, hkv, head_dim, dt))))
+    return s;
+  const size_t es = elem_bytes(dt), row_bytes = (size_t)hkv * head_dim * es;
+  // every source range must be page-locked, so that the copies below are
+  // asynchronous DMA on `stream` (checked for all segments before the first)
+  for (int32_t t = 0; t < num_segs; ++t) {
+    const size_t m = (size_t)num_slots_i(segs[t].doc_len, ratio_k);
+    const size_t span = ((m - 1) * (size_t)segs[t].row_stride) * es + row_bytes;
+    const void* unused;
+    if ((s = map_host_range(segs[t].k, span, &unused)) || (s = map_host_range(segs[t].v, span, &unused))) return s;
+  }
+  std::vector<c2kv_segment> staged(num_segs);
+  char* base = static_cast<char*>(workspace);
+  size_t off = 0;
+  for (int32_t t = 0; t < num_segs; ++t) {
+    const c2kv_segment& g = segs[t];
+    const size_t m = (size_t)num_slots_i(g.doc_len, ratio_k);
+    const size_t pitch = (size_t)g.row_stride * es;
+    void* dk = base + off;
+    off += align_up(m * row_bytes);
+    void* dv = base + off;
+    off += align_up(m * row_bytes);
+    hipError_t e;
+    if (pitch == row_bytes) {
+      e = hipMemcpyAsync(dk, g.k, m * row_bytes, hipMemcpyHostToDevice, stream);
+      if (e == hipSuccess) e = hipMemcpyAsync(dv, g.v, m * row_bytes, hipMemcpyHostToDevice, stream);
+    } else {
+      e = hipMemcpy2DAsync(dk, row_bytes, g.k, pitch, row_bytes, m, hipMemcpyHostToDevice, stream);
+      if (e == hipSuccess) e = hipMemcpy2DAsync(dv, row_bytes, g.v, pitch, row_bytes, m, hipMemcpyHostToDevice, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "host-to-device copy of a slot cache");
+    staged[t] = c2kv_segment{dk, dv, (int64_t)hkv * head_dim, g.doc_len, 0};
+  }
+  return c2kv_compose(staged.data(), num_segs, req_seg_ptr, num_reqs, pos_base, ratio_k, hkv, head_dim, rope_theta,
+                      cache_k, cache_v, cap, pos_out, cache_len_out, next_pos_out, dt, nullptr, 0, stream);
 }
 
 // ------------------------------------------------------ prefill / decode
@@ -582,34 +707,8 @@ c2kv_status c2kv_workspace_init(void* workspace, size_t ws_bytes, hipStream_t st
 
 // ------------------------------------------------- host-resident slot caches
 c2kv_status c2kv_host_device_ptr(const void* host_ptr, size_t bytes, const void** dev_ptr) {
-  if (!host_ptr || !dev_ptr) return fail(C2KV_ERR_INVALID_ARG, "host_ptr or dev_ptr is NULL");
-  if (bytes == 0) return fail(C2KV_ERR_INVALID_ARG, "bytes must be >= 1");
-  const char* first = static_cast<const char*>(host_ptr);
-  const char* last = first + (bytes - 1);
-  if (last < first) return fail(C2KV_ERR_INVALID_ARG, "host range wraps the address space");
-  hipPointerAttribute_t a0, a1;
-  std::memset(&a0, 0, sizeof(a0));
-  std::memset(&a1, 0, sizeof(a1));
-  hipError_t e0 = hipPointerGetAttributes(&a0, first);
-  hipError_t e1 = e0 == hipSuccess ? hipPointerGetAttributes(&a1, last) : hipSuccess;
-  if (e0 != hipSuccess || e1 != hipSuccess) {
-    (void)hipGetLastError();   // the query's own failure is not a launch error
-    return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) is not page-locked host memory (%s)", host_ptr, bytes,
-                hipGetErrorString(e0 != hipSuccess ? e0 : e1));
-  }
-  if (a0.type != hipMemoryTypeHost || a1.type != hipMemoryTypeHost || !a0.devicePointer || !a1.devicePointer ||
-      !a0.hostPointer || !a1.hostPointer)
-    return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) is not page-locked host memory mapped for the device",
-                host_ptr, bytes);
-  // the attributes may describe the queried address or its allocation's
-  // base; the host-side distance to the reported host address maps either
-  const char* d0 = static_cast<const char*>(a0.devicePointer) + (first - static_cast<const char*>(a0.hostPointer));
-  const char* d1 = static_cast<const char*>(a1.devicePointer) + (last - static_cast<const char*>(a1.hostPointer));
-  if (d1 - d0 != last - first)
-    return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) spans more than one page-locked allocation", host_ptr,
-                bytes);
-  *dev_ptr = d0;
-  return ok();
+  c2kv_status s = map_host_range(host_ptr, bytes, dev_ptr);
+  return s ? s : ok();
 }
 
 // ---------------------------------------------------------------- testing

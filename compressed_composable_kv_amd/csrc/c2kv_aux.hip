@@ -224,20 +224,24 @@ __global__ __launch_bounds__(256) void compose_kernel(const ComposeParams p) {
 }
 
 template <typename T, int D>
-static hipError_t launch_compose_t(const ComposeParams& p, hipStream_t st) {
+static hipError_t launch_compose_t(const ComposeParams& p, bool host_src, hipStream_t st) {
   const int units = p.total_tiles * p.nblk;
   if (units == 0) return hipSuccess;
-  // three workgroups per CU (12 waves) is the measured optimum for 1k-2k
-  // units: fewer leaves HBM idle, more adds dispatch without more bytes
-  // in flight (the loop already prefetches one unit ahead)
-  const int blocks = min(units, 3 * 256);
+  // device sources: three workgroups per CU (12 waves) is the measured
+  // optimum for 1k-2k units: fewer leaves HBM idle, more adds dispatch
+  // without more bytes in flight (the loop already prefetches one unit
+  // ahead).  Host sources: 16 workgroups (about 1 MB in flight) keep the
+  // host link busy; more concurrent readers made its transfers slower
+  // (56 GB/s at 12-16 workgroups, 48 GB/s at 192 or more).
+  const int blocks = min(units, host_src ? 16 : 3 * 256);
   hipLaunchKernelGGL((compose_kernel<T, D>), dim3(blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_compose(const ComposeParams& p, int dtype, int head_dim, hipStream_t st) {
-  if (dtype == C2KV_BF16) return head_dim == 128 ? launch_compose_t<bf16, 128>(p, st) : launch_compose_t<bf16, 64>(p, st);
-  return head_dim == 128 ? launch_compose_t<float, 128>(p, st) : launch_compose_t<float, 64>(p, st);
+hipError_t launch_compose(const ComposeParams& p, int dtype, int head_dim, bool host_src, hipStream_t st) {
+  if (dtype == C2KV_BF16)
+    return head_dim == 128 ? launch_compose_t<bf16, 128>(p, host_src, st) : launch_compose_t<bf16, 64>(p, host_src, st);
+  return head_dim == 128 ? launch_compose_t<float, 128>(p, host_src, st) : launch_compose_t<float, 64>(p, host_src, st);
 }
 
 // ----------------------------------------------------------------- append

@@ -89,7 +89,7 @@ hipError_t launch_extract_attn(const ExtractParams& p, int dtype, int head_dim, 
 hipError_t launch_cache_attn(const CacheParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_decode_attn(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t st);
-hipError_t launch_compose(const ComposeParams& p, int dtype, int head_dim, hipStream_t st);
+hipError_t launch_compose(const ComposeParams& p, int dtype, int head_dim, bool host_src, hipStream_t st);
 hipError_t launch_append(const AppendParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t st);
 

@@ -159,6 +159,58 @@ def slot_views(k: torch.Tensor, v: torch.Tensor, doc_lens: Sequence[int], ratio_
 
 # ------------------------------------------------------------- composition
 
+def _segment_table(requests, cache_k: torch.Tensor, staged: bool):
+    R, hkv, cap, d = cache_k.shape
+    _need(len(requests) == R, "one segment list per request")
+    segs, ptr, keep = [], [0], []
+    for req in requests:
+        for sk, sv, n in req:
+            _need(sk.dtype == cache_k.dtype and sv.dtype == cache_k.dtype, "segments must have the cache dtype")
+            _need(sk.dim() == 3 and sk.shape[1:] == (hkv, d) and sv.shape == sk.shape, "segment shape")
+            _need(sk.stride(2) == 1 and sk.stride(1) == d and sv.stride() == sk.stride(), "segment layout")
+            flags = 0
+            if staged:
+                # copied by the library from host memory: host addresses
+                _need(not sk.is_cuda and not sv.is_cuda and sk.is_pinned() and sv.is_pinned(),
+                      "staged compose takes pinned (page-locked) CPU segments")
+                pk, pv = sk.data_ptr(), sv.data_ptr()
+            elif sk.is_cuda and sv.is_cuda:
+                pk, pv = sk.data_ptr(), sv.data_ptr()
+            else:
+                # slot caches kept in host memory: compose reads them in place
+                pk, pv = host_device_ptr(sk), host_device_ptr(sv)
+                flags = _lib.SEGMENT_HOST
+            segs.append(Segment(pk, pv, sk.stride(0), int(n), flags))
+            keep.append((sk, sv))
+        ptr.append(len(segs))
+    _need(len(segs) > 0, "no segments")
+    return (Segment * len(segs))(*segs), _arr_i32(ptr), keep
+
+
+def _compose_call(fn, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base, pos_out, staged, workspace):
+    lib = load()
+    _dev_tensor(cache_k, "cache_k")
+    _dev_tensor(cache_v, "cache_v", cache_k.dtype)
+    R, hkv, cap, d = cache_k.shape
+    arr, ptr, keep = _segment_table(requests, cache_k, staged)
+    lens = (ctypes.c_int32 * R)()
+    nxt = (ctypes.c_int32 * R)()
+    if pos_out is not None:
+        _dev_tensor(pos_out, "pos_out", torch.int32)
+        _need(pos_out.shape == (R, cap), "pos_out must be [R][cap]")
+    base = _arr_i32(pos_base) if pos_base is not None else None
+    dt = _DT[cache_k.dtype]
+    ws, nbytes = None, 0
+    if staged:
+        need = lib.c2kv_workspace_size_compose_staged(arr, len(arr), ratio_k, hkv, d, dt)
+        _need(need > 0, "invalid staged compose arguments")
+        ws = _workspace(workspace, "compose_staged", need, cache_k.device)
+        nbytes = ws.numel()
+    check(fn(arr, len(arr), ptr, R, base, ratio_k, hkv, d, float(rope_theta), _ptr(cache_k), _ptr(cache_v), cap,
+             _ptr(pos_out), lens, nxt, dt, _ptr(ws), nbytes, _stream(cache_k.device)))
+    return list(lens), list(nxt)
+
+
 def compose(requests: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int]]], ratio_k: int,
             rope_theta: float, cache_k: torch.Tensor, cache_v: torch.Tensor,
             pos_base: Optional[Sequence[int]] = None, pos_out: Optional[torch.Tensor] = None
@@ -168,36 +220,18 @@ def compose(requests: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int]]]
     either on the device or pinned CPU tensors (stored caches kept in host
     memory, read in place across the host link).  Returns (cache_len per
     request, next position per request)."""
-    lib = load()
-    _dev_tensor(cache_k, "cache_k")
-    _dev_tensor(cache_v, "cache_v", cache_k.dtype)
-    R, hkv, cap, d = cache_k.shape
-    _need(len(requests) == R, "one segment list per request")
-    segs, ptr, keep = [], [0], []
-    for req in requests:
-        for sk, sv, n in req:
-            _need(sk.dtype == cache_k.dtype and sv.dtype == cache_k.dtype, "segments must have the cache dtype")
-            _need(sk.dim() == 3 and sk.shape[1:] == (hkv, d) and sv.shape == sk.shape, "segment shape")
-            _need(sk.stride(2) == 1 and sk.stride(1) == d and sv.stride() == sk.stride(), "segment layout")
-            if sk.is_cuda and sv.is_cuda:
-                pk, pv = sk.data_ptr(), sv.data_ptr()
-            else:
-                # slot caches kept in host memory: compose reads them in place
-                pk, pv = host_device_ptr(sk), host_device_ptr(sv)
-            segs.append(Segment(pk, pv, sk.stride(0), int(n), 0))
-            keep.append((sk, sv))
-        ptr.append(len(segs))
-    arr = (Segment * len(segs))(*segs)
-    lens = (ctypes.c_int32 * R)()
-    nxt = (ctypes.c_int32 * R)()
-    if pos_out is not None:
-        _dev_tensor(pos_out, "pos_out", torch.int32)
-        _need(pos_out.shape == (R, cap), "pos_out must be [R][cap]")
-    base = _arr_i32(pos_base) if pos_base is not None else None
-    check(lib.c2kv_compose(arr, len(segs), _arr_i32(ptr), R, base, ratio_k, hkv, d, float(rope_theta),
-                           _ptr(cache_k), _ptr(cache_v), cap, _ptr(pos_out), lens, nxt,
-                           _DT[cache_k.dtype], None, 0, _stream(cache_k.device)))
-    return list(lens), list(nxt)
+    return _compose_call(load().c2kv_compose, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base, pos_out,
+                         False, None)
+
+
+def compose_staged(requests: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int]]], ratio_k: int,
+                   rope_theta: float, cache_k: torch.Tensor, cache_v: torch.Tensor,
+                   pos_base: Optional[Sequence[int]] = None, pos_out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[List[int], List[int]]:
+    """As compose, for segments in pinned CPU memory that the library first
+    copies into a device workspace (c2kv_compose_staged)."""
+    return _compose_call(load().c2kv_compose_staged, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base,
+                         pos_out, True, workspace)
 
 
 # ------------------------------------------------ host-resident slot caches

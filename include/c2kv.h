@@ -11,6 +11,10 @@
  *   c2kv_attn_prefill   question prefill over a composed cache (GQA)
  *   c2kv_attn_decode    one decode step over a composed cache (GQA, split-K)
  *
+ * Stored slot caches may stay in page-locked host memory: compose reads them
+ * in place (c2kv_host_device_ptr) or copies them in first
+ * (c2kv_compose_staged).
+ *
  * Sources, cited by page and section:
  *   [Explainer] "C2KV: Compressed and Composable KV Cache Reuse for Efficient
  *               LLM Inference", paper-daily.com explainer page.
@@ -25,6 +29,8 @@
  * - All arguments are validated on the host BEFORE any HIP call, so a bad
  *   argument never reaches the GPU (and can be tested on a machine without
  *   one).  Device pointers are checked for NULL and 16-byte alignment only.
+ *   Host-memory ranges (the two host-pool functions) are additionally
+ *   checked with HIP pointer queries before any copy or launch.
  * - Device tensors are dense, row-major, in the element type `dt`
  *   (C2KV_BF16 or C2KV_F32).  head_dim must be 64 or 128; hq % hkv == 0;
  *   hq / hkv <= 16.
@@ -154,8 +160,15 @@ typedef struct c2kv_segment {
   const void* v;
   int64_t row_stride;   /* elements between consecutive slot rows (>= hkv*head_dim) */
   int32_t doc_len;      /* original document length n >= 1 */
-  int32_t reserved;     /* must be 0 */
+  int32_t flags;        /* 0, or C2KV_SEGMENT_HOST */
 } c2kv_segment;
+
+/* Segment flag: k and v are device addresses of page-locked host memory
+ * (from c2kv_host_device_ptr).  c2kv_compose composes such segments in
+ * launches of their own with a small grid (16 workgroups): the host link,
+ * not the GPU, bounds them, and few concurrent readers keep its transfers
+ * efficient.  Device segments keep the full grid. */
+#define C2KV_SEGMENT_HOST 1
 
 size_t c2kv_workspace_size_compose(int32_t num_segs);
 
@@ -193,7 +206,9 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs,
  * uses them, and that move, not recomputation, dominates time to first
  * token.  A c2kv_segment whose k/v are addresses returned here makes compose
  * fetch only the compressed slot rows across the host link and rotate them
- * on arrival; no staging copy in device memory is made.
+ * on arrival; no staging copy in device memory is made.  Such segments
+ * should carry flags = C2KV_SEGMENT_HOST (correct either way; the flag
+ * selects the launch shape that reads host memory fastest).
  *   host_ptr  host address inside one allocation made page-locked by
  *             hipHostMalloc / hipHostAlloc (a pinned PyTorch CPU tensor is one)
  *   bytes     number of bytes from host_ptr the device may read, >= 1
@@ -207,6 +222,33 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs,
  * raise.
  * Errors: INVALID_ARG (NULL, bytes == 0, not mapped page-locked memory). */
 c2kv_status c2kv_host_device_ptr(const void* host_ptr, size_t bytes, const void** dev_ptr);
+
+/* Compose from stored slot caches in page-locked host memory by copying
+ * them to the device first.  Same source as c2kv_host_device_ptr ([Explainer]
+ * problem section, Fig. 1: the caches move from host memory to the GPU when
+ * a request uses them).  Each segment's m slot rows of K and V are copied
+ * (async DMA on `stream`) into the workspace, packed [m][hkv][head_dim],
+ * and c2kv_compose then runs on the staged copies.  Only compressed rows
+ * cross the host link; the copy engines move them in larger transfers than
+ * kernel reads of host memory do.
+ *   segs        host [num_segs]: k/v are HOST addresses in page-locked
+ *               memory (every byte of [k, k + ((m-1)*row_stride +
+ *               hkv*head_dim) elements) is checked before the first copy)
+ *   workspace   device, >= c2kv_workspace_size_compose_staged(...) bytes;
+ *               holds the staged rows until the compose kernel has read them
+ *   all other arguments and outputs exactly as c2kv_compose.
+ * The host memory must not be written until `stream` has passed the call.
+ * Errors: as c2kv_compose, plus INVALID_ARG for memory that is not
+ * page-locked and WORKSPACE.  The size query returns 0 for invalid input. */
+size_t c2kv_workspace_size_compose_staged(const c2kv_segment* segs, int32_t num_segs, int32_t ratio_k,
+                                          int32_t hkv, int32_t head_dim, c2kv_dtype dt);
+c2kv_status c2kv_compose_staged(const c2kv_segment* segs, int32_t num_segs,
+                                const int32_t* req_seg_ptr, int32_t num_reqs,
+                                const int32_t* pos_base,
+                                int32_t ratio_k, int32_t hkv, int32_t head_dim, float rope_theta,
+                                void* cache_k, void* cache_v, int64_t cap,
+                                int32_t* pos_out, int32_t* cache_len_out, int32_t* next_pos_out,
+                                c2kv_dtype dt, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ---- attention over the composed cache ----------------------------------- */
 

@@ -118,7 +118,7 @@ def _compose(lib, segs, ptr, cap=100, k=4, d=128, hkv=2, theta=1e6, base=None):
 def test_compose_validation(lib):
     good = (FAKE, FAKE, 256, 40, 0)
     assert _compose(lib, [good], [0, 1], cap=9) == CAPACITY           # 10 slots > cap 9
-    assert _compose(lib, [(FAKE, FAKE, 256, 40, 1)], [0, 1]) == INVALID      # reserved
+    assert _compose(lib, [(FAKE, FAKE, 256, 40, 2)], [0, 1]) == INVALID      # unknown flag bit
     assert _compose(lib, [(FAKE, FAKE, 100, 40, 0)], [0, 1]) == INVALID      # stride < hkv*d
     assert _compose(lib, [(FAKE, FAKE, 256, 0, 0)], [0, 1]) == INVALID       # empty document
     assert _compose(lib, [(None, FAKE, 256, 4, 0)], [0, 1]) == INVALID
@@ -168,3 +168,22 @@ def test_host_segment_needs_pinned_memory():
     import compressed_composable_kv_amd as c2kv
     with pytest.raises(ValueError, match="pinned"):
         c2kv.host_device_ptr(torch.zeros(4, 2, 64))
+
+
+def test_compose_staged_validation(lib):
+    from compressed_composable_kv_amd._lib import Segment
+    segs = (Segment * 1)(Segment(FAKE, FAKE, 256, 40, 0))
+    # 10 slots x 2 heads x 128 x bf16, K and V, each 256-byte aligned
+    assert lib.c2kv_workspace_size_compose_staged(segs, 1, 4, 2, 128, 0) == 2 * 5120
+    assert lib.c2kv_workspace_size_compose_staged(segs, 1, 0, 2, 128, 0) == 0
+    assert lib.c2kv_workspace_size_compose_staged(segs, 1, 4, 2, 96, 0) == 0
+    lens, nxt = (ctypes.c_int32 * 1)(), (ctypes.c_int32 * 1)()
+    ptr = _arr([0, 1])
+
+    def call(cap=16, ws=FAKE, wsb=1 << 20, k=4):
+        return lib.c2kv_compose_staged(segs, 1, ptr, 1, None, k, 2, 128, 1e4, FAKE, FAKE, cap, None, lens, nxt, 0,
+                                       ws, wsb, None)
+    assert call(cap=9) == CAPACITY              # 10 slots > cap, before any HIP query
+    assert call(k=0) == INVALID
+    assert call(wsb=100) == WORKSPACE
+    assert call(ws=None) == WORKSPACE

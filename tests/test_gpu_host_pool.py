@@ -168,3 +168,102 @@ def test_host_pool_llama_layer(c2kv):
     order = W.llama_doc_order(w)
     _host_vs_device(c2kv, [order, order[:3]], pool_k, pool_v, [4096] * 8, w.ratio_k, w.rope_theta, w.dtype,
                     oracle_reqs=[0])
+
+
+# ------------------------------------------------ staged (copy, then compose)
+
+def _staged_vs_device(c2kv, reqs_docs, pool_k, pool_v, pool_n, ratio_k, theta, dt, pos_base=None, pad_heads=0):
+    """c2kv_compose_staged over pinned host segments against c2kv_compose
+    over device copies: bit for bit.  With pad_heads the host rows carry
+    extra heads, so the segments are strided views (2-D copies)."""
+    R = len(reqs_docs)
+    hkv, d = pool_k[0].shape[1], pool_k[0].shape[2]
+    Ms = [sum(O.num_slots(pool_n[t], ratio_k) for t in docs) for docs in reqs_docs]
+    cap = max(Ms) + 1
+
+    def host(x):
+        h = torch.zeros((x.shape[0], hkv + pad_heads, d), dtype=x.dtype, pin_memory=True)
+        h[:, :hkv].copy_(x)
+        return h[:, :hkv]
+    hk = [host(x) for x in pool_k]
+    hv = [host(x) for x in pool_v]
+    outs = []
+    for staged in (True, False):
+        ck = torch.zeros((R, hkv, cap, d), dtype=dt, device=DEV)
+        cv = torch.zeros_like(ck)
+        pos = torch.full((R, cap), -1, dtype=torch.int32, device=DEV)
+        if staged:
+            reqs = [[(hk[t], hv[t], pool_n[t]) for t in docs] for docs in reqs_docs]
+            res = c2kv.compose_staged(reqs, ratio_k, theta, ck, cv, pos_base=pos_base, pos_out=pos)
+        else:
+            reqs = [[(pool_k[t].to(DEV), pool_v[t].to(DEV), pool_n[t]) for t in docs] for docs in reqs_docs]
+            res = c2kv.compose(reqs, ratio_k, theta, ck, cv, pos_base=pos_base, pos_out=pos)
+        torch.cuda.synchronize()
+        outs.append((ck, cv, pos, res))
+    (sk, sv, sp, sr), (dk, dv, dp, dr) = outs
+    assert sr == dr and sr[0] == Ms
+    assert torch.equal(sk, dk) and torch.equal(sv, dv) and torch.equal(sp, dp)
+    return sk, sv
+
+
+def test_staged_tiny_and_ragged(c2kv):
+    w = W.TINY
+    rows = c2kv.packed_rows(w.doc_lens, w.ratio_k)
+    k = W.normal((rows, w.hkv, w.head_dim), w.dtype, w.wid, W.P_K)
+    v = W.normal((rows, w.hkv, w.head_dim), w.dtype, w.wid, W.P_V)
+    views = c2kv.slot_views(k, v, w.doc_lens, w.ratio_k)
+    _staged_vs_device(c2kv, [[0, 1]], [s[0].contiguous() for s in views], [s[1].contiguous() for s in views],
+                      list(w.doc_lens), w.ratio_k, w.rope_theta, w.dtype)
+    g = torch.Generator().manual_seed(47)
+    pool_n = [int(x) for x in torch.randint(1, 900, (10,), generator=g)] + [1, 17]
+    k16, hkv, d, dt = 16, 4, 128, torch.bfloat16
+    pool_k = [W.normal((O.num_slots(n, k16), hkv, d), dt, 47, W.P_K, salt=i) for i, n in enumerate(pool_n)]
+    pool_v = [W.normal((O.num_slots(n, k16), hkv, d), dt, 47, W.P_V, salt=i) for i, n in enumerate(pool_n)]
+    reqs = [[3, 1, 4, 11, 9, 2, 6], [10, 0], list(range(12))[::-1]]
+    for pad in (0, 3):
+        _staged_vs_device(c2kv, reqs, pool_k, pool_v, pool_n, k16, 1e6, dt, pos_base=[0, 5, 70000], pad_heads=pad)
+
+
+def test_staged_rejects_pageable_and_device_segments(c2kv):
+    ck = torch.zeros((1, 1, 4, 64), device=DEV)
+    seg = torch.zeros((1, 1, 64))
+    with pytest.raises(ValueError, match="pinned"):
+        c2kv.compose_staged([[(seg, seg, 4)]], 4, 1e4, ck, ck.clone())
+    with pytest.raises(ValueError, match="pinned"):
+        c2kv.compose_staged([[(seg.to(DEV), seg.to(DEV), 4)]], 4, 1e4, ck, ck.clone())
+
+
+def test_staged_graph_replays_read_current_host_values(c2kv):
+    """A graph of staged compose calls re-reads host memory on every replay:
+    after the host pool is rewritten between replays, each replay equals an
+    eager compose of the new values."""
+    pool_n, k, hkv, d, dt = [200, 77, 4096 // 4], 4, 2, 128, torch.bfloat16
+    hk = [torch.empty((O.num_slots(n, k), hkv, d), dtype=dt, pin_memory=True) for n in pool_n]
+    hv = [torch.empty(x.shape, dtype=dt, pin_memory=True) for x in hk]
+    M = sum(O.num_slots(n, k) for n in pool_n)
+    ck = torch.zeros((1, hkv, M, d), dtype=dt, device=DEV)
+    cv = torch.zeros_like(ck)
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device=DEV)
+    reqs = [[(hk[t], hv[t], pool_n[t]) for t in (2, 0, 1)]]
+
+    def fill(salt):
+        for i, n in enumerate(pool_n):
+            hk[i].copy_(W.normal(hk[i].shape, dt, 49, W.P_K, salt=10 * salt + i))
+            hv[i].copy_(W.normal(hv[i].shape, dt, 49, W.P_V, salt=10 * salt + i))
+    fill(0)
+    c2kv.compose_staged(reqs, k, 5e5, ck, cv, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        c2kv.compose_staged(reqs, k, 5e5, ck, cv, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(1, 4):
+        fill(rep)
+        ck.zero_()
+        cv.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        ek, ev = torch.zeros_like(ck), torch.zeros_like(cv)
+        c2kv.compose([[(hk[t].to(DEV), hv[t].to(DEV), pool_n[t]) for t in (2, 0, 1)]], k, 5e5, ek, ev)
+        torch.cuda.synchronize()
+        assert torch.equal(ck, ek) and torch.equal(cv, ev), f"replay {rep}"
