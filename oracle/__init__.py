@@ -15,5 +15,5 @@ from .c2kv_oracle import (  # noqa: F401
     mask_cell_counts, round_bf16, storage_round, rope_inv_freq, rope_cos_sin,
     rope_rotate, attention, attention_brute, doc_row_offsets, extract_attn,
     compose_positions, compose, append_and_attend, decode_step,
-    kv_bytes_per_token, decode_kv_bytes,
+    kv_bytes_per_token, decode_kv_bytes, rms_norm, silu, slot_row_mask, extractor_layer,
 )

@@ -424,3 +424,84 @@ def kv_bytes_per_token(layers: int, hkv: int, d: int, elem_bytes: int) -> int:
 def decode_kv_bytes(rows: int, hkv: int, d: int, elem_bytes: int) -> int:
     """K and V bytes one decode step must read for one layer and request."""
     return rows * hkv * d * 2 * elem_bytes
+
+
+# ---------------------------------------------------------------------------
+# The extractor layer around the structured attention
+# ---------------------------------------------------------------------------
+#
+# Readings (listed again in DESIGN.md):
+# R19 the frozen base layer is the pre-norm decoder layer of the base models
+#     the pages evaluate (Llama3.1-8B, Qwen2.5, Qwen3): RMSNorm with a learned
+#     gain, attention, output projection and residual add, RMSNorm, SwiGLU
+#     FFN (silu(gate) * up, then down) and residual add.
+# R20 the C2 projections replace only Q/K/V for slot rows; the attention
+#     norm's gain, the output projection and the FFN are the frozen ones for
+#     every row ([Explainer] "C2 token" section).
+# R21 at the first layer every slot row's input is the one shared learnable
+#     vector ([Explainer] "C2 token" section).
+
+
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """x [T][D] -> x / sqrt(mean(x^2) + eps) * gamma, in fp64 (reading R19)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """x * sigmoid(x) in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def slot_row_mask(doc_lens: Sequence[int], k: int) -> np.ndarray:
+    """Boolean [sumT]: True on the slot rows of the packed layout (R4)."""
+    out = []
+    for n in doc_lens:
+        out += [False] * n + [True] * num_slots(n, k)
+    return np.array(out, dtype=bool)
+
+
+def extractor_layer(x: np.ndarray, w: Dict[str, np.ndarray], doc_lens: Sequence[int], ratio_k: int,
+                    sink_len: Optional[int], hq: int, hkv: int, d: int, theta: float, eps: float,
+                    slot_embed: Optional[np.ndarray] = None
+                    ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One layer of the frozen model with the C2 extractor attached, over a
+    batch of documents that are extracted independently.
+
+    [Explainer] "C2 token" section: document tokens keep the frozen Q/K/V
+    projections and slot tokens use their own per-layer C2 Q/K/V
+    projections; both then enter one standard attention (the structured mask
+    of the structured-flow section, with RoPE at the extraction positions);
+    the output projection, the FFN and everything else stay the frozen
+    model's.  Readings R19-R21.
+
+    x [sumT][Dm] packed per document as [n doc rows | m slot rows].
+    w: attn_norm [Dm], wqkv [(hq+2hkv)d][Dm] (frozen; rows: q heads, k
+    heads, v heads), wqkv_c2 (same shape, C2), wo [Dm][hq d], ffn_norm [Dm],
+    w_gate [F][Dm], w_up [F][Dm], w_down [Dm][F].
+    slot_embed [Dm] or None: when given, every slot row's input is set to
+    it first (the first layer, R21).
+    Returns x_out [sumT][Dm] (fp64) and this layer's stored C2KV: the slot
+    rows' pre-RoPE keys and values [sum m][hkv][d] (fp64).
+    """
+    x = np.array(x, dtype=np.float64)
+    slot = slot_row_mask(doc_lens, ratio_k)
+    assert x.shape[0] == slot.shape[0]
+    if slot_embed is not None:
+        x[slot] = np.asarray(slot_embed, dtype=np.float64)
+    T = x.shape[0]
+    h = rms_norm(x, w["attn_norm"], eps)
+    qkv = np.empty((T, (hq + 2 * hkv) * d), dtype=np.float64)
+    qkv[~slot] = h[~slot] @ np.asarray(w["wqkv"], dtype=np.float64).T
+    qkv[slot] = h[slot] @ np.asarray(w["wqkv_c2"], dtype=np.float64).T
+    q = qkv[:, : hq * d].reshape(T, hq, d)
+    k = qkv[:, hq * d: (hq + hkv) * d].reshape(T, hkv, d)
+    v = qkv[:, (hq + hkv) * d:].reshape(T, hkv, d)
+    att = extract_attn(q, k, v, doc_lens, ratio_k, sink_len, theta)
+    o = np.concatenate([att[b][0] for b in range(len(doc_lens))]).reshape(T, hq * d)
+    x = x + o @ np.asarray(w["wo"], dtype=np.float64).T
+    h2 = rms_norm(x, w["ffn_norm"], eps)
+    act = silu(h2 @ np.asarray(w["w_gate"], dtype=np.float64).T) * (h2 @ np.asarray(w["w_up"], dtype=np.float64).T)
+    x = x + act @ np.asarray(w["w_down"], dtype=np.float64).T
+    return x, k[slot], v[slot]

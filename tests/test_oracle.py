@@ -435,6 +435,137 @@ def test_kv_bytes_golden():
     assert frac == g["decode_read_fraction_k4"]
 
 
+# ------------------------------------------------------ extractor layer pins
+
+LAYER = dict(dm=64, hq=4, hkv=2, d=16, ffn=96, theta=1e4, eps=1e-5)
+
+
+def _layer_weights(seed, dm=64, hq=4, hkv=2, d=16, ffn=96):
+    r = rng(seed)
+
+    def lin(o, i):
+        return r.standard_normal((o, i)) / math.sqrt(i)
+    return {"attn_norm": 1.0 + 0.1 * r.standard_normal(dm), "wqkv": lin((hq + 2 * hkv) * d, dm),
+            "wqkv_c2": lin((hq + 2 * hkv) * d, dm), "wo": lin(dm, hq * d),
+            "ffn_norm": 1.0 + 0.1 * r.standard_normal(dm), "w_gate": lin(ffn, dm), "w_up": lin(ffn, dm),
+            "w_down": lin(dm, ffn)}
+
+
+def _base_layer_torch(x, w, hq, hkv, d, theta, eps):
+    """The frozen model's layer over one document alone, written with torch
+    ops in fp64: RMSNorm by its formula, RoPE as complex multiplication,
+    causal attention by torch SDPA, SwiGLU by torch's silu."""
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    X = t(x)
+    n = X.shape[0]
+
+    def norm(z, g):
+        return z * torch.rsqrt((z * z).mean(-1, keepdim=True) + eps) * t(g)
+    h = norm(X, w["attn_norm"])
+    qkv = h @ t(w["wqkv"]).T
+    q = qkv[:, : hq * d].reshape(n, hq, d)
+    k = qkv[:, hq * d: (hq + hkv) * d].reshape(n, hkv, d)
+    v = qkv[:, (hq + hkv) * d:].reshape(n, hkv, d)
+    ang = torch.arange(n, dtype=torch.float64)[:, None] * (theta ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d))
+    rot = torch.polar(torch.ones_like(ang), ang)[:, None, :]
+
+    def rope(z):
+        c = torch.complex(z[..., : d // 2], z[..., d // 2:]) * rot
+        return torch.cat([c.real, c.imag], dim=-1)
+    G = hq // hkv
+    qt = rope(q).permute(1, 0, 2)[None]
+    kt = rope(k).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    vt = v.permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)[0].permute(1, 0, 2)
+    X = X + o.reshape(n, hq * d) @ t(w["wo"]).T
+    h2 = norm(X, w["ffn_norm"])
+    X = X + (torch.nn.functional.silu(h2 @ t(w["w_gate"]).T) * (h2 @ t(w["w_up"]).T)) @ t(w["w_down"]).T
+    return X.numpy()
+
+
+def test_rms_norm_closed_forms():
+    g = rng(3).standard_normal(8)
+    # a constant row c*1 normalises to sign(c) / sqrt(1 + eps/c^2) times the gain
+    for c in (2.0, -0.5):
+        y = O.rms_norm(np.full((1, 8), c), g, 1e-5)
+        assert np.allclose(y, np.sign(c) / math.sqrt(1 + 1e-5 / c ** 2) * g, rtol=0, atol=1e-15)
+    # with eps = 0 the result is invariant to a positive scale and has unit rms before the gain
+    x = rng(4).standard_normal((5, 8))
+    assert np.allclose(O.rms_norm(3.7 * x, np.ones(8), 0.0), O.rms_norm(x, np.ones(8), 0.0), atol=1e-14)
+    assert np.allclose((O.rms_norm(x, np.ones(8), 0.0) ** 2).mean(-1), 1.0, atol=1e-14)
+
+
+def test_silu_values():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert abs(O.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(O.silu(np.array([1.0]))[0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+
+
+def test_layer_doc_rows_equal_base_model_layer():
+    """Document tokens keep the frozen projections and never see a slot, so
+    the document rows of the extractor layer equal the frozen model's layer
+    run on the document alone."""
+    c = LAYER
+    lens, k = [37, 20], 4
+    w = _layer_weights(11)
+    rows = O.doc_row_offsets(lens, k)
+    x = rng(12).standard_normal((rows[-1], c["dm"]))
+    out, _, _ = O.extractor_layer(x, w, lens, k, None, c["hq"], c["hkv"], c["d"], c["theta"], c["eps"])
+    for b, n in enumerate(lens):
+        ref = _base_layer_torch(x[rows[b]: rows[b] + n], w, c["hq"], c["hkv"], c["d"], c["theta"], c["eps"])
+        assert np.abs(out[rows[b]: rows[b] + n] - ref).max() < 1e-5
+
+
+def test_layer_slot_kv_are_c2_projections():
+    """The stored slot K/V of a layer are the C2 projections of the slot
+    rows' normalised input, before RoPE."""
+    c = LAYER
+    lens, k = [37, 20], 4
+    w = _layer_weights(13)
+    x = rng(14).standard_normal((O.doc_row_offsets(lens, k)[-1], c["dm"]))
+    _, sk, sv = O.extractor_layer(x, w, lens, k, None, c["hq"], c["hkv"], c["d"], c["theta"], c["eps"])
+    xs = x[O.slot_row_mask(lens, k)]
+    h = xs / np.sqrt((xs * xs).mean(-1, keepdims=True) + c["eps"]) * w["attn_norm"]
+    hd, q0 = c["hkv"] * c["d"], c["hq"] * c["d"]
+    assert np.abs(sk.reshape(len(xs), hd) - h @ w["wqkv_c2"][q0: q0 + hd].T).max() < 1e-12
+    assert np.abs(sv.reshape(len(xs), hd) - h @ w["wqkv_c2"][q0 + hd:].T).max() < 1e-12
+
+
+def test_layer_slot_rows_and_c2_weights_leave_doc_rows_alone():
+    """Changing the slot rows' input or the C2 projections changes slot rows
+    and leaves every document row bit for bit the same."""
+    c = LAYER
+    lens, k = [29, 8], 4
+    w = _layer_weights(15)
+    slot = O.slot_row_mask(lens, k)
+    x = rng(16).standard_normal((len(slot), c["dm"]))
+    base, _, _ = O.extractor_layer(x, w, lens, k, None, c["hq"], c["hkv"], c["d"], c["theta"], c["eps"])
+    x2 = x.copy()
+    x2[slot] += 1.0
+    w2 = dict(w, wqkv_c2=_layer_weights(17)["wqkv_c2"])
+    for xx, ww in ((x2, w), (x, w2)):
+        out, _, _ = O.extractor_layer(xx, ww, lens, k, None, c["hq"], c["hkv"], c["d"], c["theta"], c["eps"])
+        assert np.array_equal(out[~slot], base[~slot])
+        assert np.abs(out[slot] - base[slot]).max() > 1e-3
+
+
+def test_layer_slot_embed_sets_slot_inputs():
+    """With the shared slot vector given, the slot rows' own input values no
+    longer matter, and the result equals writing that vector into them."""
+    c = LAYER
+    lens, k = [30, 9], 4
+    w = _layer_weights(18)
+    slot = O.slot_row_mask(lens, k)
+    x = rng(19).standard_normal((len(slot), c["dm"]))
+    e = rng(20).standard_normal(c["dm"])
+    a = O.extractor_layer(x, w, lens, k, None, c["hq"], c["hkv"], c["d"], c["theta"], c["eps"], slot_embed=e)
+    x2 = x.copy()
+    x2[slot] = e
+    b = O.extractor_layer(x2, w, lens, k, None, c["hq"], c["hkv"], c["d"], c["theta"], c["eps"])
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
 # --------------------------------------------------- planted-mistake checks
 
 
@@ -499,3 +630,22 @@ def test_planted_offset_mistake_caught(monkeypatch):
         pos[m0:] -= lens[0]                      # forget the first document's length
         return pos, offs, nxt
     _pins_fail(monkeypatch, "compose_positions", no_cumulative, test_positions_golden)
+
+
+def test_planted_layer_weight_mistake_caught(monkeypatch):
+    # slot rows projected with the frozen weights instead of the C2 ones
+    orig = O.c2kv_oracle.extractor_layer
+
+    def frozen_for_slots(x, w, *a, **kw):
+        return orig(x, dict(w, wqkv_c2=w["wqkv"]), *a, **kw)
+    monkeypatch.setattr(O, "extractor_layer", frozen_for_slots)
+    with pytest.raises(AssertionError):
+        test_layer_slot_kv_are_c2_projections()
+
+
+def test_planted_layer_norm_mistake_caught(monkeypatch):
+    # RMSNorm without the gain
+    monkeypatch.setattr(O.c2kv_oracle, "rms_norm", lambda x, g, eps: np.asarray(x, dtype=np.float64) / np.sqrt(
+        np.mean(np.asarray(x, dtype=np.float64) ** 2, axis=-1, keepdims=True) + eps))
+    with pytest.raises(AssertionError):
+        test_layer_doc_rows_equal_base_model_layer()
