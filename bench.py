@@ -42,6 +42,9 @@ Loading stored caches from pinned host memory (32 layers of the Llama
 shapes): compose reading the slot caches in place across the host link,
 against copying the full caches, one JSON line:
     python bench.py --host-pool
+One extractor layer (norms, frozen / C2 projections, attention, FFN) at the
+Llama3.1-8B shapes over the 8 x 4096-token batch, one JSON line:
+    python bench.py --layer
 
 One phase alone, for counter runs under rocprofv3:
     python bench.py --profile-phase extract --calls 2
@@ -207,6 +210,7 @@ def parse():
     ap.add_argument("--extract-sweep", action="store_true")
     ap.add_argument("--compose-sweep", action="store_true")
     ap.add_argument("--host-pool", action="store_true")
+    ap.add_argument("--layer", action="store_true")
     ap.add_argument("--profile-phase", choices=("extract", "compose", "prefill", "decode"),
                     help="run only this phase of the step --calls times (for counter runs), print nothing else")
     ap.add_argument("--calls", type=int, default=2)
@@ -419,6 +423,68 @@ def compose_sweep():
           flush=True)
 
 
+def layer_bench():
+    """One extractor layer at the Llama3.1-8B shapes (dm 4096, 32/8 heads of
+    128, FFN 14336, bf16, theta 5e5) over 8 documents of 4096 tokens at
+    k = 4 (40 960 packed rows): norms, frozen / C2 projections, structured
+    attention, output projection and SwiGLU FFN.  Random N(0, 1)/sqrt(fan_in)
+    weights.  FLOPs count the matrix products (dense) plus the attention's
+    visible cells.  Best of five calls, HIP events."""
+    import torch
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = W.LLAMA
+    d, hq, hkv, k, theta = w.head_dim, w.hq, w.hkv, w.ratio_k, w.rope_theta
+    dm, ffn = 4096, 14336
+    lens = list(w.doc_lens)
+    rows = c2kv.packed_rows(lens, k)
+
+    def lin(o, i, salt):
+        return (W.device_normal((o, i), torch.float32, w.wid, W.P_K, dev, salt=400 + salt) / math.sqrt(i)).to(
+            torch.bfloat16)
+    nq = (hq + 2 * hkv) * d
+    wts = {"attn_norm": torch.ones(dm, dtype=torch.bfloat16, device=dev), "wqkv": lin(nq, dm, 1),
+           "wqkv_c2": lin(nq, dm, 2), "wo": lin(dm, hq * d, 3),
+           "ffn_norm": torch.ones(dm, dtype=torch.bfloat16, device=dev), "w_gate_up": lin(2 * ffn, dm, 4),
+           "w_down": lin(dm, ffn, 5)}
+    x0 = W.device_normal((rows, dm), torch.bfloat16, w.wid, W.P_Q, dev, salt=400)
+    x = x0.clone()
+    ko = torch.empty((rows, hkv, d), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+    emb = W.device_normal((dm,), torch.bfloat16, w.wid, W.P_V, dev, salt=400)
+    ws = torch.empty(c2kv.workspace_size_extract_layer(lens, k, dm, hq, hkv, d, ffn), dtype=torch.uint8, device=dev)
+
+    def call():
+        x.copy_(x0)
+        c2kv.extract_layer(x, wts, ko, vo, lens, k, k, hq, theta, 1e-5, slot_embed=emb, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    copy_ms = None
+    best = None
+    for _ in range(5):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        x.copy_(x0)
+        e1.record()
+        c2kv.extract_layer(x, wts, ko, vo, lens, k, k, hq, theta, 1e-5, slot_embed=emb, workspace=ws)
+        e2.record()
+        torch.cuda.synchronize()
+        t = e1.elapsed_time(e2)
+        best = t if best is None else min(best, t)
+        copy_ms = e0.elapsed_time(e1)
+    gemm = 2 * rows * dm * (nq + hq * d + 2 * ffn + ffn)
+    attn = hq * 4 * d * sum(visible_cells(n, k) for n in lens)
+    tf = (gemm + attn) / (best * 1e-3) / 1e12
+    ach = achievable_peaks(torch, dev)
+    print(json.dumps({"workload": "llama31_8b_extractor_layer", "docs": len(lens), "doc_tokens": lens[0],
+                      "ratio_k": k, "rows": rows, "dm": dm, "ffn": ffn, "ms": best, "gemm_tflop": gemm / 1e12,
+                      "attn_tflop": attn / 1e12, "tflops": tf, "frac_of_peak": tf / BF16_PEAK_TFLOPS,
+                      "frac_of_achievable": tf / ach["mfma_bf16_tflops"] if ach["mfma_bf16_tflops"] else None,
+                      "input_restore_copy_ms": copy_ms}), flush=True)
+
+
 PCIE_PEAK_GBS = 64.0           # MI355X host link, PCIe 5.0 x16, one direction, GB/s
 
 
@@ -587,6 +653,9 @@ def main():
         return
     if a.host_pool:
         host_pool()
+        return
+    if a.layer:
+        layer_bench()
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this path does not shard "

@@ -33,6 +33,11 @@ class Segment(ctypes.Structure):
                 ("doc_len", c_int32), ("flags", c_int32)]
 
 
+class LayerWeights(ctypes.Structure):
+    _fields_ = [("attn_norm", c_void_p), ("wqkv", c_void_p), ("wqkv_c2", c_void_p), ("wo", c_void_p),
+                ("ffn_norm", c_void_p), ("w_gate_up", c_void_p), ("w_down", c_void_p)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "c2kv_version": (c_char_p, []),
@@ -46,6 +51,11 @@ SIGNATURES = {
                                     P_i32, c_int32, c_int32, c_int32,
                                     c_int32, c_int32, c_int32, c_float, c_int32,
                                     c_void_p, c_size_t, c_void_p]),
+    "c2kv_workspace_size_extract_layer": (c_size_t, [P_i32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                                     c_int32, c_int32]),
+    "c2kv_extract_layer": (c_int32, [c_void_p, c_void_p, ctypes.POINTER(LayerWeights), c_void_p, c_void_p,
+                                     P_i32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                     c_int32, c_float, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
     "c2kv_workspace_size_compose": (c_size_t, [c_int32]),
     "c2kv_compose": (c_int32, [ctypes.POINTER(Segment), c_int32, P_i32, c_int32, P_i32,
                                c_int32, c_int32, c_int32, c_float,

@@ -444,6 +444,164 @@ c2kv_status c2kv_extract_attn(const void* q, const void* k, const void* v, void*
   return ok();
 }
 
+// ---------------------------------------------------------- extractor layer
+}  // extern "C"
+
+namespace {
+
+struct LayerLayout {
+  ExtractLayout ex;
+  size_t h_off = 0, q_off = 0, o_off = 0, gu_off = 0, act_off = 0, ex_off = 0, ex_bytes = 0, total = 0;
+};
+
+c2kv_status layer_layout(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t dm, int32_t hq,
+                         int32_t hkv, int32_t head_dim, int32_t ffn, c2kv_dtype dt, LayerLayout& L) {
+  c2kv_status s;
+  if ((s = check_heads(hq, hkv, head_dim, dt))) return s;
+  if (dt != C2KV_BF16) return fail(C2KV_ERR_UNSUPPORTED, "the extractor layer runs in bf16 only");
+  if (dm < 128 || dm % 128 || dm > 32768) return fail(C2KV_ERR_UNSUPPORTED, "dm=%d must be a multiple of 128 up to 32768", dm);
+  if (ffn < 64 || ffn % 64 || ffn > (1 << 20)) return fail(C2KV_ERR_UNSUPPORTED, "ffn=%d must be a positive multiple of 64", ffn);
+  if ((hq * head_dim) % 128 || (hkv * head_dim) % 128)
+    return fail(C2KV_ERR_UNSUPPORTED, "hq*head_dim and hkv*head_dim must be multiples of 128");
+  if ((s = extract_layout(doc_lens, num_docs, ratio_k, hkv, head_dim, dt, L.ex))) return s;
+  const size_t T = (size_t)L.ex.rows, es = 2;
+  if ((int64_t)T * std::max(dm, 2 * ffn) >= ((int64_t)1 << 40)) return fail(C2KV_ERR_CAPACITY, "layer buffers too large");
+  size_t off = 0;
+  L.h_off = off;   off += align_up(T * dm * es);
+  L.q_off = off;   off += align_up(T * hq * head_dim * es);
+  L.o_off = off;   off += align_up(T * hq * head_dim * es);
+  L.gu_off = off;  off += align_up(T * 2 * ffn * es);
+  L.act_off = off; off += align_up(T * ffn * es);
+  L.ex_off = off;
+  L.ex_bytes = c2kv_workspace_size_extract(doc_lens, num_docs, ratio_k, hkv, head_dim, dt);
+  off += align_up(L.ex_bytes);
+  L.total = off;
+  return C2KV_OK;
+}
+
+// C = A * B^T over all rows [0, rows) with one weight matrix.
+hipError_t gemm_all_rows(const void* a, int64_t lda, const void* b, int K, int N, void* c, int64_t ldc,
+                         const void* resid, int64_t rows, hipStream_t st) {
+  GemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.a = static_cast<const bf16*>(a);
+  p.b0 = p.b1 = static_cast<const bf16*>(b);
+  p.c0 = p.c1 = p.c2 = static_cast<bf16*>(c);
+  p.r = static_cast<const bf16*>(resid);
+  p.lda = lda; p.ldc0 = p.ldc1 = p.ldc2 = ldc; p.ldr = ldc;
+  p.K = K; p.N = N; p.n1 = p.n2 = N;
+  p.num_ranges = 1;
+  p.ranges[0] = GemmRange{0, (int32_t)rows, 0, 0};
+  p.m_tiles = (int32_t)ceil_div(rows, 128);
+  p.n_tiles = N / 128;
+  return launch_gemm(p, resid != nullptr, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t c2kv_workspace_size_extract_layer(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t dm,
+                                         int32_t hq, int32_t hkv, int32_t head_dim, int32_t ffn, c2kv_dtype dt) {
+  LayerLayout L;
+  if (layer_layout(doc_lens, num_docs, ratio_k, dm, hq, hkv, head_dim, ffn, dt, L)) return 0;
+  return L.total;
+}
+
+c2kv_status c2kv_extract_layer(void* x, const void* slot_embed, const c2kv_layer_weights* w, void* k_out,
+                               void* v_out, const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k,
+                               int32_t sink_len, int32_t dm, int32_t hq, int32_t hkv, int32_t head_dim,
+                               int32_t ffn, float rope_theta, float rms_eps, c2kv_dtype dt, void* workspace,
+                               size_t ws_bytes, hipStream_t stream) {
+  c2kv_status s;
+  LayerLayout L;
+  if ((s = layer_layout(doc_lens, num_docs, ratio_k, dm, hq, hkv, head_dim, ffn, dt, L))) return s;
+  if ((s = check_theta(rope_theta))) return s;
+  if (!(rms_eps >= 0.0f) || !std::isfinite(rms_eps)) return fail(C2KV_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (sink_len < 0) return fail(C2KV_ERR_INVALID_ARG, "sink_len=%d must be >= 0", sink_len);
+  if (!w) return fail(C2KV_ERR_INVALID_ARG, "weights is NULL");
+  if ((s = check_dev(x, "x")) || (s = check_dev(k_out, "k_out")) || (s = check_dev(v_out, "v_out")) ||
+      (s = check_dev(w->attn_norm, "attn_norm")) || (s = check_dev(w->wqkv, "wqkv")) ||
+      (s = check_dev(w->wqkv_c2, "wqkv_c2")) || (s = check_dev(w->wo, "wo")) ||
+      (s = check_dev(w->ffn_norm, "ffn_norm")) || (s = check_dev(w->w_gate_up, "w_gate_up")) ||
+      (s = check_dev(w->w_down, "w_down")))
+    return s;
+  if (slot_embed && (s = check_dev(slot_embed, "slot_embed"))) return s;
+  if ((s = check_ws(workspace, ws_bytes, L.total))) return s;
+  char* ws = static_cast<char*>(workspace);
+  void* h = ws + L.h_off;
+  void* q = ws + L.q_off;
+  void* o = ws + L.o_off;
+  void* gu = ws + L.gu_off;
+  void* act = ws + L.act_off;
+  const int64_t T = L.ex.rows;
+  const int qd = hq * head_dim, kd = hkv * head_dim, nqkv = qd + 2 * kd;
+  hipError_t e;
+
+  // slot rows take the shared vector (first layer)
+  if (slot_embed) {
+    int64_t row = 0;
+    for (int32_t b0 = 0; b0 < num_docs; b0 += C2KV_MAX_BATCH) {
+      SlotFillParams fp;
+      std::memset(&fp, 0, sizeof(fp));
+      fp.x = x; fp.embed = slot_embed; fp.dm = dm;
+      int slots = 0;
+      const int cnt = std::min<int>(C2KV_MAX_BATCH, num_docs - b0);
+      for (int i = 0; i < cnt; ++i) {
+        const int32_t n = doc_lens[b0 + i], m = num_slots_i(n, ratio_k);
+        fp.docs[i] = SlotFillDoc{row + n, slots, 0};
+        slots += m;
+        row += n + m;
+      }
+      fp.num_docs = cnt;
+      if ((e = launch_slot_fill(fp, slots, stream)) != hipSuccess) return hip_fail(e, "slot fill launch");
+    }
+  }
+  if ((e = launch_rms_norm(x, w->attn_norm, h, T, dm, rms_eps, stream)) != hipSuccess) return hip_fail(e, "rms norm launch");
+
+  // q | k | v: frozen weights on document rows, C2 weights on slot rows
+  {
+    int64_t row = 0;
+    for (int32_t b0 = 0; b0 < num_docs; b0 += C2KV_MAX_BATCH) {
+      GemmParams p;
+      std::memset(&p, 0, sizeof(p));
+      p.a = static_cast<const bf16*>(h);
+      p.b0 = static_cast<const bf16*>(w->wqkv);
+      p.b1 = static_cast<const bf16*>(w->wqkv_c2);
+      p.c0 = static_cast<bf16*>(q);
+      p.c1 = static_cast<bf16*>(k_out);
+      p.c2 = static_cast<bf16*>(v_out);
+      p.lda = dm; p.ldc0 = qd; p.ldc1 = kd; p.ldc2 = kd;
+      p.K = dm; p.N = nqkv; p.n1 = qd; p.n2 = qd + kd;
+      p.n_tiles = nqkv / 128;
+      int tiles = 0, nr = 0;
+      const int cnt = std::min<int>(C2KV_MAX_BATCH, num_docs - b0);
+      for (int i = 0; i < cnt; ++i) {
+        const int32_t n = doc_lens[b0 + i], m = num_slots_i(n, ratio_k);
+        p.ranges[nr++] = GemmRange{(int32_t)row, n, 0, tiles};
+        tiles += (int)ceil_div(n, 128);
+        p.ranges[nr++] = GemmRange{(int32_t)(row + n), m, 1, tiles};
+        tiles += (int)ceil_div(m, 128);
+        row += n + m;
+      }
+      p.num_ranges = nr;
+      p.m_tiles = tiles;
+      if ((e = launch_gemm(p, false, stream)) != hipSuccess) return hip_fail(e, "qkv projection launch");
+    }
+  }
+  if ((s = c2kv_extract_attn(q, k_out, v_out, o, nullptr, doc_lens, num_docs, ratio_k, sink_len, hq, hkv, head_dim,
+                             rope_theta, dt, ws + L.ex_off, L.ex_bytes, stream)))
+    return s;
+  if ((e = gemm_all_rows(o, qd, w->wo, qd, dm, x, dm, x, T, stream)) != hipSuccess) return hip_fail(e, "output projection launch");
+  if ((e = launch_rms_norm(x, w->ffn_norm, h, T, dm, rms_eps, stream)) != hipSuccess) return hip_fail(e, "rms norm launch");
+  if ((e = gemm_all_rows(h, dm, w->w_gate_up, dm, 2 * ffn, gu, 2 * ffn, nullptr, T, stream)) != hipSuccess)
+    return hip_fail(e, "gate/up projection launch");
+  if ((e = launch_swiglu(gu, act, T, ffn, stream)) != hipSuccess) return hip_fail(e, "swiglu launch");
+  if ((e = gemm_all_rows(act, ffn, w->w_down, ffn, dm, x, dm, x, T, stream)) != hipSuccess)
+    return hip_fail(e, "down projection launch");
+  return ok();
+}
+
 // ------------------------------------------------------------ composition
 size_t c2kv_workspace_size_compose(int32_t num_segs) {
   (void)num_segs;

@@ -83,6 +83,40 @@ struct AppendParams {
   AppendReq reqs[C2KV_MAX_BATCH];
 };
 
+// Extractor layer GEMM C = A * B^T (bf16, fp32 accumulation).  A row range
+// of A uses weights b0 (sel 0) or b1 (sel 1); tile0 is its first 128-row
+// tile.  Columns [0, n1) go to c0, [n1, n2) to c1, [n2, N) to c2 (each
+// boundary a multiple of 128).  With a residual, C = r + A * B^T.
+struct GemmRange {
+  int32_t row0, rows, sel, tile0;
+};
+constexpr int kGemmRanges = 128;   // two per document of a 64-document chunk
+struct GemmParams {
+  const bf16* a;
+  const bf16* b0;
+  const bf16* b1;
+  bf16* c0;
+  bf16* c1;
+  bf16* c2;
+  const bf16* r;
+  int64_t lda, ldc0, ldc1, ldc2, ldr;
+  int32_t K, N, n1, n2, num_ranges, m_tiles, n_tiles, pad;
+  GemmRange ranges[kGemmRanges];
+};
+static_assert(sizeof(GemmParams) <= 4096, "gemm table must fit the kernel arguments");
+
+struct SlotFillDoc {
+  int64_t row0;    // first slot row of the document
+  int32_t slot0;   // index of its first slot within the launch
+  int32_t pad;
+};
+struct SlotFillParams {
+  void* x;
+  const void* embed;
+  int32_t dm, num_docs;
+  SlotFillDoc docs[C2KV_MAX_BATCH];
+};
+
 hipError_t launch_rope_table(float2* table, int npos, int head_dim, const RopeFreqs& f, hipStream_t st);
 hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_extract_attn(const ExtractParams& p, int dtype, int head_dim, bool count, hipStream_t st);
@@ -92,5 +126,10 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream
 hipError_t launch_compose(const ComposeParams& p, int dtype, int head_dim, bool host_src, hipStream_t st);
 hipError_t launch_append(const AppendParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t st);
+hipError_t launch_gemm(const GemmParams& p, bool resid, hipStream_t st);
+hipError_t launch_rms_norm(const void* x, const void* gamma, void* h, int64_t rows, int dm, float eps,
+                           hipStream_t st);
+hipError_t launch_swiglu(const void* gu, void* act, int64_t rows, int ffn, hipStream_t st);
+hipError_t launch_slot_fill(const SlotFillParams& p, int slots, hipStream_t st);
 
 }  // namespace c2kv

@@ -1,0 +1,247 @@
+// The extractor layer around the structured attention, on gfx950:
+//   * gemm_nt_kernel: C = A * B^T in bf16 with fp32 accumulation on
+//     v_mfma_f32_16x16x32_bf16, 128x128 output tiles, K in steps of 64
+//     staged through LDS (double buffered, XOR-swizzled 16-byte chunks).
+//     A row-range table picks the weight matrix per row tile (document rows
+//     take the frozen projections, slot rows the C2 ones); the epilogue
+//     either splits columns over up to three outputs (q | k | v) or adds a
+//     residual in fp32 and rounds once.
+//   * rms_norm_kernel: one workgroup per row, fp32 sum of squares.
+//   * swiglu_kernel: silu(gate) * up, rounded to bf16.
+//   * slot_fill_kernel: writes the shared slot vector into every slot row.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "c2kv_device.hpp"
+#include "c2kv_launch.hpp"
+
+namespace c2kv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGM = 128, kGN = 128, kGK = 64;
+constexpr int kGroupM = 16;   // row tiles per group of the tile order
+
+// Tile order: groups of kGroupM row tiles; inside a group the row tile
+// varies fastest, so the resident workgroups cover about 16 row tiles x 32
+// column tiles and both operand slices stay in cache while they are reused.
+__device__ __forceinline__ void gemm_tile(int b, int m_tiles, int n_tiles, int& mt, int& nt) {
+  const int group_tiles = kGroupM * n_tiles;
+  const int g = b / group_tiles, local = b % group_tiles;
+  const int gm0 = g * kGroupM;
+  const int gsz = min(kGroupM, m_tiles - gm0);
+  mt = gm0 + local % gsz;
+  nt = local / gsz;
+}
+
+template <bool RESID>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[2][2][kGM * kGK];   // [buffer][A, B]: 64 KB
+  const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int mt, nt;
+  gemm_tile((int)blockIdx.x, p.m_tiles, p.n_tiles, mt, nt);
+  int lo = 0, hi = p.num_ranges - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.ranges[mid].tile0 <= mt) lo = mid; else hi = mid - 1;
+  }
+  const GemmRange rg = p.ranges[lo];
+  const int row0 = rg.row0 + (mt - rg.tile0) * kGM;
+  const int valid = min(kGM, rg.row0 + rg.rows - row0);
+  const bf16* B = rg.sel ? p.b1 : p.b0;
+  const int n0 = nt * kGN;
+
+  // global -> LDS: 16-byte chunk c = tid + 256 i holds row c / 8, k chunk
+  // c % 8; rows past the range repeat a valid row (their results are not
+  // stored)
+  const int lr = tid >> 3, lkc = tid & 7;
+  const bf16* ga = p.a + (int64_t)(row0 + min(lr, valid - 1)) * p.lda + lkc * 8;
+  const bf16* gb = B + (int64_t)(n0 + lr) * p.K + lkc * 8;
+  const int64_t bstep = (int64_t)32 * p.K;
+  int arow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) arow[i] = min(lr + 32 * i, valid - 1) - min(lr, valid - 1);   // row offset from ga
+  const int loff0 = lr * kGK + ((lkc ^ (lr & 7)) << 3);       // (lr + 32 i) & 7 == lr & 7
+  u32x4 ra[4], rb[4];   // native vectors: arrays of HIP's uint4 struct stay in private memory
+#define C2KV_GLOAD(kt)                                                                        \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+    ra[i] = *reinterpret_cast<const u32x4*>(ga + (int64_t)arow[i] * p.lda + (kt) * kGK);      \
+    rb[i] = *reinterpret_cast<const u32x4*>(gb + i * bstep + (kt) * kGK);                    \
+  }
+#define C2KV_LSTORE(buf)                                                                      \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+    *reinterpret_cast<u32x4*>(&lds[buf][0][loff0 + i * 32 * kGK]) = ra[i];                   \
+    *reinterpret_cast<u32x4*>(&lds[buf][1][loff0 + i * 32 * kGK]) = rb[i];                   \
+  }
+
+  // C^T tiles: the weight rows (n) are the MFMA's A operand and the input
+  // rows (m) its B operand, so each lane ends with 4 consecutive columns of
+  // one output row.  Wave (wm, wn) owns rows wm*64.. and columns wn*64..
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = p.K / kGK;
+  C2KV_GLOAD(0)
+  C2KV_LSTORE(0)
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) { C2KV_GLOAD(kt + 1) }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kc = s * 4 + (lane >> 4);   // both operands: k elements 8*(lane/16).. of slab s
+      bf16x8 wf[4], xf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rn = wn * 64 + i * 16 + (lane & 15);
+        const int rm = wm * 64 + i * 16 + (lane & 15);
+        wf[i] = *reinterpret_cast<const bf16x8*>(&lds[buf][1][rn * kGK + ((kc ^ (rn & 7)) << 3)]);
+        xf[i] = *reinterpret_cast<const bf16x8*>(&lds[buf][0][rm * kGK + ((kc ^ (rm & 7)) << 3)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma16(wf[i], xf[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) { C2KV_LSTORE(buf ^ 1) }
+    __syncthreads();
+  }
+#undef C2KV_GLOAD
+#undef C2KV_LSTORE
+
+  // lane holds C[row0 + wm*64 + j*16 + lane%16][n0 + wn*64 + i*16 + 4*(lane/16) + 0..3]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ml = wm * 64 + j * 16 + (lane & 15);
+    if (ml >= valid) continue;
+    const int64_t row = row0 + ml;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + wn * 64 + i * 16 + 4 * (lane >> 4);
+      bf16* dst;
+      if (n < p.n1) dst = p.c0 + row * p.ldc0 + n;
+      else if (n < p.n2) dst = p.c1 + row * p.ldc1 + (n - p.n1);
+      else dst = p.c2 + row * p.ldc2 + (n - p.n2);
+      float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
+      if (RESID) {
+        const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(p.r + row * p.ldr + n);
+        v0 += to_f32(r4[0]);
+        v1 += to_f32(r4[1]);
+        v2 += to_f32(r4[2]);
+        v3 += to_f32(r4[3]);
+      }
+      bf16x4 o4;
+      o4[0] = from_f32<bf16>(v0);
+      o4[1] = from_f32<bf16>(v1);
+      o4[2] = from_f32<bf16>(v2);
+      o4[3] = from_f32<bf16>(v3);
+      *reinterpret_cast<bf16x4*>(dst) = o4;
+    }
+  }
+}
+
+hipError_t launch_gemm(const GemmParams& p, bool resid, hipStream_t st) {
+  const int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
+  if (tiles == 0) return hipSuccess;
+  if (resid) hipLaunchKernelGGL((gemm_nt_kernel<true>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((gemm_nt_kernel<false>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- RMSNorm
+// h[r] = bf16(x[r] / sqrt(mean(x[r]^2) + eps) * gamma), one workgroup per
+// row, 8 elements per thread and step.
+__global__ __launch_bounds__(256) void rms_norm_kernel(const bf16* __restrict__ x, const bf16* __restrict__ gamma,
+                                                       bf16* __restrict__ h, int dm, float eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int tid = (int)threadIdx.x;
+  const bf16* xr = x + row * dm;
+  float ss = 0.f;
+  for (int c = tid; c < dm / 8; c += 256) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(xr + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += to_f32(v[e]) * to_f32(v[e]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float rs = 1.0f / sqrtf(tot / (float)dm + eps);
+  bf16* hr = h + row * dm;
+  for (int c = tid; c < dm / 8; c += 256) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(xr + c * 8);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(gamma + c * 8);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = from_f32<bf16>(to_f32(v[e]) * rs * to_f32(g[e]));
+    *reinterpret_cast<bf16x8*>(hr + c * 8) = o;
+  }
+}
+
+hipError_t launch_rms_norm(const void* x, const void* gamma, void* h, int64_t rows, int dm, float eps,
+                           hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(rms_norm_kernel, dim3((unsigned)rows), dim3(256), 0, st, static_cast<const bf16*>(x),
+                     static_cast<const bf16*>(gamma), static_cast<bf16*>(h), dm, eps);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- SwiGLU
+// act[r][f] = bf16(silu(g) * u) with g = gu[r][f], u = gu[r][ffn + f].
+__global__ __launch_bounds__(256) void swiglu_kernel(const bf16* __restrict__ gu, bf16* __restrict__ act,
+                                                     int64_t rows, int ffn) {
+  const int64_t chunks = rows * (ffn / 8);
+  for (int64_t c = blockIdx.x * 256ll + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
+    const int64_t r = c / (ffn / 8);
+    const int f = (int)(c % (ffn / 8)) * 8;
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(gu + r * 2 * ffn + f);
+    const bf16x8 u = *reinterpret_cast<const bf16x8*>(gu + r * 2 * ffn + ffn + f);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float gv = to_f32(g[e]);
+      o[e] = from_f32<bf16>(gv / (1.0f + expf(-gv)) * to_f32(u[e]));
+    }
+    *reinterpret_cast<bf16x8*>(act + r * ffn + f) = o;
+  }
+}
+
+hipError_t launch_swiglu(const void* gu, void* act, int64_t rows, int ffn, hipStream_t st) {
+  const int64_t chunks = rows * (ffn / 8);
+  if (chunks == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 256 * 8);
+  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const bf16*>(gu),
+                     static_cast<bf16*>(act), rows, ffn);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------- slot fill
+// One workgroup per slot row of the launch's documents: x[row] = embed.
+__global__ __launch_bounds__(256) void slot_fill_kernel(const SlotFillParams p) {
+  const int s = (int)blockIdx.x;
+  int lo = 0, hi = p.num_docs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.docs[mid].slot0 <= s) lo = mid; else hi = mid - 1;
+  }
+  const int64_t row = p.docs[lo].row0 + (s - p.docs[lo].slot0);
+  bf16* xr = static_cast<bf16*>(p.x) + row * p.dm;
+  const bf16* e = static_cast<const bf16*>(p.embed);
+  for (int c = (int)threadIdx.x; c < p.dm / 8; c += 256)
+    *reinterpret_cast<uint4*>(xr + c * 8) = *reinterpret_cast<const uint4*>(e + c * 8);
+}
+
+hipError_t launch_slot_fill(const SlotFillParams& p, int slots, hipStream_t st) {
+  if (slots == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_fill_kernel, dim3((unsigned)slots), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace c2kv

@@ -145,6 +145,57 @@ def extract_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_lens: Se
     return o, lse
 
 
+LAYER_WEIGHTS = ("attn_norm", "wqkv", "wqkv_c2", "wo", "ffn_norm", "w_gate_up", "w_down")
+
+
+def workspace_size_extract_layer(doc_lens: Sequence[int], ratio_k: int, dm: int, hq: int, hkv: int,
+                                 head_dim: int, ffn: int) -> int:
+    return int(load().c2kv_workspace_size_extract_layer(_arr_i32(doc_lens), len(doc_lens), ratio_k, dm, hq, hkv,
+                                                        head_dim, ffn, _DT[torch.bfloat16]))
+
+
+def extract_layer(x: torch.Tensor, weights: dict, k_out: torch.Tensor, v_out: torch.Tensor,
+                  doc_lens: Sequence[int], ratio_k: int, sink_len: Optional[int], hq: int,
+                  rope_theta: float, rms_eps: float, slot_embed: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> None:
+    """One extractor layer (c2kv_extract_layer), bf16.  x [sum_T][dm] is
+    updated in place; k_out/v_out [sum_T][hkv][d] receive the layer's
+    pre-RoPE keys and values (their slot rows are the stored C2KV).
+    weights: {attn_norm [dm], wqkv and wqkv_c2 [(hq+2hkv)d][dm], wo [dm][hq d],
+    ffn_norm [dm], w_gate_up [2 ffn][dm], w_down [dm][ffn]} on the device."""
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16)
+    _dev_tensor(k_out, "k_out", torch.bfloat16)
+    _dev_tensor(v_out, "v_out", torch.bfloat16)
+    for nm in LAYER_WEIGHTS:
+        _need(nm in weights, f"weights needs {nm}")
+        _dev_tensor(weights[nm], nm, torch.bfloat16)
+    rows, dm = x.shape
+    _, hkv, d = k_out.shape
+    ffn = weights["w_down"].shape[1]
+    _need(rows == packed_rows(doc_lens, ratio_k) and k_out.shape[0] == rows and v_out.shape == k_out.shape,
+          "x/k_out/v_out rows must be the packed rows of doc_lens")
+    _need(weights["wqkv"].shape == ((hq + 2 * hkv) * d, dm) and weights["wqkv_c2"].shape == weights["wqkv"].shape,
+          "wqkv shape")
+    _need(weights["wo"].shape == (dm, hq * d) and weights["w_gate_up"].shape == (2 * ffn, dm)
+          and weights["w_down"].shape == (dm, ffn), "wo / w_gate_up / w_down shape")
+    _need(weights["attn_norm"].shape == (dm,) and weights["ffn_norm"].shape == (dm,), "norm gain shape")
+    if slot_embed is not None:
+        _dev_tensor(slot_embed, "slot_embed", torch.bfloat16)
+        _need(slot_embed.shape == (dm,), "slot_embed must be [dm]")
+    if sink_len is None:
+        sink_len = ratio_k
+    lens = _arr_i32(doc_lens)
+    nbytes = lib.c2kv_workspace_size_extract_layer(lens, len(doc_lens), ratio_k, dm, hq, hkv, d, ffn,
+                                                   _DT[torch.bfloat16])
+    _need(nbytes > 0, "invalid extractor layer arguments (shapes off the tile grid?)")
+    ws = _workspace(workspace, "layer", nbytes, x.device)
+    lw = _lib.LayerWeights(*[weights[nm].data_ptr() for nm in LAYER_WEIGHTS])
+    check(lib.c2kv_extract_layer(_ptr(x), _ptr(slot_embed), ctypes.byref(lw), _ptr(k_out), _ptr(v_out), lens,
+                                 len(doc_lens), ratio_k, sink_len, dm, hq, hkv, d, ffn, float(rope_theta),
+                                 float(rms_eps), _DT[torch.bfloat16], _ptr(ws), ws.numel(), _stream(x.device)))
+
+
 def slot_views(k: torch.Tensor, v: torch.Tensor, doc_lens: Sequence[int], ratio_k: int
                ) -> List[Tuple[torch.Tensor, torch.Tensor, int]]:
     """The stored C2KV of each document: views of its slot rows in the packed

@@ -6,6 +6,8 @@
  *
  *   c2kv_extract_attn   structured-flow attention of the extractor over one
  *                       batch of documents (doc tokens + C2 slot tokens)
+ *   c2kv_extract_layer  that attention inside a whole extractor layer
+ *                       (norms, frozen / C2 projections, FFN)
  *   c2kv_compose        RoPE-realigned concatenation of pre-RoPE slot K/V of
  *                       several documents into one contiguous cache
  *   c2kv_attn_prefill   question prefill over a composed cache (GQA)
@@ -148,6 +150,56 @@ c2kv_status c2kv_extract_attn(const void* q, const void* k, const void* v,
                               int32_t hq, int32_t hkv, int32_t head_dim,
                               float rope_theta, c2kv_dtype dt,
                               void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- extraction: one extractor layer around the attention ---------------- */
+
+/* Weights of one layer (device pointers, bf16, row-major).  [Explainer]
+ * "C2 token" section: document tokens keep the frozen Q/K/V projections,
+ * slot tokens use their own per-layer C2 projections, and everything else
+ * (output projection, FFN) is the frozen model's.  The norm and FFN form
+ * the pre-norm decoder layer of the base models the pages evaluate
+ * (Llama3.1-8B, Qwen2.5, Qwen3). */
+typedef struct c2kv_layer_weights {
+  const void* attn_norm;   /* [dm]  RMSNorm gain before attention */
+  const void* wqkv;        /* [(hq+2*hkv)*head_dim][dm] frozen Q/K/V (rows: q heads, k heads, v heads) */
+  const void* wqkv_c2;     /* same shape: the C2 projections, used for slot rows */
+  const void* wo;          /* [dm][hq*head_dim] output projection */
+  const void* ffn_norm;    /* [dm]  RMSNorm gain before the FFN */
+  const void* w_gate_up;   /* [2*ffn][dm]: gate rows, then up rows */
+  const void* w_down;      /* [dm][ffn] */
+} c2kv_layer_weights;
+
+size_t c2kv_workspace_size_extract_layer(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k,
+                                         int32_t dm, int32_t hq, int32_t hkv, int32_t head_dim,
+                                         int32_t ffn, c2kv_dtype dt);
+
+/* One layer of the frozen model with the C2 extractor attached, over a batch
+ * of independently extracted documents packed as for c2kv_extract_attn.
+ *   x           device [sum_T][dm] hidden states, updated in place:
+ *               x += attn(...) W_o^T, then x += FFN(RMSNorm(x))
+ *   slot_embed  device [dm] or NULL: when given, every slot row of x is set
+ *               to this shared vector first (the first layer: all C2 tokens
+ *               share one learnable embedding, [Explainer] "C2 token")
+ *   k_out,v_out device [sum_T][hkv][head_dim]: this layer's pre-RoPE keys
+ *               and values; their slot rows are the stored C2KV of the layer
+ * Steps: h = RMSNorm(x) * attn_norm; [q|k|v] = h W^T with W = wqkv for
+ * document rows and wqkv_c2 for slot rows; o = c2kv_extract_attn(q, k, v)
+ * (structured mask, RoPE at extraction positions, sink_len, rope_theta);
+ * x += o W_o^T; h = RMSNorm(x) * ffn_norm; x += (silu(h Wg^T) * (h Wu^T)) Wd^T.
+ * RMSNorm(x) = x / sqrt(mean(x^2) + rms_eps).  Matrix products accumulate
+ * in fp32; h, q, attention output, gate/up and the SwiGLU product are
+ * rounded to bf16, and each residual add is done in fp32 and rounded once.
+ * bf16 only.  Requires dm % 128 == 0, ffn % 64 == 0, and hq*head_dim and
+ * hkv*head_dim multiples of 128.
+ * Errors: INVALID_ARG, UNSUPPORTED (fp32, shapes off the tile grid),
+ * WORKSPACE, CAPACITY, HIP. */
+c2kv_status c2kv_extract_layer(void* x, const void* slot_embed, const c2kv_layer_weights* w,
+                               void* k_out, void* v_out,
+                               const int32_t* doc_lens, int32_t num_docs,
+                               int32_t ratio_k, int32_t sink_len,
+                               int32_t dm, int32_t hq, int32_t hkv, int32_t head_dim, int32_t ffn,
+                               float rope_theta, float rms_eps, c2kv_dtype dt,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ---- composition --------------------------------------------------------- */
 

@@ -187,3 +187,27 @@ def test_compose_staged_validation(lib):
     assert call(k=0) == INVALID
     assert call(wsb=100) == WORKSPACE
     assert call(ws=None) == WORKSPACE
+
+
+def test_extract_layer_validation(lib):
+    from compressed_composable_kv_amd._lib import LayerWeights
+    lens = _arr([100, 37])
+    # dm 256, 4/2 heads of 128, ffn 512
+    n = lib.c2kv_workspace_size_extract_layer(lens, 2, 4, 256, 4, 2, 128, 512, 0)
+    T = 100 + 25 + 37 + 10
+    assert n >= T * (256 + 2 * 512 + 2 * 512 + 512) * 2
+    assert lib.c2kv_workspace_size_extract_layer(lens, 2, 4, 256, 4, 2, 128, 512, 1) == 0     # fp32
+    assert lib.c2kv_workspace_size_extract_layer(lens, 2, 4, 200, 4, 2, 128, 512, 0) == 0     # dm off the grid
+    assert lib.c2kv_workspace_size_extract_layer(lens, 2, 4, 256, 4, 2, 128, 100, 0) == 0     # ffn off the grid
+    assert lib.c2kv_workspace_size_extract_layer(lens, 2, 4, 256, 3, 1, 64, 512, 0) == 0      # hkv*d = 64
+    w = LayerWeights(*([FAKE] * 7))
+
+    def call(dm=256, ffn=512, ws=FAKE, wsb=1 << 40, weights=w, eps=1e-5, dt=0):
+        return lib.c2kv_extract_layer(FAKE, None, ctypes.byref(weights) if weights else None, FAKE, FAKE, lens, 2,
+                                      4, 4, dm, 4, 2, 128, ffn, 5e5, eps, dt, ws, wsb, None)
+    assert call(dm=200) == UNSUPPORTED
+    assert call(dt=1) == UNSUPPORTED
+    assert call(weights=None) == INVALID
+    assert call(wsb=100) == WORKSPACE
+    assert call(eps=-1.0) == INVALID
+    assert call(weights=LayerWeights(*([FAKE] * 6 + [None]))) == INVALID
