@@ -1,7 +1,8 @@
 // The extractor layer around the structured attention, on gfx950:
 //   * gemm_nt_kernel: C = A * B^T in bf16 with fp32 accumulation on
 //     v_mfma_f32_16x16x32_bf16, 128x128 output tiles, K in steps of 64
-//     staged through LDS (double buffered, XOR-swizzled 16-byte chunks).
+//     brought into LDS by buffer_load ... lds (two stages, XOR-swizzled
+//     16-byte chunks).
 //     A row-range table picks the weight matrix per row tile (document rows
 //     take the frozen projections, slot rows the C2 ones); the epilogue
 //     either splits columns over up to three outputs (q | k | v) or adds a
@@ -18,8 +19,6 @@
 
 namespace c2kv {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kGM = 128, kGN = 128, kGK = 64;
 constexpr int kGroupM = 16;   // row tiles per group of the tile order
 
@@ -35,9 +34,14 @@ __device__ __forceinline__ void gemm_tile(int b, int m_tiles, int n_tiles, int& 
   nt = local / gsz;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <bool RESID>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 lds[2][2][kGM * kGK];   // [buffer][A, B]: 64 KB
+  __shared__ __attribute__((aligned(1024))) bf16 lds[2][2][kGM * kGK];   // [stage][A, B]: 64 KB
+  // the stages are written only by buffer_load ... lds; escape them so the
+  // compiler does not treat them as never-stored memory
+  asm volatile("" : : "r"(&lds[0][0][0]) : "memory");
   const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int mt, nt;
   gemm_tile((int)blockIdx.x, p.m_tiles, p.n_tiles, mt, nt);
@@ -52,27 +56,30 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
   const bf16* B = rg.sel ? p.b1 : p.b0;
   const int n0 = nt * kGN;
 
-  // global -> LDS: 16-byte chunk c = tid + 256 i holds row c / 8, k chunk
-  // c % 8; rows past the range repeat a valid row (their results are not
-  // stored)
-  const int lr = tid >> 3, lkc = tid & 7;
-  const bf16* ga = p.a + (int64_t)(row0 + min(lr, valid - 1)) * p.lda + lkc * 8;
-  const bf16* gb = B + (int64_t)(n0 + lr) * p.K + lkc * 8;
-  const int64_t bstep = (int64_t)32 * p.K;
-  int arow[4];
+  // LDS DMA: each tile (A or B) is 16 blocks of 1 KB (8 rows of 64 k);
+  // wave w fills blocks 4w..4w+3 of both.  Lane l of block b fills LDS slot
+  // (row b*8 + l/8, chunk l%8) with logical k chunk (l%8) ^ (row & 7), the
+  // XOR swizzle the operand reads undo.  Rows past the range repeat a valid
+  // row (their results are not stored).  The K step goes into the
+  // wave-uniform offset.
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.a + (int64_t)row0 * p.lda), 0, (int)((int64_t)valid * p.lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(B + (int64_t)n0 * p.K), 0, (int)((int64_t)kGN * p.K * 2), 0x00020000);
+  int aoff[4], boff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) arow[i] = min(lr + 32 * i, valid - 1) - min(lr, valid - 1);   // row offset from ga
-  const int loff0 = lr * kGK + ((lkc ^ (lr & 7)) << 3);       // (lr + 32 i) & 7 == lr & 7
-  u32x4 ra[4], rb[4];   // native vectors: arrays of HIP's uint4 struct stay in private memory
-#define C2KV_GLOAD(kt)                                                                        \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
-    ra[i] = *reinterpret_cast<const u32x4*>(ga + (int64_t)arow[i] * p.lda + (kt) * kGK);      \
-    rb[i] = *reinterpret_cast<const u32x4*>(gb + i * bstep + (kt) * kGK);                    \
+  for (int j = 0; j < 4; ++j) {
+    const int row = (wave * 4 + j) * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ (row & 7);
+    aoff[j] = (int)((int64_t)min(row, valid - 1) * p.lda * 2) + kc * 16;
+    boff[j] = row * p.K * 2 + kc * 16;
   }
-#define C2KV_LSTORE(buf)                                                                      \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
-    *reinterpret_cast<u32x4*>(&lds[buf][0][loff0 + i * 32 * kGK]) = ra[i];                   \
-    *reinterpret_cast<u32x4*>(&lds[buf][1][loff0 + i * 32 * kGK]) = rb[i];                   \
+#define C2KV_DMA(kt, st)                                                                                   \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                        \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void*)&lds[st][0][(wave * 4 + j) * 512], 16, aoff[j], \
+                                             (kt) * kGK * 2, 0, 0);                                      \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void*)&lds[st][1][(wave * 4 + j) * 512], 16, boff[j], \
+                                             (kt) * kGK * 2, 0, 0);                                      \
   }
 
   // C^T tiles: the weight rows (n) are the MFMA's A operand and the input
@@ -86,12 +93,14 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = p.K / kGK;
-  C2KV_GLOAD(0)
-  C2KV_LSTORE(0)
-  __syncthreads();
+  C2KV_DMA(0, 0)
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) { C2KV_GLOAD(kt + 1) }
+    // this wave's DMA of step kt has landed; after the barrier every
+    // wave's has, and every wave is done reading the other stage
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (kt + 1 < nk) { C2KV_DMA(kt + 1, buf ^ 1) }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int kc = s * 4 + (lane >> 4);   // both operands: k elements 8*(lane/16).. of slab s
@@ -108,11 +117,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mma16(wf[i], xf[j], acc[i][j]);
     }
-    if (kt + 1 < nk) { C2KV_LSTORE(buf ^ 1) }
-    __syncthreads();
   }
-#undef C2KV_GLOAD
-#undef C2KV_LSTORE
+#undef C2KV_DMA
 
   // lane holds C[row0 + wm*64 + j*16 + lane%16][n0 + wn*64 + i*16 + 4*(lane/16) + 0..3]
 #pragma unroll
