@@ -267,3 +267,18 @@ def test_staged_graph_replays_read_current_host_values(c2kv):
         c2kv.compose([[(hk[t].to(DEV), hv[t].to(DEV), pool_n[t]) for t in (2, 0, 1)]], k, 5e5, ek, ev)
         torch.cuda.synchronize()
         assert torch.equal(ck, ek) and torch.equal(cv, ev), f"replay {rep}"
+
+
+def test_host_pool_more_segments_than_one_launch(c2kv):
+    """75 segments in two requests, all in host memory and then half and
+    half: compose splits them into launches of at most 64 segments of one
+    residency."""
+    g = torch.Generator().manual_seed(53)
+    pool_n = [int(x) for x in torch.randint(1, 120, (75,), generator=g)]
+    k, hkv, d, dt = 4, 2, 64, torch.bfloat16
+    pool_k = [W.normal((O.num_slots(n, k), hkv, d), dt, 53, W.P_K, salt=i) for i, n in enumerate(pool_n)]
+    pool_v = [W.normal((O.num_slots(n, k), hkv, d), dt, 53, W.P_V, salt=i) for i, n in enumerate(pool_n)]
+    reqs = [list(range(0, 75, 2)), list(range(1, 75, 2))[::-1]]
+    for mix in (False, True):
+        _host_vs_device(c2kv, reqs, pool_k, pool_v, pool_n, k, 5e5, dt, pos_base=[0, 11], mix=mix)
+    _staged_vs_device(c2kv, reqs, pool_k, pool_v, pool_n, k, 5e5, dt, pos_base=[0, 11])

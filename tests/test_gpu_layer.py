@@ -124,3 +124,29 @@ def test_extract_layer_doc_rows_ignore_slots(c2kv):
         for u, v in zip(a, b):
             assert torch.equal(u[~slot], v[~slot])
         assert not torch.equal(a[0][slot], b[0][slot])
+
+
+def test_extract_layer_more_documents_than_one_launch(c2kv):
+    """70 short ragged documents: the q|k|v projection and the slot fill
+    run in chunks of 64 documents, and the attention in launches of 64."""
+    g = torch.Generator().manual_seed(72)
+    doc_lens = [int(x) for x in torch.randint(1, 40, (70,), generator=g)]
+    k, dm, hq, hkv, d, ffn, theta, eps = 4, 128, 2, 1, 128, 128, 1e4, 1e-5
+    rows = c2kv.packed_rows(doc_lens, k)
+    x = W.normal((rows, dm), torch.bfloat16, 72, W.P_Q)
+    w = make_weights(72, dm, hq, hkv, d, ffn)
+    embed = W.normal((dm,), torch.bfloat16, 72, W.P_V)
+    gx, gk, gv = run_layer(c2kv, x, w, doc_lens, k, hq, hkv, d, theta, eps, embed)
+    rx, rk, rv = O.extractor_layer(x.float().numpy(), oracle_weights(w, ffn), doc_lens, k, None, hq, hkv, d, theta,
+                                   eps, slot_embed=embed.float().numpy())
+    slot = O.slot_row_mask(doc_lens, k)
+    x_in = x.float().numpy().astype(np.float64)
+    x_in[slot] = embed.float().numpy()
+    got = gx.float().numpy().astype(np.float64)
+    assert np.abs(got - rx).max() <= 0.1
+    dg, dr = got - x_in, rx - x_in
+    rel = np.linalg.norm(dg - dr, axis=1) / np.maximum(np.linalg.norm(dr, axis=1), 1e-30)
+    assert rel.max() <= 3e-2, f"row-relative update error {rel.max()} at row {rel.argmax()}"
+    r2 = rk.reshape(len(rk), -1)
+    g2 = gk.float().numpy()[slot].reshape(len(rk), -1).astype(np.float64)
+    assert (np.linalg.norm(g2 - r2, axis=1) / np.linalg.norm(r2, axis=1)).max() <= 1e-2
