@@ -46,6 +46,9 @@ R11 GQA: query head h reads KV head floor(h / (Hq / Hkv)).
 R12 softmax scale 1/sqrt(d), no capping; no row is ever fully masked.
 R13 an appended key is stored in the cache dtype; attention reads the
     stored (rounded) value.  Rotated queries stay fp32 in the oracle.
+R23 the ablation without positional realignment gives every composed
+    document the offset pos_base (its extraction positions), instead of the
+    cumulative original length of the documents before it.
 """
 from __future__ import annotations
 
@@ -331,28 +334,33 @@ def extract_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, doc_lens: Sequence
 
 
 def compose_positions(doc_lens_in_order: Sequence[int], ratio_k: int,
-                      pos_base: int = 0) -> Tuple[np.ndarray, List[int], int]:
+                      pos_base: int = 0, realign: bool = True) -> Tuple[np.ndarray, List[int], int]:
     """Realigned slot positions of a composition.
 
     [Explainer] positions section: each compressed document occupies as
     many positions as its original length; later documents are shifted by
     the cumulative original length of the earlier ones (a 400-token document
     gives slots 3, 7, ..., 399 and the next document's first slot is 403).
-    Returns (positions of every composed row, per-document offsets, the
-    position just after the last document).
+    With realign=False (the experimental-results section's ablation without
+    positional realignment, reading R23) every document keeps its
+    extraction positions: its offset is pos_base, not shifted by the
+    earlier documents.  Returns (positions of every composed row,
+    per-document offsets, the position just after the last document; the
+    latter is pos_base + the sum of the lengths either way).
     """
     pos, offsets = [], []
     off = pos_base
     for n in doc_lens_in_order:
-        offsets.append(off)
-        pos.extend(off + slot_position(n, ratio_k, j) for j in range(num_slots(n, ratio_k)))
+        doc_off = off if realign else pos_base
+        offsets.append(doc_off)
+        pos.extend(doc_off + slot_position(n, ratio_k, j) for j in range(num_slots(n, ratio_k)))
         off += n
     return np.array(pos, dtype=np.int64), offsets, off
 
 
 def compose(slot_k: Sequence[np.ndarray], slot_v: Sequence[np.ndarray],
             doc_lens_in_order: Sequence[int], ratio_k: int, theta: float,
-            dtype: str, pos_base: int = 0):
+            dtype: str, pos_base: int = 0, realign: bool = True):
     """Compose pre-RoPE slot caches into one contiguous cache.
 
     [Explainer] overall-flow and positions sections: the stored slot K/V
@@ -361,10 +369,11 @@ def compose(slot_k: Sequence[np.ndarray], slot_v: Sequence[np.ndarray],
     no recomputation.  K rows are rotated in fp32 and rounded to the storage
     dtype; V rows are copied unchanged (reading R7).
 
-    slot_k[t], slot_v[t]: [m_t][Hkv][d].  Returns (cache_k [M][Hkv][d] fp32
-    values, cache_v, positions [M] int64, next position).
+    slot_k[t], slot_v[t]: [m_t][Hkv][d].  realign=False composes without
+    positional realignment (see compose_positions).  Returns (cache_k
+    [M][Hkv][d] fp32 values, cache_v, positions [M] int64, next position).
     """
-    pos, _, nxt = compose_positions(doc_lens_in_order, ratio_k, pos_base)
+    pos, _, nxt = compose_positions(doc_lens_in_order, ratio_k, pos_base, realign)
     ks = np.concatenate([np.asarray(x, dtype=np.float32) for x in slot_k], axis=0)
     vs = np.concatenate([np.asarray(x, dtype=np.float32) for x in slot_v], axis=0)
     assert ks.shape[0] == pos.shape[0]

@@ -566,6 +566,40 @@ def test_layer_slot_embed_sets_slot_inputs():
         assert np.array_equal(u, v)
 
 
+# ------------------------------------------- ablation without realignment
+
+def test_no_realignment_positions_golden():
+    """Without realignment both 400-token documents of the worked example
+    keep slots 3, 7, ..., 399 (the second document's first slot is 3, not
+    403); the question still starts after both original lengths."""
+    g = load("positions.json")
+    pos, offs, nxt = O.compose_positions([400, 400], 4, realign=False)
+    first = list(range(3, 400, 4))
+    assert pos.tolist() == first + first
+    assert offs == [0, 0] and nxt == 800
+    # with realignment, the printed 403
+    assert O.compose_positions([400, 400], 4)[0][100] == 403 == g["second_doc_first_slot"]
+
+
+def test_no_realignment_equals_each_document_alone():
+    """Composing without realignment gives, row for row, what composing each
+    document alone at the same base gives; the first document is the same
+    with or without realignment."""
+    lens, k, hkv, d = [37, 20, 9], 4, 2, 16
+    sk, sv = _slot_caches(lens, k, hkv, d, 31)
+    ck, cv, pos, _ = O.compose(sk, sv, lens, k, 1e4, "f32", 5, realign=False)
+    row = 0
+    for t, n in enumerate(lens):
+        a_k, a_v, a_pos, _ = O.compose([sk[t]], [sv[t]], [n], k, 1e4, "f32", 5)
+        m = len(a_pos)
+        assert np.array_equal(ck[row:row + m], a_k) and np.array_equal(cv[row:row + m], a_v)
+        assert np.array_equal(pos[row:row + m], a_pos)
+        row += m
+    r_k, _, r_pos, _ = O.compose(sk, sv, lens, k, 1e4, "f32", 5)
+    m0 = O.num_slots(lens[0], k)
+    assert np.array_equal(r_k[:m0], ck[:m0]) and not np.array_equal(r_pos[m0:], pos[m0:])
+
+
 # --------------------------------------------------- planted-mistake checks
 
 
