@@ -26,6 +26,7 @@ P_f32 = ctypes.POINTER(ctypes.c_float)
 
 
 SEGMENT_HOST = 1   # C2KV_SEGMENT_HOST
+SEGMENT_NO_REALIGN = 2   # C2KV_SEGMENT_NO_REALIGN
 
 
 class Segment(ctypes.Structure):

@@ -643,7 +643,8 @@ c2kv_status compose_plan(const c2kv_segment* segs, int32_t num_segs, const int32
       const c2kv_segment& g = segs[t];
       if ((s = check_dev(g.k, "segs[].k")) || (s = check_dev(g.v, "segs[].v"))) return s;
       if (g.doc_len < 1) return fail(C2KV_ERR_INVALID_ARG, "segs[%d].doc_len=%d must be >= 1", t, g.doc_len);
-      if (g.flags & ~C2KV_SEGMENT_HOST) return fail(C2KV_ERR_INVALID_ARG, "segs[%d].flags=%d has unknown bits", t, g.flags);
+      if (g.flags & ~(C2KV_SEGMENT_HOST | C2KV_SEGMENT_NO_REALIGN))
+        return fail(C2KV_ERR_INVALID_ARG, "segs[%d].flags=%d has unknown bits", t, g.flags);
       if (g.row_stride < row_elems || g.row_stride >= ((int64_t)1 << 31) || (g.row_stride * (int64_t)elem_bytes(dt)) % 16)
         return fail(C2KV_ERR_INVALID_ARG, "segs[%d].row_stride=%lld invalid (>= hkv*head_dim, 16-byte multiple)", t,
                     (long long)g.row_stride);
@@ -744,7 +745,8 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
           }
           ComposeSeg& d = p.segs[cnt++];
           d.k = g.k; d.v = g.v; d.stride = (int32_t)g.row_stride; d.n = g.doc_len;
-          d.req = r; d.out_row = out_row; d.pos_off = (int32_t)pos; d.tile0 = tiles;
+          d.req = r; d.out_row = out_row; d.tile0 = tiles;
+          d.pos_off = (int32_t)((g.flags & C2KV_SEGMENT_NO_REALIGN) ? (pos_base ? pos_base[r] : 0) : pos);
           tiles += mt;
         }
         out_row += m;
@@ -815,7 +817,7 @@ c2kv_status c2kv_compose_staged(const c2kv_segment* segs, int32_t num_segs, cons
       if (e == hipSuccess) e = hipMemcpy2DAsync(dv, row_bytes, g.v, pitch, row_bytes, m, hipMemcpyHostToDevice, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "host-to-device copy of a slot cache");
-    staged[t] = c2kv_segment{dk, dv, (int64_t)hkv * head_dim, g.doc_len, 0};
+    staged[t] = c2kv_segment{dk, dv, (int64_t)hkv * head_dim, g.doc_len, g.flags & C2KV_SEGMENT_NO_REALIGN};
   }
   return c2kv_compose(staged.data(), num_segs, req_seg_ptr, num_reqs, pos_base, ratio_k, hkv, head_dim, rope_theta,
                       cache_k, cache_v, cap, pos_out, cache_len_out, next_pos_out, dt, nullptr, 0, stream);

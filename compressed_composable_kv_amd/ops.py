@@ -210,7 +210,7 @@ def slot_views(k: torch.Tensor, v: torch.Tensor, doc_lens: Sequence[int], ratio_
 
 # ------------------------------------------------------------- composition
 
-def _segment_table(requests, cache_k: torch.Tensor, staged: bool):
+def _segment_table(requests, cache_k: torch.Tensor, staged: bool, realign: bool = True):
     R, hkv, cap, d = cache_k.shape
     _need(len(requests) == R, "one segment list per request")
     segs, ptr, keep = [], [0], []
@@ -231,6 +231,8 @@ def _segment_table(requests, cache_k: torch.Tensor, staged: bool):
                 # slot caches kept in host memory: compose reads them in place
                 pk, pv = host_device_ptr(sk), host_device_ptr(sv)
                 flags = _lib.SEGMENT_HOST
+            if not realign:
+                flags |= _lib.SEGMENT_NO_REALIGN
             segs.append(Segment(pk, pv, sk.stride(0), int(n), flags))
             keep.append((sk, sv))
         ptr.append(len(segs))
@@ -238,12 +240,13 @@ def _segment_table(requests, cache_k: torch.Tensor, staged: bool):
     return (Segment * len(segs))(*segs), _arr_i32(ptr), keep
 
 
-def _compose_call(fn, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base, pos_out, staged, workspace):
+def _compose_call(fn, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base, pos_out, staged, workspace,
+                  realign=True):
     lib = load()
     _dev_tensor(cache_k, "cache_k")
     _dev_tensor(cache_v, "cache_v", cache_k.dtype)
     R, hkv, cap, d = cache_k.shape
-    arr, ptr, keep = _segment_table(requests, cache_k, staged)
+    arr, ptr, keep = _segment_table(requests, cache_k, staged, realign)
     lens = (ctypes.c_int32 * R)()
     nxt = (ctypes.c_int32 * R)()
     if pos_out is not None:
@@ -264,25 +267,27 @@ def _compose_call(fn, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base,
 
 def compose(requests: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int]]], ratio_k: int,
             rope_theta: float, cache_k: torch.Tensor, cache_v: torch.Tensor,
-            pos_base: Optional[Sequence[int]] = None, pos_out: Optional[torch.Tensor] = None
-            ) -> Tuple[List[int], List[int]]:
+            pos_base: Optional[Sequence[int]] = None, pos_out: Optional[torch.Tensor] = None,
+            realign: bool = True) -> Tuple[List[int], List[int]]:
     """Compose per-request lists of (slot_k, slot_v, doc_len) into
     cache_k/cache_v [R][hkv][cap][d] (c2kv_compose).  A segment's tensors are
     either on the device or pinned CPU tensors (stored caches kept in host
-    memory, read in place across the host link).  Returns (cache_len per
-    request, next position per request)."""
+    memory, read in place across the host link).  realign=False is the
+    ablation without positional realignment (C2KV_SEGMENT_NO_REALIGN on
+    every segment).  Returns (cache_len per request, next position per
+    request)."""
     return _compose_call(load().c2kv_compose, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base, pos_out,
-                         False, None)
+                         False, None, realign)
 
 
 def compose_staged(requests: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int]]], ratio_k: int,
                    rope_theta: float, cache_k: torch.Tensor, cache_v: torch.Tensor,
                    pos_base: Optional[Sequence[int]] = None, pos_out: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None) -> Tuple[List[int], List[int]]:
+                   workspace: Optional[torch.Tensor] = None, realign: bool = True) -> Tuple[List[int], List[int]]:
     """As compose, for segments in pinned CPU memory that the library first
     copies into a device workspace (c2kv_compose_staged)."""
     return _compose_call(load().c2kv_compose_staged, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base,
-                         pos_out, True, workspace)
+                         pos_out, True, workspace, realign)
 
 
 # ------------------------------------------------ host-resident slot caches

@@ -212,7 +212,7 @@ typedef struct c2kv_segment {
   const void* v;
   int64_t row_stride;   /* elements between consecutive slot rows (>= hkv*head_dim) */
   int32_t doc_len;      /* original document length n >= 1 */
-  int32_t flags;        /* 0, or C2KV_SEGMENT_HOST */
+  int32_t flags;        /* 0, or C2KV_SEGMENT_HOST and/or C2KV_SEGMENT_NO_REALIGN */
 } c2kv_segment;
 
 /* Segment flag: k and v are device addresses of page-locked host memory
@@ -221,6 +221,13 @@ typedef struct c2kv_segment {
  * not the GPU, bounds them, and few concurrent readers keep its transfers
  * efficient.  Device segments keep the full grid. */
 #define C2KV_SEGMENT_HOST 1
+
+/* Segment flag for the ablation without positional realignment
+ * ([Explainer] experimental-results section: removing the realignment
+ * lowers quality): the segment's slots are rotated at their extraction
+ * positions plus pos_base only, not shifted by the original lengths of the
+ * documents before it.  Rows, lengths and next_pos_out are unchanged. */
+#define C2KV_SEGMENT_NO_REALIGN 2
 
 size_t c2kv_workspace_size_compose(int32_t num_segs);
 

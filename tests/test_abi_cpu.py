@@ -118,7 +118,7 @@ def _compose(lib, segs, ptr, cap=100, k=4, d=128, hkv=2, theta=1e6, base=None):
 def test_compose_validation(lib):
     good = (FAKE, FAKE, 256, 40, 0)
     assert _compose(lib, [good], [0, 1], cap=9) == CAPACITY           # 10 slots > cap 9
-    assert _compose(lib, [(FAKE, FAKE, 256, 40, 2)], [0, 1]) == INVALID      # unknown flag bit
+    assert _compose(lib, [(FAKE, FAKE, 256, 40, 4)], [0, 1]) == INVALID      # unknown flag bit
     assert _compose(lib, [(FAKE, FAKE, 100, 40, 0)], [0, 1]) == INVALID      # stride < hkv*d
     assert _compose(lib, [(FAKE, FAKE, 256, 0, 0)], [0, 1]) == INVALID       # empty document
     assert _compose(lib, [(None, FAKE, 256, 4, 0)], [0, 1]) == INVALID

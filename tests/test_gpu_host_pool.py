@@ -282,3 +282,29 @@ def test_host_pool_more_segments_than_one_launch(c2kv):
     for mix in (False, True):
         _host_vs_device(c2kv, reqs, pool_k, pool_v, pool_n, k, 5e5, dt, pos_base=[0, 11], mix=mix)
     _staged_vs_device(c2kv, reqs, pool_k, pool_v, pool_n, k, 5e5, dt, pos_base=[0, 11])
+
+
+def test_host_pool_without_realignment(c2kv):
+    """The no-realignment flag composes host segments exactly like device
+    ones, in place and staged."""
+    pool_n, k, hkv, d, dt = [150, 90, 33], 4, 2, 128, torch.bfloat16
+    pool_k = [W.normal((O.num_slots(n, k), hkv, d), dt, 57, W.P_K, salt=i) for i, n in enumerate(pool_n)]
+    pool_v = [W.normal((O.num_slots(n, k), hkv, d), dt, 57, W.P_V, salt=i) for i, n in enumerate(pool_n)]
+    M = sum(O.num_slots(n, k) for n in pool_n)
+    res = []
+    for src in ("device", "host", "staged"):
+        ck = torch.zeros((1, hkv, M, d), dtype=dt, device=DEV)
+        cv = torch.zeros_like(ck)
+        if src == "device":
+            segs = [(pool_k[t].to(DEV), pool_v[t].to(DEV), pool_n[t]) for t in (2, 0, 1)]
+            c2kv.compose([segs], k, 5e5, ck, cv, pos_base=[7], realign=False)
+        elif src == "host":
+            segs = [(pinned(pool_k[t]), pinned(pool_v[t]), pool_n[t]) for t in (2, 0, 1)]
+            c2kv.compose([segs], k, 5e5, ck, cv, pos_base=[7], realign=False)
+        else:
+            segs = [(pinned(pool_k[t]), pinned(pool_v[t]), pool_n[t]) for t in (2, 0, 1)]
+            c2kv.compose_staged([segs], k, 5e5, ck, cv, pos_base=[7], realign=False)
+        torch.cuda.synchronize()
+        res.append((ck, cv))
+    for ck, cv in res[1:]:
+        assert torch.equal(ck, res[0][0]) and torch.equal(cv, res[0][1])

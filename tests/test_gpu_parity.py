@@ -465,3 +465,41 @@ def test_compose_single_token_documents_and_k1(c2kv):
         pool_v = [W.normal((O.num_slots(n, k), 2, 64), torch.bfloat16, 26, W.P_V, salt=i) for i, n in enumerate(pool_n)]
         reqs = [list(range(len(pool_n))), list(range(len(pool_n)))[::-1]]
         _compose_check(c2kv, reqs, pool_k, pool_v, pool_n, k, 5e5, torch.bfloat16, pos_base=[0, 9], cap_extra=2)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_compose_without_realignment(c2kv, dt):
+    """The ablation without positional realignment: every document keeps
+    its extraction positions (offset pos_base), bit-exact positions against
+    the oracle, keys within the rotation bound, values copied; the first
+    document equals the realigned composition."""
+    g = torch.Generator().manual_seed(77)
+    pool_n = [400, 400] + [int(x) for x in torch.randint(1, 300, (5,), generator=g)]
+    k, hkv, d = 4, 2, 128
+    pool_k = [W.normal((O.num_slots(n, k), hkv, d), dt, 77, W.P_K, salt=i) for i, n in enumerate(pool_n)]
+    pool_v = [W.normal((O.num_slots(n, k), hkv, d), dt, 77, W.P_V, salt=i) for i, n in enumerate(pool_n)]
+    reqs = [[0, 1], [6, 2, 5, 3, 4]]
+    base = [0, 1000]
+    Ms = [sum(O.num_slots(pool_n[t], k) for t in r) for r in reqs]
+    cap = max(Ms)
+    out = {}
+    for realign in (False, True):
+        ck = torch.zeros((2, hkv, cap, d), dtype=dt, device=DEV)
+        cv = torch.zeros_like(ck)
+        pos = torch.full((2, cap), -1, dtype=torch.int32, device=DEV)
+        requests = [[(pool_k[t].to(DEV), pool_v[t].to(DEV), pool_n[t]) for t in r] for r in reqs]
+        lens, nxt = c2kv.compose(requests, k, 5e5, ck, cv, pos_base=base, pos_out=pos, realign=realign)
+        torch.cuda.synchronize()
+        out[realign] = (ck, cv, pos, lens, nxt)
+    ck, cv, pos, lens, nxt = out[False]
+    assert lens == Ms and nxt == [base[r] + sum(pool_n[t] for t in reqs[r]) for r in range(2)]
+    assert pos[0, :200].tolist() == list(range(3, 400, 4)) * 2
+    for r, docs in enumerate(reqs):
+        rk, rv, rpos, _ = O.compose([pool_k[t].float().numpy() for t in docs], [pool_v[t].float().numpy() for t in docs],
+                                    [pool_n[t] for t in docs], k, 5e5, dtname(dt), base[r], realign=False)
+        assert np.array_equal(pos[r, :Ms[r]].cpu().numpy(), rpos)
+        assert torch.equal(cv[r, :, :Ms[r]].transpose(0, 1).cpu(), torch.cat([pool_v[t] for t in docs]))
+        pre = np.concatenate([pool_k[t].float().numpy() for t in docs])
+        assert_rotated_close(np32(ck[r, :, :Ms[r]]).transpose(1, 0, 2), rk, pre, dtname(dt), f"request {r} keys")
+        m0 = O.num_slots(pool_n[docs[0]], k)
+        assert torch.equal(ck[r, :, :m0], out[True][0][r, :, :m0])
