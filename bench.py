@@ -16,7 +16,8 @@ The 256 decode launches of a step are replayed from one HIP graph.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
-Prints one JSON line.  Besides the step, it reports the decode rate with the
+Prints one JSON line.  Besides the step, it summarises the host-pool load
+(--host-pool) and the extractor layer (--layer) unless --no-extras, reports the decode rate with the
 256 steps spread over 16 replicas of the cache (a working set of about
 0.6 GB, above the 256 MB last-level cache) and the compose rate with
 its inputs and caches spread over 16 replicas (about 3 GB), and, when a counter summary
@@ -202,6 +203,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the host-pool load and extractor-layer summaries")
     ap.add_argument("--cpu-decode-steps", type=int, default=24)
     ap.add_argument("--cold-replicas", type=int, default=16)
     ap.add_argument("--calibration-copy-mib", type=int, default=0)
@@ -423,7 +425,7 @@ def compose_sweep():
           flush=True)
 
 
-def layer_bench():
+def layer_bench(ach=None, emit=True):
     """One extractor layer at the Llama3.1-8B shapes (dm 4096, 32/8 heads of
     128, FFN 14336, bf16, theta 5e5) over 8 documents of 4096 tokens at
     k = 4 (40 960 packed rows): norms, frozen / C2 projections, structured
@@ -477,18 +479,24 @@ def layer_bench():
     gemm = 2 * rows * dm * (nq + hq * d + 2 * ffn + ffn)
     attn = hq * 4 * d * sum(visible_cells(n, k) for n in lens)
     tf = (gemm + attn) / (best * 1e-3) / 1e12
-    ach = achievable_peaks(torch, dev)
-    print(json.dumps({"workload": "llama31_8b_extractor_layer", "docs": len(lens), "doc_tokens": lens[0],
-                      "ratio_k": k, "rows": rows, "dm": dm, "ffn": ffn, "ms": best, "gemm_tflop": gemm / 1e12,
-                      "attn_tflop": attn / 1e12, "tflops": tf, "frac_of_peak": tf / BF16_PEAK_TFLOPS,
-                      "frac_of_achievable": tf / ach["mfma_bf16_tflops"] if ach["mfma_bf16_tflops"] else None,
-                      "input_restore_copy_ms": copy_ms}), flush=True)
+    if ach is None:
+        ach = achievable_peaks(torch, dev)
+    res = {"workload": "llama31_8b_extractor_layer", "docs": len(lens), "doc_tokens": lens[0],
+           "ratio_k": k, "rows": rows, "dm": dm, "ffn": ffn, "ms": best, "gemm_tflop": gemm / 1e12,
+           "attn_tflop": attn / 1e12, "tflops": tf, "frac_of_peak": tf / BF16_PEAK_TFLOPS,
+           "frac_of_achievable": tf / ach["mfma_bf16_tflops"] if ach["mfma_bf16_tflops"] else None,
+           "input_restore_copy_ms": copy_ms}
+    del wts, x0, x, ko, vo, ws
+    torch.cuda.empty_cache()
+    if emit:
+        print(json.dumps(res), flush=True)
+    return res
 
 
 PCIE_PEAK_GBS = 64.0           # MI355X host link, PCIe 5.0 x16, one direction, GB/s
 
 
-def host_pool():
+def host_pool(emit=True):
     """Loading stored caches from host memory for one request of the
     Llama3.1-8B shapes: 8 documents of 4096 tokens, all 32 layers (8 KV
     heads, d = 128, bf16, theta 5e5), composed in the seeded order.  The
@@ -529,7 +537,7 @@ def host_pool():
     t0 = time.time()
     hk_c, hv_c = pool(m)
     hk_f, hv_f = pool(n)
-    print(f"host pools ready ({time.time() - t0:.1f} s)", flush=True)
+    print(f"host pools ready ({time.time() - t0:.1f} s)", file=sys.stderr, flush=True)
     ck_c = torch.empty((L, 1, hkv, ndoc * m, d), dtype=dt, device=dev)
     cv_c = torch.empty_like(ck_c)
     ck_f = torch.empty((L, 1, hkv, ndoc * n, d), dtype=dt, device=dev)
@@ -572,7 +580,7 @@ def host_pool():
     g_s = graph_of(staged_layers)
     c2kv_zc = best_ms(g_c.replay)
     full_zc = best_ms(g_f.replay)
-    print(f"zero-copy compose: c2kv {c2kv_zc:.2f} ms, full {full_zc:.2f} ms", flush=True)
+    print(f"zero-copy compose: c2kv {c2kv_zc:.2f} ms, full {full_zc:.2f} ms", file=sys.stderr, flush=True)
 
     def full_dma():
         ck_f.view(L, ndoc, n, hkv, d).copy_(hk_f, non_blocking=True)
@@ -582,12 +590,12 @@ def host_pool():
     torch.cuda.synchronize()
     full_d = best_ms(full_dma)
     c2kv_d = best_ms(g_s.replay)
-    print(f"dma: full {full_d:.2f} ms, c2kv staged {c2kv_d:.2f} ms", flush=True)
+    print(f"dma: full {full_d:.2f} ms, c2kv staged {c2kv_d:.2f} ms", file=sys.stderr, flush=True)
     c_bytes = 2 * L * ndoc * m * row_b
     f_bytes = 2 * L * ndoc * n * row_b
     h2d = f_bytes / (full_d * 1e-3) / 1e9
     zc = c_bytes / (c2kv_zc * 1e-3) / 1e9
-    print(json.dumps({
+    res = {
         "workload": "llama31_8b_32layer_host_pool_load", "docs": ndoc, "doc_tokens": n, "layers": L,
         "ratio_k": k, "slot_rows_per_layer": ndoc * m, "host_bytes_c2kv": c_bytes, "host_bytes_full": f_bytes,
         "c2kv_zero_copy_ms": c2kv_zc, "c2kv_staged_ms": c2kv_d, "full_zero_copy_k1_ms": full_zc,
@@ -597,7 +605,12 @@ def host_pool():
         "h2d_copy_gbs": h2d, "pcie_peak_gbs": PCIE_PEAK_GBS,
         "c2kv_zero_copy_frac_of_pcie_peak": zc / PCIE_PEAK_GBS, "c2kv_zero_copy_frac_of_h2d_copy": zc / h2d,
         "speedup_c2kv_zero_copy_vs_full_dma": full_d / c2kv_zc,
-        "speedup_c2kv_best_vs_full_best": min(full_d, full_zc) / min(c2kv_zc, c2kv_d)}), flush=True)
+        "speedup_c2kv_best_vs_full_best": min(full_d, full_zc) / min(c2kv_zc, c2kv_d)}
+    del g_c, g_f, g_s, ck_c, cv_c, ck_f, cv_f, ws_st, hk_c, hv_c, hk_f, hv_f
+    torch.cuda.empty_cache()
+    if emit:
+        print(json.dumps(res), flush=True)
+    return res
 
 
 def achievable_peaks(torch, dev):
@@ -898,6 +911,16 @@ def main():
         "wall_s": t_wall,
         "roofline": roof,
     }
+    if not a.no_extras:
+        # the paths around the step, one summary each (their own modes print the full lines)
+        hp = host_pool(emit=False)
+        line["host_pool_load"] = {k_: hp[k_] for k_ in (
+            "c2kv_zero_copy_ms", "c2kv_staged_ms", "full_dma_copy_ms", "full_zero_copy_k1_ms", "c2kv_zero_copy_gbs",
+            "h2d_copy_gbs", "c2kv_zero_copy_frac_of_pcie_peak", "speedup_c2kv_best_vs_full_best")}
+        line["host_pool_load"]["workload"] = "32 layers of the Llama shapes, 8 x 4096-token documents, k=4, from pinned host memory"
+        ly = layer_bench(ach=ach, emit=False)
+        line["extractor_layer"] = {k_: ly[k_] for k_ in ("ms", "tflops", "frac_of_peak", "frac_of_achievable")}
+        line["extractor_layer"]["workload"] = "one Llama3.1-8B-shaped extractor layer over 8 x 4096 tokens (synthetic weights)"
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, M, P, tq, a.cpu_decode_steps)
     print(json.dumps(line), flush=True)
