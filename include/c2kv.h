@@ -288,8 +288,10 @@ c2kv_status c2kv_host_device_ptr(const void* host_ptr, size_t bytes, const void*
  * a request uses them).  Each segment's m slot rows of K and V are copied
  * (async DMA on `stream`) into the workspace, packed [m][hkv][head_dim],
  * and c2kv_compose then runs on the staged copies.  Only compressed rows
- * cross the host link; the copy engines move them in larger transfers than
- * kernel reads of host memory do.
+ * cross the host link.  Where HIP executes host-to-device copies as kernels
+ * (blit kernels, as on MI355X systems), composing the host segments in
+ * place with C2KV_SEGMENT_HOST is the faster load; this entry point is for
+ * callers that want the rows staged in device memory.
  *   segs        host [num_segs]: k/v are HOST addresses in page-locked
  *               memory (every byte of [k, k + ((m-1)*row_stride +
  *               hkv*head_dim) elements) is checked before the first copy)
