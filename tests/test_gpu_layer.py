@@ -73,6 +73,8 @@ LAYER_CASES = [
     ((64, 40), 16, 512, 8, 2, 64, 384, 1e6, True),           # d = 64, G = 4, k = 16, first layer (slot vector)
     ((1, 3, 129), 4, 128, 1, 1, 128, 64, 1e4, True),        # n < k, single-token document, smallest grid
     ((200,), 4, 4096, 32, 8, 128, 14336, 5e5, False),        # Llama3.1-8B layer width, one document
+    ((150,), 8, 5120, 40, 8, 128, 17408, 1e6, True),         # Qwen3-14B layer width (G = 5)
+    ((97, 40), 16, 3584, 28, 4, 128, 18944, 1e6, False),     # Qwen2.5-7B layer width (G = 7), partial blocks
 ]
 
 
