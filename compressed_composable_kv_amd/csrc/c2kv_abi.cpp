@@ -451,7 +451,7 @@ namespace {
 
 struct LayerLayout {
   ExtractLayout ex;
-  size_t h_off = 0, q_off = 0, o_off = 0, gu_off = 0, act_off = 0, ex_off = 0, ex_bytes = 0, total = 0;
+  size_t h_off = 0, q_off = 0, o_off = 0, act_off = 0, ex_off = 0, ex_bytes = 0, total = 0;
 };
 
 c2kv_status layer_layout(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t dm, int32_t hq,
@@ -470,7 +470,6 @@ c2kv_status layer_layout(const int32_t* doc_lens, int32_t num_docs, int32_t rati
   L.h_off = off;   off += align_up(T * dm * es);
   L.q_off = off;   off += align_up(T * hq * head_dim * es);
   L.o_off = off;   off += align_up(T * hq * head_dim * es);
-  L.gu_off = off;  off += align_up(T * 2 * ffn * es);
   L.act_off = off; off += align_up(T * ffn * es);
   L.ex_off = off;
   L.ex_bytes = c2kv_workspace_size_extract(doc_lens, num_docs, ratio_k, hkv, head_dim, dt);
@@ -479,9 +478,10 @@ c2kv_status layer_layout(const int32_t* doc_lens, int32_t num_docs, int32_t rati
   return C2KV_OK;
 }
 
-// C = A * B^T over all rows [0, rows) with one weight matrix.
+// C = A * B^T over all rows [0, rows) with one weight matrix; epilogue epi
+// (kEpiResidual adds `resid`, kEpiSwiglu writes silu(gate) * up).
 hipError_t gemm_all_rows(const void* a, int64_t lda, const void* b, int K, int N, void* c, int64_t ldc,
-                         const void* resid, int64_t rows, hipStream_t st) {
+                         const void* resid, int64_t rows, int epi, hipStream_t st) {
   GemmParams p;
   std::memset(&p, 0, sizeof(p));
   p.a = static_cast<const bf16*>(a);
@@ -494,7 +494,7 @@ hipError_t gemm_all_rows(const void* a, int64_t lda, const void* b, int K, int N
   p.ranges[0] = GemmRange{0, (int32_t)rows, 0, 0};
   p.m_tiles = (int32_t)ceil_div(rows, 128);
   p.n_tiles = N / 128;
-  return launch_gemm(p, resid != nullptr, st);
+  return launch_gemm(p, epi, st);
 }
 
 }  // namespace
@@ -532,7 +532,6 @@ c2kv_status c2kv_extract_layer(void* x, const void* slot_embed, const c2kv_layer
   void* h = ws + L.h_off;
   void* q = ws + L.q_off;
   void* o = ws + L.o_off;
-  void* gu = ws + L.gu_off;
   void* act = ws + L.act_off;
   const int64_t T = L.ex.rows;
   const int qd = hq * head_dim, kd = hkv * head_dim, nqkv = qd + 2 * kd;
@@ -586,18 +585,18 @@ c2kv_status c2kv_extract_layer(void* x, const void* slot_embed, const c2kv_layer
       }
       p.num_ranges = nr;
       p.m_tiles = tiles;
-      if ((e = launch_gemm(p, false, stream)) != hipSuccess) return hip_fail(e, "qkv projection launch");
+      if ((e = launch_gemm(p, kEpiStore, stream)) != hipSuccess) return hip_fail(e, "qkv projection launch");
     }
   }
   if ((s = c2kv_extract_attn(q, k_out, v_out, o, nullptr, doc_lens, num_docs, ratio_k, sink_len, hq, hkv, head_dim,
                              rope_theta, dt, ws + L.ex_off, L.ex_bytes, stream)))
     return s;
-  if ((e = gemm_all_rows(o, qd, w->wo, qd, dm, x, dm, x, T, stream)) != hipSuccess) return hip_fail(e, "output projection launch");
+  if ((e = gemm_all_rows(o, qd, w->wo, qd, dm, x, dm, x, T, kEpiResidual, stream)) != hipSuccess)
+    return hip_fail(e, "output projection launch");
   if ((e = launch_rms_norm(x, w->ffn_norm, h, T, dm, rms_eps, stream)) != hipSuccess) return hip_fail(e, "rms norm launch");
-  if ((e = gemm_all_rows(h, dm, w->w_gate_up, dm, 2 * ffn, gu, 2 * ffn, nullptr, T, stream)) != hipSuccess)
+  if ((e = gemm_all_rows(h, dm, w->w_gate_up, dm, 2 * ffn, act, ffn, nullptr, T, kEpiSwiglu, stream)) != hipSuccess)
     return hip_fail(e, "gate/up projection launch");
-  if ((e = launch_swiglu(gu, act, T, ffn, stream)) != hipSuccess) return hip_fail(e, "swiglu launch");
-  if ((e = gemm_all_rows(act, ffn, w->w_down, ffn, dm, x, dm, x, T, stream)) != hipSuccess)
+  if ((e = gemm_all_rows(act, ffn, w->w_down, ffn, dm, x, dm, x, T, kEpiResidual, stream)) != hipSuccess)
     return hip_fail(e, "down projection launch");
   return ok();
 }

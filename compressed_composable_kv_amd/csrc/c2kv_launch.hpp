@@ -85,8 +85,12 @@ struct AppendParams {
 
 // Extractor layer GEMM C = A * B^T (bf16, fp32 accumulation).  A row range
 // of A uses weights b0 (sel 0) or b1 (sel 1); tile0 is its first 128-row
-// tile.  Columns [0, n1) go to c0, [n1, n2) to c1, [n2, N) to c2 (each
-// boundary a multiple of 128).  With a residual, C = r + A * B^T.
+// tile.  Epilogues: kEpiStore splits columns [0, n1) to c0, [n1, n2) to c1,
+// [n2, N) to c2 (each boundary a multiple of 128); kEpiResidual writes
+// C = r + A * B^T to c0; kEpiSwiglu takes weight rows in blocks of 16 gate
+// rows then the matching 16 up rows and writes silu(gate) * up to c0
+// ([rows][N / 2]).
+constexpr int kEpiStore = 0, kEpiResidual = 1, kEpiSwiglu = 2;
 struct GemmRange {
   int32_t row0, rows, sel, tile0;
 };
@@ -126,10 +130,9 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream
 hipError_t launch_compose(const ComposeParams& p, int dtype, int head_dim, bool host_src, hipStream_t st);
 hipError_t launch_append(const AppendParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t st);
-hipError_t launch_gemm(const GemmParams& p, bool resid, hipStream_t st);
+hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t st);
 hipError_t launch_rms_norm(const void* x, const void* gamma, void* h, int64_t rows, int dm, float eps,
                            hipStream_t st);
-hipError_t launch_swiglu(const void* gu, void* act, int64_t rows, int ffn, hipStream_t st);
 hipError_t launch_slot_fill(const SlotFillParams& p, int slots, hipStream_t st);
 
 }  // namespace c2kv

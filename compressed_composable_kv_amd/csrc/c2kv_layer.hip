@@ -5,10 +5,10 @@
 //     16-byte chunks).
 //     A row-range table picks the weight matrix per row tile (document rows
 //     take the frozen projections, slot rows the C2 ones); the epilogue
-//     either splits columns over up to three outputs (q | k | v) or adds a
-//     residual in fp32 and rounds once.
+//     splits columns over up to three outputs (q | k | v), adds a residual
+//     in fp32 and rounds once, or (gate/up rows interleaved in blocks of
+//     16) writes silu(gate) * up.
 //   * rms_norm_kernel: one workgroup per row, fp32 sum of squares.
-//   * swiglu_kernel: silu(gate) * up, rounded to bf16.
 //   * slot_fill_kernel: writes the shared slot vector into every slot row.
 #include <hip/hip_runtime.h>
 
@@ -36,7 +36,7 @@ __device__ __forceinline__ void gemm_tile(int b, int m_tiles, int n_tiles, int& 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <bool RESID>
+template <int EPI>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 lds[2][2][kGM * kGK];   // [stage][A, B]: 64 KB
   // the stages are written only by buffer_load ... lds; escape them so the
@@ -126,6 +126,24 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
     const int ml = wm * 64 + j * 16 + (lane & 15);
     if (ml >= valid) continue;
     const int64_t row = row0 + ml;
+    if (EPI == kEpiSwiglu) {
+      // weight rows come in blocks of 16 gate rows then the matching 16 up
+      // rows, so block i (gate) and block i + 1 (up) of this lane hold the
+      // same 4 FFN columns f: act[row][f] = silu(gate) * up
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const int n = n0 + wn * 64 + i * 16 + 4 * (lane >> 4);
+        const int f = (n >> 5) * 16 + (n & 15);
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float g = acc[i][j][e];
+          o4[e] = from_f32<bf16>(g / (1.0f + expf(-g)) * acc[i + 1][j][e]);
+        }
+        *reinterpret_cast<bf16x4*>(p.c0 + row * p.ldc0 + f) = o4;
+      }
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int n = n0 + wn * 64 + i * 16 + 4 * (lane >> 4);
@@ -134,7 +152,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
       else if (n < p.n2) dst = p.c1 + row * p.ldc1 + (n - p.n1);
       else dst = p.c2 + row * p.ldc2 + (n - p.n2);
       float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
-      if (RESID) {
+      if (EPI == kEpiResidual) {
         const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(p.r + row * p.ldr + n);
         v0 += to_f32(r4[0]);
         v1 += to_f32(r4[1]);
@@ -151,11 +169,15 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
   }
 }
 
-hipError_t launch_gemm(const GemmParams& p, bool resid, hipStream_t st) {
+hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t st) {
   const int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
   if (tiles == 0) return hipSuccess;
-  if (resid) hipLaunchKernelGGL((gemm_nt_kernel<true>), dim3((unsigned)tiles), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((gemm_nt_kernel<false>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+  if (epi == kEpiResidual)
+    hipLaunchKernelGGL((gemm_nt_kernel<kEpiResidual>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+  else if (epi == kEpiSwiglu)
+    hipLaunchKernelGGL((gemm_nt_kernel<kEpiSwiglu>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((gemm_nt_kernel<kEpiStore>), dim3((unsigned)tiles), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -196,35 +218,6 @@ hipError_t launch_rms_norm(const void* x, const void* gamma, void* h, int64_t ro
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(rms_norm_kernel, dim3((unsigned)rows), dim3(256), 0, st, static_cast<const bf16*>(x),
                      static_cast<const bf16*>(gamma), static_cast<bf16*>(h), dm, eps);
-  return hipGetLastError();
-}
-
-// -------------------------------------------------------------- SwiGLU
-// act[r][f] = bf16(silu(g) * u) with g = gu[r][f], u = gu[r][ffn + f].
-__global__ __launch_bounds__(256) void swiglu_kernel(const bf16* __restrict__ gu, bf16* __restrict__ act,
-                                                     int64_t rows, int ffn) {
-  const int64_t chunks = rows * (ffn / 8);
-  for (int64_t c = blockIdx.x * 256ll + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
-    const int64_t r = c / (ffn / 8);
-    const int f = (int)(c % (ffn / 8)) * 8;
-    const bf16x8 g = *reinterpret_cast<const bf16x8*>(gu + r * 2 * ffn + f);
-    const bf16x8 u = *reinterpret_cast<const bf16x8*>(gu + r * 2 * ffn + ffn + f);
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float gv = to_f32(g[e]);
-      o[e] = from_f32<bf16>(gv / (1.0f + expf(-gv)) * to_f32(u[e]));
-    }
-    *reinterpret_cast<bf16x8*>(act + r * ffn + f) = o;
-  }
-}
-
-hipError_t launch_swiglu(const void* gu, void* act, int64_t rows, int ffn, hipStream_t st) {
-  const int64_t chunks = rows * (ffn / 8);
-  if (chunks == 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 256 * 8);
-  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const bf16*>(gu),
-                     static_cast<bf16*>(act), rows, ffn);
   return hipGetLastError();
 }
 

@@ -148,6 +148,15 @@ def extract_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_lens: Se
 LAYER_WEIGHTS = ("attn_norm", "wqkv", "wqkv_c2", "wo", "ffn_norm", "w_gate_up", "w_down")
 
 
+def gate_up_interleave(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor:
+    """The w_gate_up layout c2kv_extract_layer takes: blocks of 16 gate rows,
+    each followed by the 16 up rows of the same FFN columns (a row
+    permutation of [gate; up])."""
+    ffn, dm = w_gate.shape
+    _need(w_up.shape == w_gate.shape and ffn % 16 == 0, "gate/up shapes")
+    return torch.stack([w_gate.reshape(ffn // 16, 16, dm), w_up.reshape(ffn // 16, 16, dm)], dim=1).reshape(2 * ffn, dm)
+
+
 def workspace_size_extract_layer(doc_lens: Sequence[int], ratio_k: int, dm: int, hq: int, hkv: int,
                                  head_dim: int, ffn: int) -> int:
     return int(load().c2kv_workspace_size_extract_layer(_arr_i32(doc_lens), len(doc_lens), ratio_k, dm, hq, hkv,
@@ -162,7 +171,8 @@ def extract_layer(x: torch.Tensor, weights: dict, k_out: torch.Tensor, v_out: to
     updated in place; k_out/v_out [sum_T][hkv][d] receive the layer's
     pre-RoPE keys and values (their slot rows are the stored C2KV).
     weights: {attn_norm [dm], wqkv and wqkv_c2 [(hq+2hkv)d][dm], wo [dm][hq d],
-    ffn_norm [dm], w_gate_up [2 ffn][dm], w_down [dm][ffn]} on the device."""
+    ffn_norm [dm], w_gate_up [2 ffn][dm] (gate_up_interleave of the gate and
+    up matrices), w_down [dm][ffn]} on the device."""
     lib = load()
     _dev_tensor(x, "x", torch.bfloat16)
     _dev_tensor(k_out, "k_out", torch.bfloat16)

@@ -165,7 +165,8 @@ typedef struct c2kv_layer_weights {
   const void* wqkv_c2;     /* same shape: the C2 projections, used for slot rows */
   const void* wo;          /* [dm][hq*head_dim] output projection */
   const void* ffn_norm;    /* [dm]  RMSNorm gain before the FFN */
-  const void* w_gate_up;   /* [2*ffn][dm]: gate rows, then up rows */
+  const void* w_gate_up;   /* [2*ffn][dm]: blocks of 16 gate rows, each followed by the 16 up rows of the
+                              same FFN columns (rows 32b..32b+15: gate 16b..16b+15; 32b+16..32b+31: up) */
   const void* w_down;      /* [dm][ffn] */
 } c2kv_layer_weights;
 
@@ -187,8 +188,9 @@ size_t c2kv_workspace_size_extract_layer(const int32_t* doc_lens, int32_t num_do
  * (structured mask, RoPE at extraction positions, sink_len, rope_theta);
  * x += o W_o^T; h = RMSNorm(x) * ffn_norm; x += (silu(h Wg^T) * (h Wu^T)) Wd^T.
  * RMSNorm(x) = x / sqrt(mean(x^2) + rms_eps).  Matrix products accumulate
- * in fp32; h, q, attention output, gate/up and the SwiGLU product are
- * rounded to bf16, and each residual add is done in fp32 and rounded once.
+ * in fp32; h, q, the attention output and the SwiGLU product (formed from
+ * the fp32 gate and up sums) are rounded to bf16, and each residual add is
+ * done in fp32 and rounded once.
  * bf16 only.  Requires dm % 128 == 0, ffn % 64 == 0, and hq*head_dim and
  * hkv*head_dim multiples of 128.
  * Errors: INVALID_ARG, UNSUPPORTED (fp32, shapes off the tile grid),

@@ -3,8 +3,8 @@
 The layer chains RMSNorm, the Q/K/V projections (frozen weights on document
 rows, C2 weights on slot rows), the structured attention, the output
 projection, RMSNorm and the SwiGLU FFN with residual adds.  The GPU path
-rounds h, q/k/v, the attention output, gate/up and the SwiGLU product to
-bf16 (fp32 accumulation); the oracle works in fp64 from the same bf16
+rounds h, q/k/v, the attention output and the SwiGLU product to bf16
+(fp32 accumulation); the oracle works in fp64 from the same bf16
 inputs.  Bar, derived from that arithmetic: per row, the layer's update
 x_out - x_in within 3e-2 relative (L2) of the oracle's and every element of
 x_out within 0.1 absolute (a few bf16 half-ulps at |x| ~ 4 plus the
@@ -43,16 +43,21 @@ def make_weights(wid, dm, hq, hkv, d, ffn, salt=0):
         "wqkv_c2": lin(nq, dm, W.P_K, 3),
         "wo": lin(dm, hq * d, W.P_V, 4),
         "ffn_norm": (1.0 + 0.1 * W.normal((dm,), torch.float32, wid, W.P_Q, salt=salt * 100 + 5)).to(torch.bfloat16),
-        "w_gate_up": lin(2 * ffn, dm, W.P_V, 6),
+        "w_gate": lin(ffn, dm, W.P_V, 6),
+        "w_up": lin(ffn, dm, W.P_V, 8),
         "w_down": lin(dm, ffn, W.P_V, 7),
     }
 
 
 def oracle_weights(w, ffn):
-    f = {k: v.float().numpy().astype(np.float64) for k, v in w.items()}
-    f["w_gate"] = f["w_gate_up"][:ffn]
-    f["w_up"] = f["w_gate_up"][ffn:]
-    return f
+    return {k: v.float().numpy().astype(np.float64) for k, v in w.items()}
+
+
+def device_weights(c2kv, w):
+    """The library's layout: gate and up rows interleaved in blocks of 16."""
+    d = {n: t.to(DEV) for n, t in w.items() if n not in ("w_gate", "w_up")}
+    d["w_gate_up"] = c2kv.gate_up_interleave(w["w_gate"], w["w_up"]).to(DEV)
+    return d
 
 
 def run_layer(c2kv, x, w, doc_lens, k, hq, hkv, d, theta, eps, embed=None):
@@ -60,7 +65,7 @@ def run_layer(c2kv, x, w, doc_lens, k, hq, hkv, d, theta, eps, embed=None):
     rows = xd.shape[0]
     ko = torch.empty((rows, hkv, d), dtype=torch.bfloat16, device=DEV)
     vo = torch.empty_like(ko)
-    wd = {n: t.to(DEV) for n, t in w.items()}
+    wd = device_weights(c2kv, w)
     c2kv.extract_layer(xd, wd, ko, vo, doc_lens, k, None, hq, theta, eps,
                        slot_embed=embed.to(DEV) if embed is not None else None)
     torch.cuda.synchronize()
