@@ -152,6 +152,7 @@ int fill_extract_chunk(const int32_t* doc_lens, int32_t first, int32_t num_docs,
 //    step), so every workgroup streams about the same number of bytes and
 //    no second, partly filled round trails the first.
 constexpr int64_t kDecodeSlots = 3 * 256;   // decode workgroups resident at once on a 256-CU MI355X
+constexpr int64_t kPrefillSlots = 256;      // prefill workgroups per launch: one per CU (two measured slower)
 struct CachePlan {
   bool decode = false;
   int32_t nug = 0, nblk_q = 0, chunk = 0;
@@ -183,7 +184,7 @@ c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, i
   P.nsplit.resize(num_reqs);
   P.chunk_r.resize(num_reqs);
   if (!decode) {
-    int64_t chunk = ceil_div(total_keys * hkv * P.nug, 256);
+    int64_t chunk = ceil_div(total_keys * hkv * P.nug, kPrefillSlots);
     chunk = std::max<int64_t>(step, ceil_div(chunk, step) * step);
     chunk = std::max<int64_t>(chunk, ceil_div(ceil_div(max_len, C2KV_MAX_SPLITS), step) * step);
     P.chunk = (int32_t)chunk;

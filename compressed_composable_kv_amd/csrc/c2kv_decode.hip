@@ -393,14 +393,17 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
 }
 
 // ---------------------------------------------------------------- merge
-// One workgroup per (output row, 32-dim slice): the split partials
+// One workgroup per (output row, DIMS-wide slice): the split partials
 // [o(D) | m | l] of that row (request of the launch, head, token) are
-// combined by log-sum-exp.  The (m, l) pairs are staged in LDS with one
-// load per split, the o slices are loaded in batches of kMergeNB splits per
-// thread with every load in flight before the arithmetic.  Rows of
-// requests with a single key chunk already hold their output.
-constexpr int kMergeDims = 32;                         // dims per workgroup
-constexpr int kMergeSG = kThreads / (kMergeDims / 4);  // split groups (32)
+// combined by log-sum-exp.  DIMS / 4 threads cover the slice and the
+// workgroup's kThreads / (DIMS / 4) groups of them take the splits in turn.
+// The (m, l) pairs are staged in LDS with one load per split, the o slices
+// are loaded in batches of kMergeNB splits per thread with every load in
+// flight before the arithmetic.  Rows of requests with a single key chunk
+// already hold their output.  Decode merges many splits per row over few
+// rows and takes 32-dim slices (more workgroups per row); prefill merges
+// fewer splits over many rows and takes whole rows.
+constexpr int kMergeDimsDecode = 32;
 constexpr int kMergeNB = 4;
 
 __device__ __forceinline__ float wave_max64(float x) {
@@ -409,11 +412,11 @@ __device__ __forceinline__ float wave_max64(float x) {
   return wave_max_16_32(x);
 }
 
-template <typename T, int D>
+template <typename T, int D, int DIMS>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
-  constexpr int DQ = D / kMergeDims, SG = kMergeSG, NB = kMergeNB;
+  constexpr int DQ = D / DIMS, TPS = DIMS / 4, SG = kThreads / TPS, NB = kMergeNB;
   __shared__ float s_m[C2KV_MAX_SPLITS], s_l[C2KV_MAX_SPLITS];
-  __shared__ __attribute__((aligned(16))) float s_acc[SG][kMergeDims];
+  __shared__ __attribute__((aligned(16))) float s_acc[SG][DIMS];
   __shared__ float s_ls[SG];
   const int row = blockIdx.x / DQ, dq = blockIdx.x % DQ;
   if (row >= p.num_rows) return;
@@ -422,8 +425,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   const int nsplit = p.nsplit[ri];
   if (nsplit <= 1) return;        // single-chunk requests were written directly
   const float* base = p.part + (int64_t)row * p.nsplit_stride * (D + 4);
-  const int sg = tid >> 3, d4 = tid & 7;
-  const int col = dq * kMergeDims + 4 * d4;
+  const int sg = tid / TPS, d4 = tid % TPS;
+  const int col = dq * DIMS + 4 * d4;
   for (int s = tid; s < nsplit; s += kThreads) {
     const float* pr = base + (int64_t)s * (D + 4);
     s_m[s] = pr[D];
@@ -456,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   *reinterpret_cast<f32x4*>(&s_acc[sg][4 * d4]) = acc;
   if (d4 == 0) s_ls[sg] = ls;
   __syncthreads();
-  if (tid < kMergeDims) {
+  if (tid < DIMS) {
     float a = 0.f, lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < SG; ++j) { a += s_acc[j][tid]; lsum += s_ls[j]; }
@@ -464,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     const int head = rem / p.tq, t = rem % p.tq;
     const int r = p.req0 + ri;
     T* orow = reinterpret_cast<T*>(p.o) + (((int64_t)r * p.tq + t) * p.hq + head) * D;
-    orow[dq * kMergeDims + tid] = from_f32<T>(a / lsum);
+    orow[dq * DIMS + tid] = from_f32<T>(a / lsum);
     if (dq == 0 && tid == 0 && p.lse)
       p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (M + __log2f(lsum)) * 0.69314718055994531f;
   }
@@ -484,7 +487,11 @@ hipError_t launch_decode_attn(const DecodeParams& p, int dtype, int head_dim, hi
 
 template <typename T, int D>
 static hipError_t launch_merge_t(const MergeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(p.num_rows * (D / kMergeDims)), dim3(kThreads), 0, st, p);
+  if (p.tq > 1)
+    hipLaunchKernelGGL((merge_kernel<T, D, D>), dim3(p.num_rows), dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((merge_kernel<T, D, kMergeDimsDecode>), dim3(p.num_rows * (D / kMergeDimsDecode)),
+                       dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
