@@ -46,6 +46,9 @@ R11 GQA: query head h reads KV head floor(h / (Hq / Hkv)).
 R12 softmax scale 1/sqrt(d), no capping; no row is ever fully masked.
 R13 an appended key is stored in the cache dtype; attention reads the
     stored (rounded) value.  Rotated queries stay fp32 in the oracle.
+R24 the anchor-token ablation: anchors (the slot rows) and document tokens
+    see each other both ways; documents stay causal among themselves and
+    anchors see every anchor; positions as for C2 slots.
 R23 the ablation without positional realignment gives every composed
     document the offset pos_base (its extraction positions), instead of the
     cumulative original length of the documents before it.
@@ -97,7 +100,7 @@ def extraction_positions(n: int, k: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
-def structured_mask(n: int, k: int, sink_len: Optional[int] = None) -> np.ndarray:
+def structured_mask(n: int, k: int, sink_len: Optional[int] = None, anchor: bool = False) -> np.ndarray:
     """Dense T x T visibility matrix, rows = queries, columns = keys.
 
     [Explainer] structured-information-flow section and its mask figure:
@@ -108,6 +111,11 @@ def structured_mask(n: int, k: int, sink_len: Optional[int] = None) -> np.ndarra
               the sink itself;
       rule 3  slots attend causally to slots, themselves included.
     Reading R3 for the sink size.
+
+    anchor=True is the experimental-results section's anchor-token ablation
+    (reading R24): the extra tokens and the document tokens see each other
+    both ways.  Document rows keep their causal mask over documents and see
+    every anchor; anchor rows see every document token and every anchor.
     """
     if sink_len is None:
         sink_len = k
@@ -125,16 +133,23 @@ def structured_mask(n: int, k: int, sink_len: Optional[int] = None) -> np.ndarra
     # rule 3: slot -> slot causal, including itself
     jj = np.arange(m)
     M[n:, n:] = jj[None, :] <= jj[:, None]
+    if anchor:
+        M[:n, n:] = True
+        M[n:, :] = True
     return M
 
 
-def visible_set(n: int, k: int, sink_len: Optional[int], row: int) -> Set[int]:
+def visible_set(n: int, k: int, sink_len: Optional[int], row: int, anchor: bool = False) -> Set[int]:
     """Visible key indices of one packed row, built directly from the rule
-    statements (not from the matrix) for brute-force checks."""
+    statements (not from the matrix) for brute-force checks.  anchor=True:
+    the anchor-token ablation (see structured_mask)."""
     if sink_len is None:
         sink_len = k
     m = num_slots(n, k)
     s = min(sink_len, n)
+    if anchor:
+        anchors = set(range(n, n + m))
+        return (set(range(row + 1)) | anchors) if row < n else (set(range(n)) | anchors)
     if row < n:
         return set(range(row + 1))
     j = row - n
@@ -309,7 +324,8 @@ def doc_row_offsets(doc_lens: Sequence[int], k: int) -> List[int]:
 
 def extract_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, doc_lens: Sequence[int],
                  ratio_k: int, sink_len: Optional[int], theta: float,
-                 docs: Optional[Sequence[int]] = None) -> Dict[int, Tuple[np.ndarray, np.ndarray]]:
+                 docs: Optional[Sequence[int]] = None,
+                 anchor: bool = False) -> Dict[int, Tuple[np.ndarray, np.ndarray]]:
     """Extraction attention of each document, run alone (offline extraction
     in the [Explainer] overall-flow section; each document is processed by
     itself).
@@ -318,7 +334,8 @@ def extract_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, doc_lens: Sequence
     document as [n doc rows | m slot rows].  Q and K are rotated at the
     extraction positions (doc token i at i, slot j at its block's last
     token), V is not (reading R7); then masked attention under the
-    structured mask.  Returns {doc: (o [T][Hq][d], lse [Hq][T])}.
+    structured mask (the anchor-token ablation's mask with anchor=True).
+    Returns {doc: (o [T][Hq][d], lse [Hq][T])}.
     """
     offs = doc_row_offsets(doc_lens, ratio_k)
     out = {}
@@ -328,7 +345,7 @@ def extract_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, doc_lens: Sequence
         pos = extraction_positions(n, ratio_k)
         qr = rope_rotate(np.asarray(q[r0:r1], dtype=np.float32), pos, theta)
         kr = rope_rotate(np.asarray(k[r0:r1], dtype=np.float32), pos, theta)
-        M = structured_mask(n, ratio_k, sink_len)
+        M = structured_mask(n, ratio_k, sink_len, anchor)
         out[b] = attention(qr, kr, np.asarray(v[r0:r1], dtype=np.float64), M)
     return out
 

@@ -600,6 +600,51 @@ def test_no_realignment_equals_each_document_alone():
     assert np.array_equal(r_k[:m0], ck[:m0]) and not np.array_equal(r_pos[m0:], pos[m0:])
 
 
+# ------------------------------------------------ anchor-token ablation
+
+@pytest.mark.parametrize("n,k", [(12, 4), (13, 4), (3, 4), (40, 16)])
+def test_anchor_mask_dense_equals_rule_sets_and_counts(n, k):
+    """The anchor ablation's mask, dense and as sets from the rule
+    statement, and its closed-form counts: documents n(n+1)/2 + n m,
+    anchors m n + m^2."""
+    m = O.num_slots(n, k)
+    M = O.structured_mask(n, k, None, anchor=True)
+    for r in range(n + m):
+        assert set(np.nonzero(M[r])[0].tolist()) == O.visible_set(n, k, None, r, anchor=True)
+    assert M[:n].sum() == n * (n + 1) // 2 + n * m
+    assert M[n:].sum() == m * n + m * m
+    # the structured mask is a subset of the anchor mask
+    S = O.structured_mask(n, k, None)
+    assert not (S & ~M).any()
+
+
+def test_anchor_attention_equals_brute_force():
+    n, k, hq, hkv, d = 21, 4, 2, 1, 8
+    m = O.num_slots(n, k)
+    r = rng(33)
+    q = r.standard_normal((n + m, hq, d))
+    kk = r.standard_normal((n + m, hkv, d))
+    v = r.standard_normal((n + m, hkv, d))
+    M = O.structured_mask(n, k, None, anchor=True)
+    o, lse = O.attention(q, kk, v, M)
+    ob, lb = O.attention_brute(q, kk, v, [O.visible_set(n, k, None, i, anchor=True) for i in range(n + m)])
+    assert np.abs(o - ob).max() < 1e-12 and np.abs(lse - lb).max() < 1e-12
+
+
+def test_anchor_extraction_changes_document_rows():
+    """Under the ablation document rows read the anchors, so they no longer
+    equal the frozen model's (they do under the structured mask)."""
+    n, k, hq, hkv, d, theta = 30, 4, 2, 1, 16, 1e4
+    m = O.num_slots(n, k)
+    r = rng(35)
+    q = r.standard_normal((n + m, hq, d)).astype(np.float32)
+    kk = r.standard_normal((n + m, hkv, d)).astype(np.float32)
+    v = r.standard_normal((n + m, hkv, d)).astype(np.float32)
+    a, _ = O.extract_attn(q, kk, v, [n], k, None, theta, anchor=True)[0]
+    s_, _ = O.extract_attn(q, kk, v, [n], k, None, theta)[0]
+    assert np.abs(a[:n] - s_[:n]).max() > 1e-3
+
+
 # --------------------------------------------------- planted-mistake checks
 
 
