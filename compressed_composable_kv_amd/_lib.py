@@ -27,6 +27,7 @@ P_f32 = ctypes.POINTER(ctypes.c_float)
 
 SEGMENT_HOST = 1   # C2KV_SEGMENT_HOST
 SEGMENT_NO_REALIGN = 2   # C2KV_SEGMENT_NO_REALIGN
+EXTRACT_ANCHOR = 1   # C2KV_EXTRACT_ANCHOR
 
 
 class Segment(ctypes.Structure):
@@ -52,6 +53,12 @@ SIGNATURES = {
                                     P_i32, c_int32, c_int32, c_int32,
                                     c_int32, c_int32, c_int32, c_float, c_int32,
                                     c_void_p, c_size_t, c_void_p]),
+    "c2kv_extract_attn_ex": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       P_i32, c_int32, c_int32, c_int32,
+                                       c_int32, c_int32, c_int32, c_float, c_int32, ctypes.c_uint32,
+                                       c_void_p, c_size_t, c_void_p]),
+    "c2kv_mask_cells_ex": (c_int32, [P_i32, c_int32, c_int32, c_int32, ctypes.c_uint32, P_u64, c_void_p, c_size_t,
+                                     c_void_p]),
     "c2kv_workspace_size_extract_layer": (c_size_t, [P_i32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                      c_int32, c_int32]),
     "c2kv_extract_layer": (c_int32, [c_void_p, c_void_p, ctypes.POINTER(LayerWeights), c_void_p, c_void_p,

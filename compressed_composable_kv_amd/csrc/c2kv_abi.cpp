@@ -405,7 +405,16 @@ c2kv_status c2kv_extract_attn(const void* q, const void* k, const void* v, void*
                               const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t sink_len,
                               int32_t hq, int32_t hkv, int32_t head_dim, float rope_theta, c2kv_dtype dt,
                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return c2kv_extract_attn_ex(q, k, v, o, lse, doc_lens, num_docs, ratio_k, sink_len, hq, hkv, head_dim, rope_theta,
+                              dt, 0u, workspace, ws_bytes, stream);
+}
+
+c2kv_status c2kv_extract_attn_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t sink_len,
+                                 int32_t hq, int32_t hkv, int32_t head_dim, float rope_theta, c2kv_dtype dt,
+                                 uint32_t flags, void* workspace, size_t ws_bytes, hipStream_t stream) {
   c2kv_status s;
+  if (flags & ~C2KV_EXTRACT_ANCHOR) return fail(C2KV_ERR_INVALID_ARG, "flags=%u has unknown bits", flags);
   if ((s = check_heads(hq, hkv, head_dim, dt))) return s;
   if ((s = check_theta(rope_theta))) return s;
   if ((s = check_dev(q, "q")) || (s = check_dev(k, "k")) || (s = check_dev(v, "v")) || (s = check_dev(o, "o")))
@@ -430,6 +439,7 @@ c2kv_status c2kv_extract_attn(const void* q, const void* k, const void* v, void*
   p.total_rows = L.rows;
   p.hq = hq; p.hkv = hkv; p.G = hq / hkv; p.ratio_k = ratio_k; p.sink_len = sink_len;
   p.scale_log2 = scale_log2(head_dim);
+  p.anchor = (flags & C2KV_EXTRACT_ANCHOR) ? 1 : 0;
   rp.k = k; rp.krot = ws + L.krot_off; rp.rope = table;
   rp.hkv = hkv; rp.ratio_k = ratio_k;
   int64_t row = 0;
@@ -876,7 +886,14 @@ size_t c2kv_workspace_size_mask_cells(void) { return 256; }
 
 c2kv_status c2kv_mask_cells(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t sink_len,
                             uint64_t* counts_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return c2kv_mask_cells_ex(doc_lens, num_docs, ratio_k, sink_len, 0u, counts_out, workspace, ws_bytes, stream);
+}
+
+c2kv_status c2kv_mask_cells_ex(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t sink_len,
+                               uint32_t flags, uint64_t* counts_out, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
   c2kv_status s;
+  if (flags & ~C2KV_EXTRACT_ANCHOR) return fail(C2KV_ERR_INVALID_ARG, "flags=%u has unknown bits", flags);
   if (!counts_out) return fail(C2KV_ERR_INVALID_ARG, "counts_out is NULL");
   if (sink_len < 0) return fail(C2KV_ERR_INVALID_ARG, "sink_len=%d must be >= 0", sink_len);
   ExtractLayout L;
@@ -890,6 +907,7 @@ c2kv_status c2kv_mask_cells(const int32_t* doc_lens, int32_t num_docs, int32_t r
   std::memset(&p, 0, sizeof(p));
   std::memset(&rp, 0, sizeof(rp));
   p.hq = 1; p.hkv = 1; p.G = 1; p.ratio_k = ratio_k; p.sink_len = sink_len; p.counts = counts;
+  p.anchor = (flags & C2KV_EXTRACT_ANCHOR) ? 1 : 0;
   p.total_rows = L.rows;
   int64_t row = 0;
   for (int32_t b = 0; b < num_docs;) {

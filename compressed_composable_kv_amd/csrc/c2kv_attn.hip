@@ -31,6 +31,8 @@ namespace c2kv {
 //   slot j, document key c:          a = -2^30, b = k, sink     (sink block + own block)
 //   slot j, slot key j':             a = 0                      (causal)
 //   cache query t, cache row c:      a = cache_len              (all cached rows + causal new rows)
+//   anchor ablation, slot keys of a document row, any key of a slot row:
+//                                    a = 2^30                   (every key below kmax)
 struct Pred {
   int kmax, a, b, sink;
   __device__ __forceinline__ bool operator()(int q, int c) const {
@@ -62,7 +64,7 @@ __device__ __forceinline__ void load8_f32<float>(const float* p, float* out) {
 
 // ===================================================== extraction kernel
 struct ExtractPlan {
-  int doc, kvh, slot_region, wvalid, head, q0, qend;
+  int doc, kvh, slot_region, wvalid, head, q0, qend, anchor;
   int nA0, nA1, nB0, nB1, nS;        // doc tiles [nA0,nA1) u [nB0,nB1), slot tiles [0,nS)
   int64_t row0;
   int n, m, ratio_k, sink;
@@ -79,6 +81,7 @@ __device__ __forceinline__ ExtractPlan extract_plan(const ExtractParams& p, int 
   P.m = dc.m;
   P.ratio_k = p.ratio_k;
   P.sink = min(p.sink_len, dc.n);
+  P.anchor = p.anchor;
   const int per = dc.nwg_doc + dc.nwg_slot;
   const int local = L - dc.wg0;
   P.kvh = local / per;
@@ -112,7 +115,12 @@ __device__ __forceinline__ ExtractPlan extract_plan(const ExtractParams& p, int 
     j1 = max(j1, a1);
   }
   if (!P.slot_region) {
-    P.nA0 = 0; P.nA1 = tmax; P.nB0 = 0; P.nB1 = 0; P.nS = 0;
+    P.nA0 = 0; P.nA1 = tmax; P.nB0 = 0; P.nB1 = 0;
+    P.nS = P.anchor ? (P.m + kBN - 1) / kBN : 0;   // anchor ablation: documents also see every slot
+  } else if (P.anchor) {
+    // anchor ablation: slots see every document token and every slot
+    P.nA0 = 0; P.nA1 = (P.n + kBN - 1) / kBN; P.nB0 = P.nB1 = P.nA1;
+    P.nS = (P.m + kBN - 1) / kBN;
   } else {
     const int ts = (P.sink + kBN - 1) / kBN;
     const int blo = (j0 * P.ratio_k) / kBN;
@@ -139,7 +147,12 @@ __device__ __forceinline__ TileSel extract_tile(const ExtractPlan& P, int it) {
   s.key0 = s.t * kBN;
   const int nkeys = s.is_slot ? P.m : P.n;
   s.nvalid = min(kBN, nkeys - s.key0);
-  if (!P.slot_region) {
+  if (P.anchor && (P.slot_region || s.is_slot)) {
+    // anchor ablation: every key of the tile's range is visible
+    s.active = P.wvalid;
+    s.masked = s.key0 + kBN > nkeys;
+    s.pred = pred_causal(nkeys, 1 << 30);
+  } else if (!P.slot_region) {
     s.active = P.wvalid && s.key0 < P.qend;
     s.masked = (s.key0 + kBN - 1 > P.q0) || (s.key0 + kBN > P.n);
     s.pred = pred_causal(P.n, 0);
@@ -554,9 +567,9 @@ __global__ __launch_bounds__(kThreads) void mask_count_kernel(const ExtractParam
     for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off);
     c_tiles += 1;
     if (tot == 0) c_empty += 1;
-    if (!P.slot_region) c_dd += tot;
-    else if (!ts.is_slot) c_sd += tot;
-    else c_ss += tot;
+    if (ts.is_slot) c_ss += tot;          // slot keys (only slot rows see them, except under the anchor ablation)
+    else if (!P.slot_region) c_dd += tot;
+    else c_sd += tot;
   }
   // one query head per KV group is counted (the mask does not depend on the head)
   if (lane == 0 && P.wvalid && (P.head % p.G) == 0) {

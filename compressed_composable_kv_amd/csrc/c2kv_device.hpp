@@ -129,6 +129,7 @@ struct ExtractParams {
   int32_t num_docs, hq, hkv, G, ratio_k, sink_len;
   int32_t total_wg, grid_wg;
   float scale_log2;
+  int32_t anchor;       // 1: the anchor-token ablation's mask (documents <-> slots both ways)
   ExtractDoc docs[C2KV_MAX_BATCH];
 };
 

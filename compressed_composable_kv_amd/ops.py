@@ -114,9 +114,10 @@ def packed_rows(doc_lens: Sequence[int], ratio_k: int) -> int:
 def extract_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_lens: Sequence[int],
                  ratio_k: int, sink_len: Optional[int] = None, rope_theta: float = 10000.0,
                  return_lse: bool = False, out: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None
+                 workspace: Optional[torch.Tensor] = None, anchor: bool = False
                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Structured-flow extraction attention (c2kv_extract_attn).
+    """Structured-flow extraction attention (c2kv_extract_attn; with
+    anchor=True the anchor-token ablation, c2kv_extract_attn_ex).
 
     q [sum_T][hq][d], k/v [sum_T][hkv][d], rows packed per document as
     [n doc | ceil(n/k) slots].  Returns (o [sum_T][hq][d], lse [hq][sum_T] or None).
@@ -139,9 +140,9 @@ def extract_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_lens: Se
     nbytes = lib.c2kv_workspace_size_extract(lens, len(doc_lens), ratio_k, hkv, d, dt)
     _need(nbytes > 0, "invalid extraction arguments")
     ws = _workspace(workspace, "extract", nbytes, q.device)
-    check(lib.c2kv_extract_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), lens, len(doc_lens),
-                                ratio_k, sink_len, hq, hkv, d, float(rope_theta), dt,
-                                _ptr(ws), ws.numel(), _stream(q.device)))
+    check(lib.c2kv_extract_attn_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), lens, len(doc_lens),
+                                   ratio_k, sink_len, hq, hkv, d, float(rope_theta), dt,
+                                   _lib.EXTRACT_ANCHOR if anchor else 0, _ptr(ws), ws.numel(), _stream(q.device)))
     return o, lse
 
 
@@ -371,7 +372,7 @@ def attn_decode(q, k_new, v_new, cache_k, cache_v, cache_len, q_pos, rope_theta,
 # ----------------------------------------------------------------- testing
 
 def mask_cells(doc_lens: Sequence[int], ratio_k: int, sink_len: Optional[int] = None,
-               device: Optional[torch.device] = None) -> Tuple[int, int, int, int, int]:
+               device: Optional[torch.device] = None, anchor: bool = False) -> Tuple[int, int, int, int, int]:
     """GPU count of visible cells (doc->doc, slot->doc, slot->slot), active
     tiles without a visible cell, and active tiles, from the extraction
     kernel's own tile enumeration (c2kv_mask_cells)."""
@@ -381,6 +382,6 @@ def mask_cells(doc_lens: Sequence[int], ratio_k: int, sink_len: Optional[int] = 
         sink_len = ratio_k
     ws = WORKSPACES.get("mask", lib.c2kv_workspace_size_mask_cells(), dev, zero=False)
     out = (ctypes.c_uint64 * 5)()
-    check(lib.c2kv_mask_cells(_arr_i32(doc_lens), len(doc_lens), ratio_k, sink_len, out,
-                              _ptr(ws), ws.numel(), _stream(dev)))
+    check(lib.c2kv_mask_cells_ex(_arr_i32(doc_lens), len(doc_lens), ratio_k, sink_len,
+                                 _lib.EXTRACT_ANCHOR if anchor else 0, out, _ptr(ws), ws.numel(), _stream(dev)))
     return tuple(int(x) for x in out)

@@ -151,6 +151,24 @@ c2kv_status c2kv_extract_attn(const void* q, const void* k, const void* v,
                               float rope_theta, c2kv_dtype dt,
                               void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Extraction with options.  flags = 0 is c2kv_extract_attn.
+ * C2KV_EXTRACT_ANCHOR: the anchor-token ablation of [Explainer]
+ * experimental-results section (the extra tokens and the document tokens
+ * see each other both ways, which entangles the cache with its context).
+ * Slot rows act as the anchors: a document row sees the document rows up to
+ * itself and every slot row of its document; a slot row sees every row of
+ * its document.  Positions, RoPE, GQA and outputs as for c2kv_extract_attn;
+ * same workspace.  Errors: as c2kv_extract_attn, INVALID_ARG for unknown
+ * flag bits. */
+#define C2KV_EXTRACT_ANCHOR 1u
+c2kv_status c2kv_extract_attn_ex(const void* q, const void* k, const void* v,
+                                 void* o, float* lse,
+                                 const int32_t* doc_lens, int32_t num_docs,
+                                 int32_t ratio_k, int32_t sink_len,
+                                 int32_t hq, int32_t hkv, int32_t head_dim,
+                                 float rope_theta, c2kv_dtype dt, uint32_t flags,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* ---- extraction: one extractor layer around the attention ---------------- */
 
 /* Weights of one layer (device pointers, bf16, row-major).  [Explainer]
@@ -383,6 +401,12 @@ size_t c2kv_workspace_size_mask_cells(void);
 c2kv_status c2kv_mask_cells(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k,
                             int32_t sink_len, uint64_t* counts_out,
                             void* workspace, size_t ws_bytes, hipStream_t stream);
+/* The same count for c2kv_extract_attn_ex's flags.  [2] counts every
+ * visible cell whose key is a slot: slot->slot, plus document->slot under
+ * C2KV_EXTRACT_ANCHOR. */
+c2kv_status c2kv_mask_cells_ex(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k,
+                               int32_t sink_len, uint32_t flags, uint64_t* counts_out,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

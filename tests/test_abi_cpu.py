@@ -211,3 +211,11 @@ def test_extract_layer_validation(lib):
     assert call(wsb=100) == WORKSPACE
     assert call(eps=-1.0) == INVALID
     assert call(weights=LayerWeights(*([FAKE] * 6 + [None]))) == INVALID
+
+
+def test_extract_ex_flag_validation(lib):
+    lens = _arr([100])
+    r = lib.c2kv_extract_attn_ex(FAKE, FAKE, FAKE, FAKE, None, lens, 1, 4, 4, 8, 2, 128, 1e4, 0, 2, FAKE, 1 << 30, None)
+    assert r == INVALID                                   # unknown flag bit
+    out = (ctypes.c_uint64 * 5)()
+    assert lib.c2kv_mask_cells_ex(lens, 1, 4, 4, 4, out, FAKE, 256, None) == INVALID

@@ -503,3 +503,46 @@ def test_compose_without_realignment(c2kv, dt):
         assert_rotated_close(np32(ck[r, :, :Ms[r]]).transpose(1, 0, 2), rk, pre, dtname(dt), f"request {r} keys")
         m0 = O.num_slots(pool_n[docs[0]], k)
         assert torch.equal(ck[r, :, :m0], out[True][0][r, :, :m0])
+
+
+# ------------------------------------------------ anchor-token ablation
+
+@pytest.mark.parametrize("doc_lens,k", [((12,), 4), ((300, 129, 7, 1000), 4), ((513, 65, 3), 8), ((1, 2, 5, 33), 4)])
+def test_anchor_mask_cells_exact(c2kv, doc_lens, k):
+    """The kernel's own enumeration under the anchor ablation: document
+    rows see their causal documents and every slot, slots see everything;
+    no enumerated tile is empty for its wave."""
+    got = c2kv.mask_cells(list(doc_lens), k, k, anchor=True)
+    dd = sum(n * (n + 1) // 2 for n in doc_lens)
+    sd = sum(O.num_slots(n, k) * n for n in doc_lens)
+    xs = sum(n * O.num_slots(n, k) + O.num_slots(n, k) ** 2 for n in doc_lens)
+    assert got[:3] == (dd, sd, xs)
+    assert got[3] == 0
+    # the structured mask's counts are unchanged by the new classification
+    assert c2kv.mask_cells(list(doc_lens), k, k)[:3] == tuple(
+        sum(x) for x in zip(*[O.mask_cell_counts(n, k, k) for n in doc_lens]))
+
+
+ANCHOR_CASES = [
+    ((64, 40), 4, 1, 1, 64, torch.float32),
+    ((300, 129, 7, 1000), 4, 8, 2, 128, torch.bfloat16),
+    ((513, 65, 3), 8, 5, 1, 128, torch.bfloat16),
+    ((1, 2, 5, 33), 4, 2, 2, 64, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", ANCHOR_CASES, ids=lambda c: f"n{'-'.join(map(str, c[0]))}_k{c[1]}_G{c[2]//c[3]}_{dtname(c[5])}")
+def test_anchor_extract_parity(c2kv, case):
+    doc_lens, k, hq, hkv, d, dt = case
+    theta = 1e4 if dt == torch.float32 else 5e5
+    q, kk, v = packed_inputs(81, doc_lens, k, hq, hkv, d, dt, c2kv, salt=ANCHOR_CASES.index(case))
+    o, lse = c2kv.extract_attn(q.to(DEV), kk.to(DEV), v.to(DEV), list(doc_lens), k, k, theta, return_lse=True,
+                               anchor=True)
+    torch.cuda.synchronize()
+    ref = O.extract_attn(q.float().numpy(), kk.float().numpy(), v.float().numpy(), list(doc_lens), k, k, theta,
+                         anchor=True)
+    offs = O.doc_row_offsets(doc_lens, k)
+    for b in range(len(doc_lens)):
+        ro, rl = ref[b]
+        assert_close(np32(o[offs[b]:offs[b + 1]]), ro, dtname(dt), f"doc {b} anchor output")
+        assert_lse_close(np32(lse[:, offs[b]:offs[b + 1]]), rl, dtname(dt), f"doc {b} anchor")
