@@ -873,8 +873,9 @@ def main():
         # one launch = one c2kv_attn_decode call: decode_attn_kernel plus
         # merge_kernel, timed per call from the graph replay
         per_launch_ms = ph[3] / S
-        traffic = committed_traffic(("decode_attn_kernel", "merge_kernel"))
-        roof = {"bound": "hbm", "kernel": "c2kv_attn_decode (decode_attn_kernel<bf16,128> + merge_kernel<bf16,128>)",
+        # the decode call's merge is the 32-dim-slice instantiation (the prefill one takes whole rows)
+        traffic = committed_traffic(("decode_attn_kernel", "merge_kernelIDF16bLi128ELi32E"))
+        roof = {"bound": "hbm", "kernel": "c2kv_attn_decode (decode_attn_kernel<bf16,128> + merge_kernel<bf16,128,32>)",
                 "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                 "traffic": traffic, "per_launch_ms": per_launch_ms, "algorithmic_per_launch": dec_bytes / S}
 
