@@ -74,13 +74,15 @@ def assert_rotated_close(got: np.ndarray, ref: np.ndarray, pre: np.ndarray, dtyp
                            f"max err {float(err.max()):.3e}; max bf16-ulp distance {bf16_ulp_diff(got, ref)}")
 
 
-def oracle_extract_rows(q, k, v, n: int, ratio_k: int, sink, theta: float, rows: Sequence[int]):
+def oracle_extract_rows(q, k, v, n: int, ratio_k: int, sink, theta: float, rows: Sequence[int],
+                        anchor: bool = False):
     """Oracle extraction outputs of selected packed rows of ONE document
     (q/k/v: that document's packed [n | m] rows as numpy).  Uses the oracle's
-    rotation, structured mask and attention on the selected query rows."""
+    rotation, structured mask (the anchor ablation's with anchor=True) and
+    attention on the selected query rows."""
     pos = O.extraction_positions(n, ratio_k)
     rows = np.asarray(rows)
     qr = O.rope_rotate(np.asarray(q[rows], np.float32), pos[rows], theta)
     kr = O.rope_rotate(np.asarray(k, np.float32), pos, theta)
-    M = O.structured_mask(n, ratio_k, sink)[rows]
+    M = O.structured_mask(n, ratio_k, sink, anchor)[rows]
     return O.attention(qr, kr, np.asarray(v, np.float64), M)

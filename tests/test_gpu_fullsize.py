@@ -15,6 +15,9 @@ benchmark times, on sampled outputs the oracle computes one by one.
 * Qwen3-14B extraction: 64 documents of 8192 tokens in one call at
   k = 4, 8, 16; sampled rows of the first and last document, every head;
   plus the GPU mask-cell counts of the whole batch.
+* The anchor-token ablation over the whole Llama batch (sampled rows, exact
+  cell counts), and the Qwen2.5 pool composed from pinned host memory
+  (bit-identical to the device-source compose).
 
 Decode step s over a cache equals the last query row of a prefill of the
 question and decode tokens 0..s (an oracle identity pinned on the CPU), so
@@ -54,11 +57,11 @@ def _doc_sample_rows(n, m):
     return doc + [n + j for j in slot]
 
 
-def _check_extract_rows(og, lg, q, k, v, n, ratio_k, sink, theta, what):
+def _check_extract_rows(og, lg, q, k, v, n, ratio_k, sink, theta, what, anchor=False):
     """og/lg: GPU output rows [rows][Hq][d] / lse [Hq][rows] of one
     document's packed rows; q/k/v: CPU inputs of the same rows."""
     rows = _doc_sample_rows(n, O.num_slots(n, ratio_k))
-    ro, rl = oracle_extract_rows(q, k, v, n, ratio_k, sink, theta, rows)
+    ro, rl = oracle_extract_rows(q, k, v, n, ratio_k, sink, theta, rows, anchor)
     assert_close(og[rows], ro, "bf16", f"{what}: sampled rows")
     assert_lse_close(lg[:, rows], rl, "bf16", f"{what}: sampled rows")
 
@@ -274,3 +277,77 @@ def test_qwen3_14b_extract_full(c2kv, ratio_k):
     got = c2kv.mask_cells(lens, ratio_k, ratio_k)
     dd, sd, ss = O.mask_cell_counts(8192, ratio_k, ratio_k)
     assert got[:3] == (64 * dd, 64 * sd, 64 * ss) and got[3] == 0
+
+
+# ------------------------------------------- anchor ablation, host-pool load
+
+def test_llama_anchor_extract_full(c2kv):
+    """The anchor-token ablation over the whole Llama batch (8 x 4096 tokens,
+    k = 4) in one call: sampled document and slot rows of the first and last
+    document, every head, against the oracle's anchor mask; exact cell
+    counts of the batch."""
+    w = W.LLAMA
+    d, hq, hkv, k, theta, dt = w.head_dim, w.hq, w.hkv, w.ratio_k, w.rope_theta, w.dtype
+    lens = list(w.doc_lens)
+    rows = c2kv.packed_rows(lens, k)
+    offs = O.doc_row_offsets(lens, k)
+    print("llama anchor ablation: extraction of 8 x 4096 in one call", flush=True)
+    q = W.normal((rows, hq, d), dt, w.wid, W.P_Q, salt=5)
+    kk = W.normal((rows, hkv, d), dt, w.wid, W.P_K, salt=5)
+    v = W.normal((rows, hkv, d), dt, w.wid, W.P_V, salt=5)
+    o, lse = c2kv.extract_attn(q.to(DEV), kk.to(DEV), v.to(DEV), lens, k, w.sink_len, theta, return_lse=True,
+                               anchor=True)
+    torch.cuda.synchronize()
+    for b in (0, len(lens) - 1):
+        r0, r1 = offs[b], offs[b + 1]
+        _check_extract_rows(np32(o[r0:r1]), np32(lse[:, r0:r1]), q[r0:r1].float().numpy(),
+                            kk[r0:r1].float().numpy(), v[r0:r1].float().numpy(), lens[b], k, w.sink_len,
+                            theta, f"anchor document {b}", anchor=True)
+    del o, lse
+    _free()
+    n, m = 4096, O.num_slots(4096, k)
+    got = c2kv.mask_cells(lens, k, k, anchor=True)
+    assert got[:3] == (8 * n * (n + 1) // 2, 8 * m * n, 8 * (n * m + m * m)) and got[3] == 0
+
+
+def test_qwen25_pool_from_host_full(c2kv):
+    """The Qwen2.5-7B pool kept in pinned host memory: all 32 requests
+    composed in one call by reading the slot caches in place, bit-identical
+    to composing device copies; positions against the oracle."""
+    w = W.QWEN25
+    d, hkv, k, theta, dt = w.head_dim, w.hkv, w.ratio_k, w.rope_theta, w.dtype
+    pool_n = W.qwen25_pool(w)
+    reqs = W.qwen25_requests(w)
+    print("qwen25 pool in host memory: generating the 64-document pool", flush=True)
+    pool_k = [W.normal((O.num_slots(n, k), hkv, d), dt, w.wid, W.P_K, salt=t) for t, n in enumerate(pool_n)]
+    pool_v = [W.normal((O.num_slots(n, k), hkv, d), dt, w.wid, W.P_V, salt=t) for t, n in enumerate(pool_n)]
+
+    def pinned(t):
+        p = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        p.copy_(t)
+        return p
+    hk = [pinned(x) for x in pool_k]
+    hv = [pinned(x) for x in pool_v]
+    dk = [x.to(DEV) for x in pool_k]
+    dv = [x.to(DEV) for x in pool_v]
+    Ms = [sum(O.num_slots(pool_n[t], k) for t in r) for r in reqs]
+    R, cap = len(reqs), max(Ms)
+    res = []
+    for src_k, src_v in ((hk, hv), (dk, dv)):
+        ck = torch.zeros((R, hkv, cap, d), dtype=dt, device=DEV)
+        cv = torch.zeros_like(ck)
+        pos = torch.full((R, cap), -1, dtype=torch.int32, device=DEV)
+        print("qwen25 pool: compose 32 requests in one call", flush=True)
+        clen, nxt = c2kv.compose([[(src_k[t], src_v[t], pool_n[t]) for t in r] for r in reqs], k, theta, ck, cv,
+                                 pos_out=pos)
+        torch.cuda.synchronize()
+        res.append((ck, cv, pos, clen, nxt))
+    (hck, hcv, hpos, hl, hn), (dck, dcv, dpos, dl, dn) = res
+    assert hl == dl == Ms and hn == dn
+    assert torch.equal(hck, dck) and torch.equal(hcv, dcv) and torch.equal(hpos, dpos)
+    gpos = hpos.cpu().numpy()
+    for r, docs in enumerate(reqs):
+        rp, _, rnext = O.compose_positions([pool_n[t] for t in docs], k)
+        assert hn[r] == rnext and np.array_equal(gpos[r, :Ms[r]], rp)
+    del res, hck, hcv, dck, dcv, dk, dv
+    _free()
