@@ -20,18 +20,25 @@
 namespace c2kv {
 
 constexpr int kGM = 128, kGN = 128, kGK = 64;
-constexpr int kGroupM = 16;   // row tiles per group of the tile order
+constexpr int kGroupM = 8;   // row tiles per group of the tile order
 
-// Tile order: groups of kGroupM row tiles; inside a group the row tile
-// varies fastest, so the resident workgroups cover about 16 row tiles x 32
-// column tiles and both operand slices stay in cache while they are reused.
-__device__ __forceinline__ void gemm_tile(int b, int m_tiles, int n_tiles, int& mt, int& nt) {
+// Tile order.  The eight XCDs each have their own L2 and receive workgroups
+// round robin, so physical workgroup p becomes logical tile
+// (p % 8) * (grid / 8) + p / 8: each XCD walks a contiguous slice of the
+// logical order.  That order takes groups of kGroupM row tiles with the row
+// tile varying fastest, so the 64 workgroups an XCD holds at once cover
+// about 8 row tiles x 8 column tiles and share each A and B panel through
+// the XCD's L2.  Returns false for the padding workgroups past the last tile.
+__device__ __forceinline__ bool gemm_tile(int p, int grid, int m_tiles, int n_tiles, int& mt, int& nt) {
+  const int t = (p & 7) * (grid >> 3) + (p >> 3);   // grid is a multiple of 8
+  if (t >= m_tiles * n_tiles) return false;
   const int group_tiles = kGroupM * n_tiles;
-  const int g = b / group_tiles, local = b % group_tiles;
+  const int g = t / group_tiles, local = t % group_tiles;
   const int gm0 = g * kGroupM;
   const int gsz = min(kGroupM, m_tiles - gm0);
   mt = gm0 + local % gsz;
   nt = local / gsz;
+  return true;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -44,7 +51,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
   asm volatile("" : : "r"(&lds[0][0][0]) : "memory");
   const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int mt, nt;
-  gemm_tile((int)blockIdx.x, p.m_tiles, p.n_tiles, mt, nt);
+  if (!gemm_tile((int)blockIdx.x, (int)gridDim.x, p.m_tiles, p.n_tiles, mt, nt)) return;
   int lo = 0, hi = p.num_ranges - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -172,12 +179,13 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmParams p) {
 hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t st) {
   const int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
   if (tiles == 0) return hipSuccess;
+  const dim3 grid((unsigned)((tiles + 7) / 8 * 8));   // a multiple of the 8 XCDs
   if (epi == kEpiResidual)
-    hipLaunchKernelGGL((gemm_nt_kernel<kEpiResidual>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_nt_kernel<kEpiResidual>), grid, dim3(256), 0, st, p);
   else if (epi == kEpiSwiglu)
-    hipLaunchKernelGGL((gemm_nt_kernel<kEpiSwiglu>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_nt_kernel<kEpiSwiglu>), grid, dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((gemm_nt_kernel<kEpiStore>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_nt_kernel<kEpiStore>), grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
