@@ -286,6 +286,39 @@ def test_extraction_doc_rows_equal_causal_model():
     assert np.abs(o[:n] - ref.numpy()).max() < 1e-12
 
 
+def _slot_rows_brute(q, kk, v, n, k, theta):
+    """Extraction outputs of every row by brute force, with the positions
+    written out here from the positions section's rule (document token i at
+    i; slot j at the last token of its block, j*k + k - 1, or n - 1 for a
+    partial last block) and visibility from the rule statements."""
+    m = (n + k - 1) // k
+    pos = [i for i in range(n)] + [min(j * k + k - 1, n - 1) for j in range(m)]
+    qr = O.rope_rotate(q, np.array(pos), theta)
+    kr = O.rope_rotate(kk, np.array(pos), theta)
+    vis = [O.visible_set(n, k, None, row) for row in range(n + m)]
+    return O.attention_brute(qr, kr, v.astype(np.float64), vis)
+
+
+@pytest.mark.parametrize("n,k", [(12, 4), (10, 4), (37, 8), (3, 4)])
+@pytest.mark.parametrize("G", [1, 2])
+def test_extraction_slot_rows_end_to_end(n, k, G):
+    """extract_attn's slot rows (and document rows) against brute-force
+    attention over q/k rotated at the slot positions the positions section
+    fixes (3, 7, ... at k = 4), with visibility sets from the mask rules."""
+    hkv, d, theta = 2, 8, 1e4
+    hq = G * hkv
+    m = O.num_slots(n, k)
+    r = rng(500 + 7 * n + k + G)
+    q = r.standard_normal((n + m, hq, d)).astype(np.float32)
+    kk = r.standard_normal((n + m, hkv, d)).astype(np.float32)
+    v = r.standard_normal((n + m, hkv, d)).astype(np.float32)
+    o, lse = O.extract_attn(q, kk, v, [n], k, None, theta)[0]
+    ob, lb = _slot_rows_brute(q, kk, v, n, k, theta)
+    assert np.abs(o[n:] - ob[n:]).max() < 1e-12
+    assert np.abs(lse[:, n:] - lb[:, n:]).max() < 1e-12
+    assert np.abs(o[:n] - ob[:n]).max() < 1e-12
+
+
 def test_extraction_multi_doc_independent():
     """Each document is extracted alone: packing several documents gives the
     same per-document results as extracting each by itself."""
@@ -728,3 +761,21 @@ def test_planted_layer_norm_mistake_caught(monkeypatch):
         np.mean(np.asarray(x, dtype=np.float64) ** 2, axis=-1, keepdims=True) + eps))
     with pytest.raises(AssertionError):
         test_layer_doc_rows_equal_base_model_layer()
+
+
+def test_planted_slot_rotation_at_block_start_caught(monkeypatch):
+    # slots rotated at the first token of their block (j*k) instead of its last
+    def at_block_start(n, k):
+        m = O.num_slots(n, k)
+        return np.array(list(range(n)) + [j * k for j in range(m)], dtype=np.int64)
+    monkeypatch.setattr(O.c2kv_oracle, "extraction_positions", at_block_start)
+    with pytest.raises(AssertionError):
+        test_extraction_slot_rows_end_to_end(12, 4, 2)
+
+
+def test_planted_slot_rotation_at_row_index_caught(monkeypatch):
+    # slots rotated at their packed row index (n + j) instead of their block's end
+    monkeypatch.setattr(O.c2kv_oracle, "extraction_positions",
+                        lambda n, k: np.arange(n + O.num_slots(n, k), dtype=np.int64))
+    with pytest.raises(AssertionError):
+        test_extraction_slot_rows_end_to_end(10, 4, 1)
