@@ -35,6 +35,12 @@ class Segment(ctypes.Structure):
                 ("doc_len", c_int32), ("flags", c_int32)]
 
 
+class TileEntry(ctypes.Structure):
+    _fields_ = [("doc", c_int32), ("kv_head", c_int32), ("q_head", c_int32), ("q_slot", c_int32),
+                ("q0", c_int32), ("q1", c_int32), ("k_slot", c_int32), ("key0", c_int32),
+                ("nkeys", c_int32), ("masked", c_int32)]
+
+
 class LayerWeights(ctypes.Structure):
     _fields_ = [("attn_norm", c_void_p), ("wqkv", c_void_p), ("wqkv_c2", c_void_p), ("wo", c_void_p),
                 ("ffn_norm", c_void_p), ("w_gate_up", c_void_p), ("w_down", c_void_p)]
@@ -87,6 +93,9 @@ SIGNATURES = {
     "c2kv_workspace_init": (c_int32, [c_void_p, c_size_t, c_void_p]),
     "c2kv_workspace_size_mask_cells": (c_size_t, []),
     "c2kv_mask_cells": (c_int32, [P_i32, c_int32, c_int32, c_int32, P_u64, c_void_p, c_size_t, c_void_p]),
+    "c2kv_workspace_size_tile_schedule": (c_size_t, []),
+    "c2kv_tile_schedule": (c_int32, [P_i32, c_int32, c_int32, c_int32, c_int32, c_int32, ctypes.c_uint32,
+                                     c_void_p, c_int64, ctypes.POINTER(c_int64), c_void_p, c_size_t, c_void_p]),
 }
 
 _lib = None

@@ -4,8 +4,8 @@
 
 Compiles every source under csrc/ for --offload-arch=gfx950 and links the
 shared library next to this file.  Also builds libc2kv_probe.so from probe/,
-a measurement tool the benchmark loads (the achievable MFMA rate); the
-library does not use it.  Always rebuilds.
+measurement tools the benchmark loads (the achievable MFMA and HBM read
+rates); the library does not use them.  Always rebuilds.
 """
 from __future__ import annotations
 
@@ -23,7 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libc2kv.so")
-PROBE_SRC = os.path.join(PKG, "probe", "mfma_peak.hip")
+PROBE_SRCS = [os.path.join(PKG, "probe", "mfma_peak.hip"), os.path.join(PKG, "probe", "hbm_read.hip")]
 PROBE_LIB = os.path.join(PKG, "libc2kv_probe.so")
 
 SOURCES = ["c2kv_attn.hip", "c2kv_decode.hip", "c2kv_aux.hip", "c2kv_layer.hip", "c2kv_abi.cpp"]
@@ -81,7 +81,7 @@ def build(jobs: int = 4) -> str:
 
 def build_probe() -> str:
     tmp = PROBE_LIB + ".tmp"
-    cmd = [HIPCC, *[f for f in CFLAGS if not f.startswith("-I")], "-shared", "-o", tmp, PROBE_SRC,
+    cmd = [HIPCC, *[f for f in CFLAGS if not f.startswith("-I")], "-shared", "-o", tmp, *PROBE_SRCS,
            "-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

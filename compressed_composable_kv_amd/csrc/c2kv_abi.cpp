@@ -156,8 +156,8 @@ constexpr int64_t kPrefillSlots = 256;      // prefill workgroups per launch: on
 struct CachePlan {
   bool decode = false;
   int32_t nug = 0, nblk_q = 0, chunk = 0;
-  std::vector<int32_t> nsplit, chunk_r;
-  size_t qrot_off = 0, part_off = 0, total = 0;
+  std::vector<int32_t> nsplit, chunk_r, pbase;   // pbase: first partial of the request within its launch
+  size_t qrot_off = 0, part_off = 0, ml_off = 0, total = 0;
 };
 
 c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, int32_t hq, int32_t hkv,
@@ -225,17 +225,24 @@ c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, i
       P.nsplit[r] = (int32_t)ceil_div(len, c);
     }
   }
+  // compact split partials: requests with more than one piece, in launch
+  // order, hq * tq * nsplit partials each
   size_t max_part = 0;
+  P.pbase.assign(num_reqs, 0);
   for (int32_t r0 = 0; r0 < num_reqs; r0 += C2KV_MAX_BATCH) {
     const int32_t r1 = std::min(num_reqs, r0 + C2KV_MAX_BATCH);
-    int32_t stride = 0;
-    for (int32_t r = r0; r < r1; ++r) stride = std::max(stride, P.nsplit[r]);
-    if (stride > 1)
-      max_part = std::max(max_part, (size_t)(r1 - r0) * hq * tq * stride * (head_dim + 4) * sizeof(float));
+    size_t cnt = 0;
+    for (int32_t r = r0; r < r1; ++r) {
+      P.pbase[r] = (int32_t)cnt;
+      if (P.nsplit[r] > 1) cnt += (size_t)hq * tq * P.nsplit[r];
+    }
+    if (cnt >= ((size_t)1 << 31)) return fail(C2KV_ERR_CAPACITY, "%zu split partials in one launch", cnt);
+    max_part = std::max(max_part, cnt);
   }
   P.qrot_off = 0;
   P.part_off = decode ? 0 : align_up((size_t)num_reqs * tq * hq * head_dim * elem_bytes(dt));
-  P.total = P.part_off + align_up(max_part);
+  P.ml_off = P.part_off + align_up(max_part * head_dim * sizeof(float));
+  P.total = P.ml_off + align_up(max_part * sizeof(float2));
   return C2KV_OK;
 }
 
@@ -253,11 +260,11 @@ c2kv_status check_dev(const void* p, const char* name) {
   return C2KV_OK;
 }
 
-c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new, void* cache_k, void* cache_v,
-                            int64_t cap, const int32_t* cache_len, const int32_t* q_pos0, int32_t num_reqs,
-                            int32_t tq, bool decode, int32_t hq, int32_t hkv, int32_t head_dim, float rope_theta,
-                            void* o, float* lse, c2kv_dtype dt, void* workspace, size_t ws_bytes,
-                            hipStream_t stream) {
+// Validation of a prefill / decode call (no HIP call); fills the plan.
+c2kv_status cache_validate(const void* q, const void* k_new, const void* v_new, void* cache_k, void* cache_v,
+                           int64_t cap, const int32_t* cache_len, const int32_t* q_pos0, int32_t num_reqs,
+                           int32_t tq, bool decode, int32_t hq, int32_t hkv, int32_t head_dim, float rope_theta,
+                           void* o, float* lse, c2kv_dtype dt, CachePlan& P) {
   c2kv_status s;
   if ((s = check_heads(hq, hkv, head_dim, dt))) return s;
   if ((s = check_theta(rope_theta))) return s;
@@ -267,20 +274,33 @@ c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new,
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(C2KV_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   if (!q_pos0) return fail(C2KV_ERR_INVALID_ARG, "q_pos is NULL");
   if (cap < 1) return fail(C2KV_ERR_INVALID_ARG, "cap=%lld must be >= 1", (long long)cap);
-  // per-head byte offsets (plus one workgroup step of 128 keys) are 32-bit
-  // in the kernels
-  if ((cap + 128) * head_dim * elem_bytes(dt) >= ((int64_t)1 << 31))
+  // per-head byte offsets are 32-bit in the kernels, including the decode
+  // wave's prefetch of its next step (up to 128 + 31 rows past a chunk)
+  if ((cap + 256) * head_dim * elem_bytes(dt) >= ((int64_t)1 << 31))
     return fail(C2KV_ERR_CAPACITY, "cap=%lld rows of one head exceed 2 GiB", (long long)cap);
-  CachePlan P;
   if ((s = cache_plan(cache_len, num_reqs, tq, hq, hkv, head_dim, dt, cap, decode, P))) return s;
   for (int32_t r = 0; r < num_reqs; ++r) {
     if (q_pos0[r] < 0 || (int64_t)q_pos0[r] + tq > (1 << 24))
       return fail(C2KV_ERR_CAPACITY, "q_pos[%d]=%d + %d tokens outside [0, 2^24]", r, q_pos0[r], tq);
   }
+  return C2KV_OK;
+}
+
+c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new, void* cache_k, void* cache_v,
+                            int64_t cap, const int32_t* cache_len, const int32_t* q_pos0, int32_t num_reqs,
+                            int32_t tq, bool decode, int32_t hq, int32_t hkv, int32_t head_dim, float rope_theta,
+                            void* o, float* lse, c2kv_dtype dt, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  c2kv_status s;
+  CachePlan P;
+  if ((s = cache_validate(q, k_new, v_new, cache_k, cache_v, cap, cache_len, q_pos0, num_reqs, tq, decode, hq, hkv,
+                          head_dim, rope_theta, o, lse, dt, P)))
+    return s;
   if ((s = check_ws(workspace, ws_bytes, P.total))) return s;
 
   char* ws = static_cast<char*>(workspace);
-  float* part = reinterpret_cast<float*>(ws + P.part_off);
+  float* part_o = reinterpret_cast<float*>(ws + P.part_off);
+  float2* part_ml = reinterpret_cast<float2*>(ws + P.ml_off);
   const RopeFreqs freqs = make_freqs(head_dim, rope_theta);
   const int32_t G = hq / hkv;
   for (int32_t r0 = 0; r0 < num_reqs; r0 += C2KV_MAX_BATCH) {
@@ -292,8 +312,9 @@ c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new,
       DecodeParams dp;
       std::memset(&dp, 0, sizeof(dp));
       dp.q = q; dp.k_new = k_new; dp.v_new = v_new; dp.kc = cache_k; dp.vc = cache_v; dp.o = o; dp.lse = lse;
-      dp.part = part; dp.cap = cap; dp.req0 = r0; dp.num_reqs = cnt; dp.hq = hq; dp.hkv = hkv; dp.G = G;
-      dp.nsplit_stride = stride; dp.scale_log2 = scale_log2(head_dim); dp.freqs = freqs;
+      dp.part_o = part_o; dp.part_ml = part_ml;
+      dp.cap = cap; dp.req0 = r0; dp.num_reqs = cnt; dp.hq = hq; dp.hkv = hkv; dp.G = G;
+      dp.scale_log2 = scale_log2(head_dim); dp.freqs = freqs;
       int64_t wg = 0;
       for (int32_t i = 0; i < cnt; ++i) {
         dp.reqs[i].wg0 = (int32_t)wg;
@@ -301,6 +322,7 @@ c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new,
         dp.reqs[i].pos = q_pos0[r0 + i];
         dp.reqs[i].nsplit = P.nsplit[r0 + i];
         dp.reqs[i].chunk = P.chunk_r[r0 + i];
+        dp.reqs[i].pbase = P.pbase[r0 + i];
         wg += (int64_t)hkv * P.nsplit[r0 + i];
       }
       dp.total_wg = (int32_t)wg;
@@ -320,15 +342,16 @@ c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new,
       CacheParams cp;
       std::memset(&cp, 0, sizeof(cp));
       cp.qrot = ws + P.qrot_off;
-      cp.kc = cache_k; cp.vc = cache_v; cp.o = o; cp.lse = lse; cp.part = part;
+      cp.kc = cache_k; cp.vc = cache_v; cp.o = o; cp.lse = lse; cp.part_o = part_o; cp.part_ml = part_ml;
       cp.cap = cap; cp.req0 = r0; cp.num_reqs = cnt; cp.tq = tq; cp.hq = hq; cp.hkv = hkv; cp.G = G;
-      cp.nblk_q = P.nblk_q; cp.nug = P.nug; cp.chunk = P.chunk; cp.nsplit_stride = stride;
+      cp.nblk_q = P.nblk_q; cp.nug = P.nug; cp.chunk = P.chunk;
       cp.scale_log2 = scale_log2(head_dim);
       int64_t wg = 0;
       for (int32_t i = 0; i < cnt; ++i) {
         cp.reqs[i].wg0 = (int32_t)wg;
         cp.reqs[i].cache_len = cache_len[r0 + i];
         cp.reqs[i].nsplit = P.nsplit[r0 + i];
+        cp.reqs[i].pbase = P.pbase[r0 + i];
         wg += (int64_t)hkv * P.nsplit[r0 + i] * P.nug;
       }
       cp.total_wg = (int32_t)wg;
@@ -339,9 +362,9 @@ c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new,
     if (stride > 1) {
       MergeParams mp;
       std::memset(&mp, 0, sizeof(mp));
-      mp.part = part; mp.o = o; mp.lse = lse; mp.req0 = r0; mp.num_rows = cnt * hq * tq; mp.hq = hq; mp.tq = tq;
-      mp.nsplit_stride = stride;
-      for (int32_t i = 0; i < cnt; ++i) mp.nsplit[i] = P.nsplit[r0 + i];
+      mp.part_o = part_o; mp.part_ml = part_ml;
+      mp.o = o; mp.lse = lse; mp.req0 = r0; mp.num_rows = cnt * hq * tq; mp.hq = hq; mp.tq = tq;
+      for (int32_t i = 0; i < cnt; ++i) { mp.nsplit[i] = P.nsplit[r0 + i]; mp.pbase[i] = P.pbase[r0 + i]; }
       e = launch_merge(mp, dt, head_dim, stream);
       if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     }
@@ -447,7 +470,7 @@ c2kv_status c2kv_extract_attn_ex(const void* q, const void* k, const void* v, vo
     const int cnt = fill_extract_chunk(doc_lens, b, num_docs, ratio_k, p.G, hkv, row, p, rp);
     e = launch_rotate_k(rp, dt, head_dim, stream);
     if (e != hipSuccess) return hip_fail(e, "key rotation kernel launch");
-    e = launch_extract_attn(p, dt, head_dim, false, stream);
+    e = launch_extract_attn(p, dt, head_dim, kExtractAttn, stream);
     if (e != hipSuccess) return hip_fail(e, "extraction attention kernel launch");
     row = rp.row_end;
     b += cnt;
@@ -912,7 +935,7 @@ c2kv_status c2kv_mask_cells_ex(const int32_t* doc_lens, int32_t num_docs, int32_
   int64_t row = 0;
   for (int32_t b = 0; b < num_docs;) {
     const int cnt = fill_extract_chunk(doc_lens, b, num_docs, ratio_k, 1, 1, row, p, rp);
-    e = launch_extract_attn(p, C2KV_F32, 64, true, stream);
+    e = launch_extract_attn(p, C2KV_F32, 64, kExtractCount, stream);
     if (e != hipSuccess) return hip_fail(e, "mask count kernel launch");
     row = rp.row_end;
     b += cnt;
@@ -923,6 +946,54 @@ c2kv_status c2kv_mask_cells_ex(const int32_t* doc_lens, int32_t num_docs, int32_
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   std::memcpy(counts_out, host, sizeof(host));
+  return ok();
+}
+
+size_t c2kv_workspace_size_tile_schedule(void) { return 256; }
+
+c2kv_status c2kv_tile_schedule(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t sink_len,
+                               int32_t hq, int32_t hkv, uint32_t flags, c2kv_tile_entry* entries,
+                               int64_t capacity, int64_t* count_out, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
+  c2kv_status s;
+  if (flags & ~C2KV_EXTRACT_ANCHOR) return fail(C2KV_ERR_INVALID_ARG, "flags=%u has unknown bits", flags);
+  if (!count_out) return fail(C2KV_ERR_INVALID_ARG, "count_out is NULL");
+  if (sink_len < 0) return fail(C2KV_ERR_INVALID_ARG, "sink_len=%d must be >= 0", sink_len);
+  if ((s = check_heads(hq, hkv, 64, C2KV_F32))) return s;
+  if (capacity < 0) return fail(C2KV_ERR_INVALID_ARG, "capacity=%lld must be >= 0", (long long)capacity);
+  if (capacity > 0 && (s = check_dev(entries, "entries"))) return s;
+  ExtractLayout L;
+  if ((s = extract_layout(doc_lens, num_docs, ratio_k, hkv, 64, C2KV_F32, L))) return s;
+  if ((s = check_ws(workspace, ws_bytes, c2kv_workspace_size_tile_schedule()))) return s;
+  uint64_t* counter = static_cast<uint64_t*>(workspace);
+  hipError_t e = launch_fill_zero(counter, 64, stream);
+  if (e != hipSuccess) return hip_fail(e, "fill kernel launch");
+  ExtractParams p;
+  RotateParams rp;
+  std::memset(&p, 0, sizeof(p));
+  std::memset(&rp, 0, sizeof(rp));
+  p.hq = hq; p.hkv = hkv; p.G = hq / hkv; p.ratio_k = ratio_k; p.sink_len = sink_len;
+  p.counts = counter; p.entries = entries; p.entry_cap = capacity;
+  p.anchor = (flags & C2KV_EXTRACT_ANCHOR) ? 1 : 0;
+  p.total_rows = L.rows;
+  int64_t row = 0;
+  for (int32_t b = 0; b < num_docs;) {
+    const int cnt = fill_extract_chunk(doc_lens, b, num_docs, ratio_k, p.G, hkv, row, p, rp);
+    p.doc_base = b;
+    e = launch_extract_attn(p, C2KV_F32, 64, kExtractDump, stream);
+    if (e != hipSuccess) return hip_fail(e, "tile dump kernel launch");
+    row = rp.row_end;
+    b += cnt;
+  }
+  uint64_t total = 0;
+  e = hipMemcpyAsync(&total, counter, sizeof(total), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  *count_out = (int64_t)total;
+  if ((int64_t)total > capacity && (entries || capacity > 0))
+    return fail(C2KV_ERR_CAPACITY, "the schedule has %llu entries, capacity is %lld", (unsigned long long)total,
+                (long long)capacity);
   return ok();
 }
 

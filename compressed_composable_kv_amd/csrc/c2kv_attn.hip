@@ -132,6 +132,25 @@ __device__ __forceinline__ ExtractPlan extract_plan(const ExtractParams& p, int 
   return P;
 }
 
+// Whether every cell of the document key tile [a, a + kBN) is visible to
+// every slot row j in [q0, q1) (slot j sees the sink [0, s) and its own block
+// [jk, min(n, jk + k))).  A row whose own block starts inside the sink
+// (jk <= s) sees one interval [0, max(s, min(n, jk + k))), the smallest such
+// row binding; a row whose block starts past the sink sees two separate
+// intervals, so the tile must lie in that row's own block, which no two rows
+// share.
+__device__ __forceinline__ bool slot_doc_tile_full(int a, int n, int k, int s, int q0, int q1) {
+  const int b = a + kBN;
+  if (b > n) return false;
+  if (b <= s) return true;
+  const int jm = s / k + 1;                    // rows j < jm start inside the sink
+  if (q0 < jm && b > max(s, min(n, q0 * k + k))) return false;
+  const int sep0 = max(q0, jm);
+  if (q1 - sep0 >= 2) return false;
+  if (q1 - sep0 == 1 && (a < sep0 * k || b > min(n, sep0 * k + k))) return false;
+  return true;
+}
+
 // Tile `it` of the plan: whether it holds a document or slot key range,
 // its index, and the visibility predicate / activity of the calling wave.
 struct TileSel {
@@ -161,7 +180,7 @@ __device__ __forceinline__ TileSel extract_tile(const ExtractPlan& P, int it) {
     const int blo = (P.q0 * P.ratio_k) / kBN;
     const int bhi = (min(P.n, P.qend * P.ratio_k) + kBN - 1) / kBN;
     s.active = P.wvalid && (s.t < ts || (s.t >= blo && s.t < bhi));
-    s.masked = 1;
+    s.masked = !slot_doc_tile_full(s.key0, P.n, P.ratio_k, P.sink, P.q0, P.qend);
     s.pred = pred_slot_doc(P.n, P.ratio_k, P.sink);
   } else {
     s.active = P.wvalid && s.key0 < P.qend;
@@ -581,6 +600,43 @@ __global__ __launch_bounds__(kThreads) void mask_count_kernel(const ExtractParam
   }
 }
 
+// Tile-schedule twin of the extraction kernel: the same plan and tile
+// enumeration; every (unit, tile) pair a wave computes is written out.
+__global__ __launch_bounds__(kThreads) void tile_dump_kernel(const ExtractParams p) {
+  const int L = xcd_logical(blockIdx.x, p.grid_wg);
+  if (L >= p.total_wg) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const ExtractPlan P = extract_plan(p, L, wave);
+  if (!P.wvalid) return;
+  const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
+  int cnt = 0;
+  for (int it = 0; it < ntiles; ++it) cnt += extract_tile(P, it).active ? 1 : 0;
+  unsigned long long base = 0;
+  if (lane == 0) base = atomicAdd(reinterpret_cast<unsigned long long*>(p.counts), (unsigned long long)cnt);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)base);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(base >> 32));
+  long long idx = (long long)(((unsigned long long)hi << 32) | lo);
+  for (int it = 0; it < ntiles; ++it) {
+    const TileSel ts = extract_tile(P, it);
+    if (!ts.active) continue;
+    if (lane == 0 && idx < p.entry_cap) {
+      c2kv_tile_entry e;
+      e.doc = p.doc_base + P.doc;
+      e.kv_head = P.kvh;
+      e.q_head = P.head;
+      e.q_slot = P.slot_region;
+      e.q0 = P.q0;
+      e.q1 = P.qend;
+      e.k_slot = ts.is_slot;
+      e.key0 = ts.key0;
+      e.nkeys = ts.nvalid;
+      e.masked = ts.masked ? 1 : 0;
+      p.entries[idx] = e;
+    }
+    ++idx;
+  }
+}
+
 // ============================================== attention over the cache
 // LDS DMA of one K tile and one row-major V tile (KB bytes each) of cache
 // rows; this wave fills 1 KB blocks wave*NDMA .. +NDMA-1 of each.
@@ -710,8 +766,9 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void cache_attn_kerne
       if (g == 0 && p.lse)
         p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (m2 + __log2f(lt)) * 0.69314718055994531f;
     } else {
-      float* prow = p.part + ((((int64_t)ri * p.hq + head) * p.tq + t) * p.nsplit_stride + split) * (D + 4);
-      if (g == 0) { prow[D] = W.m[qb] == -INFINITY ? -INFINITY : m2; prow[D + 1] = lt; }
+      const int64_t idx = (int64_t)rq.pbase + ((int64_t)head * p.tq + t) * rq.nsplit + split;
+      float* prow = p.part_o + idx * D;
+      if (g == 0) p.part_ml[idx] = make_float2(W.m[qb] == -INFINITY ? -INFINITY : m2, lt);
 #pragma unroll
       for (int db = 0; db < XAttn<T, D>::DB; ++db)
         *reinterpret_cast<f32x4*>(prow + 16 * db + 4 * g) = W.o[db][qb];
@@ -721,20 +778,22 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void cache_attn_kerne
 
 // ------------------------------------------------------------ launchers
 template <typename T, int D>
-static hipError_t launch_extract_t(const ExtractParams& p, bool count, hipStream_t st) {
-  if (count) {
+static hipError_t launch_extract_t(const ExtractParams& p, int mode, hipStream_t st) {
+  if (mode == kExtractCount) {
     hipLaunchKernelGGL(mask_count_kernel, dim3(p.grid_wg), dim3(kThreads), 0, st, p);
+  } else if (mode == kExtractDump) {
+    hipLaunchKernelGGL(tile_dump_kernel, dim3(p.grid_wg), dim3(kThreads), 0, st, p);
   } else {
     hipLaunchKernelGGL((extract_attn_kernel<T, D>), dim3(p.grid_wg), dim3(kThreads), 0, st, p);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_extract_attn(const ExtractParams& p, int dtype, int head_dim, bool count, hipStream_t st) {
+hipError_t launch_extract_attn(const ExtractParams& p, int dtype, int head_dim, int mode, hipStream_t st) {
   if (dtype == C2KV_BF16) {
-    return head_dim == 128 ? launch_extract_t<bf16, 128>(p, count, st) : launch_extract_t<bf16, 64>(p, count, st);
+    return head_dim == 128 ? launch_extract_t<bf16, 128>(p, mode, st) : launch_extract_t<bf16, 64>(p, mode, st);
   }
-  return head_dim == 128 ? launch_extract_t<float, 128>(p, count, st) : launch_extract_t<float, 64>(p, count, st);
+  return head_dim == 128 ? launch_extract_t<float, 128>(p, mode, st) : launch_extract_t<float, 64>(p, mode, st);
 }
 
 template <typename T, int D>

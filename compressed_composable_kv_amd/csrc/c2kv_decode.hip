@@ -35,6 +35,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Wait for this wave's outstanding vector-memory operations (incl. LDS DMA).
 __device__ __forceinline__ void dec_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of them are outstanding (the counter retires in
+// issue order, so every older operation has completed).  gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at
+// their maxima.
+template <int N>
+__device__ __forceinline__ void dec_wait_vmem_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 typedef __attribute__((address_space(3))) void dec_lds_void;
 typedef short dec_s4 __attribute__((ext_vector_type(4)));
@@ -79,7 +88,11 @@ __device__ __forceinline__ void dma_v_tile(__amdgpu_buffer_rsrc_t rs, char* tile
 
 // K A-operand of one 32-key step through a buffer resource (rows past its
 // end read as zeros): lane (r16, g) takes, for each 16-key block kb, the 8
-// elements 32 ks + 8 g .. +7 of key key0 + 16 kb + r16.
+// elements 32 ks + 8 g .. +7 of key key0 + 16 kb + r16.  It issues
+// kDecKLoads<T, D> vector loads.
+template <typename T, int D>
+constexpr int kDecKLoads = 2 * (D / 32) * (sizeof(T) == 2 ? 1 : 2);
+
 template <typename T, int D>
 __device__ __forceinline__ void dec_load_k(typename ElemTraits<T>::v8 (&ka)[2][D / 32], __amdgpu_buffer_rsrc_t rs,
                                            int key0, int r16, int g) {
@@ -270,7 +283,6 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
     const int key0 = k0 + 32 * st;
     if (st != wave) {
       wave_lds_sync();   // previous step's V^T reads are done before the DMA refills the tile
-      dec_load_k<T, D>(ka, krs, key0, r16, g);
       dma_v_tile<NDMA>(vrs, vt, voff, key0 * RB);
     }
     const bool has_new = newk >= key0 && newk < key0 + 32;   // wave-uniform
@@ -307,6 +319,11 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
       s[0] = mma16(ka[0][ks], qB[ks], s[0]);
       s[1] = mma16(ka[1][ks], qB[ks], s[1]);
     }
+    // ---- the wave's next step's K, in flight during this step's softmax
+    // and P V (unconditional: past the resource it reads zeros, and the
+    // V wait below counts on these loads being the newest)
+    V8 kn[2][KS];
+    dec_load_k<T, D>(kn, krs, key0 + 32 * kWaves, r16, g);
     // ---- online softmax over the step (column = head, 8 keys per lane)
     float x[2][4];
     float mx = -INFINITY;
@@ -336,7 +353,7 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
     m = mnew;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    dec_wait_vmem();   // the V tile has landed in LDS
+    dec_wait_vmem_upto<kDecKLoads<T, D>>();   // the V tile has landed in LDS (only the K prefetch may be in flight)
     if (has_new) {
       // patch the new token's value row (zeros from the DMA) and append it
       const int row = newk - key0;
@@ -349,6 +366,10 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
     wave_lds_sync();
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = mma16(vt_operand<T, D>(vt, db, r16, g), pB, o[db]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[kb][ks] = kn[kb][ks];
   }
 
   // ---- combine the four waves (LDS reused), then write output or partial
@@ -385,24 +406,24 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
       orow[d] = from_f32<T>(acc / ls);
       if (d == 0 && p.lse) p.lse[(int64_t)r * p.hq + head] = (M + __log2f(ls)) * 0.69314718055994531f;
     } else {
-      float* prow = p.part + (((int64_t)ri * p.hq + head) * p.nsplit_stride + split) * (D + 4);
-      prow[d] = acc;
-      if (d == 0) { prow[D] = M; prow[D + 1] = ls; }
+      const int64_t idx = (int64_t)rq.pbase + (int64_t)head * rq.nsplit + split;
+      p.part_o[idx * D + d] = acc;
+      if (d == 0) p.part_ml[idx] = make_float2(M, ls);
     }
   }
 }
 
 // ---------------------------------------------------------------- merge
-// One workgroup per (output row, DIMS-wide slice): the split partials
-// [o(D) | m | l] of that row (request of the launch, head, token) are
-// combined by log-sum-exp.  DIMS / 4 threads cover the slice and the
-// workgroup's kThreads / (DIMS / 4) groups of them take the splits in turn.
-// The (m, l) pairs are staged in LDS with one load per split, the o slices
-// are loaded in batches of kMergeNB splits per thread with every load in
-// flight before the arithmetic.  Rows of requests with a single key chunk
-// already hold their output.  Decode merges many splits per row over few
-// rows and takes 32-dim slices (more workgroups per row); prefill merges
-// fewer splits over many rows and takes whole rows.
+// One workgroup per (output row, DIMS-wide slice): the split partials of
+// that row (request of the launch, head, token) are combined by
+// log-sum-exp.  The row's (m, l) pairs are contiguous and staged in LDS
+// with one 8-byte load per split; DIMS / 4 threads cover the slice and the
+// workgroup's kThreads / (DIMS / 4) groups of them take the splits in turn,
+// with batches of kMergeNB o slices per thread in flight before the
+// arithmetic.  Rows of requests with a single key chunk already hold their
+// output.  Decode merges many splits per row over few rows and takes 32-dim
+// slices (more workgroups per row); prefill merges fewer splits over many
+// rows and takes whole rows.
 constexpr int kMergeDimsDecode = 32;
 constexpr int kMergeNB = 4;
 
@@ -415,31 +436,30 @@ __device__ __forceinline__ float wave_max64(float x) {
 template <typename T, int D, int DIMS>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   constexpr int DQ = D / DIMS, TPS = DIMS / 4, SG = kThreads / TPS, NB = kMergeNB;
-  __shared__ float s_m[C2KV_MAX_SPLITS], s_l[C2KV_MAX_SPLITS];
+  __shared__ float2 s_ml[C2KV_MAX_SPLITS];
   __shared__ __attribute__((aligned(16))) float s_acc[SG][DIMS];
   __shared__ float s_ls[SG];
   const int row = blockIdx.x / DQ, dq = blockIdx.x % DQ;
   if (row >= p.num_rows) return;
   const int tid = threadIdx.x;
   const int ri = row / (p.hq * p.tq);
+  const int rem = row % (p.hq * p.tq);          // head * tq + t
   const int nsplit = p.nsplit[ri];
   if (nsplit <= 1) return;        // single-chunk requests were written directly
-  const float* base = p.part + (int64_t)row * p.nsplit_stride * (D + 4);
+  const int64_t idx0 = (int64_t)p.pbase[ri] + (int64_t)rem * nsplit;
+  const float* base = p.part_o + idx0 * D;
+  const float2* ml = p.part_ml + idx0;
   const int sg = tid / TPS, d4 = tid % TPS;
   const int col = dq * DIMS + 4 * d4;
-  for (int s = tid; s < nsplit; s += kThreads) {
-    const float* pr = base + (int64_t)s * (D + 4);
-    s_m[s] = pr[D];
-    s_l[s] = pr[D + 1];
-  }
+  for (int s = tid; s < nsplit; s += kThreads) s_ml[s] = ml[s];
   // first batch of o slices in flight while the maxima are reduced
   f32x4 os[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    os[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(sg + SG * i, nsplit - 1) * (D + 4) + col);
+    os[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(sg + SG * i, nsplit - 1) * D + col);
   __syncthreads();
   float M = -INFINITY;
-  for (int s = tid & 63; s < nsplit; s += 64) M = fmaxf(M, s_m[s]);
+  for (int s = tid & 63; s < nsplit; s += 64) M = fmaxf(M, s_ml[s].x);
   M = wave_max64(M);              // every wave holds the row maximum
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float ls = 0.f;
@@ -447,14 +467,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int s = s0 + SG * i;
-      const float w = (s < nsplit && s_m[s] != -INFINITY) ? __builtin_amdgcn_exp2f(s_m[s] - M) : 0.f;
+      const float2 sm = s_ml[min(s, nsplit - 1)];
+      const float w = (s < nsplit && sm.x != -INFINITY) ? __builtin_amdgcn_exp2f(sm.x - M) : 0.f;
       acc += os[i] * w;
-      if (s < nsplit) ls += s_l[s] * w;
+      if (s < nsplit) ls += sm.y * w;
     }
     if (s0 + SG * NB >= nsplit) break;
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-      os[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(s0 + SG * (NB + i), nsplit - 1) * (D + 4) + col);
+      os[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(s0 + SG * (NB + i), nsplit - 1) * D + col);
   }
   *reinterpret_cast<f32x4*>(&s_acc[sg][4 * d4]) = acc;
   if (d4 == 0) s_ls[sg] = ls;
@@ -463,7 +484,6 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     float a = 0.f, lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < SG; ++j) { a += s_acc[j][tid]; lsum += s_ls[j]; }
-    const int rem = row % (p.hq * p.tq);
     const int head = rem / p.tq, t = rem % p.tq;
     const int r = p.req0 + ri;
     T* orow = reinterpret_cast<T*>(p.o) + (((int64_t)r * p.tq + t) * p.hq + head) * D;

@@ -22,6 +22,7 @@ constexpr int kQW = 32;        // query rows per wave (two 16-row MFMA blocks)
 constexpr int kWaves = 4;      // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxHalfDim = 64;
+static_assert(kBN == C2KV_EXTRACT_TILE_KEYS && kQW == C2KV_EXTRACT_UNIT_ROWS, "tile shape is part of the ABI");
 
 template <typename T> struct ElemTraits;
 template <> struct ElemTraits<bf16> {
@@ -124,12 +125,15 @@ struct ExtractParams {
   void* o;              // [rows][hq][D]
   float* lse;           // [hq][rows] or null
   const float2* rope;   // [max_n][D/2] (cos, sin)
-  uint64_t* counts;     // mask-count mode: 5 counters
+  uint64_t* counts;     // mask-count mode: 5 counters; tile-dump mode: [0] entries found
+  c2kv_tile_entry* entries;  // tile-dump mode: output table
+  int64_t entry_cap;    // tile-dump mode: entries that fit
   int64_t total_rows;
   int32_t num_docs, hq, hkv, G, ratio_k, sink_len;
   int32_t total_wg, grid_wg;
   float scale_log2;
   int32_t anchor;       // 1: the anchor-token ablation's mask (documents <-> slots both ways)
+  int32_t doc_base;     // index of docs[0] in the caller's document list
   ExtractDoc docs[C2KV_MAX_BATCH];
 };
 
@@ -137,22 +141,25 @@ struct CacheReq {
   int32_t wg0;       // first logical workgroup of the request
   int32_t cache_len; // rows before the appended question
   int32_t nsplit;    // key chunks
-  int32_t pad;
+  int32_t pbase;     // first split partial of the request (when nsplit > 1)
 };
 
-// Split partial rows are laid out [request of launch][head][token][split]
-// with (D + 4) floats each: o (unnormalised, D), running max m (log2
-// domain), sum l, two pad words.
+// Split partials of a launch are compact: request ri's partial of (head,
+// token t, split) has index pbase[ri] + (head * tq + t) * nsplit[ri] + split,
+// with its unnormalised o in part_o[index][D] and its (running max m in the
+// log2 domain, sum l) in part_ml[index], so the (m, l) pairs of one output
+// row are contiguous.
 struct CacheParams {
   const void* qrot;     // [R][tq][hq][D] rotated queries (workspace)
   const void* kc;       // [R][hkv][cap][D]
   const void* vc;
   void* o;              // [R][tq][hq][D]
   float* lse;           // [R][hq][tq] or null
-  float* part;          // split partials
+  float* part_o;        // split partials: o
+  float2* part_ml;      // split partials: (m, l)
   int64_t cap;
   int32_t req0;         // first request of this launch (global index)
-  int32_t num_reqs, tq, hq, hkv, G, nblk_q, nug, chunk, nsplit_stride;
+  int32_t num_reqs, tq, hq, hkv, G, nblk_q, nug, chunk;
   int32_t total_wg, grid_wg;
   float scale_log2;
   CacheReq reqs[C2KV_MAX_BATCH];
@@ -164,6 +171,7 @@ struct DecodeReq {
   int32_t pos;       // position of the new token
   int32_t nsplit;    // key pieces of the request
   int32_t chunk;     // keys per piece (a multiple of 32)
+  int32_t pbase;     // first split partial of the request (when nsplit > 1)
 };
 
 struct DecodeParams {
@@ -174,20 +182,23 @@ struct DecodeParams {
   void* vc;
   void* o;              // [R][hq][D]
   float* lse;           // [R][hq] or null
-  float* part;          // split partials (see CacheParams)
+  float* part_o;        // split partials (see CacheParams)
+  float2* part_ml;
   int64_t cap;
-  int32_t req0, num_reqs, hq, hkv, G, nsplit_stride, total_wg;
+  int32_t req0, num_reqs, hq, hkv, G, total_wg;
   float scale_log2;
   RopeFreqs freqs;
   DecodeReq reqs[C2KV_MAX_BATCH];
 };
 
 struct MergeParams {
-  const float* part;
+  const float* part_o;
+  const float2* part_ml;
   void* o;              // [R][tq][hq][D]
   float* lse;           // [R][hq][tq] or null
-  int32_t req0, num_rows, hq, tq, nsplit_stride, pad;
+  int32_t req0, num_rows, hq, tq;
   int32_t nsplit[C2KV_MAX_BATCH];
+  int32_t pbase[C2KV_MAX_BATCH];
 };
 
 }  // namespace c2kv

@@ -123,7 +123,8 @@ struct SlotFillParams {
 
 hipError_t launch_rope_table(float2* table, int npos, int head_dim, const RopeFreqs& f, hipStream_t st);
 hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipStream_t st);
-hipError_t launch_extract_attn(const ExtractParams& p, int dtype, int head_dim, bool count, hipStream_t st);
+constexpr int kExtractAttn = 0, kExtractCount = 1, kExtractDump = 2;   // launch_extract_attn modes
+hipError_t launch_extract_attn(const ExtractParams& p, int dtype, int head_dim, int mode, hipStream_t st);
 hipError_t launch_cache_attn(const CacheParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_decode_attn(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t st);

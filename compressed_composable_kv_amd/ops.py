@@ -385,3 +385,31 @@ def mask_cells(doc_lens: Sequence[int], ratio_k: int, sink_len: Optional[int] = 
     check(lib.c2kv_mask_cells_ex(_arr_i32(doc_lens), len(doc_lens), ratio_k, sink_len,
                                  _lib.EXTRACT_ANCHOR if anchor else 0, out, _ptr(ws), ws.numel(), _stream(dev)))
     return tuple(int(x) for x in out)
+
+
+TILE_FIELDS = tuple(f for f, _ in _lib.TileEntry._fields_)
+
+
+def tile_schedule(doc_lens: Sequence[int], ratio_k: int, sink_len: Optional[int] = None, hq: int = 1,
+                  hkv: int = 1, anchor: bool = False, device: Optional[torch.device] = None) -> torch.Tensor:
+    """The extraction kernel's tile schedule (c2kv_tile_schedule): one row
+    per (unit, key tile) pair it computes, columns TILE_FIELDS (doc, kv_head,
+    q_head, q_slot, q0, q1, k_slot, key0, nkeys, masked), as an int32 CPU
+    tensor in unspecified order."""
+    lib = load()
+    dev = device or torch.device("cuda", torch.cuda.current_device())
+    if sink_len is None:
+        sink_len = ratio_k
+    ws = WORKSPACES.get("tiles", lib.c2kv_workspace_size_tile_schedule(), dev, zero=False)
+    lens = _arr_i32(doc_lens)
+    flags = _lib.EXTRACT_ANCHOR if anchor else 0
+    count = ctypes.c_int64()
+    check(lib.c2kv_tile_schedule(lens, len(doc_lens), ratio_k, sink_len, hq, hkv, flags, None, 0,
+                                 ctypes.byref(count), _ptr(ws), ws.numel(), _stream(dev)))
+    n = count.value
+    nf = len(TILE_FIELDS)
+    buf = torch.empty((max(1, n), nf), dtype=torch.int32, device=dev)
+    check(lib.c2kv_tile_schedule(lens, len(doc_lens), ratio_k, sink_len, hq, hkv, flags, _ptr(buf), n,
+                                 ctypes.byref(count), _ptr(ws), ws.numel(), _stream(dev)))
+    _need(count.value == n, "tile schedule changed between calls")
+    return buf[:n].cpu()

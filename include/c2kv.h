@@ -351,7 +351,7 @@ size_t c2kv_workspace_size_prefill(const int32_t* cache_len, int32_t num_reqs, i
  * and value are written to row cache_len[r] + t.  Token t attends to every
  * row < cache_len[r] and to question rows <= t.  GQA as for extraction.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, CAPACITY (cache_len + tq > cap,
- * or (cap + 128) rows of one KV head reach 2 GiB), HIP. */
+ * or (cap + 256) rows of one KV head reach 2 GiB), HIP. */
 c2kv_status c2kv_attn_prefill(const void* q, const void* k_new, const void* v_new,
                               void* cache_k, void* cache_v, int64_t cap,
                               const int32_t* cache_len, const int32_t* q_pos0,
@@ -407,6 +407,47 @@ c2kv_status c2kv_mask_cells(const int32_t* doc_lens, int32_t num_docs, int32_t r
 c2kv_status c2kv_mask_cells_ex(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k,
                                int32_t sink_len, uint32_t flags, uint64_t* counts_out,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Tile schedule of c2kv_extract_attn_ex, dumped for coverage tests.  The
+ * extraction kernel gives each wave a unit of C2KV_EXTRACT_UNIT_ROWS query
+ * rows of one query head (document rows or slot rows of one document) and
+ * walks key tiles of C2KV_EXTRACT_TILE_KEYS keys; tiles in which no cell is
+ * visible under the mask are never enumerated, and the visibility predicate
+ * is applied only on tiles the entry marks `masked`.  [Explainer]
+ * "structured information flow" section, its mask figure and three rules
+ * (document rows causal and blind to slots; slot j sees the sink block and
+ * its own block; slots causal among themselves).  One entry per (unit, key
+ * tile) pair the kernel computes, exactly as the attention launch with the
+ * same arguments enumerates them. */
+#define C2KV_EXTRACT_TILE_KEYS 64
+#define C2KV_EXTRACT_UNIT_ROWS 32
+typedef struct c2kv_tile_entry {
+  int32_t doc;       /* document index into doc_lens */
+  int32_t kv_head;   /* KV head of the key tile */
+  int32_t q_head;    /* query head of the unit */
+  int32_t q_slot;    /* 1: the unit's query rows are slots, 0: document tokens */
+  int32_t q0, q1;    /* query rows [q0, q1) of the unit, counted within its region */
+  int32_t k_slot;    /* 1: the tile's keys are slots, 0: document tokens */
+  int32_t key0;      /* first key of the tile, counted within its region */
+  int32_t nkeys;     /* keys of the tile inside the region (<= C2KV_EXTRACT_TILE_KEYS) */
+  int32_t masked;    /* 1: some cell of the tile is hidden from some row of the unit
+                        (the kernel applies the predicate); 0: every cell is visible */
+} c2kv_tile_entry;
+
+size_t c2kv_workspace_size_tile_schedule(void);
+/* Enumerate the tile schedule for doc_lens[num_docs] at ratio k, sink
+ * length, hq query heads over hkv KV heads and extraction flags (0 or
+ * C2KV_EXTRACT_ANCHOR).
+ *   entries    device [capacity] c2kv_tile_entry, or NULL with capacity 0
+ *              to count only; entry order is unspecified
+ *   count_out  host: number of entries of the schedule
+ * Synchronises `stream`.  Errors: INVALID_ARG, UNSUPPORTED (hq/hkv > 16),
+ * WORKSPACE, CAPACITY (count_out > capacity: the first `capacity` entries
+ * written are an arbitrary subset), HIP. */
+c2kv_status c2kv_tile_schedule(const int32_t* doc_lens, int32_t num_docs, int32_t ratio_k, int32_t sink_len,
+                               int32_t hq, int32_t hkv, uint32_t flags, c2kv_tile_entry* entries,
+                               int64_t capacity, int64_t* count_out, void* workspace, size_t ws_bytes,
+                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -251,6 +251,99 @@ def test_longctx_decode_full(c2kv, ndocs):
     _free()
 
 
+# ------------------------------------- full-cache comparator (uncompressed)
+
+@pytest.mark.parametrize("ndocs", [16, 32], ids=lambda n: f"{4 * n}k")
+def test_full_cache_decode_full(c2kv, ndocs):
+    """The uncompressed comparator of the long-context sweep at 64k and 128k
+    rows per request: 64 requests of the Llama shapes in one launch (the
+    benchmark's launch shape), two steps; the first and last request
+    checked against the oracle."""
+    w = W.LONGCTX
+    d, hq, hkv, theta, dt = w.head_dim, w.hq, w.hkv, w.rope_theta, w.dtype
+    R, S = w.num_reqs, 2
+    L = 4096 * ndocs
+    cap = L + S
+    print(f"full cache {L}: {R} requests x {L} rows", flush=True)
+    ck = W.device_normal((R, hkv, cap, d), dt, w.wid, W.P_K, DEV, salt=500 + ndocs)
+    cv = W.device_normal((R, hkv, cap, d), dt, w.wid, W.P_V, DEV, salt=500 + ndocs)
+    checked = (0, R - 1)
+    ref_in = {r: (ck[r, :, :L].transpose(0, 1).float().cpu().numpy(), cv[r, :, :L].transpose(0, 1).float().cpu().numpy())
+              for r in checked}
+    qs = W.normal((S, R, hq, d), dt, w.wid, W.P_DEC_Q, salt=500 + ndocs)
+    ks = W.normal((S, R, hkv, d), dt, w.wid, W.P_NEW_KV, salt=500 + ndocs)
+    vs = W.normal((S, R, hkv, d), dt, w.wid, W.P_NEW_KV, salt=600 + ndocs)
+    outs = []
+    for s_ in range(S):
+        o_s, l_s = c2kv.attn_decode(qs[s_].to(DEV), ks[s_].to(DEV), vs[s_].to(DEV), ck, cv, [L + s_] * R,
+                                    [L + s_] * R, theta, return_lse=True)
+        outs.append((np32(o_s), np32(l_s)))
+    torch.cuda.synchronize()
+    for r in checked:
+        rk, rv = ref_in[r]
+        ro, rl, _, _ = O.append_and_attend(qs[:, r].float().numpy(), ks[:, r].float().numpy(), vs[:, r].float().numpy(),
+                                           rk, rv, L, theta, "bf16")
+        for s_ in range(S):
+            assert_close(outs[s_][0][r], ro[s_], "bf16", f"full {L}: request {r} step {s_}")
+            assert_lse_close(outs[s_][1][r], rl[:, s_], "bf16", f"full {L}: request {r} step {s_}")
+    del ck, cv
+    _free()
+
+
+def test_full_cache_reuse_llama_k1_compose_then_decode(c2kv):
+    """Full-cache reuse: the 8 Llama documents' whole pre-RoPE K/V (4096
+    tokens each) composed at k = 1 in the seeded order (every token a slot,
+    realigned at the cumulative original lengths: 32768 rows), then a
+    64-token question prefill and two decode steps over it, against the
+    oracle's compose, prefill and decode."""
+    w = W.LLAMA
+    d, hq, hkv, theta, dt = w.head_dim, w.hq, w.hkv, w.rope_theta, w.dtype
+    order = W.llama_doc_order(w)
+    pool_k = [W.normal((4096, hkv, d), dt, w.wid, W.P_K, salt=700 + i) for i in range(8)]
+    pool_v = [W.normal((4096, hkv, d), dt, w.wid, W.P_V, salt=700 + i) for i in range(8)]
+    M, tq, S = 8 * 4096, 8, 2
+    cap = M + tq + S
+    ck = torch.zeros((1, hkv, cap, d), dtype=dt, device=DEV)
+    cv = torch.zeros_like(ck)
+    dk = [x.to(DEV) for x in pool_k]
+    dv = [x.to(DEV) for x in pool_v]
+    lens, nxt = c2kv.compose([[(dk[t], dv[t], 4096) for t in order]], 1, theta, ck, cv)
+    assert lens == [M] and nxt == [M]
+    qp = W.normal((1, tq, hq, d), dt, w.wid, W.P_PREFILL, salt=700)
+    kp = W.normal((1, tq, hkv, d), dt, w.wid, W.P_NEW_KV, salt=700)
+    vp = W.normal((1, tq, hkv, d), dt, w.wid, W.P_NEW_KV, salt=701)
+    op, lp = c2kv.attn_prefill(qp.to(DEV), kp.to(DEV), vp.to(DEV), ck, cv, [M], [M], theta, return_lse=True)
+    qd = W.normal((S, 1, hq, d), dt, w.wid, W.P_DEC_Q, salt=700)
+    kd = W.normal((S, 1, hkv, d), dt, w.wid, W.P_NEW_KV, salt=702)
+    vd = W.normal((S, 1, hkv, d), dt, w.wid, W.P_NEW_KV, salt=703)
+    dec = []
+    for s_ in range(S):
+        o_s, l_s = c2kv.attn_decode(qd[s_].to(DEV), kd[s_].to(DEV), vd[s_].to(DEV), ck, cv, [M + tq + s_],
+                                    [M + tq + s_], theta, return_lse=True)
+        dec.append((np32(o_s)[0], np32(l_s)[0]))
+    torch.cuda.synchronize()
+    rk, rv, rpos, rnext = O.compose([pool_k[t].float().numpy() for t in order], [pool_v[t].float().numpy() for t in order],
+                                    [4096] * 8, 1, theta, "bf16")
+    assert rnext == M and np.array_equal(rpos, np.arange(M))
+    gk = np32(ck[0, :, :M]).transpose(1, 0, 2)
+    pre = np.concatenate([pool_k[t].float().numpy() for t in order])
+    assert_rotated_close(gk, rk, pre, "bf16", "k=1 composed keys")
+    # the oracle continues from its own composed cache
+    ro, rl, _, _ = O.append_and_attend(qp[0].float().numpy(), kp[0].float().numpy(), vp[0].float().numpy(),
+                                       rk, rv, M, theta, "bf16")
+    assert_close(np32(op)[0], ro, "bf16", "k=1 prefill")
+    assert_lse_close(np32(lp)[0], rl, "bf16", "k=1 prefill")
+    qs = np.concatenate([qp[0].float().numpy(), qd[:, 0].float().numpy()])
+    ks_ = np.concatenate([kp[0].float().numpy(), kd[:, 0].float().numpy()])
+    vs_ = np.concatenate([vp[0].float().numpy(), vd[:, 0].float().numpy()])
+    ro2, rl2, _, _ = O.append_and_attend(qs, ks_, vs_, rk, rv, M, theta, "bf16")
+    for s_ in range(S):
+        assert_close(dec[s_][0], ro2[tq + s_], "bf16", f"k=1 decode step {s_}")
+        assert_lse_close(dec[s_][1], rl2[:, tq + s_], "bf16", f"k=1 decode step {s_}")
+    del ck, cv, dk, dv
+    _free()
+
+
 # ------------------------------------------------- Qwen3-14B extraction
 
 @pytest.mark.parametrize("ratio_k", [4, 8, 16])

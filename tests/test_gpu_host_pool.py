@@ -30,6 +30,10 @@ def c2kv():
     return m
 
 
+def dtname(dt):
+    return "bf16" if dt == torch.bfloat16 else "f32"
+
+
 def pinned(t: torch.Tensor) -> torch.Tensor:
     p = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
     p.copy_(t)
@@ -203,6 +207,17 @@ def _staged_vs_device(c2kv, reqs_docs, pool_k, pool_v, pool_n, ratio_k, theta, d
     (sk, sv, sp, sr), (dk, dv, dp, dr) = outs
     assert sr == dr and sr[0] == Ms
     assert torch.equal(sk, dk) and torch.equal(sv, dv) and torch.equal(sp, dp)
+    # and the staged result against the oracle's composition
+    for r, docs in enumerate(reqs_docs):
+        base = pos_base[r] if pos_base else 0
+        rk, rv, rpos, rnext = O.compose([pool_k[t].float().numpy() for t in docs],
+                                        [pool_v[t].float().numpy() for t in docs],
+                                        [pool_n[t] for t in docs], ratio_k, theta, dtname(dt), base)
+        assert sr[1][r] == rnext
+        assert np.array_equal(sp[r, :Ms[r]].cpu().numpy(), rpos)
+        assert torch.equal(sv[r, :, :Ms[r]].transpose(0, 1).cpu(), torch.cat([pool_v[t] for t in docs]))
+        pre = np.concatenate([pool_k[t].float().numpy() for t in docs])
+        assert_rotated_close(np32(sk[r, :, :Ms[r]]).transpose(1, 0, 2), rk, pre, dtname(dt), f"staged request {r}")
     return sk, sv
 
 
