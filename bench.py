@@ -1,54 +1,50 @@
 #!/usr/bin/env python3
 """Benchmark of the C2KV hot path on one MI355X.
 
-One step = one pass of the whole hot path over the Llama3.1-8B-shaped
-single-layer workload (bf16, 32 query / 8 KV heads, head_dim 128, RoPE theta
-5e5): structured-flow extraction attention of 8 documents x 4096 tokens at
-k = 4 (1024 slots each, sink = first 4 tokens), composition of their slot
-caches in a seeded order into an 8192-slot cache covering 32768 original
-positions, a 64-token question prefill, and 256 decode steps with random
-query vectors (batch 1).  Inputs are synthetic N(0, 1) tensors resident in
-HBM before timing starts.
+Metric: C2KV decode-attention KV read rate (GB/s of algorithmic bytes, and
+its fraction of the 8 TB/s HBM peak) together with the extraction's
+masked-attention rate (TFLOP/s of visible cells, and its fraction of the
+2.5 PFLOP/s dense bf16 MFMA peak).  Each part is measured on the largest
+workload of its kind that fits one GPU:
 
-The metric is the decode attention's KV read rate (GB/s, algorithmic bytes)
-together with the extraction's masked-attention TFLOP/s (visible cells only).
-The 256 decode launches of a step are replayed from one HIP graph.
+  headline (value, roofline)  long-context decode, Llama3.1-8B shapes (32/8
+      heads, d 128, bf16, theta 5e5), all 32 layers attention-only, 64
+      requests, composed context of 32 documents of 4096 tokens at k = 4:
+      32 768 composed slots covering 131 072 original tokens.  One step is
+      one decode call per layer (32 calls, each appending a row and reading
+      every cache row of the 64 requests).  The 32 layer caches cycle over a
+      pool of distinct layer buffers, each far above the 256 MB last-level
+      cache; the K timed steps are replayed from one HIP graph.
+  extraction_roofline  Qwen3-14B-shaped extraction (40/8 heads, d 128,
+      theta 1e6): 64 documents of 8192 tokens at k = 4, 40 attention-only
+      layers over two buffer sets.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+Reported alongside, in the same JSON line:
+  longctx_sweep   decode at 16k/32k/64k/128k original tokens (4096..32768
+                  slots), C2KV and the uncompressed full-cache comparator
+  extraction      Qwen3-14B extraction at k = 4, 8 and 16
+  qwen25          the Qwen2.5-7B pool (64 documents, k = 16, lengths
+                  uniform on 1024..8192): decode of 32 requests composed
+                  from 8..32 documents each, and their composition (minimum
+                  traffic basis), both over replicas well above the
+                  last-level cache
+  llama_layer     the Llama3.1-8B single layer pass: extraction of 8 x 4096
+                  tokens, composition into 8192 slots, 64-token prefill and
+                  256 decode steps (batch 1), decode over cache replicas
+  host_pool_load, extractor_layer  (unless --no-extras)
+  achievable      rates this GPU sustains, measured live: dense bf16 MFMA
+                  (probe), a streaming HBM read (probe), a device copy
+  cpu_baseline    the oracle on a bounded sample, timed on the host cores
 
-Prints one JSON line.  Besides the step, it summarises the host-pool load
-(--host-pool) and the extractor layer (--layer) unless --no-extras, reports the decode rate with the
-256 steps spread over 16 replicas of the cache (a working set of about
-0.6 GB, above the 256 MB last-level cache) and the compose rate with
-its inputs and caches spread over 16 replicas (about 3 GB), and, when a counter summary
-for the current decode sources is committed under profiles/, the HBM
-traffic the hardware counters measured for one decode call.  It also
-measures, live, the rates this GPU sustains (dense bf16 MFMA from the probe
-library, HBM from a 1 GiB device copy) and reports each kernel against them
-as well as against the published peaks, and times compose from a graph of
-20 back-to-back calls.
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 
-Decode sweep over the other decode workloads (one JSON line each, not the
-step): the Qwen2.5-7B pool (32 requests composed from 64 ragged documents
-at k = 16) and the long-context sweep (64 requests at 16k..128k original
-tokens at k = 4, with the uncompressed cache of the same original length as
-the comparator), each a graph of decode calls over caches well above the
-last-level cache:
-    python bench.py --decode-sweep
-Extraction at the Qwen3-14B shapes (k = 4, 8, 16; 40 layers over two buffer
-sets) and compose of the Qwen2.5-7B pool, one JSON line each:
-    python bench.py --extract-sweep
-    python bench.py --compose-sweep
-Loading stored caches from pinned host memory (32 layers of the Llama
-shapes): compose reading the slot caches in place across the host link,
-against copying the full caches, one JSON line:
-    python bench.py --host-pool
-One extractor layer (norms, frozen / C2 projections, attention, FFN) at the
-Llama3.1-8B shapes over the 8 x 4096-token batch, one JSON line:
-    python bench.py --layer
+Inputs are synthetic N(0, 1) tensors resident in HBM before timing starts.
 
-One phase alone, for counter runs under rocprofv3:
-    python bench.py --profile-phase extract --calls 2
+Sections on their own (one JSON line each), e.g. for profiler runs:
+    python bench.py --only headline|longctx|extract|qwen25|llama
+One phase of a workload alone, for counter runs under rocprofv3:
+    python bench.py --profile-phase decode128k|compose_qwen25|extract_qwen3|extract|compose|prefill|decode
+Older single-purpose modes: --decode-sweep, --extract-sweep, --compose-sweep, --host-pool, --layer.
 
 Profiling helpers (no GPU work):
     python bench.py --summarize DIR [DIR2] --out FILE --cmd "COMMAND"
@@ -71,15 +67,20 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PCIE_PEAK_GBS = 64.0           # MI355X host link, PCIe 5.0 x16, one direction, GB/s
 
 # sources that define the decode call's kernels and launch shapes; a counter
 # summary applies to the build whose sources hash to the recorded value
 DECODE_SOURCES = ("compressed_composable_kv_amd/csrc/c2kv_decode.hip",
                   "compressed_composable_kv_amd/csrc/c2kv_device.hpp",
-                  "compressed_composable_kv_amd/csrc/c2kv_launch.hpp",
-                  "compressed_composable_kv_amd/csrc/c2kv_abi.cpp")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_decode_llama31_8b_1layer.txt")
+                  "compressed_composable_kv_amd/csrc/c2kv_cache.cpp")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_decode_llama31_8b_longctx_128k.txt")
 CALIB_KERNEL = "neg_kernel"    # torch.neg over int32: reads and writes N MiB
+POOL_BYTES = 96 << 30          # device memory given to a pool of layer buffers
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
 
 
 def sources_sha(paths=DECODE_SOURCES) -> str:
@@ -169,16 +170,16 @@ def summarize(dirs, out, cmd, calib_mib):
     print("\n".join(lines))
 
 
-def committed_traffic(kernel_keys):
-    """HBM bytes per decode call from the committed counter summary, or
-    None when there is none or the decode sources changed since."""
+def committed_traffic(kernel_keys, path=PMC_SUMMARY, sources=DECODE_SOURCES):
+    """HBM bytes per call from a committed counter summary, or None when
+    there is none or the sources changed since it was taken."""
     try:
-        with open(PMC_SUMMARY) as f:
+        with open(path) as f:
             js = [l for l in f if l.startswith("# json: ")]
         info = json.loads(js[-1][len("# json: "):])
     except (OSError, IndexError, ValueError):
         return None
-    if info.get("sources_sha") != sources_sha():
+    if info.get("sources_sha") != sources_sha(sources):
         return None
     tot = 0.0
     for key in kernel_keys:
@@ -197,6 +198,12 @@ def visible_cells(n: int, k: int) -> int:
     return n * (n + 1) // 2 + sd + m * (m + 1) // 2
 
 
+def decode_call_bytes(lens, hq, hkv, d, es=2):
+    """Algorithmic bytes of one decode call: every cache row (the new one
+    included) of K and V read once, plus q, o, k_new and v_new."""
+    return sum((L + 1) * hkv * d * es * 2 for L in lens) + len(lens) * (2 * hq + 2 * hkv) * d * es
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,7 +211,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the host-pool load and extractor-layer summaries")
-    ap.add_argument("--cpu-decode-steps", type=int, default=24)
+    ap.add_argument("--only", choices=("headline", "longctx", "extract", "qwen25", "llama"))
     ap.add_argument("--cold-replicas", type=int, default=16)
     ap.add_argument("--calibration-copy-mib", type=int, default=0)
     ap.add_argument("--summarize", nargs="+", metavar="DIR")
@@ -213,18 +220,536 @@ def parse():
     ap.add_argument("--compose-sweep", action="store_true")
     ap.add_argument("--host-pool", action="store_true")
     ap.add_argument("--layer", action="store_true")
-    ap.add_argument("--profile-phase", choices=("extract", "compose", "prefill", "decode"),
-                    help="run only this phase of the step --calls times (for counter runs), print nothing else")
+    ap.add_argument("--profile-phase", choices=("decode128k", "compose_qwen25", "extract_qwen3",
+                                                "extract", "compose", "prefill", "decode"),
+                    help="run only this phase (for rocprofv3 counter runs)")
     ap.add_argument("--calls", type=int, default=2)
     ap.add_argument("--out")
     ap.add_argument("--cmd", default="")
     return ap.parse_args()
 
 
-def cpu_baseline(w, M, P, tq, nsteps):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    `nsteps` decode steps over the full composed cache (M slots + question),
-    and the extraction of one document (all 32 heads)."""
+# ------------------------------------------------------------ timing helpers
+
+def _torch():
+    import torch
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    return torch, dev
+
+
+def fill_normal(torch, shape, dtype, seed, dev):
+    """Bulk N(0, 1) device tensor drawn directly in its dtype (timing
+    inputs: values do not change the work)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return torch.empty(tuple(int(s) for s in shape), dtype=dtype, device=dev).normal_(generator=g)
+
+
+def capture(torch, fn):
+    """fn run once eagerly on a side stream, then captured in a HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(torch, g, reps=1):
+    """Milliseconds per replay of g (HIP events around `reps` back-to-back
+    replays on the stream they run on), after one untimed replay."""
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def free(torch):
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def achievable_peaks(torch, dev):
+    """Rates this GPU sustains, measured live: dense bf16 MFMA from the probe
+    library (independent MFMA chains on register operands), a streaming read
+    of 4 GiB (probe library: read bytes per second, the ceiling for
+    read-dominated kernels such as decode), and a 1 GiB device copy (read +
+    write bytes per second).  They sit below the published peaks because the
+    chip holds a lower clock under sustained load than its nominal 2.4 GHz,
+    and HBM never delivers its full pin rate."""
+    import ctypes
+    from compressed_composable_kv_amd import build_lib
+    mfma = read = None
+    read_blocks = None
+    if os.path.exists(build_lib.PROBE_LIB):
+        lib = ctypes.CDLL(build_lib.PROBE_LIB)
+        lib.c2kv_probe_mfma_bf16.restype = ctypes.c_double
+        lib.c2kv_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+        ms = ctypes.c_float()
+        rates = [lib.c2kv_probe_mfma_bf16(512, 512, 4000, ctypes.byref(ms)) for _ in range(3)]
+        mfma = max(rates) if max(rates) > 0 else None
+        lib.c2kv_probe_hbm_read.restype = ctypes.c_double
+        lib.c2kv_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
+                                            ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+        buf = torch.ones(4 << 30, dtype=torch.uint8, device=dev)
+        out = torch.empty(4 * 256 * 8192, dtype=torch.uint8, device=dev)
+        for blocks in (2048, 4096, 8192):
+            r = lib.c2kv_probe_hbm_read(buf.data_ptr(), buf.numel(), out.data_ptr(), out.numel(), blocks, 5,
+                                        ctypes.byref(ms))
+            if r > 0 and (read is None or r > read):
+                read, read_blocks = r, blocks
+        del buf, out
+    n = 1 << 29                                   # 1 GiB of bf16
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        best = t if best is None else min(best, t)
+    del src, dst
+    free(torch)
+    return {"mfma_bf16_tflops": mfma, "hbm_read_gbs": read, "hbm_copy_gbs": 2 * 2 * n / (best * 1e-3) / 1e9,
+            "how": "MFMA: probe/mfma_peak.hip, 512 workgroups x 8 waves, 16 independent chains per wave; "
+                   f"HBM read: probe/hbm_read.hip streaming 4 GiB ({read_blocks} workgroups), best of 5; "
+                   "copy: torch copy of 1 GiB, read + write bytes, best of 3"}
+
+
+def _frac(x, peak):
+    return x / peak if (x is not None and peak) else None
+
+
+# ------------------------------------------- long-context decode (32 layers)
+
+def longctx_decode(torch, dev, ndocs, full, steps, warmup, pool_bytes=POOL_BYTES, emit=False):
+    """Decode over the long-context workload: 64 requests of the Llama
+    shapes, all 32 layers, composed context of `ndocs` documents of 4096
+    tokens at k = 4 (C2KV: ndocs * 1024 slots per request) or the
+    uncompressed cache of the same original length (full = True).  The 32
+    layer calls of a step go to a pool of P distinct layer buffers (layer l
+    uses buffer l mod P; P from the memory budget, at most 32), each layer
+    buffer far above the last-level cache.  `warmup` eager steps, then
+    `steps` steps captured in one HIP graph, replayed once untimed and once
+    timed (HIP events around the replay).  Layers that share a buffer append
+    to the same row of it, which changes no amount of work."""
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+    w = W.LONGCTX
+    d, hq, hkv, theta, dt = w.head_dim, w.hq, w.hkv, w.rope_theta, w.dtype
+    R, layers = w.num_reqs, w.layers
+    L_orig = 4096 * ndocs
+    M = L_orig if full else ndocs * c2kv.num_slots(4096, w.ratio_k)
+    cap = M + warmup + steps + 8
+    layer_bytes = 2 * R * hkv * cap * d * 2
+    P = int(max(2, min(layers, pool_bytes // layer_bytes)))
+    t0 = time.time()
+    bufs = [(fill_normal(torch, (R, hkv, cap, d), dt, 4_000_000 + 10 * i, dev),
+             fill_normal(torch, (R, hkv, cap, d), dt, 4_000_001 + 10 * i, dev)) for i in range(P)]
+    qd = fill_normal(torch, (layers, R, hq, d), dt, 4_100_000 + ndocs, dev)
+    kd = fill_normal(torch, (layers, R, hkv, d), dt, 4_100_001 + ndocs, dev)
+    vd = fill_normal(torch, (layers, R, hkv, d), dt, 4_100_002 + ndocs, dev)
+    ws = torch.empty(max(c2kv.workspace_size_decode([M + s] * R, hq, hkv, d, dt) for s in range(warmup + steps + 1)),
+                     dtype=torch.uint8, device=dev)
+    free(torch)
+    log(f"longctx {L_orig // 1024}k {'full' if full else 'c2kv'}: {P} layer buffers of {layer_bytes / 1e9:.2f} GB "
+        f"ready ({time.time() - t0:.1f} s)")
+
+    def step(s):
+        for layer in range(layers):
+            ck, cv = bufs[layer % P]
+            c2kv.attn_decode(qd[layer], kd[layer], vd[layer], ck, cv, [M + s] * R, [L_orig + s] * R, theta,
+                             workspace=ws)
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    g = capture(torch, lambda: [step(warmup + s) for s in range(steps)])
+    ms = time_replays(torch, g, 1)
+    nbytes = sum(decode_call_bytes([M + warmup + s] * R, hq, hkv, d) for s in range(steps)) * layers
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": f"llama31_8b_longctx_{L_orig // 1024}k_{'full' if full else 'c2kv'}",
+           "cache": "uncompressed comparator" if full else "composed, k=4",
+           "original_tokens": L_orig, "rows_per_request": M, "requests": R, "layers": layers,
+           "layer_buffers": P, "layer_buffer_gb": layer_bytes / 1e9, "steps": steps, "warmup": warmup,
+           "ms_per_step": ms / steps, "ms_per_call": ms / (steps * layers),
+           "bytes_per_step": nbytes / steps, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    del g, bufs, qd, kd, vd, ws
+    free(torch)
+    if emit:
+        print(json.dumps(res), flush=True)
+    return res
+
+
+def longctx_sweep(torch, dev, headline=None, emit=False):
+    """C2KV and full-cache decode at 16k..128k original tokens (32 layers,
+    64 requests); the 128k C2KV entry is the headline's own run when given."""
+    import workloads as W
+    out = []
+    for nd in W.longctx_doc_counts():
+        c = headline if (headline is not None and nd == 32) else longctx_decode(torch, dev, nd, False, 4, 1)
+        f = longctx_decode(torch, dev, nd, True, 2 if nd >= 16 else 4, 1)
+        row = {"original_tokens": 4096 * nd, "c2kv_ms_per_step": c["ms_per_step"], "c2kv_gbs": c["gbs"],
+               "c2kv_hbm_frac": c["hbm_frac"], "c2kv_layer_buffers": c["layer_buffers"],
+               "full_ms_per_step": f["ms_per_step"], "full_gbs": f["gbs"], "full_hbm_frac": f["hbm_frac"],
+               "full_layer_buffers": f["layer_buffers"], "speedup_c2kv_vs_full": f["ms_per_step"] / c["ms_per_step"]}
+        log(f"longctx {nd * 4}k: c2kv {c['ms_per_step']:.2f} ms/step {c['gbs']:.0f} GB/s, "
+            f"full {f['ms_per_step']:.2f} ms/step {f['gbs']:.0f} GB/s")
+        out.append(row)
+        if emit:
+            print(json.dumps(row), flush=True)
+    return out
+
+
+# --------------------------------------------- Qwen3-14B extraction (40 layers)
+
+def qwen3_extract(torch, dev, k, emit=False):
+    """Extraction at the Qwen3-14B shapes (40 query / 8 KV heads, d = 128,
+    theta 1e6, bf16): 64 documents of 8192 tokens at ratio k (sink = k), 40
+    attention-only layer calls alternating over two input/output buffer
+    sets (eager, HIP events around the 40 calls, after two untimed calls)."""
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+    w = W.QWEN3_14B
+    d, hq, hkv, dt = w.head_dim, w.hq, w.hkv, w.dtype
+    lens = list(w.doc_lens)
+    rows = c2kv.packed_rows(lens, k)
+    sets = []
+    for b in range(2):
+        q = fill_normal(torch, (rows, hq, d), dt, 5_000_000 + 10 * k + b, dev)
+        kk = fill_normal(torch, (rows, hkv, d), dt, 5_100_000 + 10 * k + b, dev)
+        v = fill_normal(torch, (rows, hkv, d), dt, 5_200_000 + 10 * k + b, dev)
+        sets.append((q, kk, v, torch.empty_like(q)))
+    ws = torch.empty(c2kv.workspace_size_extract(lens, k, hkv, d, dt), dtype=torch.uint8, device=dev)
+
+    def layer(i):
+        q, kk, v, o = sets[i % 2]
+        c2kv.extract_attn(q, kk, v, lens, k, k, w.rope_theta, out=o, workspace=ws)
+    layer(0)
+    layer(1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(w.layers):
+        layer(i)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3
+    flops_call = hq * 4 * d * sum(visible_cells(n, k) for n in lens)
+    tf = w.layers * flops_call / sec / 1e12
+    res = {"workload": f"qwen3_14b_extract_k{k}", "docs": len(lens), "doc_tokens": lens[0], "ratio_k": k,
+           "layers": w.layers, "seconds_40_layers": sec, "ms_per_call": sec * 1e3 / w.layers,
+           "flop_per_call": flops_call, "pflop_40_layers": w.layers * flops_call / 1e15, "tflops": tf,
+           "frac_of_peak": tf / BF16_PEAK_TFLOPS,
+           "target_seconds_at_half_peak": w.layers * flops_call / (0.5 * BF16_PEAK_TFLOPS * 1e12)}
+    del sets, ws
+    free(torch)
+    if emit:
+        print(json.dumps(res), flush=True)
+    return res
+
+
+# -------------------------------------------------- Qwen2.5-7B pool (decode, compose)
+
+def qwen25(torch, dev, replicas=8, steps=16, emit=False):
+    """The Qwen2.5-7B pool (28/4 heads, d = 128, theta 1e6, k = 16; 64
+    documents with lengths uniform on 1024..8192): 32 requests composing
+    seeded subsets of 8..32 documents in seeded order.
+      decode   `steps` steps of all 32 requests from one graph, step s over
+               replica s mod `replicas` of the composed caches (each replica
+               holds every request's cache; the set spans several GB)
+      compose  one call per replica of (pool, caches) from one graph;
+               rates on the algorithmic basis (every composed row read and
+               written) and the minimum-traffic basis (each pool document
+               read once, every composed row written)."""
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+    w = W.QWEN25
+    d, hq, hkv, dt, k, theta = w.head_dim, w.hq, w.hkv, w.dtype, w.ratio_k, w.rope_theta
+    pool = W.qwen25_pool(w)
+    reqs = W.qwen25_requests(w)
+    slots = [c2kv.num_slots(n, k) for n in pool]
+    Ms = [sum(slots[t] for t in r) for r in reqs]
+    R = len(reqs)
+    cap = max(Ms) + steps + 2
+    # decode over cache replicas
+    reps = [(fill_normal(torch, (R, hkv, cap, d), dt, 3_000_000 + 2 * i, dev),
+             fill_normal(torch, (R, hkv, cap, d), dt, 3_000_001 + 2 * i, dev)) for i in range(replicas)]
+    qd = fill_normal(torch, (steps, R, hq, d), dt, 3_100_000, dev)
+    kd = fill_normal(torch, (steps, R, hkv, d), dt, 3_100_001, dev)
+    vd = fill_normal(torch, (steps, R, hkv, d), dt, 3_100_002, dev)
+    nxt = [sum(pool[t] for t in r) for r in reqs]
+    ws = torch.empty(max(c2kv.workspace_size_decode([x + s for x in Ms], hq, hkv, d, dt) for s in range(steps)),
+                     dtype=torch.uint8, device=dev)
+
+    def dec():
+        for s in range(steps):
+            ck, cv = reps[s % replicas]
+            c2kv.attn_decode(qd[s], kd[s], vd[s], ck, cv, [x + s for x in Ms], [x + s for x in nxt], theta,
+                             workspace=ws)
+    g = capture(torch, dec)
+    dms = time_replays(torch, g, 3)
+    dbytes = sum(decode_call_bytes([x + s for x in Ms], hq, hkv, d) for s in range(steps))
+    del g, reps, qd, kd, vd, ws
+    free(torch)
+    # compose over replicas of the pool and the caches
+    creps = []
+    for i in range(replicas):
+        kv = [(fill_normal(torch, (m, hkv, d), dt, 3_200_000 + 1000 * i + 2 * t, dev),
+               fill_normal(torch, (m, hkv, d), dt, 3_200_001 + 1000 * i + 2 * t, dev)) for t, m in enumerate(slots)]
+        requests = [[(kv[t][0], kv[t][1], pool[t]) for t in r] for r in reqs]
+        ck = torch.empty((R, hkv, max(Ms), d), dtype=dt, device=dev)
+        creps.append((requests, ck, torch.empty_like(ck)))
+    g = capture(torch, lambda: [c2kv.compose(rq, k, theta, ck, cv) for rq, ck, cv in creps])
+    cms = time_replays(torch, g, 3) / replicas
+    alg = 4 * sum(Ms) * hkv * d * 2
+    used = sorted({t for r in reqs for t in r})
+    minimum = 2 * sum(slots[t] for t in used) * hkv * d * 2 + 2 * sum(Ms) * hkv * d * 2
+    del g, creps
+    free(torch)
+    res = {"workload": "qwen25_7b_pool", "requests": R, "composed_rows": sum(Ms), "rows_min": min(Ms),
+           "rows_max": max(Ms), "replicas": replicas,
+           "decode_us_per_step": dms * 1e3 / steps, "decode_bytes_per_step": dbytes / steps,
+           "decode_gbs": dbytes / (dms * 1e-3) / 1e9, "decode_hbm_frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "compose_us_per_call": cms * 1e3, "compose_algorithmic_bytes": alg, "compose_min_traffic_bytes": minimum,
+           "compose_gbs_algorithmic": alg / (cms * 1e-3) / 1e9,
+           "compose_gbs_min_traffic": minimum / (cms * 1e-3) / 1e9,
+           "compose_hbm_frac_min_traffic": minimum / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if emit:
+        print(json.dumps(res), flush=True)
+    return res
+
+
+# ------------------------------------------ Llama3.1-8B single layer (the old step)
+
+def llama_layer_step(torch, dev, steps, warmup, replicas=16, emit=False, profile_phase=None, calls=2,
+                     calibration_copy_mib=0):
+    """The Llama3.1-8B single-layer pass (bf16, 32/8 heads, d = 128, theta
+    5e5): extraction of 8 documents x 4096 tokens at k = 4 (sink 4),
+    composition of their slot caches in a seeded order into 8192 slots
+    covering 32768 positions, a 64-token question prefill and 256 decode
+    steps (batch 1, one graph).  Reports each phase per pass, and decode and
+    compose again over `replicas` copies of their inputs and caches so the
+    working set is far above the last-level cache (these are the figures of
+    record for the two small HBM-bound steps)."""
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+    w = W.LLAMA
+    d, hq, hkv, k, theta, dt = w.head_dim, w.hq, w.hkv, w.ratio_k, w.rope_theta, w.dtype
+    lens = list(w.doc_lens)
+    rows = c2kv.packed_rows(lens, k)
+    q = W.device_normal((rows, hq, d), dt, w.wid, W.P_Q, dev)
+    kk = W.device_normal((rows, hkv, d), dt, w.wid, W.P_K, dev)
+    v = W.device_normal((rows, hkv, d), dt, w.wid, W.P_V, dev)
+    o_ext = torch.empty_like(q)
+    order = W.llama_doc_order(w)
+    views = c2kv.slot_views(kk, v, lens, k)
+    requests = [[views[t] for t in order]]
+    M = sum(c2kv.num_slots(n, k) for n in lens)
+    P = sum(lens)
+    tq, S = w.tq, w.decode_steps
+    cap = M + tq + S
+    ck = torch.zeros((1, hkv, cap, d), dtype=dt, device=dev)
+    cv = torch.zeros_like(ck)
+    qp = W.device_normal((1, tq, hq, d), dt, w.wid, W.P_PREFILL, dev)
+    kp = W.device_normal((1, tq, hkv, d), dt, w.wid, W.P_NEW_KV, dev)
+    vp = W.device_normal((1, tq, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=1)
+    qd = W.device_normal((S, 1, hq, d), dt, w.wid, W.P_DEC_Q, dev)
+    kd = W.device_normal((S, 1, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=2)
+    vd = W.device_normal((S, 1, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=3)
+    ws_ext = torch.empty(c2kv.workspace_size_extract(lens, k, hkv, d, dt), dtype=torch.uint8, device=dev)
+    ws_pre = torch.empty(c2kv.workspace_size_prefill([M], tq, hq, hkv, d, dt), dtype=torch.uint8, device=dev)
+    ws_dec = torch.empty(max(c2kv.workspace_size_decode([M + tq + s], hq, hkv, d, dt) for s in range(S)),
+                         dtype=torch.uint8, device=dev)
+
+    def extract():
+        c2kv.extract_attn(q, kk, v, lens, k, w.sink_len, theta, out=o_ext, workspace=ws_ext)
+
+    def compose():
+        c2kv.compose(requests, k, theta, ck, cv)
+
+    def prefill():
+        c2kv.attn_prefill(qp, kp, vp, ck, cv, [M], [P], theta, workspace=ws_pre)
+
+    def decode_loop():
+        for s in range(S):
+            c2kv.attn_decode(qd[s], kd[s], vd[s], ck, cv, [M + tq + s], [P + tq + s], theta, workspace=ws_dec)
+
+    if profile_phase:
+        fn = {"extract": extract, "compose": compose, "prefill": prefill,
+              "decode": lambda: c2kv.attn_decode(qd[0], kd[0], vd[0], ck, cv, [M + tq], [P + tq], theta,
+                                                 workspace=ws_dec)}[profile_phase]
+        if profile_phase in ("prefill", "decode"):
+            compose()
+        if calibration_copy_mib:
+            _calibration_copy(torch, dev, calibration_copy_mib)
+        for _ in range(calls):
+            fn()
+        torch.cuda.synchronize()
+        print(f"{profile_phase}: {calls} calls done", flush=True)
+        return None
+
+    extract(); compose(); prefill(); decode_loop()
+    torch.cuda.synchronize()
+    graph = capture(torch, decode_loop)
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        extract()
+        if ev: ev[1].record()
+        compose()
+        if ev: ev[2].record()
+        prefill()
+        if ev: ev[3].record()
+        graph.replay()
+        if ev: ev[4].record()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ph = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(4)]
+    del graph
+    # decode over cache replicas (working set ~0.55 GB)
+    reps = [(ck.clone(), cv.clone()) for _ in range(replicas)]
+    gcold = capture(torch, lambda: [c2kv.attn_decode(qd[s], kd[s], vd[s], reps[s % replicas][0],
+                                                     reps[s % replicas][1], [M + tq + s], [P + tq + s], theta,
+                                                     workspace=ws_dec) for s in range(S)])
+    cold_ms = time_replays(torch, gcold, 3)
+    del gcold, reps
+    free(torch)
+    # compose over replicas of its inputs and caches (~3 GB)
+    creps = []
+    for _ in range(replicas):
+        kk_r, v_r = kk.clone(), v.clone()
+        vw = c2kv.slot_views(kk_r, v_r, lens, k)
+        creps.append(([[vw[t] for t in order]], torch.empty_like(ck), torch.empty_like(cv), kk_r, v_r))
+    gcc = capture(torch, lambda: [c2kv.compose(rq, k, theta, a, b) for rq, a, b, _, _ in creps])
+    comp_cold_ms = time_replays(torch, gcc, 3) / replicas
+    del gcc, creps
+    free(torch)
+    es = 2
+    ext_flops = hq * 4 * d * sum(visible_cells(n, k) for n in lens)
+    comp_bytes = 4 * M * hkv * d * es
+    pre_flops = 4 * d * hq * tq * (M + (tq + 1) / 2)
+    pre_bytes = (M + tq) * hkv * d * es * 2 + tq * (2 * hq + 2 * hkv) * d * es
+    dec_bytes = sum(decode_call_bytes([M + tq + s], hq, hkv, d) for s in range(S))
+    res = {"workload": "llama31_8b_1layer: extract 8 docs x 4096 tok (k=4, sink 4), compose 8192 slots "
+                       "(32768 positions), prefill 64, 256 decode steps, batch 1",
+           "steps": steps, "phase_ms": {"extract": ph[0], "compose": ph[1], "prefill": ph[2], "decode_256": ph[3]},
+           "extraction_tflops": ext_flops / (ph[0] * 1e-3) / 1e12,
+           "extraction_frac": ext_flops / (ph[0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+           "compose_us_eager": ph[1] * 1e3, "compose_us_cold": comp_cold_ms * 1e3,
+           "compose_gbs_cold": comp_bytes / (comp_cold_ms * 1e-3) / 1e9,
+           "compose_hbm_frac_cold": comp_bytes / (comp_cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "prefill_us": ph[2] * 1e3, "prefill_tflops": pre_flops / (ph[2] * 1e-3) / 1e12,
+           "prefill_gbs": pre_bytes / (ph[2] * 1e-3) / 1e9,
+           "prefill_roofline_floor_us": max(pre_bytes / (HBM_PEAK_GBS * 1e9), pre_flops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6,
+           "decode_us_per_step_warm": ph[3] * 1e3 / S, "decode_us_per_step_cold": cold_ms * 1e3 / S,
+           "decode_gbs_cold": dec_bytes / (cold_ms * 1e-3) / 1e9,
+           "decode_hbm_frac_cold": dec_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "decode_gbs_warm_mall": dec_bytes / (ph[3] * 1e-3) / 1e9, "cache_replicas": replicas}
+    del q, kk, v, o_ext, ck, cv, ws_ext, ws_pre, ws_dec
+    free(torch)
+    if emit:
+        print(json.dumps(res), flush=True)
+    return res
+
+
+def _calibration_copy(torch, dev, mib):
+    src = torch.ones(mib * 262144, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def profile_phase(a):
+    """One phase alone for counter runs (FETCH_SIZE / WRITE_SIZE, SQ)."""
+    torch, dev = _torch()
+    import compressed_composable_kv_amd as c2kv
+    import workloads as W
+    if a.profile_phase in ("extract", "compose", "prefill", "decode"):
+        llama_layer_step(torch, dev, 1, 0, profile_phase=a.profile_phase, calls=a.calls,
+                         calibration_copy_mib=a.calibration_copy_mib)
+        return
+    if a.profile_phase == "decode128k":
+        w = W.LONGCTX
+        d, hq, hkv, theta, dt = w.head_dim, w.hq, w.hkv, w.rope_theta, w.dtype
+        R, M, L = w.num_reqs, 32 * 1024, 32 * 4096
+        ck = fill_normal(torch, (R, hkv, M + 8, d), dt, 7, dev)
+        cv = fill_normal(torch, (R, hkv, M + 8, d), dt, 8, dev)
+        q = fill_normal(torch, (R, hq, d), dt, 9, dev)
+        kn = fill_normal(torch, (R, hkv, d), dt, 10, dev)
+        ws = torch.empty(c2kv.workspace_size_decode([M] * R, hq, hkv, d, dt), dtype=torch.uint8, device=dev)
+        fn = lambda: c2kv.attn_decode(q, kn, kn, ck, cv, [M] * R, [L] * R, theta, workspace=ws)  # noqa: E731
+    elif a.profile_phase == "compose_qwen25":
+        w = W.QWEN25
+        d, hkv, dt, k = w.head_dim, w.hkv, w.dtype, w.ratio_k
+        pool, reqs = W.qwen25_pool(w), W.qwen25_requests(w)
+        slots = [c2kv.num_slots(n, k) for n in pool]
+        kv = [(fill_normal(torch, (m, hkv, d), dt, 11 + 2 * t, dev), fill_normal(torch, (m, hkv, d), dt, 12 + 2 * t, dev))
+              for t, m in enumerate(slots)]
+        requests = [[(kv[t][0], kv[t][1], pool[t]) for t in r] for r in reqs]
+        Mx = max(sum(slots[t] for t in r) for r in reqs)
+        ck = torch.empty((len(reqs), hkv, Mx, d), dtype=dt, device=dev)
+        cv = torch.empty_like(ck)
+        fn = lambda: c2kv.compose(requests, k, w.rope_theta, ck, cv)  # noqa: E731
+    else:   # extract_qwen3
+        w = W.QWEN3_14B
+        d, hq, hkv, dt, k = w.head_dim, w.hq, w.hkv, w.dtype, 4
+        lens = list(w.doc_lens)
+        rows = c2kv.packed_rows(lens, k)
+        q = fill_normal(torch, (rows, hq, d), dt, 13, dev)
+        kk = fill_normal(torch, (rows, hkv, d), dt, 14, dev)
+        v = fill_normal(torch, (rows, hkv, d), dt, 15, dev)
+        o = torch.empty_like(q)
+        ws = torch.empty(c2kv.workspace_size_extract(lens, k, hkv, d, dt), dtype=torch.uint8, device=dev)
+        fn = lambda: c2kv.extract_attn(q, kk, v, lens, k, k, w.rope_theta, out=o, workspace=ws)  # noqa: E731
+    if a.calibration_copy_mib:
+        _calibration_copy(torch, dev, a.calibration_copy_mib)
+    for _ in range(a.calls):
+        fn()
+    torch.cuda.synchronize()
+    print(f"{a.profile_phase}: {a.calls} calls done", flush=True)
+
+
+# --------------------------------------------------------------- CPU baseline
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(nsteps=16):
+    """The oracle, as it stands, on a bounded sample of the benchmark's
+    workloads, on the host cores: `nsteps` decode steps of one request and
+    one layer of the 128k long-context workload (32 768 composed slots,
+    32/8 heads, d = 128), and the extraction of one 8192-token Qwen3-14B
+    document at k = 4 for one KV-head group (5 query heads) of one layer."""
     import numpy as np
     import oracle as O
     import workloads as W
@@ -232,197 +757,39 @@ def cpu_baseline(w, M, P, tq, nsteps):
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = 1
+        threads = None
+    w = W.LONGCTX
     d, hq, hkv = w.head_dim, w.hq, w.hkv
-    L0 = M + tq
-    ck = W.normal((L0, hkv, d), w.dtype, 90, W.P_K).float().numpy()
-    cv = W.normal((L0, hkv, d), w.dtype, 90, W.P_V).float().numpy()
+    M = 32 * 1024
+    ck = W.normal((M, hkv, d), w.dtype, 90, W.P_K).float().numpy()
+    cv = W.normal((M, hkv, d), w.dtype, 90, W.P_V).float().numpy()
     t0 = time.perf_counter()
     nbytes = 0
     for s in range(nsteps):
         q = W.normal((hq, d), w.dtype, 90, W.P_DEC_Q, salt=s).float().numpy()
         kn = W.normal((hkv, d), w.dtype, 90, W.P_NEW_KV, salt=s).float().numpy()
         vn = W.normal((hkv, d), w.dtype, 90, W.P_NEW_KV, salt=1000 + s).float().numpy()
-        _, _, ck, cv = O.decode_step(q, kn, vn, ck, cv, P + tq + s, w.rope_theta, "bf16")
-        nbytes += ck.shape[0] * hkv * d * 2 * 2
+        _, _, ck, cv = O.decode_step(q, kn, vn, ck, cv, 131072 + s, w.rope_theta, "bf16")
+        nbytes += decode_call_bytes([ck.shape[0] - 1], hq, hkv, d)
     dec_s = time.perf_counter() - t0
-    n, k = w.doc_lens[0], w.ratio_k
+    w5 = W.QWEN3_14B
+    n, k, G = 8192, 4, w5.hq // w5.hkv
     rows = n + O.num_slots(n, k)
-    q = W.normal((rows, hq, d), w.dtype, 91, W.P_Q).float().numpy()
-    kk = W.normal((rows, hkv, d), w.dtype, 91, W.P_K).float().numpy()
-    v = W.normal((rows, hkv, d), w.dtype, 91, W.P_V).float().numpy()
+    q = W.normal((rows, G, d), w5.dtype, 91, W.P_Q).float().numpy()
+    kk = W.normal((rows, 1, d), w5.dtype, 91, W.P_K).float().numpy()
+    v = W.normal((rows, 1, d), w5.dtype, 91, W.P_V).float().numpy()
     t0 = time.perf_counter()
-    O.extract_attn(q, kk, v, [n], k, w.sink_len, w.rope_theta)
+    O.extract_attn(q, kk, v, [n], k, k, w5.rope_theta)
     ext_s = time.perf_counter() - t0
-    ext_flops = hq * 4 * d * visible_cells(n, k)
+    ext_flops = G * 4 * d * visible_cells(n, k)
     return {
         "value": nbytes / dec_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-        "sample": f"{nsteps} decode steps over the full {L0}-row composed cache (32/8 heads, d=128), "
-                  f"plus extraction of 1 of the 8 documents (all 32 heads)",
+        "sample": f"{nsteps} decode steps of 1 request x 1 layer over the 128k long-context cache ({M} composed "
+                  f"slots, 32/8 heads, d=128), plus extraction of one 8192-token Qwen3-14B document at k=4 for "
+                  f"one KV-head group (5 query heads)",
         "decode_seconds": dec_s, "extraction_tflops": ext_flops / ext_s / 1e12, "extraction_seconds": ext_s,
-        "host_cores": len(os.sched_getaffinity(0)),
-    }
-
-
-def decode_sweep():
-    """Decode rate (algorithmic KV bytes per second) of the other decode
-    workloads; caches are device-generated N(0, 1) rows (decode time does
-    not depend on their values)."""
-    import torch
-    import compressed_composable_kv_amd as c2kv
-    import workloads as W
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-
-    def run(name, lens, w, steps, extra):
-        d, hq, hkv, dt = w.head_dim, w.hq, w.hkv, w.dtype
-        R = len(lens)
-        cap = max(lens) + steps
-        ck = W.device_normal((R, hkv, cap, d), dt, w.wid, W.P_K, dev, salt=7)
-        cv = W.device_normal((R, hkv, cap, d), dt, w.wid, W.P_V, dev, salt=7)
-        qd = W.device_normal((steps, R, hq, d), dt, w.wid, W.P_DEC_Q, dev, salt=7)
-        kd = W.device_normal((steps, R, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=7)
-        vd = W.device_normal((steps, R, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=8)
-        ws = torch.empty(max(c2kv.workspace_size_decode([x + s for x in lens], hq, hkv, d, dt)
-                             for s in range(steps)), dtype=torch.uint8, device=dev)
-
-        def loop():
-            for s in range(steps):
-                c2kv.attn_decode(qd[s], kd[s], vd[s], ck, cv, [x + s for x in lens], [4 * x + s for x in lens],
-                                 w.rope_theta, workspace=ws)
-        loop()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            loop()
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(3):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (3 * steps)
-        nbytes = sum((x + steps / 2 + 1) * hkv * d * 2 * 2 + (2 * hq + 2 * hkv) * d * 2 for x in lens)
-        gbs = nbytes / (us * 1e-6) / 1e9
-        print(json.dumps({"workload": name, "requests": R, "rows_min": min(lens), "rows_max": max(lens),
-                          "us_per_step": us, "kv_bytes_per_step": nbytes, "gbs": gbs,
-                          "hbm_frac": gbs / HBM_PEAK_GBS, **extra}), flush=True)
-        del ck, cv, g
-        torch.cuda.empty_cache()
-
-    w3 = W.QWEN25
-    pool = W.qwen25_pool(w3)
-    lens3 = [sum(c2kv.num_slots(pool[t], w3.ratio_k) for t in r) for r in W.qwen25_requests(w3)]
-    run("qwen25_7b_pool_decode", lens3, w3, 32, {"cache": "composed, k=16"})
-    w4 = W.LONGCTX
-    for nd in W.longctx_doc_counts():
-        L = 4096 * nd
-        run(f"llama31_8b_longctx_{L // 1024}k_c2kv", [nd * c2kv.num_slots(4096, w4.ratio_k)] * w4.num_reqs, w4, 8,
-            {"cache": "composed, k=4", "original_tokens": L})
-        run(f"llama31_8b_longctx_{L // 1024}k_full", [L] * w4.num_reqs, w4, 4,
-            {"cache": "uncompressed comparator", "original_tokens": L})
-
-
-def extract_sweep():
-    """Extraction throughput at the Qwen3-14B shapes (40 query / 8 KV heads,
-    d = 128, theta 1e6, bf16): 64 documents of 8192 tokens at k = 4, 8, 16
-    (sink = k), 40 attention-only layers whose calls alternate over two
-    input/output buffer sets.  One JSON line per k."""
-    import torch
-    import compressed_composable_kv_amd as c2kv
-    import workloads as W
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    w = W.QWEN3_14B
-    d, hq, hkv, dt = w.head_dim, w.hq, w.hkv, w.dtype
-    lens = list(w.doc_lens)
-    ach = achievable_peaks(torch, dev)
-    for k in (4, 8, 16):
-        rows = c2kv.packed_rows(lens, k)
-        sets = []
-        for b in range(2):
-            q = W.device_normal((rows, hq, d), dt, w.wid, W.P_Q, dev, salt=10 * k + b)
-            kk = W.device_normal((rows, hkv, d), dt, w.wid, W.P_K, dev, salt=10 * k + b)
-            v = W.device_normal((rows, hkv, d), dt, w.wid, W.P_V, dev, salt=10 * k + b)
-            sets.append((q, kk, v, torch.empty_like(q)))
-        ws = torch.empty(c2kv.workspace_size_extract(lens, k, hkv, d, dt), dtype=torch.uint8, device=dev)
-
-        def layer(i):
-            q, kk, v, o = sets[i % 2]
-            c2kv.extract_attn(q, kk, v, lens, k, k, w.rope_theta, out=o, workspace=ws)
-        layer(0)
-        layer(1)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(w.layers):
-            layer(i)
-        e1.record()
-        torch.cuda.synchronize()
-        sec = e0.elapsed_time(e1) / 1e3
-        flops = w.layers * hq * 4 * d * sum(visible_cells(n, k) for n in lens)
-        tf = flops / sec / 1e12
-        print(json.dumps({"workload": f"qwen3_14b_extract_k{k}", "docs": len(lens), "doc_tokens": lens[0],
-                          "ratio_k": k, "layers": w.layers, "seconds_40_layers": sec, "pflop": flops / 1e15,
-                          "tflops": tf, "frac_of_peak": tf / BF16_PEAK_TFLOPS,
-                          "frac_of_achievable": tf / ach["mfma_bf16_tflops"] if ach["mfma_bf16_tflops"] else None,
-                          "target_seconds_at_half_peak": flops / (0.5 * BF16_PEAK_TFLOPS * 1e12)}), flush=True)
-        del sets, ws
-        torch.cuda.empty_cache()
-
-
-def compose_sweep():
-    """Compose throughput of the Qwen2.5-7B pool workload: 64 pre-extracted
-    documents (k = 16, lengths uniform on 1024..8192, slot K/V N(0, 1)), 32
-    requests each composing a seeded subset of 8..32 documents in seeded
-    order.  Reports algorithmic bytes (read and write every composed row)
-    and minimum traffic (the pool read once plus the writes), per call from
-    a graph of 10 calls."""
-    import torch
-    import compressed_composable_kv_amd as c2kv
-    import workloads as W
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    w = W.QWEN25
-    d, hkv, dt, k = w.head_dim, w.hkv, w.dtype, w.ratio_k
-    pool = W.qwen25_pool(w)
-    reqs = W.qwen25_requests(w)
-    slots = [c2kv.num_slots(n, k) for n in pool]
-    kv = [(W.device_normal((m, hkv, d), dt, w.wid, W.P_K, dev, salt=100 + i),
-           W.device_normal((m, hkv, d), dt, w.wid, W.P_V, dev, salt=100 + i)) for i, m in enumerate(slots)]
-    requests = [[(kv[t][0], kv[t][1], pool[t]) for t in r] for r in reqs]
-    M = [sum(slots[t] for t in r) for r in reqs]
-    cap = max(M) + 128
-    ck = torch.empty((len(reqs), hkv, cap, d), dtype=dt, device=dev)
-    cv = torch.empty_like(ck)
-    c2kv.compose(requests, k, w.rope_theta, ck, cv)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(10):
-            c2kv.compose(requests, k, w.rope_theta, ck, cv)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(3):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / 30
-    es = 2
-    alg = 4 * sum(M) * hkv * d * es
-    used = sorted({t for r in reqs for t in r})
-    minimum = 2 * sum(slots[t] for t in used) * hkv * d * es + 2 * sum(M) * hkv * d * es
-    ach = achievable_peaks(torch, dev)
-    print(json.dumps({"workload": "qwen25_7b_pool_compose", "requests": len(reqs), "composed_rows": sum(M),
-                      "us_per_call": us, "algorithmic_bytes": alg, "min_traffic_bytes": minimum,
-                      "gbs_algorithmic": alg / (us * 1e-6) / 1e9, "gbs_min_traffic": minimum / (us * 1e-6) / 1e9,
-                      "frac_of_peak_min_traffic": minimum / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                      "frac_of_achievable_min_traffic": minimum / (us * 1e-6) / 1e9 / ach["hbm_copy_gbs"]}),
-          flush=True)
+        "host_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+        "threads_note": "cores = BLAS threads numpy used (threadpoolctl)"}
 
 
 def layer_bench(ach=None, emit=True):
@@ -491,9 +858,6 @@ def layer_bench(ach=None, emit=True):
     if emit:
         print(json.dumps(res), flush=True)
     return res
-
-
-PCIE_PEAK_GBS = 64.0           # MI355X host link, PCIe 5.0 x16, one direction, GB/s
 
 
 def host_pool(emit=True):
@@ -613,56 +977,17 @@ def host_pool(emit=True):
     return res
 
 
-def achievable_peaks(torch, dev):
-    """Rates this GPU sustains, measured live: dense bf16 MFMA from the probe
-    library (independent MFMA chains on register operands, 4 waves per SIMD),
-    and HBM from a 1 GiB device-to-device copy (read + write bytes).  They
-    sit below the published peaks because the chip holds a lower clock under
-    sustained load than its nominal 2.4 GHz."""
-    import ctypes
-    from compressed_composable_kv_amd import build_lib
-    mfma = None
-    if os.path.exists(build_lib.PROBE_LIB):
-        lib = ctypes.CDLL(build_lib.PROBE_LIB)
-        lib.c2kv_probe_mfma_bf16.restype = ctypes.c_double
-        lib.c2kv_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
-        ms = ctypes.c_float()
-        rates = [lib.c2kv_probe_mfma_bf16(512, 512, 4000, ctypes.byref(ms)) for _ in range(3)]
-        mfma = max(rates) if max(rates) > 0 else None
-    n = 1 << 29                                   # 1 GiB of bf16
-    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    best = None
-    for _ in range(3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1)
-        best = t if best is None else min(best, t)
-    del src, dst
-    torch.cuda.empty_cache()
-    return {"mfma_bf16_tflops": mfma, "hbm_copy_gbs": 2 * 2 * n / (best * 1e-3) / 1e9,
-            "how": "MFMA: probe/mfma_peak.hip, 512 workgroups x 8 waves, 16 independent chains per wave; "
-                   "HBM: torch copy of 1 GiB, read + write bytes over the best of 3"}
-
-
 def main():
     a = parse()
     if a.summarize:
         summarize(a.summarize, a.out, a.cmd, a.calibration_copy_mib)
         return
-    if a.decode_sweep:
-        decode_sweep()
-        return
-    if a.extract_sweep:
-        extract_sweep()
-        return
-    if a.compose_sweep:
-        compose_sweep()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this path does not shard "
+              f"across GPUs).", file=sys.stderr)
+        sys.exit(2)
+    if a.profile_phase:
+        profile_phase(a)
         return
     if a.host_pool:
         host_pool()
@@ -670,250 +995,93 @@ def main():
     if a.layer:
         layer_bench()
         return
-    if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this path does not shard "
-              f"across GPUs).", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import compressed_composable_kv_amd as c2kv
-    import workloads as W
-
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    w = W.LLAMA
-    d, hq, hkv, k, theta, dt = w.head_dim, w.hq, w.hkv, w.ratio_k, w.rope_theta, w.dtype
-    lens = list(w.doc_lens)
-    rows = c2kv.packed_rows(lens, k)
-    q = W.device_normal((rows, hq, d), dt, w.wid, W.P_Q, dev)
-    kk = W.device_normal((rows, hkv, d), dt, w.wid, W.P_K, dev)
-    v = W.device_normal((rows, hkv, d), dt, w.wid, W.P_V, dev)
-    o_ext = torch.empty_like(q)
-    order = W.llama_doc_order(w)
-    views = c2kv.slot_views(kk, v, lens, k)
-    requests = [[views[t] for t in order]]
-    M = sum(c2kv.num_slots(n, k) for n in lens)
-    P = sum(lens)
-    tq, S = w.tq, w.decode_steps
-    cap = M + tq + S
-    ck = torch.zeros((1, hkv, cap, d), dtype=dt, device=dev)
-    cv = torch.zeros_like(ck)
-    qp = W.device_normal((1, tq, hq, d), dt, w.wid, W.P_PREFILL, dev)
-    kp = W.device_normal((1, tq, hkv, d), dt, w.wid, W.P_NEW_KV, dev)
-    vp = W.device_normal((1, tq, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=1)
-    qd = W.device_normal((S, 1, hq, d), dt, w.wid, W.P_DEC_Q, dev)
-    kd = W.device_normal((S, 1, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=2)
-    vd = W.device_normal((S, 1, hkv, d), dt, w.wid, W.P_NEW_KV, dev, salt=3)
-    ws_ext = torch.empty(c2kv.workspace_size_extract(lens, k, hkv, d, dt), dtype=torch.uint8, device=dev)
-    ws_pre = torch.empty(c2kv.workspace_size_prefill([M], tq, hq, hkv, d, dt), dtype=torch.uint8, device=dev)
-    ws_dec = torch.empty(max(c2kv.workspace_size_decode([M + tq + s], hq, hkv, d, dt) for s in range(S)),
-                         dtype=torch.uint8, device=dev)
-
-    def extract():
-        c2kv.extract_attn(q, kk, v, lens, k, w.sink_len, theta, out=o_ext, workspace=ws_ext)
-
-    def compose():
-        c2kv.compose(requests, k, theta, ck, cv)
-
-    def prefill():
-        c2kv.attn_prefill(qp, kp, vp, ck, cv, [M], [P], theta, workspace=ws_pre)
-
-    def decode_loop():
-        for s in range(S):
-            c2kv.attn_decode(qd[s], kd[s], vd[s], ck, cv, [M + tq + s], [P + tq + s], theta, workspace=ws_dec)
-
-    if a.profile_phase:
-        fn = {"extract": extract, "compose": compose, "prefill": prefill,
-              "decode": lambda: c2kv.attn_decode(qd[0], kd[0], vd[0], ck, cv, [M + tq], [P + tq], theta,
-                                                 workspace=ws_dec)}[a.profile_phase]
-        if a.profile_phase in ("prefill", "decode"):
-            compose()
-        for _ in range(a.calls):
-            fn()
-        torch.cuda.synchronize()
-        print(f"{a.profile_phase}: {a.calls} calls done", flush=True)
+    torch, dev = _torch()
+    if a.decode_sweep:
+        longctx_sweep(torch, dev, emit=True)
+        qwen25(torch, dev, emit=True)
+        return
+    if a.extract_sweep:
+        for k in (4, 8, 16):
+            qwen3_extract(torch, dev, k, emit=True)
+        return
+    if a.compose_sweep:
+        qwen25(torch, dev, emit=True)
+        return
+    if a.only:
+        if a.only == "headline":
+            longctx_decode(torch, dev, 32, False, a.steps, a.warmup, emit=True)
+        elif a.only == "longctx":
+            longctx_sweep(torch, dev, emit=True)
+        elif a.only == "extract":
+            qwen3_extract(torch, dev, 4, emit=True)
+        elif a.only == "qwen25":
+            qwen25(torch, dev, emit=True)
+        else:
+            llama_layer_step(torch, dev, a.steps, a.warmup, emit=True)
         return
 
-    # eager pass (also the reference for the graph), then capture the decode loop
-    extract(); compose(); prefill(); decode_loop()
-    torch.cuda.synchronize()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        decode_loop()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        decode_loop()
-    torch.cuda.synchronize()
-
-    def step(ev=None):
-        if ev: ev[0].record()
-        extract()
-        if ev: ev[1].record()
-        compose()
-        if ev: ev[2].record()
-        prefill()
-        if ev: ev[3].record()
-        graph.replay()
-        if ev: ev[4].record()
-
-    if a.calibration_copy_mib:
-        src = torch.ones(a.calibration_copy_mib * 262144, dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record()
-    for i in range(a.steps):
-        step(evs[i])
-    stop.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(stop)
-
-    # decode with the steps spread over replicas of the cache (working set
-    # above the last-level cache); not part of the step
-    cold_gbs = None
-    if a.cold_replicas > 1:
-        reps = [(ck.clone(), cv.clone()) for _ in range(a.cold_replicas)]
-        torch.cuda.synchronize()
-        gcold = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gcold):
-            for s in range(S):
-                rk_, rv_ = reps[s % a.cold_replicas]
-                c2kv.attn_decode(qd[s], kd[s], vd[s], rk_, rv_, [M + tq + s], [P + tq + s], theta, workspace=ws_dec)
-        gcold.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(3):
-            gcold.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        cold_ms = e0.elapsed_time(e1) / 3
-        del gcold, reps
-        torch.cuda.empty_cache()
-    # compose with its inputs and caches spread over replicas (each call
-    # reads and writes a different copy: a working set of about 3 GB, far
-    # above the last-level cache); not part of the step
-    comp_cold_gbs = None
-    if a.cold_replicas > 1:
-        creps = []
-        for _ in range(a.cold_replicas):
-            kk_r, v_r = kk.clone(), v.clone()
-            vw = c2kv.slot_views(kk_r, v_r, lens, k)
-            creps.append(([[vw[t] for t in order]], torch.empty_like(ck), torch.empty_like(cv), kk_r, v_r))
-        torch.cuda.synchronize()
-        gcc = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gcc):
-            for req_r, ck_r, cv_r, _, _ in creps:
-                c2kv.compose(req_r, k, theta, ck_r, cv_r)
-        gcc.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(3):
-            gcc.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        comp_cold_ms = e0.elapsed_time(e1) / (3 * a.cold_replicas)
-        comp_cold_gbs = 4 * M * hkv * d * 2 / (comp_cold_ms * 1e-3) / 1e9
-        del gcc, creps
-        torch.cuda.empty_cache()
-    # compose on its own: 20 back-to-back calls from a graph, per-call time
-    # without the launch gap of a single eager call; not part of the step
-    gcomp = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gcomp):
-        for _ in range(20):
-            compose()
-    gcomp.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        gcomp.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    comp_graph_ms = e0.elapsed_time(e1) / 100
-    del gcomp
+    t_all = time.time()
     ach = achievable_peaks(torch, dev)
+    log(f"achievable: {json.dumps(ach)}")
+    # headline: 32-layer decode at 128k original tokens, 64 requests (timed K steps)
+    head = longctx_decode(torch, dev, 32, False, a.steps, a.warmup)
+    log(f"headline: {head['ms_per_step']:.3f} ms/step, {head['gbs']:.0f} GB/s")
+    sweep = longctx_sweep(torch, dev, headline=head)
+    ext = {}
+    for k in (4, 8, 16):
+        ext[k] = qwen3_extract(torch, dev, k)
+        log(f"qwen3-14b extraction k={k}: {ext[k]['seconds_40_layers']:.3f} s / 40 layers, {ext[k]['tflops']:.0f} TFLOP/s")
+    q25 = qwen25(torch, dev)
+    log(f"qwen2.5 pool: decode {q25['decode_us_per_step']:.1f} us/step {q25['decode_gbs']:.0f} GB/s, compose "
+        f"{q25['compose_us_per_call']:.1f} us")
+    lla = llama_layer_step(torch, dev, steps=5, warmup=2)
+    log(f"llama layer: {json.dumps(lla['phase_ms'])}")
 
-    ph = [0.0] * 4
-    for e in evs:
-        for j in range(4):
-            ph[j] += e[j].elapsed_time(e[j + 1])
-    ph = [x / a.steps for x in ph]   # ms per step
-    ms_step = total_ms / a.steps
-
-    es = 2
-    ext_flops = hq * 4 * d * sum(visible_cells(n, k) for n in lens)
-    comp_bytes = 4 * M * hkv * d * es
-    pre_flops = 4 * d * hq * tq * (M + (tq + 1) / 2)
-    dec_bytes = sum((M + tq + s + 1) * hkv * d * es * 2 + (2 * hq + 2 * hkv) * d * es for s in range(S))
-    ext_tflops = ext_flops / (ph[0] * 1e-3) / 1e12
-    dec_gbs = dec_bytes / (ph[3] * 1e-3) / 1e9
-    if a.cold_replicas > 1:
-        cold_gbs = dec_bytes / (cold_ms * 1e-3) / 1e9
-    comp_gbs = comp_bytes / (ph[1] * 1e-3) / 1e9
-
-    # dominant kernel of the step: the phase with the largest share of the step
-    if ph[0] >= ph[3]:
-        roof = {"bound": "mfma", "kernel": "extract_attn_kernel<bf16,128>", "achieved": ext_tflops,
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ext_tflops / BF16_PEAK_TFLOPS,
-                "traffic": None, "per_launch_ms": ph[0], "algorithmic_per_launch": ext_flops}
-    else:
-        # one launch = one c2kv_attn_decode call: decode_attn_kernel plus
-        # merge_kernel, timed per call from the graph replay
-        per_launch_ms = ph[3] / S
-        # the decode call's merge is the 32-dim-slice instantiation (the prefill one takes whole rows)
-        traffic = committed_traffic(("decode_attn_kernel", "merge_kernelIDF16bLi128ELi32E"))
-        roof = {"bound": "hbm", "kernel": "c2kv_attn_decode (decode_attn_kernel<bf16,128> + merge_kernel<bf16,128,32>)",
-                "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
-                "traffic": traffic, "per_launch_ms": per_launch_ms, "algorithmic_per_launch": dec_bytes / S}
-
+    dec_traffic = committed_traffic(("decode_attn_kernel", "merge_kernelIDF16bLi128ELi32E"))
+    roof = {"bound": "hbm", "kernel": "c2kv_attn_decode (decode_attn_kernel<bf16,128> + merge_kernel<bf16,128,32>)",
+            "achieved": head["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["gbs"] / HBM_PEAK_GBS,
+            "traffic": dec_traffic, "per_launch_ms": head["ms_per_call"],
+            "algorithmic_per_launch": head["bytes_per_step"] / head["layers"],
+            "frac_of_achievable_read": _frac(head["gbs"], ach["hbm_read_gbs"]),
+            "workload": "one decode call: 64 requests x 32768 composed slots (128k original tokens), 8 KV heads"}
+    e4 = ext[4]
+    ext_roof = {"bound": "mfma", "kernel": "extract_attn_kernel<bf16,128> (+ rotate_k_kernel, rope_table_kernel)",
+                "achieved": e4["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": e4["frac_of_peak"],
+                "traffic": None, "per_launch_ms": e4["ms_per_call"], "algorithmic_per_launch": e4["flop_per_call"],
+                "frac_of_achievable_mfma": _frac(e4["tflops"], ach["mfma_bf16_tflops"]),
+                "workload": "one layer call: 64 documents x 8192 tokens at k=4, 40/8 heads"}
     line = {
         "metric": "C2KV decode-attn KV GB/s (% HBM peak) + extraction masked-attn TFLOP/s",
-        "value": dec_gbs,
+        "value": head["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic N(0,1) Q/K/V of the workload's shapes, resident in HBM",
-        "config": {"workload": "llama31_8b_1layer: extract 8 docs x 4096 tok (k=4, sink 4), compose 8192 slots "
-                               "(32768 positions), prefill 64, 256 decode steps, batch 1",
-                   "hq": hq, "hkv": hkv, "head_dim": d, "rope_theta": theta, "decode_graph": True},
-        "hbm_frac": dec_gbs / HBM_PEAK_GBS,
-        "extraction_tflops": ext_tflops,
-        "extraction_frac": ext_tflops / BF16_PEAK_TFLOPS,
-        "phase_ms": {"extract": ph[0], "compose": ph[1], "prefill": ph[2], "decode_256": ph[3]},
-        "compose_gbs": comp_gbs,
-        "compose_gbs_graph": comp_bytes / (comp_graph_ms * 1e-3) / 1e9,
-        "compose_gbs_cache_replicas": comp_cold_gbs,
-        "achievable": ach,
-        "extraction_frac_of_achievable": ext_tflops / ach["mfma_bf16_tflops"] if ach["mfma_bf16_tflops"] else None,
-        "decode_frac_of_achievable": dec_gbs / ach["hbm_copy_gbs"],
-        "compose_graph_frac_of_achievable": comp_bytes / (comp_graph_ms * 1e-3) / 1e9 / ach["hbm_copy_gbs"],
-        "decode_gbs_cache_replicas": cold_gbs,
-        "cache_replicas": a.cold_replicas,
-        "prefill_tflops": pre_flops / (ph[2] * 1e-3) / 1e12,
-        "wall_s": t_wall,
+        "data": "synthetic N(0,1) Q/K/V of the workloads' shapes, resident in HBM",
+        "config": {"workload": "llama31_8b_longctx_128k_decode: Llama3.1-8B shapes (32/8 heads, d=128, theta 5e5), "
+                               "32 attention-only layers, 64 requests, composed context of 32 documents x 4096 "
+                               "tokens at k=4 (32768 slots, 131072 original tokens); one step = one decode call per "
+                               "layer; extraction measured on qwen3_14b_extract (64 docs x 8192 tokens, k=4/8/16, "
+                               "40 layers)",
+                   "hq": 32, "hkv": 8, "head_dim": 128, "rope_theta": 500000.0, "requests": 64, "layers": 32,
+                   "layer_buffers": head["layer_buffers"], "decode_graph": True},
+        "hbm_frac": head["gbs"] / HBM_PEAK_GBS,
+        "extraction_tflops": e4["tflops"],
+        "extraction_frac": e4["frac_of_peak"],
         "roofline": roof,
+        "extraction_roofline": ext_roof,
+        "longctx_sweep": sweep,
+        "extraction": [ext[k] for k in (4, 8, 16)],
+        "qwen25": q25,
+        "llama_layer": lla,
+        "achievable": ach,
     }
     if not a.no_extras:
-        # the paths around the step, one summary each (their own modes print the full lines)
         hp = host_pool(emit=False)
         line["host_pool_load"] = {k_: hp[k_] for k_ in (
             "c2kv_zero_copy_ms", "c2kv_staged_ms", "full_dma_copy_ms", "full_zero_copy_k1_ms", "c2kv_zero_copy_gbs",
@@ -922,8 +1090,9 @@ def main():
         ly = layer_bench(ach=ach, emit=False)
         line["extractor_layer"] = {k_: ly[k_] for k_ in ("ms", "tflops", "frac_of_peak", "frac_of_achievable")}
         line["extractor_layer"]["workload"] = "one Llama3.1-8B-shaped extractor layer over 8 x 4096 tokens (synthetic weights)"
+    line["gpu_sections_wall_s"] = time.time() - t_all
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, M, P, tq, a.cpu_decode_steps)
+        line["cpu_baseline"] = cpu_baseline(8)
     print(json.dumps(line), flush=True)
 
 

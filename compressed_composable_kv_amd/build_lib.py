@@ -26,7 +26,7 @@ LIB = os.path.join(PKG, "libc2kv.so")
 PROBE_SRCS = [os.path.join(PKG, "probe", "mfma_peak.hip"), os.path.join(PKG, "probe", "hbm_read.hip")]
 PROBE_LIB = os.path.join(PKG, "libc2kv_probe.so")
 
-SOURCES = ["c2kv_attn.hip", "c2kv_decode.hip", "c2kv_aux.hip", "c2kv_layer.hip", "c2kv_abi.cpp"]
+SOURCES = ["c2kv_attn.hip", "c2kv_decode.hip", "c2kv_aux.hip", "c2kv_layer.hip", "c2kv_abi.cpp", "c2kv_cache.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
