@@ -90,6 +90,9 @@ SIGNATURES = {
     "c2kv_attn_decode": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                    P_i32, P_i32, c_int32, c_int32, c_int32, c_int32, c_float,
                                    c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]),
+    "c2kv_attn_decode_noalloc": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                                           P_i32, P_i32, c_int32, c_int32, c_int32, c_int32, c_float,
+                                           c_void_p, c_void_p, c_int32, c_void_p]),
     "c2kv_workspace_init": (c_int32, [c_void_p, c_size_t, c_void_p]),
     "c2kv_workspace_size_mask_cells": (c_size_t, []),
     "c2kv_mask_cells": (c_int32, [P_i32, c_int32, c_int32, c_int32, P_u64, c_void_p, c_size_t, c_void_p]),

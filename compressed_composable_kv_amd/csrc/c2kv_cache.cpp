@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "c2kv.h"
@@ -272,3 +273,59 @@ c2kv_status c2kv_attn_decode(const void* q, const void* k_new, const void* v_new
 }
 
 }  // extern "C"
+
+namespace {
+
+// Split-K partials of c2kv_attn_decode_noalloc: one array per GPU, never
+// freed.  Host code uses only the per-device addresses from
+// hipGetSymbolAddress, never the array's name.
+__device__ __align__(256) char scratch[C2KV_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the stream's device, looked up once per device
+// with that device current.
+c2kv_status scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(C2KV_ERR_UNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (e2 != hipSuccess) return hip_fail(e2, "hipSetDevice");
+    if (!p || !aligned256(p)) return fail(C2KV_ERR_HIP, "scratch address %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return C2KV_OK;
+}
+
+}  // namespace
+
+extern "C" c2kv_status c2kv_attn_decode_noalloc(const void* q, const void* k_new, const void* v_new, void* cache_k,
+                                                void* cache_v, int64_t cap, const int32_t* cache_len,
+                                                const int32_t* q_pos, int32_t num_reqs, int32_t hq, int32_t hkv,
+                                                int32_t head_dim, float rope_theta, void* o, float* lse,
+                                                c2kv_dtype dt, hipStream_t stream) {
+  c2kv_status s;
+  // the same validation as c2kv_attn_decode, before any HIP call
+  CachePlan P;
+  if ((s = cache_validate(q, k_new, v_new, cache_k, cache_v, cap, cache_len, q_pos, num_reqs, 1, true, hq, hkv,
+                          head_dim, rope_theta, o, lse, dt, P)))
+    return s;
+  if (P.total > C2KV_NOALLOC_SCRATCH_BYTES)
+    return fail(C2KV_ERR_WORKSPACE, "the step needs %zu bytes of split scratch; the static scratch holds %u", P.total,
+                (unsigned)C2KV_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((s = scratch_for_stream(stream, &ws))) return s;
+  return cache_attention(q, k_new, v_new, cache_k, cache_v, cap, cache_len, q_pos, num_reqs, 1, true, hq, hkv,
+                         head_dim, rope_theta, o, lse, dt, ws, C2KV_NOALLOC_SCRATCH_BYTES, stream);
+}

@@ -369,6 +369,30 @@ def attn_decode(q, k_new, v_new, cache_k, cache_v, cache_len, q_pos, rope_theta,
                        return_lse, None, workspace)
 
 
+def attn_decode_noalloc(q, k_new, v_new, cache_k, cache_v, cache_len, q_pos, rope_theta, return_lse=False,
+                        out=None, lse_out=None):
+    """One decode step that allocates no device memory in the library
+    (c2kv_attn_decode_noalloc): the split partials live in the library's
+    static per-GPU scratch.  With `out` (and `lse_out`) given, nothing is
+    allocated here either.  Calls that overlap in time on one GPU race."""
+    lib = load()
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (cache_k, "cache_k"), (cache_v, "cache_v")):
+        _dev_tensor(t, nm, cache_k.dtype)
+    R, hkv, cap, d = cache_k.shape
+    hq = q.shape[-2]
+    _need(len(cache_len) == R and len(q_pos) == R, "cache_len/q_pos need one entry per request")
+    _need(q.shape == (R, hq, d) and k_new.shape == (R, hkv, d) and v_new.shape == k_new.shape, "decode shapes")
+    o = out if out is not None else torch.empty_like(q)
+    _dev_tensor(o, "out", q.dtype)
+    lse = lse_out
+    if return_lse and lse is None:
+        lse = torch.empty((R, hq), dtype=torch.float32, device=q.device)
+    check(lib.c2kv_attn_decode_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cache_k), _ptr(cache_v), cap,
+                                       _arr_i32(cache_len), _arr_i32(q_pos), R, hq, hkv, d, float(rope_theta),
+                                       _ptr(o), _ptr(lse), _DT[cache_k.dtype], _stream(q.device)))
+    return o, lse
+
+
 # ----------------------------------------------------------------- testing
 
 def mask_cells(doc_lens: Sequence[int], ratio_k: int, sink_len: Optional[int] = None,

@@ -381,6 +381,27 @@ c2kv_status c2kv_attn_decode(const void* q, const void* k_new, const void* v_new
                              void* o, float* lse, c2kv_dtype dt,
                              void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* One decode step exactly as c2kv_attn_decode, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation): the split-K partials live in a static
+ * device array of C2KV_NOALLOC_SCRATCH_BYTES bytes per GPU, held until the
+ * process ends, instead of a caller workspace.  Arguments, layouts, results
+ * and errors as c2kv_attn_decode without workspace / ws_bytes.  The array's
+ * address is looked up once per device, on the first call there.  Every call
+ * on one GPU shares that GPU's array, which keeps the last call's partials:
+ * calls that overlap in time on one GPU (on different streams, or from
+ * several threads without ordering) race, and the caller must order them.
+ * Nothing in the array needs clearing between calls.  Allocates nothing.
+ * Errors: as c2kv_attn_decode, plus WORKSPACE when the step's split
+ * partials (c2kv_workspace_size_decode) exceed the array. */
+#define C2KV_NOALLOC_SCRATCH_BYTES (8u << 20)
+c2kv_status c2kv_attn_decode_noalloc(const void* q, const void* k_new, const void* v_new,
+                                     void* cache_k, void* cache_v, int64_t cap,
+                                     const int32_t* cache_len, const int32_t* q_pos,
+                                     int32_t num_reqs, int32_t hq, int32_t hkv,
+                                     int32_t head_dim, float rope_theta,
+                                     void* o, float* lse, c2kv_dtype dt, hipStream_t stream);
+
 /* Zero `ws_bytes` (a multiple of 4) bytes of device memory with a fill
  * kernel on `stream` (no hipMemset, so it may be captured in a graph).  No
  * entry point requires a zeroed workspace; this is a convenience. */
