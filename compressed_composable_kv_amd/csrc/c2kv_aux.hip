@@ -140,6 +140,12 @@ hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipSt
 // position.  Workgroups loop over units with the next unit's loads issued
 // before the current unit's rotation and stores, so reads and writes of
 // the cache stream overlap.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ void store_nt(T* dst, const uint4& v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(dst));
+}
+
 template <typename T, int D>
 struct ComposeUnit {
   static constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE;
@@ -195,10 +201,12 @@ struct ComposeUnit {
       const int64_t dst = (((int64_t)sg.req * p.hkv + h) * p.cap + sg.out_row + j) * D + c * CE;
       T* kd = reinterpret_cast<T*>(p.cache_k) + dst;
       T* vd = reinterpret_cast<T*>(p.cache_v) + dst;
-      *reinterpret_cast<uint4*>(kd) = kl;
-      *reinterpret_cast<uint4*>(kd + H) = kh;
-      *reinterpret_cast<uint4*>(vd) = vl;
-      *reinterpret_cast<uint4*>(vd + H) = vh;
+      // the composed cache is written once and read by later calls:
+      // streaming (non-temporal) stores
+      store_nt(kd, kl);
+      store_nt(kd + H, kh);
+      store_nt(vd, vl);
+      store_nt(vd + H, vh);
     };
     put(h0, kl0, kh0, vl0, vh0);
     if (h0 + 1 < p.hkv) put(h0 + 1, kl1, kh1, vl1, vh1);

