@@ -282,9 +282,9 @@ def free(torch):
 
 def achievable_peaks(torch, dev):
     """Rates this GPU sustains, measured live: dense bf16 MFMA from the probe
-    library (independent MFMA chains on register operands), a streaming read
-    of 4 GiB (probe library: read bytes per second, the ceiling for
-    read-dominated kernels such as decode), and a 1 GiB device copy (read +
+    library (independent MFMA chains on register operands), a non-temporal
+    streaming read of 16 GiB (probe library: read bytes per second, the
+    ceiling for read-dominated kernels such as decode), and a 1 GiB device copy (read +
     write bytes per second).  They sit below the published peaks because the
     chip holds a lower clock under sustained load than its nominal 2.4 GHz,
     and HBM never delivers its full pin rate."""
@@ -302,9 +302,9 @@ def achievable_peaks(torch, dev):
         lib.c2kv_probe_hbm_read.restype = ctypes.c_double
         lib.c2kv_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
-        buf = torch.ones(4 << 30, dtype=torch.uint8, device=dev)
-        out = torch.empty(4 * 256 * 8192, dtype=torch.uint8, device=dev)
-        for blocks in (2048, 4096, 8192):
+        buf = torch.ones(16 << 30, dtype=torch.uint8, device=dev)
+        out = torch.empty(4 * 256 * 16384, dtype=torch.uint8, device=dev)
+        for blocks in (4096, 8192, 16384):
             r = lib.c2kv_probe_hbm_read(buf.data_ptr(), buf.numel(), out.data_ptr(), out.numel(), blocks, 5,
                                         ctypes.byref(ms))
             if r > 0 and (read is None or r > read):
@@ -328,7 +328,7 @@ def achievable_peaks(torch, dev):
     free(torch)
     return {"mfma_bf16_tflops": mfma, "hbm_read_gbs": read, "hbm_copy_gbs": 2 * 2 * n / (best * 1e-3) / 1e9,
             "how": "MFMA: probe/mfma_peak.hip, 512 workgroups x 8 waves, 16 independent chains per wave; "
-                   f"HBM read: probe/hbm_read.hip streaming 4 GiB ({read_blocks} workgroups), best of 5; "
+                   f"HBM read: probe/hbm_read.hip, non-temporal streaming read of 16 GiB ({read_blocks} workgroups), best of 5; "
                    "copy: torch copy of 1 GiB, read + write bytes, best of 3"}
 
 
