@@ -534,37 +534,66 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
   const ComposeTiling tl = compose_tiling((int)elem_bytes(dt), head_dim, hkv);
   const int rpt = tl.rpt;
   p.rpt = tl.rpt; p.gpb = tl.gpb; p.nblk = tl.nblk;
-  int cnt = 0;
+  int ndocs = 0, nocc = 0, nruns = 0;
   int32_t tiles = 0;
+  int32_t open_req = -1;      // request of the run being filled (-1: none)
   bool host_pass = false;
   auto flush = [&]() -> hipError_t {
-    if (cnt == 0) return hipSuccess;
-    p.num_segs = cnt;
+    if (nocc == 0) return hipSuccess;
+    p.num_occ = nocc;
+    p.num_runs = nruns;
+    p.run_occ0[nruns] = (uint16_t)nocc;
     p.total_tiles = tiles;
     hipError_t e = launch_compose(p, dt, head_dim, host_pass, stream);
-    cnt = 0;
+    ndocs = nocc = nruns = 0;
     tiles = 0;
+    open_req = -1;
     return e;
   };
-  // device segments first, then host-resident ones in launches of their own
+  auto doc_index = [&](const c2kv_segment& g) -> int {
+    for (int i = 0; i < ndocs; ++i) {
+      const ComposeDoc& d = p.docs[i];
+      if (d.k == g.k && d.v == g.v && d.stride == (int32_t)g.row_stride && d.n == g.doc_len) return i;
+    }
+    return -1;
+  };
+  // device segments first, then host-resident ones in launches of their own;
+  // a run is broken wherever a segment of the other kind (or of another
+  // launch) intervenes, so rows and positions advance only inside a run
   for (int pass = 0; pass < 2; ++pass) {
     host_pass = pass == 1;
     for (int32_t r = 0; r < num_reqs; ++r) {
       int32_t out_row = 0;
       int64_t pos = pos_base ? pos_base[r] : 0;
+      open_req = -1;
       for (int32_t t = req_seg_ptr[r]; t < req_seg_ptr[r + 1]; ++t) {
         const c2kv_segment& g = segs[t];
         const int32_t m = num_slots_i(g.doc_len, ratio_k);
         const int32_t mt = (m + rpt - 1) / rpt;
-        if (((g.flags & C2KV_SEGMENT_HOST) != 0) == host_pass) {
-          if (cnt == kComposeSegs || (int64_t)tiles + mt >= ((int64_t)1 << 24)) {
+        if (((g.flags & C2KV_SEGMENT_HOST) != 0) != host_pass) {
+          open_req = -1;
+        } else {
+          int di = doc_index(g);
+          if (nocc == kComposeOcc || (di < 0 && ndocs == kComposeDocs) ||
+              (open_req != r && nruns == kComposeRuns) || (int64_t)tiles + mt >= ((int64_t)1 << 24)) {
             hipError_t e = flush();
             if (e != hipSuccess) return hip_fail(e, "compose kernel launch");
+            di = -1;
           }
-          ComposeSeg& d = p.segs[cnt++];
-          d.k = g.k; d.v = g.v; d.stride = (int32_t)g.row_stride; d.n = g.doc_len;
-          d.req = r; d.out_row = out_row; d.tile0 = tiles;
-          d.pos_off = (int32_t)((g.flags & C2KV_SEGMENT_NO_REALIGN) ? (pos_base ? pos_base[r] : 0) : pos);
+          if (di < 0) {
+            di = ndocs++;
+            p.docs[di] = ComposeDoc{g.k, g.v, (int32_t)g.row_stride, g.doc_len};
+          }
+          if (open_req != r) {
+            p.run_req[nruns] = r;
+            p.run_row0[nruns] = out_row;
+            p.run_pos0[nruns] = (int32_t)pos;
+            p.run_base[nruns] = pos_base ? pos_base[r] : 0;
+            p.run_occ0[nruns] = (uint16_t)nocc;
+            ++nruns;
+            open_req = r;
+          }
+          p.occ_doc[nocc++] = (uint8_t)(di | ((g.flags & C2KV_SEGMENT_NO_REALIGN) ? kComposeNoRealign : 0));
           tiles += mt;
         }
         out_row += m;

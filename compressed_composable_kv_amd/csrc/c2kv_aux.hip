@@ -129,21 +129,113 @@ hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipSt
 }
 
 // ---------------------------------------------------------------- compose
-// Work unit = (row tile of ONE segment, block of gpb pairs of KV heads; see
-// ComposeTiling); a thread owns one 16-byte chunk of the low half of a row
-// (and the matching chunk of the high half) of one head pair and rotates it
-// for both heads with one set of cos/sin.  Consecutive threads take the
-// chunks, then the head pairs, then the rows, so a unit reads whole source
-// rows (all heads of a slot row are contiguous).  The
-// unit's segment is found by a uniform search of the segment table; its
-// realigned position is the document offset plus the slot's extraction
-// position.  Workgroups loop over units with the next unit's loads issued
-// before the current unit's rotation and stores, so reads and writes of
-// the cache stream overlap.
+// Work unit = (row tile of ONE document occurrence, block of gpb pairs of KV
+// heads; see ComposeTiling); a thread owns one 16-byte chunk of the low half
+// of a row (and the matching chunk of the high half) of one head pair and
+// rotates it for both heads with one set of cos/sin.  Consecutive threads
+// take the chunks, then the head pairs, then the rows, so a unit reads whole
+// source rows (all heads of a slot row are contiguous).  Each workgroup
+// first rebuilds the occurrence table in LDS (first row tile, cache row and
+// position offset of every occurrence, by prefix sums over the launch
+// table); a unit finds its occurrence by a binary search over the first
+// tiles.  The realigned position of slot j is the occurrence's offset plus
+// the slot's extraction position.  Workgroups loop over units with the next
+// unit's loads issued before the current unit's rotation and stores, so
+// reads and writes of the cache stream overlap.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <typename T>
 __device__ __forceinline__ void store_nt(T* dst, const uint4& v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(dst));
+}
+
+struct ComposeOccTable {
+  int tile0[kComposeOcc + 1];   // first row tile of each occurrence; [num_occ] = total tiles
+  int row[kComposeOcc];         // cache row of the occurrence's slot 0
+  int pos[kComposeOcc];         // position offset of the occurrence
+  int req[kComposeOcc];         // request (global index)
+  long long scan_n[kComposeOcc];   // global exclusive prefix of original lengths
+  int scan_m[kComposeOcc];         // global exclusive prefix of slot counts
+  long long wsum_n[4];
+  int wsum_t[4], wsum_m[4];
+};
+
+// Inclusive scan over the 64 lanes of a wave.
+template <typename X>
+__device__ __forceinline__ X wave_incl_scan(X x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const X y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ void compose_build_table(const ComposeParams& p, ComposeOccTable& tb) {
+  constexpr int PER = kComposeOcc / 256;   // occurrences per thread
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int tl[PER], ml[PER], rl[PER];
+  long long nl[PER];
+  int st = 0, sm = 0;
+  long long sn = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int o = PER * t + i;
+    tl[i] = ml[i] = 0;
+    nl[i] = 0;
+    rl[i] = 0;
+    if (o < p.num_occ) {
+      const ComposeDoc& dc = p.docs[p.occ_doc[o] & (kComposeNoRealign - 1)];
+      const int m = (dc.n + p.ratio_k - 1) / p.ratio_k;
+      ml[i] = m;
+      tl[i] = (m + p.rpt - 1) / p.rpt;
+      nl[i] = dc.n;
+      int lo = 0, hi = p.num_runs - 1;          // run of the occurrence
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int)p.run_occ0[mid] <= o) lo = mid; else hi = mid - 1;
+      }
+      rl[i] = lo;
+    }
+    st += tl[i];
+    sm += ml[i];
+    sn += nl[i];
+  }
+  // exclusive prefixes of the per-thread sums across the workgroup
+  const int it = wave_incl_scan(st), im = wave_incl_scan(sm);
+  const long long in_ = wave_incl_scan(sn);
+  if (lane == 63) { tb.wsum_t[wave] = it; tb.wsum_m[wave] = im; tb.wsum_n[wave] = in_; }
+  __syncthreads();
+  int bt = it - st, bm = im - sm;
+  long long bn = in_ - sn;
+  for (int w = 0; w < wave; ++w) { bt += tb.wsum_t[w]; bm += tb.wsum_m[w]; bn += tb.wsum_n[w]; }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int o = PER * t + i;
+    if (o < p.num_occ) {
+      tb.tile0[o] = bt;
+      tb.scan_m[o] = bm;
+      tb.scan_n[o] = bn;
+    }
+    bt += tl[i];
+    bm += ml[i];
+    bn += nl[i];
+  }
+  if (t == 255) tb.tile0[p.num_occ] = bt;   // every thread's bt ends at the grand total
+  __syncthreads();
+  // cache rows and position offsets relative to the start of each run
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int o = PER * t + i;
+    if (o < p.num_occ) {
+      const int r = rl[i], f = p.run_occ0[r];
+      tb.row[o] = p.run_row0[r] + (tb.scan_m[o] - tb.scan_m[f]);
+      tb.pos[o] = (p.occ_doc[o] & kComposeNoRealign) ? p.run_base[r]
+                                                     : p.run_pos0[r] + (int)(tb.scan_n[o] - tb.scan_n[f]);
+      tb.req[o] = p.run_req[r];
+    }
+  }
+  __syncthreads();
 }
 
 template <typename T, int D>
@@ -151,33 +243,33 @@ struct ComposeUnit {
   static constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE;
   uint4 kl0, kh0, vl0, vh0, kl1, kh1, vl1, vh1;
   float fr[CE];
-  int seg, j, c, h0, cpos;
+  int occ, j, c, h0, cpos;
   bool live;
 
-  __device__ __forceinline__ void load(const ComposeParams& p, int u) {
+  __device__ __forceinline__ void load(const ComposeParams& p, const ComposeOccTable& tb, int u) {
     const int tile = u / p.nblk, blk = u % p.nblk;
     const int t = (int)threadIdx.x;
     const int hgrp = blk * p.gpb + (t / TPH) % p.gpb;
-    int lo_s = 0, hi_s = p.num_segs - 1;
-    while (lo_s < hi_s) {
-      const int mid = (lo_s + hi_s + 1) >> 1;
-      if (p.segs[mid].tile0 <= tile) lo_s = mid; else hi_s = mid - 1;
+    int lo = 0, hi = p.num_occ - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tb.tile0[mid] <= tile) lo = mid; else hi = mid - 1;
     }
-    seg = lo_s;
-    const ComposeSeg& sg = p.segs[seg];
-    const int m = (sg.n + p.ratio_k - 1) / p.ratio_k;
-    j = (tile - sg.tile0) * p.rpt + t / (TPH * p.gpb);
+    occ = __builtin_amdgcn_readfirstlane(lo);   // uniform: every lane searched for the same tile
+    const ComposeDoc& dc = p.docs[p.occ_doc[occ] & (kComposeNoRealign - 1)];
+    const int m = (dc.n + p.ratio_k - 1) / p.ratio_k;
+    j = (tile - tb.tile0[occ]) * p.rpt + t / (TPH * p.gpb);
     c = t % TPH;
     live = j < m && 2 * hgrp < p.hkv;   // padded head pairs load a valid head and store nothing
     const int jj = live ? j : m - 1;     // dead lanes load a valid row
-    cpos = sg.pos_off + min(jj * p.ratio_k + p.ratio_k - 1, sg.n - 1);
+    cpos = tb.pos[occ] + min(jj * p.ratio_k + p.ratio_k - 1, dc.n - 1);
 #pragma unroll
     for (int e = 0; e < CE; e += 4) {
       const f32x4 f4 = *reinterpret_cast<const f32x4*>(&p.freqs.f[c * CE + e]);
       fr[e] = f4[0]; fr[e + 1] = f4[1]; fr[e + 2] = f4[2]; fr[e + 3] = f4[3];
     }
-    const T* ksrc = reinterpret_cast<const T*>(sg.k) + (int64_t)jj * sg.stride + c * CE;
-    const T* vsrc = reinterpret_cast<const T*>(sg.v) + (int64_t)jj * sg.stride + c * CE;
+    const T* ksrc = reinterpret_cast<const T*>(dc.k) + (int64_t)jj * dc.stride + c * CE;
+    const T* vsrc = reinterpret_cast<const T*>(dc.v) + (int64_t)jj * dc.stride + c * CE;
     h0 = min(hgrp * 2, p.hkv - 1);
     const int h1 = min(h0 + 1, p.hkv - 1);
     kl0 = *reinterpret_cast<const uint4*>(ksrc + h0 * D);
@@ -190,15 +282,15 @@ struct ComposeUnit {
     vh1 = *reinterpret_cast<const uint4*>(vsrc + h1 * D + H);
   }
 
-  __device__ __forceinline__ void store(const ComposeParams& p) {
+  __device__ __forceinline__ void store(const ComposeParams& p, const ComposeOccTable& tb) {
     if (!live) return;
-    const ComposeSeg& sg = p.segs[seg];
+    const int req = tb.req[occ], row0 = tb.row[occ];
     float cs[CE], sn[CE];
 #pragma unroll
     for (int e = 0; e < CE; ++e) rope_cs(cpos, fr[e], cs[e], sn[e]);
     auto put = [&](int h, uint4 kl, uint4 kh, const uint4& vl, const uint4& vh) {
       rotate_chunk<T>(kl, kh, cs, sn);
-      const int64_t dst = (((int64_t)sg.req * p.hkv + h) * p.cap + sg.out_row + j) * D + c * CE;
+      const int64_t dst = (((int64_t)req * p.hkv + h) * p.cap + row0 + j) * D + c * CE;
       T* kd = reinterpret_cast<T*>(p.cache_k) + dst;
       T* vd = reinterpret_cast<T*>(p.cache_v) + dst;
       // the composed cache is written once and read by later calls:
@@ -210,22 +302,24 @@ struct ComposeUnit {
     };
     put(h0, kl0, kh0, vl0, vh0);
     if (h0 + 1 < p.hkv) put(h0 + 1, kl1, kh1, vl1, vh1);
-    if (p.pos_out && h0 == 0 && c == 0) p.pos_out[(int64_t)sg.req * p.cap + sg.out_row + j] = cpos;
+    if (p.pos_out && h0 == 0 && c == 0) p.pos_out[(int64_t)req * p.cap + row0 + j] = cpos;
   }
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void compose_kernel(const ComposeParams p) {
   static_assert(kComposeHPT == 2, "two heads per thread");
+  __shared__ ComposeOccTable tb;
   const int total = p.total_tiles * p.nblk;
   int u = blockIdx.x;
   if (u >= total) return;
+  compose_build_table(p, tb);
   ComposeUnit<T, D> cur, nxt;
-  cur.load(p, u);
+  cur.load(p, tb, u);
   for (; u < total; u += gridDim.x) {
     const bool more = u + (int)gridDim.x < total;
-    if (more) nxt.load(p, u + gridDim.x);
-    cur.store(p);
+    if (more) nxt.load(p, tb, u + gridDim.x);
+    cur.store(p, tb);
     if (!more) break;
     cur = nxt;
   }

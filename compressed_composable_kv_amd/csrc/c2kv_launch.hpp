@@ -22,29 +22,40 @@ struct RotateParams {
   RotDoc docs[C2KV_MAX_BATCH];
 };
 
-// One document segment of a compose launch (passed as a kernel argument).
-struct ComposeSeg {
+// Compose launch table (kernel arguments, no device-side table): the
+// distinct documents of the launch once, each occurrence of a document in a
+// request as a one-byte index, and "runs" -- maximal sequences of
+// consecutive segments of one request that go to the launch.  The kernel
+// rebuilds every occurrence's first row tile, cache row and position offset
+// with prefix sums over the occurrences (cache rows and positions advance by
+// each document's slot count and original length within a run).
+struct ComposeDoc {
   const void* k;
   const void* v;
   int32_t stride;      // elements between slot rows
   int32_t n;           // original document length
-  int32_t req;         // request index
-  int32_t out_row;     // first cache row of this segment
-  int32_t pos_off;     // position offset of the document
-  int32_t tile0;       // first row tile of this segment within the launch
 };
-constexpr int kComposeSegs = 64;   // segments per launch (kernel-argument table)
-constexpr int kComposeHPT = 2;     // KV heads per thread
+constexpr int kComposeDocs = 64;     // distinct documents per launch
+constexpr int kComposeOcc = 1024;    // document occurrences per launch
+constexpr int kComposeRuns = 64;     // runs per launch
+constexpr int kComposeNoRealign = 0x80;   // occurrence flag: keep extraction positions (offset = pos_base)
+constexpr int kComposeHPT = 2;       // KV heads per thread
 
 struct ComposeParams {
   void* cache_k;
   void* cache_v;
   int32_t* pos_out;
   int64_t cap;
-  int32_t num_segs, hkv, ratio_k, total_tiles;
+  int32_t num_occ, num_runs, hkv, ratio_k, total_tiles;
   int32_t rpt, gpb, nblk;   // rows per tile, head pairs per unit, units per tile (ComposeTiling)
   RopeFreqs freqs;
-  ComposeSeg segs[kComposeSegs];
+  ComposeDoc docs[kComposeDocs];
+  int32_t run_req[kComposeRuns];    // request of the run
+  int32_t run_row0[kComposeRuns];   // cache row of the run's first occurrence
+  int32_t run_pos0[kComposeRuns];   // realigned position offset of the run's first occurrence
+  int32_t run_base[kComposeRuns];   // pos_base of the run's request (offset without realignment)
+  uint16_t run_occ0[kComposeRuns + 1];   // first occurrence of each run; [num_runs] = num_occ
+  uint8_t occ_doc[kComposeOcc];     // document index | kComposeNoRealign
 };
 static_assert(sizeof(ComposeParams) <= 4096, "compose table must fit the kernel arguments");
 

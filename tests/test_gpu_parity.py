@@ -157,6 +157,20 @@ def test_compose_multi_request_ragged(c2kv, dt):
     _compose_check(c2kv, reqs, pool_k, pool_v, pool_n, k, 1e6, dt, pos_base=[0, 5, 100000, 3, 0], cap_extra=3)
 
 
+def test_compose_launch_table_limits(c2kv):
+    """More document occurrences (1120), requests (70) and distinct
+    documents (80) than one compose launch's table holds, with documents
+    repeated within and across requests: the table is cut into several
+    launches, each rebuilding cache rows and positions from its runs."""
+    g = torch.Generator().manual_seed(71)
+    pool_n = [int(x) for x in torch.randint(1, 60, (80,), generator=g)]
+    k, hkv, d, dt = 4, 2, 64, torch.bfloat16
+    pool_k = [W.normal((O.num_slots(n, k), hkv, d), dt, 71, W.P_K, salt=i) for i, n in enumerate(pool_n)]
+    pool_v = [W.normal((O.num_slots(n, k), hkv, d), dt, 71, W.P_V, salt=i) for i, n in enumerate(pool_n)]
+    reqs = [[int(x) for x in torch.randint(0, 80, (16,), generator=g)] for _ in range(70)]
+    _compose_check(c2kv, reqs, pool_k, pool_v, pool_n, k, 1e4, dt, pos_base=[3 * r for r in range(70)], cap_extra=1)
+
+
 @pytest.mark.parametrize("hkv,d,dt", [(5, 64, torch.float32), (6, 128, torch.bfloat16), (80, 128, torch.bfloat16)])
 def test_compose_head_counts(c2kv, hkv, d, dt):
     """Head counts whose pairs do not fill a power of two (a workgroup's
