@@ -538,16 +538,23 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
   int32_t tiles = 0;
   int32_t open_req = -1;      // request of the run being filled (-1: none)
   bool host_pass = false;
+  std::vector<int32_t> doc_cnt(kComposeDocs, 0);
   auto flush = [&]() -> hipError_t {
     if (nocc == 0) return hipSuccess;
+    p.num_docs = ndocs;
     p.num_occ = nocc;
     p.num_runs = nruns;
     p.run_occ0[nruns] = (uint16_t)nocc;
-    p.total_tiles = tiles;
+    // units: row tiles x head blocks x occurrence groups of each document
+    int64_t units = 0;
+    for (int d = 0; d < ndocs; ++d)
+      units += ceil_div(num_slots_i(p.docs[d].n, ratio_k), rpt) * tl.nblk * ceil_div(doc_cnt[d], kComposeGroup);
+    p.total_units = (int32_t)units;
     hipError_t e = launch_compose(p, dt, head_dim, host_pass, stream);
     ndocs = nocc = nruns = 0;
     tiles = 0;
     open_req = -1;
+    std::fill(doc_cnt.begin(), doc_cnt.end(), 0);
     return e;
   };
   auto doc_index = [&](const c2kv_segment& g) -> int {
@@ -594,6 +601,7 @@ c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs, const int32
             open_req = r;
           }
           p.occ_doc[nocc++] = (uint8_t)(di | ((g.flags & C2KV_SEGMENT_NO_REALIGN) ? kComposeNoRealign : 0));
+          ++doc_cnt[di];
           tiles += mt;
         }
         out_row += m;

@@ -129,34 +129,41 @@ hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipSt
 }
 
 // ---------------------------------------------------------------- compose
-// Work unit = (row tile of ONE document occurrence, block of gpb pairs of KV
-// heads; see ComposeTiling); a thread owns one 16-byte chunk of the low half
-// of a row (and the matching chunk of the high half) of one head pair and
-// rotates it for both heads with one set of cos/sin.  Consecutive threads
-// take the chunks, then the head pairs, then the rows, so a unit reads whole
-// source rows (all heads of a slot row are contiguous).  Each workgroup
-// first rebuilds the occurrence table in LDS (first row tile, cache row and
-// position offset of every occurrence, by prefix sums over the launch
-// table); a unit finds its occurrence by a binary search over the first
-// tiles.  The realigned position of slot j is the occurrence's offset plus
-// the slot's extraction position.  Workgroups loop over units with the next
-// unit's loads issued before the current unit's rotation and stores, so
-// reads and writes of the cache stream overlap.
+// Work unit = (row tile of one DOCUMENT of the launch, block of gpb pairs of
+// KV heads (see ComposeTiling), group of up to kComposeGroup occurrences of
+// that document).  A thread owns one 16-byte chunk of the low half of a row
+// (and the matching chunk of the high half) of one head pair: it loads the
+// document's pre-RoPE rows once and, for every occurrence of the group,
+// rotates the keys at that occurrence's realigned positions and writes keys
+// and values to that occurrence's cache rows.  A document reused by several
+// requests is therefore read once per group instead of once per request,
+// and the cache writes dominate the traffic.  Consecutive threads take the
+// chunks, then the head pairs, then the rows, so a unit reads whole source
+// rows.  Each workgroup first rebuilds the launch's tables in LDS (cache row
+// and position offset of every occurrence by prefix sums over the runs; the
+// occurrences of each document; the units of each document); a unit finds
+// its document by a binary search over the documents' first units.  The
+// realigned position of slot j of an occurrence is the occurrence's offset
+// plus the slot's extraction position.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <typename T>
 __device__ __forceinline__ void store_nt(T* dst, const uint4& v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(dst));
 }
 
-struct ComposeOccTable {
-  int tile0[kComposeOcc + 1];   // first row tile of each occurrence; [num_occ] = total tiles
+struct ComposeTable {
   int row[kComposeOcc];         // cache row of the occurrence's slot 0
   int pos[kComposeOcc];         // position offset of the occurrence
   int req[kComposeOcc];         // request (global index)
   long long scan_n[kComposeOcc];   // global exclusive prefix of original lengths
   int scan_m[kComposeOcc];         // global exclusive prefix of slot counts
+  short by_doc[kComposeOcc];    // occurrences grouped by document, in occurrence order
+  short rank[kComposeOcc];      // rank of the occurrence among those of its document
+  int doc_occ0[kComposeDocs + 1];   // first entry of each document in by_doc
+  int doc_unit0[kComposeDocs + 1];  // first unit of each document; [num_docs] = total units
+  int doc_cnt[kComposeDocs];
   long long wsum_n[4];
-  int wsum_t[4], wsum_m[4];
+  int wsum_m[4];
 };
 
 // Inclusive scan over the 64 lanes of a wave.
@@ -171,25 +178,26 @@ __device__ __forceinline__ X wave_incl_scan(X x) {
   return x;
 }
 
-__device__ void compose_build_table(const ComposeParams& p, ComposeOccTable& tb) {
+__device__ void compose_build_table(const ComposeParams& p, ComposeTable& tb) {
   constexpr int PER = kComposeOcc / 256;   // occurrences per thread
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  int tl[PER], ml[PER], rl[PER];
+  if (t < kComposeDocs) tb.doc_cnt[t] = 0;
+  int ml[PER], rl[PER], dl[PER];
   long long nl[PER];
-  int st = 0, sm = 0;
+  int sm = 0;
   long long sn = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int o = PER * t + i;
-    tl[i] = ml[i] = 0;
+    ml[i] = 0;
     nl[i] = 0;
     rl[i] = 0;
+    dl[i] = 0;
     if (o < p.num_occ) {
-      const ComposeDoc& dc = p.docs[p.occ_doc[o] & (kComposeNoRealign - 1)];
-      const int m = (dc.n + p.ratio_k - 1) / p.ratio_k;
-      ml[i] = m;
-      tl[i] = (m + p.rpt - 1) / p.rpt;
-      nl[i] = dc.n;
+      dl[i] = p.occ_doc[o] & (kComposeNoRealign - 1);
+      const int n = p.docs[dl[i]].n;
+      ml[i] = (n + p.ratio_k - 1) / p.ratio_k;
+      nl[i] = n;
       int lo = 0, hi = p.num_runs - 1;          // run of the occurrence
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -197,33 +205,74 @@ __device__ void compose_build_table(const ComposeParams& p, ComposeOccTable& tb)
       }
       rl[i] = lo;
     }
-    st += tl[i];
     sm += ml[i];
     sn += nl[i];
   }
   // exclusive prefixes of the per-thread sums across the workgroup
-  const int it = wave_incl_scan(st), im = wave_incl_scan(sm);
+  const int im = wave_incl_scan(sm);
   const long long in_ = wave_incl_scan(sn);
-  if (lane == 63) { tb.wsum_t[wave] = it; tb.wsum_m[wave] = im; tb.wsum_n[wave] = in_; }
+  if (lane == 63) { tb.wsum_m[wave] = im; tb.wsum_n[wave] = in_; }
   __syncthreads();
-  int bt = it - st, bm = im - sm;
+  int bm = im - sm;
   long long bn = in_ - sn;
-  for (int w = 0; w < wave; ++w) { bt += tb.wsum_t[w]; bm += tb.wsum_m[w]; bn += tb.wsum_n[w]; }
+  for (int w = 0; w < wave; ++w) { bm += tb.wsum_m[w]; bn += tb.wsum_n[w]; }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int o = PER * t + i;
     if (o < p.num_occ) {
-      tb.tile0[o] = bt;
       tb.scan_m[o] = bm;
       tb.scan_n[o] = bn;
     }
-    bt += tl[i];
     bm += ml[i];
     bn += nl[i];
   }
-  if (t == 255) tb.tile0[p.num_occ] = bt;   // every thread's bt ends at the grand total
+  // stable rank of every occurrence among those of its document, so that
+  // every workgroup groups the occurrences identically: wave 0 walks them 64
+  // at a time; lanes holding the same document find each other by comparing
+  // the document index bit by bit through ballots, and the highest such lane
+  // advances the document's running count
+  if (wave == 0) {
+    for (int c0 = 0; c0 < p.num_occ; c0 += 64) {
+      const int o = c0 + lane;
+      const bool valid = o < p.num_occ;
+      const int dd = valid ? (p.occ_doc[o] & (kComposeNoRealign - 1)) : kComposeNoRealign - 1;
+      uint64_t same = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 7; ++b) {
+        const bool bit = (dd >> b) & 1;
+        const uint64_t mb = __ballot(bit);
+        same &= bit ? mb : ~mb;
+      }
+      const int below = __popcll(same & ((1ull << lane) - 1));
+      const int base = valid ? tb.doc_cnt[dd] : 0;
+      __builtin_amdgcn_wave_barrier();   // every lane has read its base before any lane updates it
+      if (valid) {
+        tb.rank[o] = (short)(base + below);
+        if ((same >> lane) == 1ull) tb.doc_cnt[dd] = base + __popcll(same);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
   __syncthreads();
-  // cache rows and position offsets relative to the start of each run
+  // per document: first by_doc entry and first unit (sequential over <= 64 documents)
+  if (t == 0) {
+    int occ0 = 0, unit0 = 0;
+    for (int d = 0; d < p.num_docs; ++d) {
+      tb.doc_occ0[d] = occ0;
+      tb.doc_unit0[d] = unit0;
+      const int m = (p.docs[d].n + p.ratio_k - 1) / p.ratio_k;
+      const int c = tb.doc_cnt[d];
+      occ0 += c;
+      unit0 += ((m + p.rpt - 1) / p.rpt) * p.nblk * ((c + kComposeGroup - 1) / kComposeGroup);
+    }
+    tb.doc_occ0[p.num_docs] = occ0;
+    tb.doc_unit0[p.num_docs] = unit0;
+  }
+  __syncthreads();
+  // cache rows and position offsets relative to the start of each run; the
+  // occurrence lists of the documents
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int o = PER * t + i;
@@ -233,6 +282,7 @@ __device__ void compose_build_table(const ComposeParams& p, ComposeOccTable& tb)
       tb.pos[o] = (p.occ_doc[o] & kComposeNoRealign) ? p.run_base[r]
                                                      : p.run_pos0[r] + (int)(tb.scan_n[o] - tb.scan_n[f]);
       tb.req[o] = p.run_req[r];
+      tb.by_doc[tb.doc_occ0[dl[i]] + tb.rank[o]] = (short)o;
     }
   }
   __syncthreads();
@@ -243,26 +293,32 @@ struct ComposeUnit {
   static constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE;
   uint4 kl0, kh0, vl0, vh0, kl1, kh1, vl1, vh1;
   float fr[CE];
-  int occ, j, c, h0, cpos;
+  int doc, g0, g1, j, c, h0, spos;
   bool live;
 
-  __device__ __forceinline__ void load(const ComposeParams& p, const ComposeOccTable& tb, int u) {
-    const int tile = u / p.nblk, blk = u % p.nblk;
+  __device__ __forceinline__ void load(const ComposeParams& p, const ComposeTable& tb, int u) {
     const int t = (int)threadIdx.x;
-    const int hgrp = blk * p.gpb + (t / TPH) % p.gpb;
-    int lo = 0, hi = p.num_occ - 1;
+    int lo = 0, hi = p.num_docs - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (tb.tile0[mid] <= tile) lo = mid; else hi = mid - 1;
+      if (tb.doc_unit0[mid] <= u) lo = mid; else hi = mid - 1;
     }
-    occ = __builtin_amdgcn_readfirstlane(lo);   // uniform: every lane searched for the same tile
-    const ComposeDoc& dc = p.docs[p.occ_doc[occ] & (kComposeNoRealign - 1)];
+    doc = __builtin_amdgcn_readfirstlane(lo);   // uniform: every lane searched for the same unit
+    const ComposeDoc& dc = p.docs[doc];
     const int m = (dc.n + p.ratio_k - 1) / p.ratio_k;
-    j = (tile - tb.tile0[occ]) * p.rpt + t / (TPH * p.gpb);
+    const int cnt = tb.doc_cnt[doc];
+    const int ngrp = (cnt + kComposeGroup - 1) / kComposeGroup;
+    const int local = u - tb.doc_unit0[doc];
+    const int grp = local % ngrp, rest = local / ngrp;   // groups of one tile run back to back
+    const int tile = rest / p.nblk, blk = rest % p.nblk;
+    g0 = tb.doc_occ0[doc] + grp * kComposeGroup;
+    g1 = min(g0 + kComposeGroup, tb.doc_occ0[doc] + cnt);
+    const int hgrp = blk * p.gpb + (t / TPH) % p.gpb;
+    j = tile * p.rpt + t / (TPH * p.gpb);
     c = t % TPH;
     live = j < m && 2 * hgrp < p.hkv;   // padded head pairs load a valid head and store nothing
     const int jj = live ? j : m - 1;     // dead lanes load a valid row
-    cpos = tb.pos[occ] + min(jj * p.ratio_k + p.ratio_k - 1, dc.n - 1);
+    spos = min(jj * p.ratio_k + p.ratio_k - 1, dc.n - 1);
 #pragma unroll
     for (int e = 0; e < CE; e += 4) {
       const f32x4 f4 = *reinterpret_cast<const f32x4*>(&p.freqs.f[c * CE + e]);
@@ -282,52 +338,55 @@ struct ComposeUnit {
     vh1 = *reinterpret_cast<const uint4*>(vsrc + h1 * D + H);
   }
 
-  __device__ __forceinline__ void store(const ComposeParams& p, const ComposeOccTable& tb) {
+  __device__ __forceinline__ void store(const ComposeParams& p, const ComposeTable& tb) {
     if (!live) return;
-    const int req = tb.req[occ], row0 = tb.row[occ];
-    float cs[CE], sn[CE];
+    for (int gi = g0; gi < g1; ++gi) {
+      const int o = tb.by_doc[gi];
+      const int req = tb.req[o], row0 = tb.row[o];
+      const int cpos = tb.pos[o] + spos;
+      float cs[CE], sn[CE];
 #pragma unroll
-    for (int e = 0; e < CE; ++e) rope_cs(cpos, fr[e], cs[e], sn[e]);
-    auto put = [&](int h, uint4 kl, uint4 kh, const uint4& vl, const uint4& vh) {
-      rotate_chunk<T>(kl, kh, cs, sn);
-      const int64_t dst = (((int64_t)req * p.hkv + h) * p.cap + row0 + j) * D + c * CE;
-      T* kd = reinterpret_cast<T*>(p.cache_k) + dst;
-      T* vd = reinterpret_cast<T*>(p.cache_v) + dst;
-      // the composed cache is written once and read by later calls:
-      // streaming (non-temporal) stores
-      store_nt(kd, kl);
-      store_nt(kd + H, kh);
-      store_nt(vd, vl);
-      store_nt(vd + H, vh);
-    };
-    put(h0, kl0, kh0, vl0, vh0);
-    if (h0 + 1 < p.hkv) put(h0 + 1, kl1, kh1, vl1, vh1);
-    if (p.pos_out && h0 == 0 && c == 0) p.pos_out[(int64_t)req * p.cap + row0 + j] = cpos;
+      for (int e = 0; e < CE; ++e) rope_cs(cpos, fr[e], cs[e], sn[e]);
+      auto put = [&](int h, uint4 kl, uint4 kh, const uint4& vl, const uint4& vh) {
+        rotate_chunk<T>(kl, kh, cs, sn);
+        const int64_t dst = (((int64_t)req * p.hkv + h) * p.cap + row0 + j) * D + c * CE;
+        T* kd = reinterpret_cast<T*>(p.cache_k) + dst;
+        T* vd = reinterpret_cast<T*>(p.cache_v) + dst;
+        // the composed cache is written once and read by later calls:
+        // streaming (non-temporal) stores
+        store_nt(kd, kl);
+        store_nt(kd + H, kh);
+        store_nt(vd, vl);
+        store_nt(vd + H, vh);
+      };
+      put(h0, kl0, kh0, vl0, vh0);
+      if (h0 + 1 < p.hkv) put(h0 + 1, kl1, kh1, vl1, vh1);
+      if (p.pos_out && h0 == 0 && c == 0) p.pos_out[(int64_t)req * p.cap + row0 + j] = cpos;
+    }
   }
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void compose_kernel(const ComposeParams p) {
+__global__ __launch_bounds__(256, 3) void compose_kernel(const ComposeParams p) {
   static_assert(kComposeHPT == 2, "two heads per thread");
-  __shared__ ComposeOccTable tb;
-  const int total = p.total_tiles * p.nblk;
+  __shared__ ComposeTable tb;
   int u = blockIdx.x;
-  if (u >= total) return;
+  if (u >= p.total_units) return;
   compose_build_table(p, tb);
-  ComposeUnit<T, D> cur, nxt;
-  cur.load(p, tb, u);
+  const int total = tb.doc_unit0[p.num_docs];
+  // one unit in flight per wave: a unit's loads are amortised over the
+  // stores of its whole occurrence group, and three workgroups per CU keep
+  // other waves' loads in flight meanwhile
   for (; u < total; u += gridDim.x) {
-    const bool more = u + (int)gridDim.x < total;
-    if (more) nxt.load(p, tb, u + gridDim.x);
+    ComposeUnit<T, D> cur;
+    cur.load(p, tb, u);
     cur.store(p, tb);
-    if (!more) break;
-    cur = nxt;
   }
 }
 
 template <typename T, int D>
 static hipError_t launch_compose_t(const ComposeParams& p, bool host_src, hipStream_t st) {
-  const int units = p.total_tiles * p.nblk;
+  const int units = p.total_units;
   if (units == 0) return hipSuccess;
   // device sources: three workgroups per CU (12 waves) is the measured
   // optimum for 1k-2k units: fewer leaves HBM idle, more adds dispatch

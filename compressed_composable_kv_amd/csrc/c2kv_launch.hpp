@@ -26,9 +26,11 @@ struct RotateParams {
 // distinct documents of the launch once, each occurrence of a document in a
 // request as a one-byte index, and "runs" -- maximal sequences of
 // consecutive segments of one request that go to the launch.  The kernel
-// rebuilds every occurrence's first row tile, cache row and position offset
-// with prefix sums over the occurrences (cache rows and positions advance by
-// each document's slot count and original length within a run).
+// rebuilds every occurrence's cache row and position offset with prefix
+// sums over the occurrences (cache rows and positions advance by each
+// document's slot count and original length within a run) and groups the
+// occurrences by document.  total_units is the launch's work units (an
+// upper bound is enough: it sizes the grid).
 struct ComposeDoc {
   const void* k;
   const void* v;
@@ -40,13 +42,14 @@ constexpr int kComposeOcc = 1024;    // document occurrences per launch
 constexpr int kComposeRuns = 64;     // runs per launch
 constexpr int kComposeNoRealign = 0x80;   // occurrence flag: keep extraction positions (offset = pos_base)
 constexpr int kComposeHPT = 2;       // KV heads per thread
+constexpr int kComposeGroup = 4;     // occurrences of one document written per work unit
 
 struct ComposeParams {
   void* cache_k;
   void* cache_v;
   int32_t* pos_out;
   int64_t cap;
-  int32_t num_occ, num_runs, hkv, ratio_k, total_tiles;
+  int32_t num_docs, num_occ, num_runs, hkv, ratio_k, total_units;
   int32_t rpt, gpb, nblk;   // rows per tile, head pairs per unit, units per tile (ComposeTiling)
   RopeFreqs freqs;
   ComposeDoc docs[kComposeDocs];
