@@ -159,6 +159,10 @@ struct ComposeTable {
   int scan_m[kComposeOcc];         // global exclusive prefix of slot counts
   short by_doc[kComposeOcc];    // occurrences grouped by document, in occurrence order
   short rank[kComposeOcc];      // rank of the occurrence among those of its document
+  unsigned char occ[kComposeOcc];   // copy of the launch table's occurrence bytes
+  int doc_n[kComposeDocs];          // copies of the launch table's small arrays
+  int run_occ0[kComposeRuns + 1], run_row0[kComposeRuns], run_pos0[kComposeRuns], run_base[kComposeRuns];
+  int run_req[kComposeRuns];
   int doc_occ0[kComposeDocs + 1];   // first entry of each document in by_doc
   int doc_unit0[kComposeDocs + 1];  // first unit of each document; [num_docs] = total units
   int doc_cnt[kComposeDocs];
@@ -180,8 +184,23 @@ __device__ __forceinline__ X wave_incl_scan(X x) {
 
 __device__ void compose_build_table(const ComposeParams& p, ComposeTable& tb) {
   constexpr int PER = kComposeOcc / 256;   // occurrences per thread
+  static_assert(PER == 4, "one 32-bit word of occurrence bytes per thread");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  if (t < kComposeDocs) tb.doc_cnt[t] = 0;
+  // one round of independent loads of the launch table into LDS
+  if (t < kComposeDocs) {
+    tb.doc_cnt[t] = 0;
+    if (t < p.num_docs) tb.doc_n[t] = p.docs[t].n;
+  }
+  if (t <= p.num_runs) tb.run_occ0[t] = p.run_occ0[t];
+  if (t < p.num_runs) {
+    tb.run_row0[t] = p.run_row0[t];
+    tb.run_pos0[t] = p.run_pos0[t];
+    tb.run_base[t] = p.run_base[t];
+    tb.run_req[t] = p.run_req[t];
+  }
+  if (PER * t < p.num_occ)
+    *reinterpret_cast<uint32_t*>(&tb.occ[PER * t]) = *reinterpret_cast<const uint32_t*>(&p.occ_doc[PER * t]);
+  __syncthreads();
   int ml[PER], rl[PER], dl[PER];
   long long nl[PER];
   int sm = 0;
@@ -194,14 +213,14 @@ __device__ void compose_build_table(const ComposeParams& p, ComposeTable& tb) {
     rl[i] = 0;
     dl[i] = 0;
     if (o < p.num_occ) {
-      dl[i] = p.occ_doc[o] & (kComposeNoRealign - 1);
-      const int n = p.docs[dl[i]].n;
+      dl[i] = tb.occ[o] & (kComposeNoRealign - 1);
+      const int n = tb.doc_n[dl[i]];
       ml[i] = (n + p.ratio_k - 1) / p.ratio_k;
       nl[i] = n;
       int lo = 0, hi = p.num_runs - 1;          // run of the occurrence
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if ((int)p.run_occ0[mid] <= o) lo = mid; else hi = mid - 1;
+        if (tb.run_occ0[mid] <= o) lo = mid; else hi = mid - 1;
       }
       rl[i] = lo;
     }
@@ -235,7 +254,7 @@ __device__ void compose_build_table(const ComposeParams& p, ComposeTable& tb) {
     for (int c0 = 0; c0 < p.num_occ; c0 += 64) {
       const int o = c0 + lane;
       const bool valid = o < p.num_occ;
-      const int dd = valid ? (p.occ_doc[o] & (kComposeNoRealign - 1)) : kComposeNoRealign - 1;
+      const int dd = valid ? (tb.occ[o] & (kComposeNoRealign - 1)) : kComposeNoRealign - 1;
       uint64_t same = __ballot(valid);
 #pragma unroll
       for (int b = 0; b < 7; ++b) {
@@ -256,19 +275,24 @@ __device__ void compose_build_table(const ComposeParams& p, ComposeTable& tb) {
     }
   }
   __syncthreads();
-  // per document: first by_doc entry and first unit (sequential over <= 64 documents)
-  if (t == 0) {
-    int occ0 = 0, unit0 = 0;
-    for (int d = 0; d < p.num_docs; ++d) {
-      tb.doc_occ0[d] = occ0;
-      tb.doc_unit0[d] = unit0;
-      const int m = (p.docs[d].n + p.ratio_k - 1) / p.ratio_k;
-      const int c = tb.doc_cnt[d];
-      occ0 += c;
-      unit0 += ((m + p.rpt - 1) / p.rpt) * p.nblk * ((c + kComposeGroup - 1) / kComposeGroup);
+  // per document (one per lane of wave 0): first by_doc entry and first unit
+  static_assert(kComposeDocs == 64, "one wave covers the documents");
+  if (wave == 0) {
+    int c = 0, nu = 0;
+    if (lane < p.num_docs) {
+      const int m = (tb.doc_n[lane] + p.ratio_k - 1) / p.ratio_k;
+      c = tb.doc_cnt[lane];
+      nu = ((m + p.rpt - 1) / p.rpt) * p.nblk * ((c + kComposeGroup - 1) / kComposeGroup);
     }
-    tb.doc_occ0[p.num_docs] = occ0;
-    tb.doc_unit0[p.num_docs] = unit0;
+    const int ic = wave_incl_scan(c), iu = wave_incl_scan(nu);
+    if (lane < p.num_docs) {
+      tb.doc_occ0[lane] = ic - c;
+      tb.doc_unit0[lane] = iu - nu;
+    }
+    if (lane == 63) {
+      tb.doc_occ0[p.num_docs] = ic;
+      tb.doc_unit0[p.num_docs] = iu;
+    }
   }
   __syncthreads();
   // cache rows and position offsets relative to the start of each run; the
@@ -277,11 +301,11 @@ __device__ void compose_build_table(const ComposeParams& p, ComposeTable& tb) {
   for (int i = 0; i < PER; ++i) {
     const int o = PER * t + i;
     if (o < p.num_occ) {
-      const int r = rl[i], f = p.run_occ0[r];
-      tb.row[o] = p.run_row0[r] + (tb.scan_m[o] - tb.scan_m[f]);
-      tb.pos[o] = (p.occ_doc[o] & kComposeNoRealign) ? p.run_base[r]
-                                                     : p.run_pos0[r] + (int)(tb.scan_n[o] - tb.scan_n[f]);
-      tb.req[o] = p.run_req[r];
+      const int r = rl[i], f = tb.run_occ0[r];
+      tb.row[o] = tb.run_row0[r] + (tb.scan_m[o] - tb.scan_m[f]);
+      tb.pos[o] = (tb.occ[o] & kComposeNoRealign) ? tb.run_base[r]
+                                                 : tb.run_pos0[r] + (int)(tb.scan_n[o] - tb.scan_n[f]);
+      tb.req[o] = tb.run_req[r];
       tb.by_doc[tb.doc_occ0[dl[i]] + tb.rank[o]] = (short)o;
     }
   }

@@ -58,7 +58,7 @@ struct ComposeParams {
   int32_t run_pos0[kComposeRuns];   // realigned position offset of the run's first occurrence
   int32_t run_base[kComposeRuns];   // pos_base of the run's request (offset without realignment)
   uint16_t run_occ0[kComposeRuns + 1];   // first occurrence of each run; [num_runs] = num_occ
-  uint8_t occ_doc[kComposeOcc];     // document index | kComposeNoRealign
+  alignas(4) uint8_t occ_doc[kComposeOcc];   // document index | kComposeNoRealign
 };
 static_assert(sizeof(ComposeParams) <= 4096, "compose table must fit the kernel arguments");
 
