@@ -75,6 +75,12 @@ DECODE_SOURCES = ("compressed_composable_kv_amd/csrc/c2kv_decode.hip",
                   "compressed_composable_kv_amd/csrc/c2kv_device.hpp",
                   "compressed_composable_kv_amd/csrc/c2kv_cache.cpp")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_decode_llama31_8b_longctx_128k.txt")
+# the same for the compose kernel and its launch table
+COMPOSE_SOURCES = ("compressed_composable_kv_amd/csrc/c2kv_aux.hip",
+                   "compressed_composable_kv_amd/csrc/c2kv_launch.hpp",
+                   "compressed_composable_kv_amd/csrc/c2kv_device.hpp",
+                   "compressed_composable_kv_amd/csrc/c2kv_abi.cpp")
+COMPOSE_PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_compose_qwen25_7b_pool.txt")
 CALIB_KERNEL = "neg_kernel"    # torch.neg over int32: reads and writes N MiB
 POOL_BYTES = 96 << 30          # device memory given to a pool of layer buffers
 
@@ -163,14 +169,14 @@ def summarize(dirs, out, cmd, calib_mib):
             traffic[short] = t
             lines.append(f"{cs['FETCH_SIZE'][1]:11d} {cs['FETCH_SIZE'][0]:10.1f} {cs['WRITE_SIZE'][0]:10.1f} "
                          f"{t / 1e6:18.3f}  {short}")
-        lines.append("# json: " + json.dumps({"sources_sha": sources_sha(), "fetch_scale": fs, "write_scale": ws,
-                                              "traffic_bytes": traffic}))
+        lines.append("# json: " + json.dumps({"sources_sha": sources_sha(), "compose_sources_sha": sources_sha(COMPOSE_SOURCES),
+                                              "fetch_scale": fs, "write_scale": ws, "traffic_bytes": traffic}))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def committed_traffic(kernel_keys, path=PMC_SUMMARY, sources=DECODE_SOURCES):
+def committed_traffic(kernel_keys, path=PMC_SUMMARY, sources=DECODE_SOURCES, sha_key="sources_sha"):
     """HBM bytes per call from a committed counter summary, or None when
     there is none or the sources changed since it was taken."""
     try:
@@ -179,7 +185,7 @@ def committed_traffic(kernel_keys, path=PMC_SUMMARY, sources=DECODE_SOURCES):
         info = json.loads(js[-1][len("# json: "):])
     except (OSError, IndexError, ValueError):
         return None
-    if info.get("sources_sha") != sources_sha(sources):
+    if info.get(sha_key) != sources_sha(sources):
         return None
     tot = 0.0
     for key in kernel_keys:
@@ -529,7 +535,9 @@ def qwen25(torch, dev, replicas=8, steps=16, emit=False):
            "compose_us_per_call": cms * 1e3, "compose_algorithmic_bytes": alg, "compose_min_traffic_bytes": minimum,
            "compose_gbs_algorithmic": alg / (cms * 1e-3) / 1e9,
            "compose_gbs_min_traffic": minimum / (cms * 1e-3) / 1e9,
-           "compose_hbm_frac_min_traffic": minimum / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+           "compose_hbm_frac_min_traffic": minimum / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "compose_traffic_bytes": committed_traffic(("compose_kernel",), COMPOSE_PMC_SUMMARY, COMPOSE_SOURCES,
+                                                      "compose_sources_sha")}
     if emit:
         print(json.dumps(res), flush=True)
     return res
@@ -1037,8 +1045,11 @@ def main():
     lla = llama_layer_step(torch, dev, steps=5, warmup=2)
     log(f"llama layer: {json.dumps(lla['phase_ms'])}")
 
-    dec_traffic = committed_traffic(("decode_attn_kernel", "merge_kernelIDF16bLi128ELi32E"))
-    roof = {"bound": "hbm", "kernel": "c2kv_attn_decode (decode_attn_kernel<bf16,128> + merge_kernel<bf16,128,32>)",
+    # at this size every (request, KV head) is one key piece: a decode call is
+    # one decode_attn_kernel launch, with no merge launch
+    dec_traffic = committed_traffic(("decode_attn_kernel",))
+    roof = {"bound": "hbm", "kernel": "c2kv_attn_decode: decode_attn_kernel<bf16,128> (one key piece per request and "
+                                      "KV head at this size, so no merge launch)",
             "achieved": head["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["gbs"] / HBM_PEAK_GBS,
             "traffic": dec_traffic, "per_launch_ms": head["ms_per_call"],
             "algorithmic_per_launch": head["bytes_per_step"] / head["layers"],
