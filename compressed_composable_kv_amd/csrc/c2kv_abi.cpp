@@ -165,7 +165,12 @@ extern "C" {
 const char* c2kv_version(void) { return "c2kv-mi355x 0.1.0 (gfx950)"; }
 
 const char* c2kv_status_string(c2kv_status s) {
-  switch (s) {
+  // C callers may pass any int; read it as one (a C++ enum load of a value
+  // outside the enumerators' range is undefined)
+  int v;
+  static_assert(sizeof(v) == sizeof(s), "c2kv_status is an int");
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case C2KV_OK: return "ok";
     case C2KV_ERR_INVALID_ARG: return "invalid argument";
     case C2KV_ERR_UNSUPPORTED: return "unsupported";
@@ -482,14 +487,16 @@ c2kv_status compose_plan(const c2kv_segment* segs, int32_t num_segs, const int32
 c2kv_status map_host_range(const void* host_ptr, size_t bytes, const void** dev_ptr) {
   if (!host_ptr || !dev_ptr) return fail(C2KV_ERR_INVALID_ARG, "host_ptr or dev_ptr is NULL");
   if (bytes == 0) return fail(C2KV_ERR_INVALID_ARG, "bytes must be >= 1");
-  const char* first = static_cast<const char*>(host_ptr);
-  const char* last = first + (bytes - 1);
-  if (last < first) return fail(C2KV_ERR_INVALID_ARG, "host range wraps the address space");
+  // address arithmetic in integers: a range that wraps is rejected before
+  // any pointer is formed from it
+  const uintptr_t first = reinterpret_cast<uintptr_t>(host_ptr);
+  if (bytes - 1 > UINTPTR_MAX - first) return fail(C2KV_ERR_INVALID_ARG, "host range wraps the address space");
+  const uintptr_t last = first + (bytes - 1);
   hipPointerAttribute_t a0, a1;
   std::memset(&a0, 0, sizeof(a0));
   std::memset(&a1, 0, sizeof(a1));
-  hipError_t e0 = hipPointerGetAttributes(&a0, first);
-  hipError_t e1 = e0 == hipSuccess ? hipPointerGetAttributes(&a1, last) : hipSuccess;
+  hipError_t e0 = hipPointerGetAttributes(&a0, reinterpret_cast<const void*>(first));
+  hipError_t e1 = e0 == hipSuccess ? hipPointerGetAttributes(&a1, reinterpret_cast<const void*>(last)) : hipSuccess;
   if (e0 != hipSuccess || e1 != hipSuccess) {
     (void)hipGetLastError();   // the query's own failure is not a launch error
     return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) is not page-locked host memory (%s)", host_ptr, bytes,
@@ -501,12 +508,12 @@ c2kv_status map_host_range(const void* host_ptr, size_t bytes, const void** dev_
                 host_ptr, bytes);
   // the attributes may describe the queried address or its allocation's
   // base; the host-side distance to the reported host address maps either
-  const char* d0 = static_cast<const char*>(a0.devicePointer) + (first - static_cast<const char*>(a0.hostPointer));
-  const char* d1 = static_cast<const char*>(a1.devicePointer) + (last - static_cast<const char*>(a1.hostPointer));
+  const uintptr_t d0 = reinterpret_cast<uintptr_t>(a0.devicePointer) + (first - reinterpret_cast<uintptr_t>(a0.hostPointer));
+  const uintptr_t d1 = reinterpret_cast<uintptr_t>(a1.devicePointer) + (last - reinterpret_cast<uintptr_t>(a1.hostPointer));
   if (d1 - d0 != last - first)
     return fail(C2KV_ERR_INVALID_ARG, "host range [%p, +%zu) spans more than one page-locked allocation", host_ptr,
                 bytes);
-  *dev_ptr = d0;
+  *dev_ptr = reinterpret_cast<const void*>(d0);
   return C2KV_OK;
 }
 

@@ -64,6 +64,11 @@ WORKSPACES = _Workspaces()
 
 def _workspace(given: Optional[torch.Tensor], key: str, nbytes: int, device: torch.device) -> torch.Tensor:
     if given is None:
+        # a captured graph keeps the address it saw; a cached buffer can be
+        # replaced (and freed) by a later, larger call, so capture needs a
+        # workspace that the caller owns for the graph's lifetime
+        _need(not torch.cuda.is_current_stream_capturing(),
+              "pass an explicit workspace= when capturing a graph (size it with workspace_size_*)")
         return WORKSPACES.get(key, nbytes, device, zero=False)
     _dev_tensor(given, "workspace", torch.uint8)
     _need(given.numel() >= nbytes, f"workspace has {given.numel()} bytes, {nbytes} needed")
@@ -251,6 +256,27 @@ def _segment_table(requests, cache_k: torch.Tensor, staged: bool, realign: bool 
     return (Segment * len(segs))(*segs), _arr_i32(ptr), keep
 
 
+class _HostHolds:
+    """Pinned host segments of eager compose calls, kept referenced until an
+    event recorded after the launch has completed, so that the host
+    allocator cannot hand their blocks out while a kernel or copy still
+    reads them.  Under graph capture the caller keeps them alive for as
+    long as the graph may be replayed."""
+
+    def __init__(self):
+        self._held = []
+
+    def hold(self, tensors, device: torch.device) -> None:
+        self._held = [(ev, t) for ev, t in self._held if not ev.query()]
+        if tensors and not torch.cuda.is_current_stream_capturing():
+            ev = torch.cuda.Event()
+            ev.record(torch.cuda.current_stream(device))
+            self._held.append((ev, tensors))
+
+
+HOST_HOLDS = _HostHolds()
+
+
 def _compose_call(fn, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base, pos_out, staged, workspace,
                   realign=True):
     lib = load()
@@ -273,6 +299,7 @@ def _compose_call(fn, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base,
         nbytes = ws.numel()
     check(fn(arr, len(arr), ptr, R, base, ratio_k, hkv, d, float(rope_theta), _ptr(cache_k), _ptr(cache_v), cap,
              _ptr(pos_out), lens, nxt, dt, _ptr(ws), nbytes, _stream(cache_k.device)))
+    HOST_HOLDS.hold([t for pair in keep for t in pair if not t.is_cuda], cache_k.device)
     return list(lens), list(nxt)
 
 
@@ -285,8 +312,10 @@ def compose(requests: Sequence[Sequence[Tuple[torch.Tensor, torch.Tensor, int]]]
     either on the device or pinned CPU tensors (stored caches kept in host
     memory, read in place across the host link).  realign=False is the
     ablation without positional realignment (C2KV_SEGMENT_NO_REALIGN on
-    every segment).  Returns (cache_len per request, next position per
-    request)."""
+    every segment).  Pinned CPU segments stay referenced here until the
+    launch has read them; under graph capture the caller keeps them alive
+    while the graph may be replayed.  Returns (cache_len per request, next
+    position per request)."""
     return _compose_call(load().c2kv_compose, requests, ratio_k, rope_theta, cache_k, cache_v, pos_base, pos_out,
                          False, None, realign)
 

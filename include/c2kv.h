@@ -50,8 +50,10 @@
  * - Per-call tables (documents, requests) are passed to the GPU as kernel
  *   arguments in chunks of at most C2KV_MAX_BATCH entries per launch, so
  *   extract/prefill/decode perform no host-to-device copies and may be
- *   captured in a HIP graph.  Compose passes its segment table the same way
- *   (at most 64 segments per launch) and needs no workspace.
+ *   captured in a HIP graph.  Compose passes its table the same way (the
+ *   distinct documents, one byte per occurrence and the requests' runs of
+ *   occurrences: up to 64 documents, 1024 occurrences and 64 runs per
+ *   launch) and needs no workspace.
  */
 #ifndef C2KV_H_
 #define C2KV_H_
@@ -267,6 +269,9 @@ size_t c2kv_workspace_size_compose(int32_t num_segs);
  *   cache_len_out host [num_reqs]: number of composed rows per request
  *   next_pos_out  host [num_reqs] or NULL: pos_base + sum of the request's
  *                 document lengths (where the question starts)
+ * Asynchronous on `stream`: the segments' memory (device or host) must stay
+ * allocated and unwritten until `stream` has passed the call, and for as
+ * long as a graph that captured the call may be replayed.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, CAPACITY (a request needs more
  * than cap rows, or a position exceeds 2^24), HIP. */
 c2kv_status c2kv_compose(const c2kv_segment* segs, int32_t num_segs,
@@ -318,7 +323,8 @@ c2kv_status c2kv_host_device_ptr(const void* host_ptr, size_t bytes, const void*
  *   workspace   device, >= c2kv_workspace_size_compose_staged(...) bytes;
  *               holds the staged rows until the compose kernel has read them
  *   all other arguments and outputs exactly as c2kv_compose.
- * The host memory must not be written until `stream` has passed the call.
+ * The host memory must stay allocated and unwritten until `stream` has
+ * passed the call.
  * Errors: as c2kv_compose, plus INVALID_ARG for memory that is not
  * page-locked and WORKSPACE.  The size query returns 0 for invalid input. */
 size_t c2kv_workspace_size_compose_staged(const c2kv_segment* segs, int32_t num_segs, int32_t ratio_k,

@@ -219,3 +219,12 @@ def test_extract_ex_flag_validation(lib):
     assert r == INVALID                                   # unknown flag bit
     out = (ctypes.c_uint64 * 5)()
     assert lib.c2kv_mask_cells_ex(lens, 1, 4, 4, 4, out, FAKE, 256, None) == INVALID
+
+
+def test_implicit_workspace_refused_under_capture(monkeypatch):
+    # a graph keeps the workspace address it captured; the binding's cached
+    # workspaces can be replaced later, so capture needs an explicit one
+    import compressed_composable_kv_amd.ops as ops
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+    with pytest.raises(ValueError, match="explicit workspace"):
+        ops._workspace(None, "cache", 1024, torch.device("cuda", 0))
