@@ -651,23 +651,54 @@ __device__ __forceinline__ void kv_rows_dma(char* stage, __amdgpu_buffer_rsrc_t 
   }
 }
 
-// Question prefill over a composed cache, split-K over the keys.  A
-// workgroup owns (request, KV head, key chunk, group of 4 units); a unit is
-// 32 question rows of one query head.  K and V tiles of 64 keys come from
-// the cache by LDS DMA (double buffered, rows past the chunk read as zeros)
-// and feed the same tile code as extraction; V stays row-major and its
-// transposed operand is read with ds_read_b64_tr_b16.
+// Question prefill over a composed cache, split-K over the keys, with the
+// question's RoPE and append fused in.  A workgroup owns (request, KV head,
+// key chunk, group of 4 units); a unit is 32 question rows of one query head.
+// The workgroup has two groups of 4 waves holding the same 4 units: group 0
+// takes the chunk's even 64-key tiles and group 1 its odd ones, so each SIMD
+// runs two waves (one wave's MFMAs overlap the other's softmax), and the two
+// halves are combined in LDS at the end, without more split partials.
+//   * Queries are loaded pre-RoPE and rotated in registers at q_pos0 + t,
+//     then rounded to the storage type for the MFMAs.  The cos/sin of the
+//     workgroup's question tokens are computed once per workgroup into a
+//     table in the second stage, which the DMA fills only after the
+//     rotation.
+//   * The tile code picks its group's half of a stage with a wave-uniform
+//     branch on constant offsets; the compiler then sees that the DMA into
+//     one stage never aliases the LDS reads of the other and inserts no
+//     vector-memory wait inside the tile.
+//   * K and V tiles come from the cache by LDS DMA, a pair of tiles (one per
+//     group) per stage, double buffered where two stages fit 128 KB.
+//   * Rows at or past cache_len are the question's own keys and values.
+//     Before its first DMA, every workgroup whose chunk holds such rows
+//     rotates those keys at their positions, copies the values, and writes
+//     both into the cache; the unit groups of a chunk write the same bytes.
+//     A workgroup-scope fence and a barrier order these stores before the
+//     workgroup's own DMA of the rows.
+//   * The same tile code as extraction; V stays row-major and its transposed
+//     operand is read with ds_read_b64_tr_b16.
+constexpr int kPWaves = 2 * kWaves;        // waves per prefill workgroup: two groups
+constexpr int kPThreads = 64 * kPWaves;
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void cache_attn_kernel(const CacheParams p) {
+__global__ __launch_bounds__(kPThreads, 1) void prefill_attn_kernel(const CacheParams p) {
   using X = XTile<T, D>;
+  using A = XAttn<T, D>;
   constexpr int RB = X::RB, CPR = X::CPR, KB = X::KBYTES;     // V tile is KB bytes too
   constexpr int NDMA = KB / 1024 / kWaves;                    // per wave, per tensor
-  __shared__ __attribute__((aligned(1024))) char stage0[2 * KB];
-  __shared__ __attribute__((aligned(1024))) char stage1[2 * KB];
-  asm volatile("" : : "r"(stage0), "r"(stage1) : "memory");
+  constexpr int PSTAGE = 2 * X::STAGE;                        // one tile per group
+  constexpr int NPS = 2 * PSTAGE <= 128 * 1024 ? 2 : 1;       // pair stages
+  constexpr int CE = Chunk<T>::CE, H = D / 2, HC = CPR / 2;   // elements per chunk, half row, chunks per half
+  // two distinct arrays, so the compiler sees that the DMA into one stage
+  // never aliases the LDS reads of the other (no vmcnt wait before them)
+  __shared__ __attribute__((aligned(1024))) char ring0[PSTAGE];
+  __shared__ __attribute__((aligned(1024))) char ring1[NPS == 2 ? PSTAGE : 16];
+  asm volatile("" : : "r"(ring0), "r"(ring1) : "memory");
   const int L = xcd_logical(blockIdx.x, p.grid_wg);
   if (L >= p.total_wg) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = wave / kWaves, wq = wave % kWaves;
+  const int r16 = lane & 15, g = lane >> 4;
   int ri = 0;
   while (ri + 1 < p.num_reqs && p.reqs[ri + 1].wg0 <= L) ++ri;
   const CacheReq rq = p.reqs[ri];
@@ -678,7 +709,7 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void cache_attn_kerne
   const int rem = local % per_kvh;
   const int split = rem / p.nug, ug = rem % p.nug;
   const int G = p.G;
-  const int u = ug * kWaves + wave;
+  const int u = ug * kWaves + wq;
   const int nunits = p.nblk_q * G;
   const bool wvalid = u < nunits;
   const int blk = u / G, head = kvh * G + (u % G);
@@ -693,84 +724,207 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void cache_attn_kerne
   int koff[NDMA], voff[NDMA];
 #pragma unroll
   for (int j = 0; j < NDMA; ++j) {
-    const int byte = (wave * NDMA + j) * 1024 + lane * 16;
+    const int byte = (wq * NDMA + j) * 1024 + lane * 16;
     const int row = byte / RB, pc = (byte % RB) / 16;
     koff[j] = row * RB + ((pc ^ k_swz<CPR>(row)) << 4);
     voff[j] = row * RB + ((pc ^ (2 * vr_swz<RB>(row))) << 4);
   }
-  auto issue = [&](int it, char* stage) {
-    kv_rows_dma<NDMA, KB>(stage, krs, vrs, koff, voff, (ks0 + it * kBN) * RB, wave);
-  };
   const int ntiles = (ks1 - ks0 + kBN - 1) / kBN;
-  if (ntiles > 0) issue(0, stage0);
-
-  XAttn<T, D> W;
-  W.init();
-  {
-    const int r16 = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int t = t0 + 16 * qb + r16;
-      const bool ok = wvalid && t < t1;
-      const T* qrow = reinterpret_cast<const T*>(p.qrot) + (((int64_t)r * p.tq + (ok ? t : 0)) * p.hq + head) * D;
-#pragma unroll
-      for (int k = 0; k < D / 32; ++k) {
-        float x[8];
-        load8_f32<T>(qrow + 32 * k + 8 * g, x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) W.qB[qb][k][e] = from_f32<T>(ok ? x[e] : 0.f);
-      }
-    }
-  }
-  const Pred pred = pred_causal(ks1, rq.cache_len);
-  auto compute = [&](int it, const char* stage) {
-    const int key0 = ks0 + it * kBN;
-    if (!(wvalid && key0 < rq.cache_len + t1)) return;
-    if ((key0 + kBN - 1 > rq.cache_len + t0) || (key0 + kBN > ks1))
-      W.template tile<true>(stage, lane, p.scale_log2, pred, t0, key0);
-    else
-      W.template tile<false>(stage, lane, p.scale_log2, pred, t0, key0);
+  const int npairs = (ntiles + 1) / 2;
+  // this group's tile of pair j into pair stage `ps` (each group's 4 waves
+  // fill their own tile; tiles past the chunk read as zeros)
+  auto issue_pair = [&](int j, char* ps) {
+    const int it = 2 * j + grp;
+    // (the tile's byte offset is wave-uniform: keep it in an SGPR)
+    kv_rows_dma<NDMA, KB>(ps + grp * X::STAGE, krs, vrs, koff, voff,
+                          __builtin_amdgcn_readfirstlane((ks0 + it * kBN) * RB), wq);
   };
-  for (int it = 0; it < ntiles; it += 2) {
-    wait_vmem();
-    __syncthreads();
-    if (it + 1 < ntiles) issue(it + 1, stage1);
-    compute(it, stage0);
-    if (it + 1 >= ntiles) break;
-    wait_vmem();
-    __syncthreads();
-    if (it + 2 < ntiles) issue(it + 2, stage0);
-    compute(it + 1, stage1);
-  }
+  // RoPE frequencies this thread uses, loaded first: a thread keeps one
+  // chunk column of the new rows and one frequency of the cos/sin table
+  // (kPThreads is a multiple of HC and of H)
+  static_assert(kPThreads % HC == 0 && kPThreads % H == 0, "fixed columns per thread");
+  float fq[CE];
+#pragma unroll
+  for (int e = 0; e < CE; ++e) fq[e] = p.freqs.f[(tid % HC) * CE + e];
+  const float ftab = p.freqs.f[tid % H];
 
-  // ---- final rows (one key chunk) or split partials [o(D) | m | l | pad],
-  // m in log2 units
-  if (!wvalid) return;
-  const int r16 = lane & 15, g = lane >> 4;
+  // ---- the chunk's question rows (keys rotated at q_pos0 + (row -
+  // cache_len), values copied) go to the cache before any DMA reads them
+  if (max(ks0, rq.cache_len) < ks1) {
+    for (int item = tid; item < (ks1 - max(ks0, rq.cache_len)) * HC; item += kPThreads) {
+      const int row = max(ks0, rq.cache_len) + item / HC, c = item % HC;
+      const int t = row - rq.cache_len;
+      const int64_t src = (((int64_t)r * p.tq + t) * p.hkv + kvh) * D + c * CE;
+      const T* ksrc = reinterpret_cast<const T*>(p.k_new) + src;
+      const T* vsrc = reinterpret_cast<const T*>(p.v_new) + src;
+      uint4 klo = *reinterpret_cast<const uint4*>(ksrc);
+      uint4 khi = *reinterpret_cast<const uint4*>(ksrc + H);
+      const uint4 vlo = *reinterpret_cast<const uint4*>(vsrc);
+      const uint4 vhi = *reinterpret_cast<const uint4*>(vsrc + H);
+      float cs[CE], sn[CE];
+#pragma unroll
+      for (int e = 0; e < CE; ++e) rope_cs(rq.pos0 + t, fq[e], cs[e], sn[e]);
+      rotate_chunk<T>(klo, khi, cs, sn);
+      T* kd = reinterpret_cast<T*>(p.kc) + (head_base + row) * D + c * CE;
+      T* vd = reinterpret_cast<T*>(p.vc) + (head_base + row) * D + c * CE;
+      *reinterpret_cast<uint4*>(kd) = klo;
+      *reinterpret_cast<uint4*>(kd + H) = khi;
+      *reinterpret_cast<uint4*>(vd) = vlo;
+      *reinterpret_cast<uint4*>(vd + H) = vhi;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+  // ---- the wave's raw queries (rows past the unit read row t0 and are
+  // zeroed), issued before the first DMA so that the rotation waits for
+  // them only; then the cos/sin of the workgroup's tokens [tlo, thi) (at
+  // most 4 blocks of 32) into the stage that pair 1 (pair 0 with one stage)
+  // fills
+  using V8 = typename ElemTraits<T>::v8;
+  V8 qlo[2][D / 64], qhi[2][D / 64];   // kept packed until the rotation
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lt = W.ls[qb][0];   // every lane of a column holds its sum
+    const int t = t0 + 16 * qb + r16;
+    const int tt = (wvalid && t < t1) ? t : (wvalid ? t0 : 0);
+    const T* qrow = reinterpret_cast<const T*>(p.q) + (((int64_t)r * p.tq + tt) * p.hq + head) * D;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      qlo[qb][k] = *reinterpret_cast<const V8*>(qrow + 32 * k + 8 * g);
+      qhi[qb][k] = *reinterpret_cast<const V8*>(qrow + H + 32 * k + 8 * g);
+    }
+  }
+  if constexpr (NPS == 2) issue_pair(0, ring0);
+  const int ulo = ug * kWaves, uhi = min(nunits, ulo + kWaves) - 1;
+  const int tlo = (ulo / G) * kQW, thi = min(p.tq, (uhi / G + 1) * kQW);
+  float2* cs_tab = reinterpret_cast<float2*>(NPS == 2 ? ring1 : ring0);
+  static_assert(4 * kQW * H * sizeof(float2) <= PSTAGE, "cos/sin table fits one stage");
+  for (int i = tid; i < (thi - tlo) * H; i += kPThreads) {
+    float c, sn;
+    rope_cs(rq.pos0 + tlo + i / H, ftab, c, sn);
+    cs_tab[i] = make_float2(c, sn);
+  }
+  lds_barrier();   // the table is complete (the DMA of pair 0 stays in flight)
+  A W;
+  W.init();
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int t = t0 + 16 * qb + r16;
+    const bool ok = wvalid && t < t1;
+    const float2* cs_row = cs_tab + (ok ? t - tlo : 0) * H;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 cs = cs_row[32 * k + 8 * g + e];
+        float y0, y1;
+        rope_pair(static_cast<float>(qlo[qb][k][e]), static_cast<float>(qhi[qb][k][e]), cs.x, cs.y, y0, y1);
+        W.qB[qb][k][e] = from_f32<T>(ok ? y0 : 0.f);
+        W.qB[qb][k + D / 64][e] = from_f32<T>(ok ? y1 : 0.f);
+      }
+  }
+  if constexpr (NPS == 1) {
+    __syncthreads();   // every wave is done with the table
+    issue_pair(0, ring0);
+  }
+
+  const Pred pred = pred_causal(ks1, rq.cache_len);
+  auto run_pair = [&](int j, const char* cur, char* nxt) {
+    wait_vmcnt<0>();   // this wave's share of pair j has landed
+    __syncthreads();   // both tiles of pair j are in LDS; pair j - 1 (and the table) is no longer read
+    if (NPS == 2 && j + 1 < npairs) issue_pair(j + 1, nxt);
+    const int it = 2 * j + grp;
+    const int key0 = ks0 + it * kBN;
+    if (it < ntiles && wvalid && key0 < rq.cache_len + t1) {
+      const bool masked = (key0 + kBN - 1 > rq.cache_len + t0) || (key0 + kBN > ks1);
+      if (grp == 0) {
+        if (masked) W.template tile<true>(cur, lane, p.scale_log2, pred, t0, key0);
+        else W.template tile<false>(cur, lane, p.scale_log2, pred, t0, key0);
+      } else {
+        if (masked) W.template tile<true>(cur + X::STAGE, lane, p.scale_log2, pred, t0, key0);
+        else W.template tile<false>(cur + X::STAGE, lane, p.scale_log2, pred, t0, key0);
+      }
+    }
+    if (NPS == 1 && j + 1 < npairs) {
+      __syncthreads();   // pair j is no longer read
+      issue_pair(j + 1, nxt);
+    }
+  };
+  if constexpr (NPS == 2) {
+    for (int j = 0; j < npairs; j += 2) {
+      run_pair(j, ring0, ring1);
+      if (j + 1 >= npairs) break;
+      run_pair(j + 1, ring1, ring0);
+    }
+  } else {
+    for (int j = 0; j < npairs; ++j) run_pair(j, ring0, ring0);
+  }
+
+  // ---- combine the groups: group 1 leaves (o, m, l) in LDS, group 0 merges
+  // them into its own (both hold the same rows in the same lanes)
+  constexpr int NV = A::DB * 2 * 4 + 4;                       // floats per lane
+  // (waves 0-1 of a group exchange through the first stage, 2-3 through the
+  // second; with one stage, all through it)
+  float* cmb = NPS == 2 ? reinterpret_cast<float*>(wq < 2 ? ring0 : ring1) + (wq & 1) * NV * 64 + lane
+                        : reinterpret_cast<float*>(ring0) + wq * NV * 64 + lane;
+  static_assert(kWaves / NPS * NV * 64 * sizeof(float) <= PSTAGE, "exchange fits the stages");
+  __syncthreads();   // no wave reads a tile any more
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < A::DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cmb[((db * 2 + qb) * 4 + i) * 64] = W.o[db][qb][i];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      cmb[(A::DB * 8 + qb) * 64] = W.m[qb];
+      cmb[(A::DB * 8 + 2 + qb) * 64] = W.ls[qb][0];
+    }
+  }
+  __syncthreads();
+  if (grp == 1 || !wvalid) return;
+  float lt[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float m1 = cmb[(A::DB * 8 + qb) * 64], l1 = cmb[(A::DB * 8 + 2 + qb) * 64];
+    const float m0 = W.m[qb], l0 = W.ls[qb][0];
+    const float mm = fmaxf(m0, m1);
+    const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - mm) * p.scale_log2);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - mm) * p.scale_log2);
+#pragma unroll
+    for (int db = 0; db < A::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        W.o[db][qb][i] = W.o[db][qb][i] * a0 + cmb[((db * 2 + qb) * 4 + i) * 64] * a1;
+    lt[qb] = l0 * a0 + l1 * a1;
+    W.m[qb] = mm;
+  }
+
+  // ---- final rows (one key chunk) or split partials, m in log2 units
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
     const float m2 = W.m[qb] * p.scale_log2;
     const int t = t0 + 16 * qb + r16;
     if (t >= t1) continue;
     if (rq.nsplit == 1) {
-      const float inv = 1.f / lt;
+      const float inv = 1.f / lt[qb];
       T* orow = reinterpret_cast<T*>(p.o) + (((int64_t)r * p.tq + t) * p.hq + head) * D;
 #pragma unroll
-      for (int db = 0; db < XAttn<T, D>::DB; ++db) {
+      for (int db = 0; db < A::DB; ++db) {
         typename ElemTraits<T>::v4 outv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) outv[i] = from_f32<T>(W.o[db][qb][i] * inv);
         *reinterpret_cast<typename ElemTraits<T>::v4*>(orow + 16 * db + 4 * g) = outv;
       }
       if (g == 0 && p.lse)
-        p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (m2 + __log2f(lt)) * 0.69314718055994531f;
+        p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (m2 + __log2f(lt[qb])) * 0.69314718055994531f;
     } else {
       const int64_t idx = (int64_t)rq.pbase + ((int64_t)head * p.tq + t) * rq.nsplit + split;
       float* prow = p.part_o + idx * D;
-      if (g == 0) p.part_ml[idx] = make_float2(W.m[qb] == -INFINITY ? -INFINITY : m2, lt);
+      if (g == 0) p.part_ml[idx] = make_float2(W.m[qb] == -INFINITY ? -INFINITY : m2, lt[qb]);
 #pragma unroll
-      for (int db = 0; db < XAttn<T, D>::DB; ++db)
+      for (int db = 0; db < A::DB; ++db)
         *reinterpret_cast<f32x4*>(prow + 16 * db + 4 * g) = W.o[db][qb];
     }
   }
@@ -797,16 +951,16 @@ hipError_t launch_extract_attn(const ExtractParams& p, int dtype, int head_dim, 
 }
 
 template <typename T, int D>
-static hipError_t launch_cache_t(const CacheParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((cache_attn_kernel<T, D>), dim3(p.grid_wg), dim3(kThreads), 0, st, p);
+static hipError_t launch_prefill_t(const CacheParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_attn_kernel<T, D>), dim3(p.grid_wg), dim3(kPThreads), 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_cache_attn(const CacheParams& p, int dtype, int head_dim, hipStream_t st) {
+hipError_t launch_prefill_attn(const CacheParams& p, int dtype, int head_dim, hipStream_t st) {
   if (dtype == C2KV_BF16) {
-    return head_dim == 128 ? launch_cache_t<bf16, 128>(p, st) : launch_cache_t<bf16, 64>(p, st);
+    return head_dim == 128 ? launch_prefill_t<bf16, 128>(p, st) : launch_prefill_t<bf16, 64>(p, st);
   }
-  return head_dim == 128 ? launch_cache_t<float, 128>(p, st) : launch_cache_t<float, 64>(p, st);
+  return head_dim == 128 ? launch_prefill_t<float, 128>(p, st) : launch_prefill_t<float, 64>(p, st);
 }
 
 }  // namespace c2kv

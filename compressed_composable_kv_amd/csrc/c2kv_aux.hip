@@ -5,8 +5,6 @@
 //     C2KV explainer's positions section: every document keeps its original
 //     length in positions, later documents are offset by the lengths before
 //     them, slot j sits at its block's last token),
-//   * append: rotation of question/decode queries and keys, with the new keys
-//     and values written into the cache,
 //   * a zero-fill kernel for workspaces.
 //
 // Every RoPE'd element pair (x_i, x_{i+d/2}) is handled by one thread that
@@ -16,53 +14,6 @@
 #include "c2kv_launch.hpp"
 
 namespace c2kv {
-
-template <typename T> struct Chunk;
-template <> struct Chunk<bf16> {
-  static constexpr int CE = 8;
-  __device__ static void unpack(const uint4& u, float* f) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-  __device__ static uint4 pack(const float* f) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16 a = static_cast<bf16>(f[2 * i]);
-      const bf16 b = static_cast<bf16>(f[2 * i + 1]);
-      w[i] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-  }
-};
-template <> struct Chunk<float> {
-  static constexpr int CE = 4;
-  __device__ static void unpack(const uint4& u, float* f) {
-    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
-    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
-  }
-  __device__ static uint4 pack(const float* f) {
-    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
-  }
-};
-
-// Rotate one chunk pair (lo = elements [i0, i0+CE), hi = the same + d/2)
-// with per-element (cos, sin).
-template <typename T>
-__device__ __forceinline__ void rotate_chunk(uint4& lo, uint4& hi, const float* c, const float* s) {
-  constexpr int CE = Chunk<T>::CE;
-  float a[CE], b[CE], y0[CE], y1[CE];
-  Chunk<T>::unpack(lo, a);
-  Chunk<T>::unpack(hi, b);
-#pragma unroll
-  for (int e = 0; e < CE; ++e) rope_pair(a[e], b[e], c[e], s[e], y0[e], y1[e]);
-  lo = Chunk<T>::pack(y0);
-  hi = Chunk<T>::pack(y1);
-}
 
 // ------------------------------------------------------------ RoPE table
 __global__ void rope_table_kernel(float2* table, int npos, int half, const RopeFreqs f) {
@@ -427,78 +378,6 @@ hipError_t launch_compose(const ComposeParams& p, int dtype, int head_dim, bool 
   if (dtype == C2KV_BF16)
     return head_dim == 128 ? launch_compose_t<bf16, 128>(p, host_src, st) : launch_compose_t<bf16, 64>(p, host_src, st);
   return head_dim == 128 ? launch_compose_t<float, 128>(p, host_src, st) : launch_compose_t<float, 64>(p, host_src, st);
-}
-
-// ----------------------------------------------------------------- append
-// One workgroup per (request, token): the token's cos/sin are computed once
-// into LDS, then the threads loop over (head, chunk) pairs.  Heads [0, hq)
-// are query heads (rotated and written to the workspace), heads
-// [hq, hq+hkv) are new keys (rotated into the cache) together with their
-// values (copied).
-template <typename T, int D>
-__global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
-  constexpr int CE = Chunk<T>::CE, H = D / 2, TPH = H / CE;
-  __shared__ float2 s_cs[H];
-  const int tok = blockIdx.x;                  // grid = num_reqs * tq
-  const int ri = tok / p.tq, t = tok % p.tq;
-  const int r = p.req0 + ri;
-  const AppendReq rq = p.reqs[ri];
-  const int pos = rq.pos0 + t;
-  if ((int)threadIdx.x < H) {
-    float c, sn;
-    rope_cs(pos, p.freqs.f[threadIdx.x], c, sn);
-    s_cs[threadIdx.x] = make_float2(c, sn);
-  }
-  __syncthreads();
-  const int nh = p.hq + p.hkv;
-  for (int item = threadIdx.x; item < nh * TPH; item += blockDim.x) {
-    const int h = item / TPH, c = item % TPH;
-    float cs[CE], sn[CE];
-#pragma unroll
-    for (int e = 0; e < CE; ++e) {
-      const float2 v = s_cs[c * CE + e];
-      cs[e] = v.x;
-      sn[e] = v.y;
-    }
-    if (h < p.hq) {
-      const int64_t off = (((int64_t)r * p.tq + t) * p.hq + h) * D + c * CE;
-      const T* src = reinterpret_cast<const T*>(p.q) + off;
-      T* dst = reinterpret_cast<T*>(p.qrot) + off;
-      uint4 lo = *reinterpret_cast<const uint4*>(src);
-      uint4 hi = *reinterpret_cast<const uint4*>(src + H);
-      rotate_chunk<T>(lo, hi, cs, sn);
-      *reinterpret_cast<uint4*>(dst) = lo;
-      *reinterpret_cast<uint4*>(dst + H) = hi;
-    } else {
-      const int kvh = h - p.hq;
-      const int64_t soff = (((int64_t)r * p.tq + t) * p.hkv + kvh) * D + c * CE;
-      const int64_t doff = (((int64_t)r * p.hkv + kvh) * p.cap + rq.cache_len + t) * D + c * CE;
-      const T* ks = reinterpret_cast<const T*>(p.k_new) + soff;
-      const T* vs = reinterpret_cast<const T*>(p.v_new) + soff;
-      uint4 lo = *reinterpret_cast<const uint4*>(ks);
-      uint4 hi = *reinterpret_cast<const uint4*>(ks + H);
-      rotate_chunk<T>(lo, hi, cs, sn);
-      T* kd = reinterpret_cast<T*>(p.cache_k) + doff;
-      T* vd = reinterpret_cast<T*>(p.cache_v) + doff;
-      *reinterpret_cast<uint4*>(kd) = lo;
-      *reinterpret_cast<uint4*>(kd + H) = hi;
-      *reinterpret_cast<uint4*>(vd) = *reinterpret_cast<const uint4*>(vs);
-      *reinterpret_cast<uint4*>(vd + H) = *reinterpret_cast<const uint4*>(vs + H);
-    }
-  }
-}
-
-template <typename T, int D>
-static hipError_t launch_append_t(const AppendParams& p, hipStream_t st) {
-  const int64_t blocks = (int64_t)p.num_reqs * p.tq;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((append_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_append(const AppendParams& p, int dtype, int head_dim, hipStream_t st) {
-  if (dtype == C2KV_BF16) return head_dim == 128 ? launch_append_t<bf16, 128>(p, st) : launch_append_t<bf16, 64>(p, st);
-  return head_dim == 128 ? launch_append_t<float, 128>(p, st) : launch_append_t<float, 64>(p, st);
 }
 
 // --------------------------------------------------------------- zero fill

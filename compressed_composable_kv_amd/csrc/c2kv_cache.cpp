@@ -35,7 +35,7 @@ struct CachePlan {
   bool decode = false;
   int32_t nug = 0, nblk_q = 0, chunk = 0;
   std::vector<int32_t> nsplit, chunk_r, pbase;   // pbase: first partial of the request within its launch
-  size_t qrot_off = 0, part_off = 0, ml_off = 0, total = 0;
+  size_t part_off = 0, ml_off = 0, total = 0;
 };
 
 c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, int32_t hq, int32_t hkv,
@@ -58,7 +58,7 @@ c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, i
     total_keys += c + tq;
     max_len = std::max(max_len, c + tq);
   }
-  const int64_t step = decode ? 4 * 32 : kBN;        // keys per workgroup step (all waves)
+  const int64_t step = decode ? 4 * 32 : 2 * kBN;    // keys per workgroup step (all waves)
   P.nsplit.resize(num_reqs);
   P.chunk_r.resize(num_reqs);
   if (!decode) {
@@ -117,8 +117,7 @@ c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, i
     if (cnt >= ((size_t)1 << 31)) return fail(C2KV_ERR_CAPACITY, "%zu split partials in one launch", cnt);
     max_part = std::max(max_part, cnt);
   }
-  P.qrot_off = 0;
-  P.part_off = decode ? 0 : align_up((size_t)num_reqs * tq * hq * head_dim * elem_bytes(dt));
+  P.part_off = 0;
   P.ml_off = P.part_off + align_up(max_part * head_dim * sizeof(float));
   P.total = P.ml_off + align_up(max_part * sizeof(float2));
   return C2KV_OK;
@@ -193,35 +192,27 @@ c2kv_status cache_attention(const void* q, const void* k_new, const void* v_new,
       e = launch_decode_attn(dp, dt, head_dim, stream);
       if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     } else {
-      AppendParams ap;
-      std::memset(&ap, 0, sizeof(ap));
-      ap.q = q; ap.k_new = k_new; ap.v_new = v_new;
-      ap.qrot = ws + P.qrot_off;
-      ap.cache_k = cache_k; ap.cache_v = cache_v; ap.cap = cap;
-      ap.req0 = r0; ap.num_reqs = cnt; ap.tq = tq; ap.hq = hq; ap.hkv = hkv;
-      ap.freqs = freqs;
-      for (int32_t i = 0; i < cnt; ++i) { ap.reqs[i].cache_len = cache_len[r0 + i]; ap.reqs[i].pos0 = q_pos0[r0 + i]; }
-      e = launch_append(ap, dt, head_dim, stream);
-      if (e != hipSuccess) return hip_fail(e, "append kernel launch");
       CacheParams cp;
       std::memset(&cp, 0, sizeof(cp));
-      cp.qrot = ws + P.qrot_off;
+      cp.q = q; cp.k_new = k_new; cp.v_new = v_new;
       cp.kc = cache_k; cp.vc = cache_v; cp.o = o; cp.lse = lse; cp.part_o = part_o; cp.part_ml = part_ml;
       cp.cap = cap; cp.req0 = r0; cp.num_reqs = cnt; cp.tq = tq; cp.hq = hq; cp.hkv = hkv; cp.G = G;
       cp.nblk_q = P.nblk_q; cp.nug = P.nug; cp.chunk = P.chunk;
       cp.scale_log2 = scale_log2(head_dim);
+      cp.freqs = freqs;
       int64_t wg = 0;
       for (int32_t i = 0; i < cnt; ++i) {
         cp.reqs[i].wg0 = (int32_t)wg;
         cp.reqs[i].cache_len = cache_len[r0 + i];
         cp.reqs[i].nsplit = P.nsplit[r0 + i];
         cp.reqs[i].pbase = P.pbase[r0 + i];
+        cp.reqs[i].pos0 = q_pos0[r0 + i];
         wg += (int64_t)hkv * P.nsplit[r0 + i] * P.nug;
       }
       cp.total_wg = (int32_t)wg;
       cp.grid_wg = (int32_t)((wg + 7) / 8 * 8);
-      e = launch_cache_attn(cp, dt, head_dim, stream);
-      if (e != hipSuccess) return hip_fail(e, "cache attention kernel launch");
+      e = launch_prefill_attn(cp, dt, head_dim, stream);
+      if (e != hipSuccess) return hip_fail(e, "prefill attention kernel launch");
     }
     if (stride > 1) {
       MergeParams mp;

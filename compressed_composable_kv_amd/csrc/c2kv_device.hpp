@@ -82,6 +82,76 @@ struct RopeFreqs {
   float f[kMaxHalfDim];
 };
 
+// 16-byte chunks of CE elements, unpacked to and packed from fp32.
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16> {
+  static constexpr int CE = 8;
+  __device__ static void unpack(const uint4& u, float* f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static uint4 pack(const float* f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16 a = static_cast<bf16>(f[2 * i]);
+      const bf16 b = static_cast<bf16>(f[2 * i + 1]);
+      w[i] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct Chunk<float> {
+  static constexpr int CE = 4;
+  __device__ static void unpack(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+};
+
+// Rotate one chunk pair (lo = elements [i0, i0+CE), hi = the same + d/2)
+// with per-element (cos, sin).
+template <typename T>
+__device__ __forceinline__ void rotate_chunk(uint4& lo, uint4& hi, const float* c, const float* s) {
+  constexpr int CE = Chunk<T>::CE;
+  float a[CE], b[CE], y0[CE], y1[CE];
+  Chunk<T>::unpack(lo, a);
+  Chunk<T>::unpack(hi, b);
+#pragma unroll
+  for (int e = 0; e < CE; ++e) rope_pair(a[e], b[e], c[e], s[e], y0[e], y1[e]);
+  lo = Chunk<T>::pack(y0);
+  hi = Chunk<T>::pack(y1);
+}
+
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wave's LDS operations (lgkmcnt 0), not for its vector-memory operations,
+// so DMA and global loads in flight stay in flight (__syncthreads would
+// wait for them too).  The empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations (loads,
+// stores, LDS DMA) are outstanding; the counter retires in issue order, so
+// every older operation has completed.  gfx9 encoding: vmcnt bits [3:0] and
+// [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // ---------------------------------------------------------------- waves
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
 // l^48) with gfx950's VALU lane swaps instead of LDS permutes: with both
@@ -142,6 +212,7 @@ struct CacheReq {
   int32_t cache_len; // rows before the appended question
   int32_t nsplit;    // key chunks
   int32_t pbase;     // first split partial of the request (when nsplit > 1)
+  int32_t pos0;      // position of the first question token
 };
 
 // Split partials of a launch are compact: request ri's partial of (head,
@@ -150,9 +221,11 @@ struct CacheReq {
 // log2 domain, sum l) in part_ml[index], so the (m, l) pairs of one output
 // row are contiguous.
 struct CacheParams {
-  const void* qrot;     // [R][tq][hq][D] rotated queries (workspace)
-  const void* kc;       // [R][hkv][cap][D]
-  const void* vc;
+  const void* q;        // [R][tq][hq][D] pre-RoPE question queries
+  const void* k_new;    // [R][tq][hkv][D] pre-RoPE question keys
+  const void* v_new;    // [R][tq][hkv][D]
+  void* kc;             // [R][hkv][cap][D]
+  void* vc;
   void* o;              // [R][tq][hq][D]
   float* lse;           // [R][hq][tq] or null
   float* part_o;        // split partials: o
@@ -162,6 +235,7 @@ struct CacheParams {
   int32_t num_reqs, tq, hq, hkv, G, nblk_q, nug, chunk;
   int32_t total_wg, grid_wg;
   float scale_log2;
+  RopeFreqs freqs;
   CacheReq reqs[C2KV_MAX_BATCH];
 };
 

@@ -81,21 +81,6 @@ inline ComposeTiling compose_tiling(int dtype_bytes, int head_dim, int hkv) {
   return ComposeTiling{256 / tph / gpb, gpb, (pairs + gpb - 1) / gpb};
 }
 
-struct AppendReq {
-  int32_t cache_len, pos0;
-};
-struct AppendParams {
-  const void* q;
-  const void* k_new;
-  const void* v_new;
-  void* qrot;
-  void* cache_k;
-  void* cache_v;
-  int64_t cap;
-  int32_t req0, num_reqs, tq, hq, hkv, pad;
-  RopeFreqs freqs;
-  AppendReq reqs[C2KV_MAX_BATCH];
-};
 
 // Extractor layer GEMM C = A * B^T (bf16, fp32 accumulation).  A row range
 // of A uses weights b0 (sel 0) or b1 (sel 1); tile0 is its first 128-row
@@ -139,11 +124,10 @@ hipError_t launch_rope_table(float2* table, int npos, int head_dim, const RopeFr
 hipError_t launch_rotate_k(const RotateParams& p, int dtype, int head_dim, hipStream_t st);
 constexpr int kExtractAttn = 0, kExtractCount = 1, kExtractDump = 2;   // launch_extract_attn modes
 hipError_t launch_extract_attn(const ExtractParams& p, int dtype, int head_dim, int mode, hipStream_t st);
-hipError_t launch_cache_attn(const CacheParams& p, int dtype, int head_dim, hipStream_t st);
+hipError_t launch_prefill_attn(const CacheParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_decode_attn(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_compose(const ComposeParams& p, int dtype, int head_dim, bool host_src, hipStream_t st);
-hipError_t launch_append(const AppendParams& p, int dtype, int head_dim, hipStream_t st);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t st);
 hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t st);
 hipError_t launch_rms_norm(const void* x, const void* gamma, void* h, int64_t rows, int dm, float eps,
