@@ -266,6 +266,39 @@ def test_prefill_parity_ragged(c2kv, tq, hq, hkv, dt):
         assert torch.equal(ckd[r, :, lens[r] + tq:].cpu(), ck[r, :, lens[r] + tq:])
 
 
+@pytest.mark.parametrize("tq,hq,hkv,d,dt", [(300, 4, 4, 128, torch.bfloat16), (150, 4, 2, 128, torch.float32),
+                                            (200, 14, 2, 64, torch.bfloat16)])
+def test_prefill_long_question(c2kv, tq, hq, hkv, d, dt):
+    """A question longer than a key chunk: its new rows fall into several
+    chunks, whose workgroups each rotate and write their own before reading
+    them; four query blocks per workgroup at G = 1 (the largest cos/sin
+    table); fp32 at d = 128 (one LDS stage); an empty cache."""
+    theta = 1e6
+    lens = [1000, 37, 0]
+    R = len(lens)
+    cap = max(lens) + tq + 5
+    ck = W.normal((R, hkv, cap, d), dt, 26, W.P_K)
+    cv = W.normal((R, hkv, cap, d), dt, 26, W.P_V)
+    q = W.normal((R, tq, hq, d), dt, 26, W.P_PREFILL)
+    kn = W.normal((R, tq, hkv, d), dt, 26, W.P_NEW_KV)
+    vn = W.normal((R, tq, hkv, d), dt, 26, W.P_NEW_KV, salt=1)
+    qpos = [5 * lens[r] + 3 for r in range(R)]
+    ckd, cvd = ck.to(DEV), cv.to(DEV)
+    o, lse = c2kv.attn_prefill(q.to(DEV), kn.to(DEV), vn.to(DEV), ckd, cvd, lens, qpos, theta, return_lse=True)
+    for r in range(R):
+        rk = ck[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        rv = cv[r, :, :lens[r]].transpose(0, 1).float().numpy()
+        ro, rl, rk2, _ = O.append_and_attend(q[r].float().numpy(), kn[r].float().numpy(), vn[r].float().numpy(),
+                                             rk, rv, qpos[r], theta, dtname(dt))
+        assert_close(np32(o[r]), ro, dtname(dt), f"request {r}")
+        assert_lse_close(np32(lse[r]), rl, dtname(dt), f"request {r}")
+        gk = np32(ckd[r, :, :lens[r] + tq]).transpose(1, 0, 2)
+        assert_rotated_close(gk[lens[r]:], rk2[lens[r]:], kn[r].float().numpy(), dtname(dt), f"appended keys {r}")
+        assert torch.equal(cvd[r, :, lens[r]:lens[r] + tq].transpose(0, 1).cpu(), vn[r])
+        assert torch.equal(ckd[r, :, :lens[r]].cpu(), ck[r, :, :lens[r]])
+        assert torch.equal(ckd[r, :, lens[r] + tq:].cpu(), ck[r, :, lens[r] + tq:])
+
+
 @pytest.mark.parametrize("hq,hkv,d,dt", [(32, 8, 128, torch.bfloat16), (28, 4, 128, torch.bfloat16),
                                          (40, 8, 128, torch.bfloat16), (3, 3, 64, torch.float32)])
 def test_decode_parity_varlen(c2kv, hq, hkv, d, dt):
