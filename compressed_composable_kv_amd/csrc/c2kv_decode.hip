@@ -420,18 +420,19 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
 }
 
 // ---------------------------------------------------------------- merge
-// One workgroup per (output row, DIMS-wide slice): the split partials of
-// that row (request of the launch, head, token) are combined by
-// log-sum-exp.  The row's (m, l) pairs are contiguous and staged in LDS
-// with one 8-byte load per split; DIMS / 4 threads cover the slice and the
-// workgroup's kThreads / (DIMS / 4) groups of them take the splits in turn,
-// with batches of kMergeNB o slices per thread in flight before the
-// arithmetic.  Rows of requests with a single key chunk already hold their
-// output.  Decode merges many splits per row over few rows and takes 32-dim
-// slices (more workgroups per row); prefill merges fewer splits over many
-// rows and takes whole rows.
-constexpr int kMergeDimsDecode = 32;
-constexpr int kMergeNB = 4;
+// The split partials of each output row (request of the launch, head,
+// token) are combined by log-sum-exp.  WPR waves take one row: many rows
+// with few splits each (a decode batch, a prefill) take one wave per row,
+// few rows with many splits (decode of one request) take the workgroup's
+// four waves per row.  Lane s of every wave of the row holds the (m, l) of
+// split s (splits past 64 in further rounds); the row's 2 * WPR half-waves
+// take the splits in turn, each lane covering D/32 consecutive dims, with
+// kMergeNB partial rows per half-wave in flight, the first batch loaded
+// together with the (m, l) pairs before the maximum is known.  The
+// half-waves are added with one lane swap and, with WPR = 4, through LDS.
+// Rows of requests with a single key chunk already hold their output.
+constexpr int kMergeNB = 8;
+constexpr int kMergeRowsPerWave = 512;   // at least this many rows: one wave per row
 
 __device__ __forceinline__ float wave_max64(float x) {
 #pragma unroll
@@ -439,15 +440,19 @@ __device__ __forceinline__ float wave_max64(float x) {
   return wave_max_16_32(x);
 }
 
-template <typename T, int D, int DIMS>
+template <int N> struct MergeVec;
+template <> struct MergeVec<4> { using type = f32x4; };
+template <> struct MergeVec<2> { using type = float2; };
+
+template <typename T, int D, int WPR>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
-  constexpr int DQ = D / DIMS, TPS = DIMS / 4, SG = kThreads / TPS, NB = kMergeNB;
-  __shared__ float2 s_ml[C2KV_MAX_SPLITS];
-  __shared__ __attribute__((aligned(16))) float s_acc[SG][DIMS];
-  __shared__ float s_ls[SG];
-  const int row = blockIdx.x / DQ, dq = blockIdx.x % DQ;
+  constexpr int DPL = D / 32, NB = kMergeNB, HW = 2 * WPR;   // dims per lane, half-waves per row
+  static_assert(WPR == 1 || WPR == kWaves, "one wave or the whole workgroup per row");
+  using VF = typename MergeVec<DPL>::type;
+  __shared__ float s_red[WPR > 1 ? kWaves * (D + 1) : 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = WPR == 1 ? blockIdx.x * kWaves + wave : blockIdx.x;
   if (row >= p.num_rows) return;
-  const int tid = threadIdx.x;
   const int ri = row / (p.hq * p.tq);
   const int rem = row % (p.hq * p.tq);          // head * tq + t
   const int nsplit = p.nsplit[ri];
@@ -455,47 +460,68 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   const int64_t idx0 = (int64_t)p.pbase[ri] + (int64_t)rem * nsplit;
   const float* base = p.part_o + idx0 * D;
   const float2* ml = p.part_ml + idx0;
-  const int sg = tid / TPS, d4 = tid % TPS;
-  const int col = dq * DIMS + 4 * d4;
-  for (int s = tid; s < nsplit; s += kThreads) s_ml[s] = ml[s];
-  // first batch of o slices in flight while the maxima are reduced
-  f32x4 os[NB];
+  const int half = lane >> 5, col = (lane & 31) * DPL;
+  const int hw = (WPR == 1 ? 0 : 2 * wave) + half;     // this half-wave's first split
+  auto load_o = [&](int s) { return *reinterpret_cast<const VF*>(base + (int64_t)min(s, nsplit - 1) * D + col); };
+  // (m, l) of the first 64 splits, and the first batch of partial rows
+  const float2 ml0 = ml[min(lane, nsplit - 1)];
+  VF os[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
-    os[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(sg + SG * i, nsplit - 1) * D + col);
-  __syncthreads();
-  float M = -INFINITY;
-  for (int s = tid & 63; s < nsplit; s += 64) M = fmaxf(M, s_ml[s].x);
-  M = wave_max64(M);              // every wave holds the row maximum
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NB; ++i) os[i] = load_o(hw + HW * i);
+  float M = lane < nsplit ? ml0.x : -INFINITY;
+  for (int s = lane + 64; s < nsplit; s += 64) M = fmaxf(M, ml[s].x);
+  M = wave_max64(M);
+  auto split_ml = [&](int s) {
+    // splits below 64 come from their lane, the rest from memory
+    const float2 v = make_float2(__shfl(ml0.x, s & 63), __shfl(ml0.y, s & 63));
+    return s < 64 ? v : ml[min(s, nsplit - 1)];
+  };
+  VF acc;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
   float ls = 0.f;
-  for (int s0 = sg;; s0 += SG * NB) {
+  for (int s0 = hw;; s0 += HW * NB) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int s = s0 + SG * i;
-      const float2 sm = s_ml[min(s, nsplit - 1)];
+      const int s = s0 + HW * i;
+      const float2 sm = split_ml(s);
       const float w = (s < nsplit && sm.x != -INFINITY) ? __builtin_amdgcn_exp2f(sm.x - M) : 0.f;
-      acc += os[i] * w;
-      if (s < nsplit) ls += sm.y * w;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += os[i][e] * w;
+      ls += s < nsplit ? sm.y * w : 0.f;
     }
-    if (s0 + SG * NB >= nsplit) break;
+    if (s0 + HW * NB >= nsplit) break;
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
-      os[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(s0 + SG * (NB + i), nsplit - 1) * D + col);
+    for (int i = 0; i < NB; ++i) os[i] = load_o(s0 + HW * (NB + i));
   }
-  *reinterpret_cast<f32x4*>(&s_acc[sg][4 * d4]) = acc;
-  if (d4 == 0) s_ls[sg] = ls;
-  __syncthreads();
-  if (tid < DIMS) {
-    float a = 0.f, lsum = 0.f;
+  // add the odd half-wave into the even one (lanes l and l ^ 32)
 #pragma unroll
-    for (int j = 0; j < SG; ++j) { a += s_acc[j][tid]; lsum += s_ls[j]; }
+  for (int e = 0; e < DPL; ++e) acc[e] += __shfl_xor(acc[e], 32);
+  ls += __shfl_xor(ls, 32);
+  if constexpr (WPR > 1) {
+    if (half == 0) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) s_red[wave * (D + 1) + col + e] = acc[e];
+      if (lane == 0) s_red[wave * (D + 1) + D] = ls;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < WPR; ++w) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += s_red[w * (D + 1) + col + e];
+      ls += s_red[w * (D + 1) + D];
+    }
+  }
+  if (half == 0) {
     const int head = rem / p.tq, t = rem % p.tq;
     const int r = p.req0 + ri;
-    T* orow = reinterpret_cast<T*>(p.o) + (((int64_t)r * p.tq + t) * p.hq + head) * D;
-    orow[dq * DIMS + tid] = from_f32<T>(a / lsum);
-    if (dq == 0 && tid == 0 && p.lse)
-      p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (M + __log2f(lsum)) * 0.69314718055994531f;
+    T* orow = reinterpret_cast<T*>(p.o) + (((int64_t)r * p.tq + t) * p.hq + head) * D + col;
+    const float inv = 1.f / ls;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) orow[e] = from_f32<T>(acc[e] * inv);
+    if (lane == 0 && p.lse)
+      p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (M + __log2f(ls)) * 0.69314718055994531f;
   }
 }
 
@@ -513,11 +539,10 @@ hipError_t launch_decode_attn(const DecodeParams& p, int dtype, int head_dim, hi
 
 template <typename T, int D>
 static hipError_t launch_merge_t(const MergeParams& p, hipStream_t st) {
-  if (p.tq > 1)
-    hipLaunchKernelGGL((merge_kernel<T, D, D>), dim3(p.num_rows), dim3(kThreads), 0, st, p);
+  if (p.num_rows >= kMergeRowsPerWave)
+    hipLaunchKernelGGL((merge_kernel<T, D, 1>), dim3((p.num_rows + kWaves - 1) / kWaves), dim3(kThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((merge_kernel<T, D, kMergeDimsDecode>), dim3(p.num_rows * (D / kMergeDimsDecode)),
-                       dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((merge_kernel<T, D, kWaves>), dim3(p.num_rows), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
