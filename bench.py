@@ -310,7 +310,7 @@ def achievable_peaks(torch, dev):
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
         buf = torch.ones(16 << 30, dtype=torch.uint8, device=dev)
         out = torch.empty(4 * 256 * 16384, dtype=torch.uint8, device=dev)
-        for blocks in (4096, 8192, 16384):
+        for blocks in (256, 512, 1024, 2048):
             r = lib.c2kv_probe_hbm_read(buf.data_ptr(), buf.numel(), out.data_ptr(), out.numel(), blocks, 5,
                                         ctypes.byref(ms))
             if r > 0 and (read is None or r > read):
@@ -334,7 +334,8 @@ def achievable_peaks(torch, dev):
     free(torch)
     return {"mfma_bf16_tflops": mfma, "hbm_read_gbs": read, "hbm_copy_gbs": 2 * 2 * n / (best * 1e-3) / 1e9,
             "how": "MFMA: probe/mfma_peak.hip, 512 workgroups x 8 waves, 16 independent chains per wave; "
-                   f"HBM read: probe/hbm_read.hip, non-temporal streaming read of 16 GiB ({read_blocks} workgroups), best of 5; "
+                   f"HBM read: probe/hbm_read.hip, non-temporal streaming read of 16 GiB, a contiguous share per "
+                   f"workgroup ({read_blocks} workgroups; best of 256-2048), best of 5; "
                    "copy: torch copy of 1 GiB, read + write bytes, best of 3"}
 
 
