@@ -31,7 +31,7 @@ namespace {
 //    no second, partly filled round trails the first.
 constexpr int64_t kDecodeSlots = 3 * 256;   // decode workgroups resident at once on a 256-CU MI355X
 // Minimum 128-key workgroup steps per decode piece.  Measured on the Llama
-// layer's batch-1 decode (8 KV heads x 8193 keys), one box: 14.6 us per
+// layer's batch-1 decode (8 KV heads x 8193 keys) on one MI355X: 14.6 us per
 // step at 1 step per piece, 15.5 at 2, 13.0 at 3, 14.6 at 4, 18.1 at 6;
 // the Qwen2.5 pool (pieces of about 9 steps) is unaffected.
 constexpr int64_t kDecodeMinSteps = 3;
