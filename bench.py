@@ -90,11 +90,18 @@ def log(msg):
 
 
 def sources_sha(paths=DECODE_SOURCES) -> str:
+    """Hash of the sources' code: comments and blank space are dropped
+    first, so an edit to the wording of a comment does not retire a counter
+    summary taken from the same code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for pth in paths:
-        with open(os.path.join(ROOT, pth), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, pth), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
