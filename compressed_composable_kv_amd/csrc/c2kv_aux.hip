@@ -116,7 +116,8 @@ struct ComposeTable {
   int run_req[kComposeRuns];
   int doc_occ0[kComposeDocs + 1];   // first entry of each document in by_doc
   int doc_unit0[kComposeDocs + 1];  // first unit of each document; [num_docs] = total units
-  int doc_cnt[kComposeDocs];
+  int doc_cnt[kComposeDocs];        // occurrences of each document
+  int rank_cnt[kComposeDocs];       // running counts of the ranking pass
   long long wsum_n[4];
   int wsum_m[4];
 };
@@ -133,25 +134,74 @@ __device__ __forceinline__ X wave_incl_scan(X x) {
   return x;
 }
 
-__device__ void compose_build_table(const ComposeParams& p, ComposeTable& tb) {
+// The table is built in two phases.  Phase A (the launch table into LDS,
+// each document's occurrence count by an LDS histogram, and each document's
+// first occurrence entry and first unit) is all a unit needs to find its
+// document and load its rows; phase B (the stable grouping of occurrences
+// by document, and each occurrence's cache row, position offset and
+// request) is needed only to store.  The kernel issues its first unit's
+// loads between the two, so phase B runs while they are in flight.
+__device__ void compose_table_a(const ComposeParams& p, ComposeTable& tb) {
   constexpr int PER = kComposeOcc / 256;   // occurrences per thread
   static_assert(PER == 4, "one 32-bit word of occurrence bytes per thread");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  // one round of independent loads of the launch table into LDS
+  // one round of independent loads of the launch table (kernel arguments),
+  // all issued before any is used: indices are clamped so that no load
+  // waits behind a branch on another one
+  const int td = min(t, kComposeDocs - 1), tr = min(t, kComposeRuns - 1);
+  const int ld_n = p.docs[td].n;
+  const int ld_occ0 = p.run_occ0[min(t, kComposeRuns)];
+  const int ld_row0 = p.run_row0[tr], ld_pos0 = p.run_pos0[tr], ld_base = p.run_base[tr], ld_req = p.run_req[tr];
+  const uint32_t ld_occ = *reinterpret_cast<const uint32_t*>(&p.occ_doc[PER * min(t, kComposeOcc / PER - 1)]);
+  const int num_docs = p.num_docs, num_runs = p.num_runs, num_occ = p.num_occ;
+  // (the empty asm makes every load above complete here, in one wait,
+  // instead of each being sunk into the branch that stores it)
+  asm volatile("" : : "v"(ld_n), "v"(ld_occ0), "v"(ld_row0), "v"(ld_pos0), "v"(ld_base), "v"(ld_req), "v"(ld_occ),
+               "s"(num_docs), "s"(num_runs), "s"(num_occ));
   if (t < kComposeDocs) {
     tb.doc_cnt[t] = 0;
-    if (t < p.num_docs) tb.doc_n[t] = p.docs[t].n;
+    tb.rank_cnt[t] = 0;
+    if (t < num_docs) tb.doc_n[t] = ld_n;
   }
-  if (t <= p.num_runs) tb.run_occ0[t] = p.run_occ0[t];
-  if (t < p.num_runs) {
-    tb.run_row0[t] = p.run_row0[t];
-    tb.run_pos0[t] = p.run_pos0[t];
-    tb.run_base[t] = p.run_base[t];
-    tb.run_req[t] = p.run_req[t];
+  if (t <= num_runs) tb.run_occ0[t] = ld_occ0;
+  if (t < num_runs) {
+    tb.run_row0[t] = ld_row0;
+    tb.run_pos0[t] = ld_pos0;
+    tb.run_base[t] = ld_base;
+    tb.run_req[t] = ld_req;
   }
-  if (PER * t < p.num_occ)
-    *reinterpret_cast<uint32_t*>(&tb.occ[PER * t]) = *reinterpret_cast<const uint32_t*>(&p.occ_doc[PER * t]);
+  if (PER * t < num_occ) *reinterpret_cast<uint32_t*>(&tb.occ[PER * t]) = ld_occ;
   __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (PER * t + i < num_occ) atomicAdd(&tb.doc_cnt[(ld_occ >> (8 * i)) & (kComposeNoRealign - 1)], 1);
+  __syncthreads();
+  // per document (one per lane of wave 0): first by_doc entry and first unit
+  static_assert(kComposeDocs == 64, "one wave covers the documents");
+  if (wave == 0) {
+    int c = 0, nu = 0;
+    if (lane < num_docs) {
+      const int m = (tb.doc_n[lane] + p.ratio_k - 1) / p.ratio_k;
+      c = tb.doc_cnt[lane];
+      nu = ((m + p.rpt - 1) / p.rpt) * p.nblk * ((c + kComposeGroup - 1) / kComposeGroup);
+    }
+    const int ic = wave_incl_scan(c), iu = wave_incl_scan(nu);
+    if (lane < num_docs) {
+      tb.doc_occ0[lane] = ic - c;
+      tb.doc_unit0[lane] = iu - nu;
+    }
+    if (lane == 63) {
+      tb.doc_occ0[num_docs] = ic;
+      tb.doc_unit0[num_docs] = iu;
+    }
+  }
+  __syncthreads();
+}
+
+// (its barriers order LDS only, so the first unit's loads stay in flight)
+__device__ void compose_table_b(const ComposeParams& p, ComposeTable& tb) {
+  constexpr int PER = kComposeOcc / 256;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int ml[PER], rl[PER], dl[PER];
   long long nl[PER];
   int sm = 0;
@@ -182,7 +232,7 @@ __device__ void compose_build_table(const ComposeParams& p, ComposeTable& tb) {
   const int im = wave_incl_scan(sm);
   const long long in_ = wave_incl_scan(sn);
   if (lane == 63) { tb.wsum_m[wave] = im; tb.wsum_n[wave] = in_; }
-  __syncthreads();
+  lds_barrier();
   int bm = im - sm;
   long long bn = in_ - sn;
   for (int w = 0; w < wave; ++w) { bm += tb.wsum_m[w]; bn += tb.wsum_n[w]; }
@@ -214,38 +264,18 @@ __device__ void compose_build_table(const ComposeParams& p, ComposeTable& tb) {
         same &= bit ? mb : ~mb;
       }
       const int below = __popcll(same & ((1ull << lane) - 1));
-      const int base = valid ? tb.doc_cnt[dd] : 0;
+      const int base = valid ? tb.rank_cnt[dd] : 0;
       __builtin_amdgcn_wave_barrier();   // every lane has read its base before any lane updates it
       if (valid) {
         tb.rank[o] = (short)(base + below);
-        if ((same >> lane) == 1ull) tb.doc_cnt[dd] = base + __popcll(same);
+        if ((same >> lane) == 1ull) tb.rank_cnt[dd] = base + __popcll(same);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
-  __syncthreads();
-  // per document (one per lane of wave 0): first by_doc entry and first unit
-  static_assert(kComposeDocs == 64, "one wave covers the documents");
-  if (wave == 0) {
-    int c = 0, nu = 0;
-    if (lane < p.num_docs) {
-      const int m = (tb.doc_n[lane] + p.ratio_k - 1) / p.ratio_k;
-      c = tb.doc_cnt[lane];
-      nu = ((m + p.rpt - 1) / p.rpt) * p.nblk * ((c + kComposeGroup - 1) / kComposeGroup);
-    }
-    const int ic = wave_incl_scan(c), iu = wave_incl_scan(nu);
-    if (lane < p.num_docs) {
-      tb.doc_occ0[lane] = ic - c;
-      tb.doc_unit0[lane] = iu - nu;
-    }
-    if (lane == 63) {
-      tb.doc_occ0[p.num_docs] = ic;
-      tb.doc_unit0[p.num_docs] = iu;
-    }
-  }
-  __syncthreads();
+  lds_barrier();
   // cache rows and position offsets relative to the start of each run; the
   // occurrence lists of the documents
 #pragma unroll
@@ -260,7 +290,7 @@ __device__ void compose_build_table(const ComposeParams& p, ComposeTable& tb) {
       tb.by_doc[tb.doc_occ0[dl[i]] + tb.rank[o]] = (short)o;
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 template <typename T, int D>
@@ -347,15 +377,20 @@ __global__ __launch_bounds__(256, 3) void compose_kernel(const ComposeParams p) 
   __shared__ ComposeTable tb;
   int u = blockIdx.x;
   if (u >= p.total_units) return;
-  compose_build_table(p, tb);
+  compose_table_a(p, tb);
   const int total = tb.doc_unit0[p.num_docs];
   // one unit in flight per wave: a unit's loads are amortised over the
   // stores of its whole occurrence group, and three workgroups per CU keep
-  // other waves' loads in flight meanwhile
-  for (; u < total; u += gridDim.x) {
-    ComposeUnit<T, D> cur;
-    cur.load(p, tb, u);
+  // other waves' loads in flight meanwhile.  The first unit's loads are
+  // issued before the second phase of the table, which runs under them.
+  ComposeUnit<T, D> cur;
+  cur.load(p, tb, u);
+  compose_table_b(p, tb);
+  for (;;) {
     cur.store(p, tb);
+    u += gridDim.x;
+    if (u >= total) break;
+    cur.load(p, tb, u);
   }
 }
 
@@ -365,8 +400,7 @@ static hipError_t launch_compose_t(const ComposeParams& p, bool host_src, hipStr
   if (units == 0) return hipSuccess;
   // device sources: three workgroups per CU (12 waves) is the measured
   // optimum for 1k-2k units: fewer leaves HBM idle, more adds dispatch
-  // without more bytes in flight (the loop already prefetches one unit
-  // ahead).  Host sources: 16 workgroups (about 1 MB in flight) keep the
+  // without more bytes in flight.  Host sources: 16 workgroups (about 1 MB in flight) keep the
   // host link busy; more concurrent readers made its transfers slower
   // (56 GB/s at 12-16 workgroups, 48 GB/s at 192 or more).
   const int blocks = min(units, host_src ? 16 : 3 * 256);
