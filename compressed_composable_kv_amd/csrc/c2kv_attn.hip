@@ -72,8 +72,7 @@ struct ExtractPlan {
 
 __device__ __forceinline__ ExtractPlan extract_plan(const ExtractParams& p, int L, int wave) {
   ExtractPlan P;
-  int b = 0;
-  while (b + 1 < p.num_docs && p.docs[b + 1].wg0 <= L) ++b;
+  const int b = request_of(p.docs, p.num_docs, L);
   const ExtractDoc& dc = p.docs[b];
   P.doc = b;
   P.row0 = dc.row0;
@@ -699,8 +698,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_attn_kernel(const CacheP
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = wave / kWaves, wq = wave % kWaves;
   const int r16 = lane & 15, g = lane >> 4;
-  int ri = 0;
-  while (ri + 1 < p.num_reqs && p.reqs[ri + 1].wg0 <= L) ++ri;
+  const int ri = request_of(p.reqs, p.num_reqs, L);
   const CacheReq rq = p.reqs[ri];
   const int r = p.req0 + ri;
   const int per_kvh = rq.nsplit * p.nug;

@@ -202,8 +202,7 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
   if (L >= p.total_wg) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  int ri = 0;
-  while (ri + 1 < p.num_reqs && p.reqs[ri + 1].wg0 <= L) ++ri;
+  const int ri = request_of(p.reqs, p.num_reqs, L);
   const DecodeReq rq = p.reqs[ri];
   const int r = p.req0 + ri;
   const int local = L - rq.wg0;

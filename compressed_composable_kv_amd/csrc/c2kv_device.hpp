@@ -130,6 +130,20 @@ __device__ __forceinline__ void rotate_chunk(uint4& lo, uint4& hi, const float* 
   hi = Chunk<T>::pack(y1);
 }
 
+// Index of the request (or document) that workgroup L belongs to, given
+// the entries' first workgroups wg0 (ascending, the first 0) in a
+// kernel-argument table of up to 64 entries: one lane-indexed load and a
+// ballot, instead of a walk whose every step waits for a kernel-argument
+// load.
+template <typename Req>
+__device__ __forceinline__ int request_of(const Req* reqs, int num_reqs, int L) {
+  if (num_reqs == 1) return 0;
+  const int lane = threadIdx.x & 63;
+  const int w = reqs[min(lane, num_reqs - 1)].wg0;
+  const uint64_t le = __ballot(lane < num_reqs && w <= L);
+  return __builtin_amdgcn_readfirstlane(__popcll(le) - 1);
+}
+
 // Workgroup barrier for data exchanged through LDS only: waits for this
 // wave's LDS operations (lgkmcnt 0), not for its vector-memory operations,
 // so DMA and global loads in flight stay in flight (__syncthreads would
