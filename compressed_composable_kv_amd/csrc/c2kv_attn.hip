@@ -12,13 +12,18 @@
 // Tile shapes.  A workgroup is 4 waves; each wave owns one "unit" = 32 query
 // rows of one query head, and all units of a workgroup share one KV head, so
 // the K/V tiles staged in LDS (64 keys, double buffered) serve every wave.
-// S^T = K Q^T is computed with v_mfma_f32_16x16x32_bf16 (keys on the M side,
-// queries on the N side), so each lane's accumulators belong to ONE query:
-// softmax row statistics need two cross-lane steps and the O^T rescale is a
-// per-lane scalar.  P^T goes straight from the S^T accumulators into the B
-// operand of O^T += V^T P^T.  Tiles arrive by LDS DMA; extraction stages V^T
-// tiles from a transposed workspace, prefill stages row-major V tiles of the
-// cache and reads the V^T operand with transposing LDS reads.
+// S^T = K Q^T puts keys on the M side and queries on the N side, so each
+// lane's accumulators belong to ONE query and the O^T rescale is a per-lane
+// scalar; P^T goes straight from the S^T accumulators into the B operand of
+// O^T += V^T P^T.  Two tiles:
+//   * XAttn32 (bf16 extraction): v_mfma_f32_32x32x16_bf16, one query per
+//     lane, row statistics in one lane swap;
+//   * XAttn (fp32 extraction, prefill): v_mfma_f32_16x16x32_bf16 (fp32:
+//     16x16x4 steps), two 16-query blocks per wave, row statistics in two
+//     lane swaps.
+// K and V tiles arrive row-major by LDS DMA (K from the rotated-key
+// workspace or the cache, V from the input or the cache), and the V^T
+// operand is read with transposing LDS reads.
 #include "c2kv_device.hpp"
 #include "c2kv_launch.hpp"
 
@@ -266,9 +271,25 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Swizzles of the bf16 32x32 tile (XAttn32), for rows of RB = 2 D bytes.
+// K: a quarter wave reads 16 distinct rows at one 16-byte chunk, so the
+// chunk is XORed with the row's position among the rows that share a
+// 256-byte bank span.  V: a half wave reads 4 consecutive rows at two
+// adjacent 32-byte pairs, so the pair is XORed with twice the row's
+// position among 4 rows, counted in bank spans; both give 8 (V) or 16 (K)
+// distinct bank groups per access.
+template <int CPR>
+__device__ __forceinline__ int k32_swz(int row) { return (row / (16 / CPR)) & (CPR - 1); }
+template <int RB>
+__device__ __forceinline__ int v32_swz(int row) {
+  constexpr int PP = RB / 32;   // 32-byte pairs per row
+  return 2 * ((row / (8 / PP)) & (PP / 2 - 1));
+}
+
 // Per-lane part of the DMA byte offsets (loop invariant); the tile's own
-// offset is wave-uniform and goes into the instructions' SGPR offset.
-template <typename T, int D>
+// offset is wave-uniform and goes into the instructions' SGPR offset.  M32
+// selects the swizzles of the 32x32 tile.
+template <typename T, int D, bool M32 = false>
 struct DmaLanes {
   using X = XTile<T, D>;
   int k[X::KBLK / kWaves];
@@ -278,20 +299,22 @@ struct DmaLanes {
     for (int j = 0; j < X::KBLK / kWaves; ++j) {
       const int byte = (wave * (X::KBLK / kWaves) + j) * 1024 + lane * 16;
       const int row = byte / X::RB, pc = (byte % X::RB) / 16;
-      k[j] = row * hkv * X::RB + (pc ^ k_swz<X::CPR>(row)) * 16;
+      const int sw = M32 ? k32_swz<X::CPR>(row) : k_swz<X::CPR>(row);
+      k[j] = row * hkv * X::RB + (pc ^ sw) * 16;
     }
 #pragma unroll
     for (int j = 0; j < X::KBLK / kWaves; ++j) {
       const int byte = (wave * (X::KBLK / kWaves) + j) * 1024 + lane * 16;
       const int row = byte / X::RB, pc = (byte % X::RB) / 16;
-      v[j] = row * hkv * X::RB + ((pc ^ (2 * vr_swz<X::RB>(row))) << 4);
+      const int sw = M32 ? v32_swz<X::RB>(row) : vr_swz<X::RB>(row);
+      v[j] = row * hkv * X::RB + ((pc ^ (2 * sw)) << 4);
     }
   }
 };
 
-template <typename T, int D>
+template <typename T, int D, bool M32>
 __device__ __forceinline__ void dma_tile(char* stage, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                         const DmaLanes<T, D>& ln, int ksoff, int vsoff, int wave) {
+                                         const DmaLanes<T, D, M32>& ln, int ksoff, int vsoff, int wave) {
   using X = XTile<T, D>;
 #pragma unroll
   for (int j = 0; j < X::KBLK / kWaves; ++j) {
@@ -557,6 +580,247 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void extract_attn_ker
         p.lse[(int64_t)P.head * p.total_rows + prow] =
             (W.m[qb] * p.scale_log2 + __log2f(lt)) * 0.69314718055994531f;
     }
+  }
+}
+
+// --------------------------------------------- bf16 extraction, 32x32 tiles
+// The bf16 extraction tile on v_mfma_f32_32x32x16_bf16.  S^T = K Q^T puts the
+// wave's 32 queries on the N side: lane l holds query l%32 and, in its two
+// 16-register accumulators, 32 of the tile's 64 keys, while lane l^32 holds
+// the other 32 keys of the same query.  Row statistics take one lane swap,
+// every per-row quantity (reference max, rescale factor, running sum) is one
+// scalar per lane, and each MFMA carries twice the work of a 16x16x32 one
+// for the same operand registers.
+//
+// Key order.  S^T block kb reads K row 32 kb + (m with bits 2 and 3
+// swapped) as its row m.  Register i of lane half h then holds key
+// 32 kb + 16 (i/8) + 8 h + i%8: registers 8c' .. 8c'+7 are 8 consecutive
+// keys, which is the P^T operand of PV step c = 2 kb + c' (keys
+// 16 c + 8 h + e), and the V^T operand reads 8 consecutive keys per dim.
+// Running sums come from v_dot2_f32_bf16 over the bf16 probabilities the PV
+// MFMAs use, one partial per lane half, added at the end.
+
+// V^T operand of PV step c for dims 32 db .. +31: lane l gets dim
+// 32 db + l%32 of keys 16 c + 8 (l/32) + e, e = 0..7.  ds_read_b64_tr_b16:
+// within each 16 lanes, output lane j element a is element j%4 of the 4
+// values addressed by source lane 4a + j/4, so source lane s addresses
+// 4 dims (4 (s%4) ..) of key row (s/4) of a 4-key group.
+template <int D>
+__device__ __forceinline__ bf16x8 vrow32_operand(const char* vt, int c, int db, int lane) {
+  constexpr int RB = 2 * D;
+  const int grp = lane >> 4, h = grp >> 1, dh = grp & 1, sl = lane & 15;
+  pf_s4 x[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = 16 * c + 8 * h + 4 * t + (sl >> 2);
+    const int off = row * RB + 32 * ((2 * db + dh) ^ v32_swz<RB>(row)) + 8 * (sl & 3);
+    x[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) pf_s4*)(vt + off));
+  }
+  typedef short s8 __attribute__((ext_vector_type(8)));
+  const s8 v = {x[0][0], x[0][1], x[0][2], x[0][3], x[1][0], x[1][1], x[1][2], x[1][3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int D>
+struct XAttn32 {
+  using X = XTile<bf16, D>;
+  static constexpr int KS = D / 16, DB = D / 32;
+
+  bf16x8 qB[KS];
+  f32x16 o[DB];
+  float ls;    // running sum of this lane half's probabilities
+  float m;     // reference max of the raw scores
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+    ls = 0.f;
+    m = -INFINITY;
+  }
+
+  template <bool kMasked>
+  __device__ __forceinline__ void tile(const char* stage, int lane, float sl2, const Pred& pred, int q0, int key0) {
+    const int r = lane & 31, h = lane >> 5;
+    const char* ks = stage;
+    const char* vt = stage + X::KBYTES;
+    const int krow = (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);   // bits 2 and 3 swapped
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = 32 * kb + krow;
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(ks + row * X::RB + (((2 * k + h) ^ k32_swz<X::CPR>(row)) << 4));
+        s[kb] = mma32(a, qB[k], s[kb]);
+      }
+    }
+    float x[2][16];
+    float mx = -INFINITY;
+    const int q = q0 + r;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = s[kb][i];
+        if constexpr (kMasked) {
+          const int key = key0 + 32 * kb + 16 * (i >> 3) + 8 * h + (i & 7);
+          v = pred(q, key) ? v : -INFINITY;
+        }
+        x[kb][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = half_max_32(mx);
+    // Lazy rescaling, as in the 16x16 tile: the reference max moves only
+    // when the tile's max exceeds it by more than kLazyLog2 (log2 units).
+    const bool grow = (mx - m) * sl2 > kLazyLog2;
+    const float mnew = grow ? mx : m;
+    const float mneg = mnew == -INFINITY ? 0.f : -mnew * sl2;
+    float alpha = grow ? __builtin_amdgcn_exp2f(__builtin_fmaf(m, sl2, mneg)) : 1.f;
+    bf16x8 pB[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pB[2 * kb + (i >> 3)][i & 7] = from_f32<bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][i], sl2, mneg)));
+    m = mnew;
+    if (__ballot(alpha != 1.f)) {
+      asm volatile("" : "+v"(alpha));
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      ls *= alpha;
+    }
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one2 = {from_f32<bf16>(1.f), from_f32<bf16>(1.f)};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = mma32(vrow32_operand<D>(vt, c, db, lane), pB[c], o[db]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {pB[c][2 * e], pB[c][2 * e + 1]};
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
+      }
+    }
+  }
+};
+
+// The bf16 extraction kernel on XAttn32: the plan, tile enumeration, DMA
+// schedule and rotation of extract_attn_kernel, with the 32x32 tile's
+// swizzles, query operand layout and output layout.
+template <int D>
+__global__ __launch_bounds__(kThreads, (kXMinWaves<bf16, D>)) void extract_attn32_kernel(const ExtractParams p) {
+  using T = bf16;
+  using X = XTile<T, D>;
+  using A = XAttn32<D>;
+  __shared__ __attribute__((aligned(1024))) char stage0[X::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[X::STAGE];
+  asm volatile("" : : "r"(stage0), "r"(stage1) : "memory");
+  const int L = xcd_logical(blockIdx.x, p.grid_wg);
+  if (L >= p.total_wg) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const ExtractPlan P = extract_plan(p, L, wave);
+  const int hq = p.hq, hkv = p.hkv;
+  const int64_t qrow_off = P.slot_region ? P.n : 0;
+  const int64_t doc_rows = (int64_t)P.n + P.m;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(p.krot) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
+      (int)(doc_rows * hkv * X::RB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(p.v) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
+      (int)(doc_rows * hkv * X::RB), 0x00020000);
+  DmaLanes<T, D, true> lanes;
+  lanes.init(hkv, wave, lane);
+  auto issue = [&](int it, char* stage) {
+    const TileSel ts = extract_tile(P, it);
+    const int krow0 = (ts.is_slot ? P.n : 0) + ts.key0;
+    dma_tile<T, D>(stage, krs, vrs, lanes, krow0 * hkv * X::RB, krow0 * hkv * X::RB, wave);
+  };
+  const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
+
+  A W;
+  W.init();
+  const int r = lane & 31, h = lane >> 5;
+  // ---- queries: lane (r, h) loads dims 16 kk + 8 h .. +7 of each half of
+  // query q0 + r, rotates them at the extraction position and keeps them as
+  // the B operand; every load goes out before the first tile's DMA, and
+  // unconditionally (a row outside the wave's range reads the wave's first
+  // row and is zeroed), so one wait covers them while the tile is in flight.
+  {
+    constexpr int H = D / 2, QH = A::KS / 2;
+    float lo[QH][8], hi[QH][8];
+    f32x4 cs4[QH][4];
+    const int ql = P.q0 + r;
+    const bool ok = P.wvalid && ql < P.qend;
+    const int qc = ok ? ql : P.q0;
+    const int pos = P.slot_region ? min(qc * P.ratio_k + P.ratio_k - 1, P.n - 1) : qc;
+    const T* qrow = reinterpret_cast<const T*>(p.q) + ((P.row0 + qrow_off + qc) * hq + P.head) * (int64_t)D;
+    const f32x4* crow = reinterpret_cast<const f32x4*>(p.rope + (int64_t)pos * H);
+#pragma unroll
+    for (int kk = 0; kk < QH; ++kk) {
+      load8_f32<T>(qrow + 16 * kk + 8 * h, lo[kk]);
+      load8_f32<T>(qrow + H + 16 * kk + 8 * h, hi[kk]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cs4[kk][j] = crow[8 * kk + 4 * h + j];
+    }
+    issue(0, stage0);
+#pragma unroll
+    for (int kk = 0; kk < QH; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const f32x4 c = cs4[kk][e >> 1];
+        const float cc = ok ? c[2 * (e & 1)] : 1.f, sn = ok ? c[2 * (e & 1) + 1] : 0.f;
+        float y0, y1;
+        rope_pair(ok ? lo[kk][e] : 0.f, ok ? hi[kk][e] : 0.f, cc, sn, y0, y1);
+        W.qB[kk][e] = from_f32<T>(y0);
+        W.qB[kk + QH][e] = from_f32<T>(y1);
+      }
+  }
+
+  auto compute = [&](int it, const char* stage) {
+    const TileSel ts = extract_tile(P, it);
+    if (!ts.active) return;
+    if (ts.masked) W.template tile<true>(stage, lane, p.scale_log2, ts.pred, P.q0, ts.key0);
+    else W.template tile<false>(stage, lane, p.scale_log2, ts.pred, P.q0, ts.key0);
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 < ntiles) issue(it + 1, stage1);
+    compute(it, stage0);
+    if (it + 1 >= ntiles) break;
+    wait_vmem();
+    __syncthreads();
+    if (it + 2 < ntiles) issue(it + 2, stage0);
+    compute(it + 1, stage1);
+  }
+
+  // ---- normalise and write rows: register i of block db is dim
+  // 32 db + 8 (i/4) + 4 h + i%4 of query q0 + r
+  if (!P.wvalid) return;
+  const float lt = half_sum_32(W.ls);
+  const float inv = 1.f / lt;
+  const int ql = P.q0 + r;
+  if (ql < P.qend) {
+    const int64_t prow = P.row0 + qrow_off + ql;
+    T* orow = reinterpret_cast<T*>(p.o) + (prow * hq + P.head) * (int64_t)D;
+#pragma unroll
+    for (int db = 0; db < A::DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 outv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) outv[e] = from_f32<T>(W.o[db][4 * g4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g4 + 4 * h) = outv;
+      }
+    if (h == 0 && p.lse)
+      p.lse[(int64_t)P.head * p.total_rows + prow] = (W.m * p.scale_log2 + __log2f(lt)) * 0.69314718055994531f;
   }
 }
 
@@ -935,6 +1199,8 @@ static hipError_t launch_extract_t(const ExtractParams& p, int mode, hipStream_t
     hipLaunchKernelGGL(mask_count_kernel, dim3(p.grid_wg), dim3(kThreads), 0, st, p);
   } else if (mode == kExtractDump) {
     hipLaunchKernelGGL(tile_dump_kernel, dim3(p.grid_wg), dim3(kThreads), 0, st, p);
+  } else if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((extract_attn32_kernel<D>), dim3(p.grid_wg), dim3(kThreads), 0, st, p);
   } else {
     hipLaunchKernelGGL((extract_attn_kernel<T, D>), dim3(p.grid_wg), dim3(kThreads), 0, st, p);
   }

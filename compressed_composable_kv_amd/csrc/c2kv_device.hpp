@@ -51,6 +51,15 @@ __device__ __forceinline__ f32x4 mma16(const f32x8& a, const f32x8& b, f32x4 c) 
   return c;
 }
 
+// D[32x32] += A[32x16] * B[16x32].  Lane l supplies A row l%32 and B column
+// l%32, each with 8 k-elements of half l/32 (paired alike in A and B, so the
+// k order does not matter).  Result register i of lane l holds D row
+// 8*(i/4) + 4*(l/32) + i%4, column l%32.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mma32(const bf16x8& a, const bf16x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
@@ -180,6 +189,16 @@ __device__ __forceinline__ float wave_max_16_32(float x) {
 __device__ __forceinline__ float wave_sum_16_32(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Reductions over lanes l and l^32 (one v_permlane32_swap).
+__device__ __forceinline__ float half_max_32(float x) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float half_sum_32(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
