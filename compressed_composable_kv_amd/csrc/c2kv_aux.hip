@@ -42,8 +42,24 @@ __global__ void rotate_k_kernel(const RotateParams p) {
   const int64_t row = p.row_begin + idx / per_row;
   if (row >= p.row_end) return;
   const int h = (int)((idx % per_row) / TPH), c = (int)(idx % TPH);
-  int b = 0;
-  while (b + 1 < p.num_docs && p.docs[b + 1].row0 <= row) ++b;
+  // the row's document: when every wave lies in one row (a multiple of 64
+  // threads per row), one lane-indexed load of the 64-entry table and a
+  // ballot; otherwise a binary search over the documents' first rows
+  int b;
+  if (per_row % 64 == 0) {
+    static_assert(C2KV_MAX_BATCH == 64, "one table entry per lane");
+    const int lane = threadIdx.x & 63;
+    const int64_t r0 = p.docs[lane].row0;   // entries past num_docs are masked
+    b = (int)__popcll(__ballot(lane < p.num_docs && r0 <= row)) - 1;
+  } else {
+    int lo = 0, hi = p.num_docs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.docs[mid].row0 <= row) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+  }
   const int local = (int)(row - p.docs[b].row0);
   const int n = p.docs[b].n;
   const int pos = local < n ? local : min((local - n) * p.ratio_k + p.ratio_k - 1, n - 1);

@@ -8,7 +8,7 @@
 
 namespace c2kv {
 
-// Document table of the K pre-rotation and V transpose kernels.
+// Document table of the K pre-rotation kernel.
 struct RotDoc {
   int64_t row0;
   int32_t n, m;

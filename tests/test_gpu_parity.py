@@ -50,6 +50,11 @@ EXTRACT_CASES = [
     ((200, 131), 4, 2, 4, 2, 64, torch.bfloat16),               # sink shorter than k
     ((180,), 4, 0, 2, 1, 128, torch.float32),                   # no sink
     ((96, 70), 4, 9, 4, 4, 64, torch.float32),                  # sink longer than k
+    # bf16 on the 32x32 tile at both head sizes, with the predicates above
+    ((180,), 4, 0, 2, 1, 128, torch.bfloat16),                  # no sink
+    ((96, 70), 4, 9, 4, 4, 64, torch.bfloat16),                 # sink longer than k
+    ((1, 2, 5, 33), 4, 4, 2, 2, 64, torch.bfloat16),            # n < k, single token
+    ((700, 333), 4, 4, 10, 2, 64, torch.bfloat16),              # G = 5, ragged, several tiles
 ]
 
 
