@@ -471,9 +471,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   for (int s = lane + 64; s < nsplit; s += 64) M = fmaxf(M, ml[s].x);
   M = wave_max64(M);
   auto split_ml = [&](int s) {
-    // splits below 64 come from their lane, the rest from memory
-    const float2 v = make_float2(__shfl(ml0.x, s & 63), __shfl(ml0.y, s & 63));
-    return s < 64 ? v : ml[min(s, nsplit - 1)];
+    // splits below 64 come from their lane, the rest from memory (selected
+    // as values: a conditional between the shuffled value and the memory
+    // operand as lvalues makes the compiler spill the former to scratch and
+    // load either through a flat pointer)
+    float2 v = make_float2(__shfl(ml0.x, s & 63), __shfl(ml0.y, s & 63));
+    if (s >= 64) {
+      const float2 g = ml[min(s, nsplit - 1)];
+      v = g;
+    }
+    return v;
   };
   VF acc;
 #pragma unroll
