@@ -55,6 +55,7 @@ EXTRACT_CASES = [
     ((96, 70), 4, 9, 4, 4, 64, torch.bfloat16),                 # sink longer than k
     ((1, 2, 5, 33), 4, 4, 2, 2, 64, torch.bfloat16),            # n < k, single token
     ((700, 333), 4, 4, 10, 2, 64, torch.bfloat16),              # G = 5, ragged, several tiles
+    ((517, 64), 8, 8, 3, 3, 128, torch.bfloat16),               # G = 1
 ]
 
 
