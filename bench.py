@@ -1074,7 +1074,7 @@ def main():
             "frac_of_achievable_read": _frac(head["gbs"], ach["hbm_read_gbs"]),
             "workload": "one decode call: 64 requests x 32768 composed slots (128k original tokens), 8 KV heads"}
     e4 = ext[4]
-    ext_roof = {"bound": "mfma", "kernel": "extract_attn32_kernel<128> (+ rotate_k_kernel, rope_table_kernel)",
+    ext_roof = {"bound": "mfma", "kernel": "extract_attn_kernel<bf16,128,XAttn32<128>> (+ rotate_k_kernel, rope_table_kernel)",
                 "achieved": e4["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": e4["frac_of_peak"],
                 "traffic": None, "per_launch_ms": e4["ms_per_call"], "algorithmic_per_launch": e4["flop_per_call"],
                 "frac_of_achievable_mfma": _frac(e4["tflops"], ach["mfma_bf16_tflops"]),

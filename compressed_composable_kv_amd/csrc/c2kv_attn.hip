@@ -288,7 +288,7 @@ __device__ __forceinline__ int v32_swz(int row) {
 
 // Per-lane part of the DMA byte offsets (loop invariant); the tile's own
 // offset is wave-uniform and goes into the instructions' SGPR offset.  M32
-// selects the swizzles of the 32x32 tile.
+// selects the swizzles of the 32x32 tile (specialization below).
 template <typename T, int D, bool M32 = false>
 struct DmaLanes {
   using X = XTile<T, D>;
@@ -299,32 +299,82 @@ struct DmaLanes {
     for (int j = 0; j < X::KBLK / kWaves; ++j) {
       const int byte = (wave * (X::KBLK / kWaves) + j) * 1024 + lane * 16;
       const int row = byte / X::RB, pc = (byte % X::RB) / 16;
-      const int sw = M32 ? k32_swz<X::CPR>(row) : k_swz<X::CPR>(row);
+      int sw;
+      if constexpr (M32) sw = k32_swz<X::CPR>(row);
+      else sw = k_swz<X::CPR>(row);
       k[j] = row * hkv * X::RB + (pc ^ sw) * 16;
     }
 #pragma unroll
     for (int j = 0; j < X::KBLK / kWaves; ++j) {
       const int byte = (wave * (X::KBLK / kWaves) + j) * 1024 + lane * 16;
       const int row = byte / X::RB, pc = (byte % X::RB) / 16;
-      const int sw = M32 ? v32_swz<X::RB>(row) : vr_swz<X::RB>(row);
+      int sw;
+      if constexpr (M32) sw = v32_swz<X::RB>(row);
+      else sw = vr_swz<X::RB>(row);
       v[j] = row * hkv * X::RB + ((pc ^ (2 * sw)) << 4);
     }
   }
 };
 
+// The 32x32 tile's swizzles repeat every 16 rows (K) and every 4 rows (V),
+// so a wave's K blocks need only one per-lane offset per 16-row period and
+// its V blocks one offset in all: the blocks further on differ by whole
+// rows, a wave-uniform amount that goes into the SGPR offset.  At d = 128
+// that is 5 registers where one per block takes 8.
+template <typename T, int D>
+struct DmaLanes<T, D, true> {
+  using X = XTile<T, D>;
+  static_assert(sizeof(T) == 2, "the 32x32 tile is bf16");
+  static constexpr int NB = X::KBLK / kWaves;          // 1 KB blocks per wave and tensor
+  static constexpr int RPB = 1024 / X::RB;             // rows per block
+  static constexpr int KP = (16 / RPB) < NB ? 16 / RPB : NB;   // blocks per 16-row K period
+  static_assert(NB % KP == 0 && RPB % 4 == 0, "swizzle periods align with the blocks");
+  int k[KP];
+  int v;
+  __device__ __forceinline__ void init(int hkv, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      const int byte = (wave * NB + j) * 1024 + lane * 16;
+      const int row = byte / X::RB, pc = (byte % X::RB) / 16;
+      k[j] = row * hkv * X::RB + (pc ^ k32_swz<X::CPR>(row)) * 16;
+    }
+    const int byte = wave * NB * 1024 + lane * 16;
+    const int row = byte / X::RB, pc = (byte % X::RB) / 16;
+    v = row * hkv * X::RB + ((pc ^ (2 * v32_swz<X::RB>(row))) << 4);
+  }
+};
+
 template <typename T, int D, bool M32>
 __device__ __forceinline__ void dma_tile(char* stage, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                         const DmaLanes<T, D, M32>& ln, int ksoff, int vsoff, int wave) {
+                                         const DmaLanes<T, D, M32>& ln, int ksoff, int vsoff, int wave, int hkv) {
   using X = XTile<T, D>;
+  if constexpr (M32) {
+    using L = DmaLanes<T, D, true>;
+    const int rowb = hkv * X::RB;
 #pragma unroll
-  for (int j = 0; j < X::KBLK / kWaves; ++j) {
-    const int b = wave * (X::KBLK / kWaves) + j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(stage + b * 1024), 16, ln.k[j], ksoff, 0, 0);
-  }
+    for (int j = 0; j < L::NB; ++j) {
+      const int b = wave * L::NB + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(stage + b * 1024), 16, ln.k[j % L::KP],
+                                               ksoff + (j / L::KP) * 16 * rowb, 0, 0);
+    }
 #pragma unroll
-  for (int j = 0; j < X::KBLK / kWaves; ++j) {
-    const int b = wave * (X::KBLK / kWaves) + j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(stage + X::KBYTES + b * 1024), 16, ln.v[j], vsoff, 0, 0);
+    for (int j = 0; j < L::NB; ++j) {
+      const int b = wave * L::NB + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(stage + X::KBYTES + b * 1024), 16, ln.v,
+                                               vsoff + j * L::RPB * rowb, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < X::KBLK / kWaves; ++j) {
+      const int b = wave * (X::KBLK / kWaves) + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(stage + b * 1024), 16, ln.k[j], ksoff, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < X::KBLK / kWaves; ++j) {
+      const int b = wave * (X::KBLK / kWaves) + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(stage + X::KBYTES + b * 1024), 16, ln.v[j], vsoff,
+                                               0, 0);
+    }
   }
 }
 
@@ -454,52 +504,20 @@ struct XAttn {
       ls[1] = mma16(ones_v8<T>(), pB[c][1], ls[1]);
     }
   }
-};
 
-template <typename T, int D>
-constexpr int kXMinWaves = (2 * XTile<T, D>::STAGE * 2 <= 160 * 1024) ? 2 : 1;
+  static constexpr bool kM32 = false;   // LDS swizzles of this tile (DmaLanes)
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void extract_attn_kernel(const ExtractParams p) {
-  using X = XTile<T, D>;
-  __shared__ __attribute__((aligned(1024))) char stage0[X::STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[X::STAGE];
-  // The stages are written only by buffer_load ... lds; escape them so the
-  // compiler does not treat them as never-stored memory.
-  asm volatile("" : : "r"(stage0), "r"(stage1) : "memory");
-  const int L = xcd_logical(blockIdx.x, p.grid_wg);
-  if (L >= p.total_wg) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const ExtractPlan P = extract_plan(p, L, wave);
-  const int hq = p.hq, hkv = p.hkv;
-  const int64_t qrow_off = P.slot_region ? P.n : 0;
-  // buffer resources: this document's rotated keys and its values, KV head
-  // kvh; reads past the document's rows return zeros
-  const int64_t doc_rows = (int64_t)P.n + P.m;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const char*>(p.krot) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
-      (int)(doc_rows * hkv * X::RB), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const char*>(p.v) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
-      (int)(doc_rows * hkv * X::RB), 0x00020000);
-  DmaLanes<T, D> lanes;
-  lanes.init(hkv, wave, lane);
-  auto issue = [&](int it, char* stage) {
-    const TileSel ts = extract_tile(P, it);
-    const int krow0 = (ts.is_slot ? P.n : 0) + ts.key0;
-    dma_tile<T, D>(stage, krs, vrs, lanes, krow0 * hkv * X::RB, krow0 * hkv * X::RB, wave);
-  };
-  const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
-
-  XAttn<T, D> W;
-  W.init();
-  // ---- queries: load, rotate at the extraction positions, keep as B operand.
-  // Every query and cos/sin load is issued before the first tile's DMA, and
+  // Queries of the wave's unit: lane (r16, g) loads dims 32 k + 8 g .. +7 of
+  // each half of queries q0 + r16 and q0 + 16 + r16, rotates them at the
+  // extraction positions and keeps them as the B operand.  Every query and
+  // cos/sin load is issued before issue_first() (the first tile's DMA), and
   // unconditionally (a row outside the wave's range reads the wave's first
   // row, or the region's row 0, and is zeroed afterwards): the vector-memory
   // counter retires in order, so one wait then covers all of them while the
   // tile is still in flight.
-  {
+  template <typename Issue>
+  __device__ __forceinline__ void load_queries(const ExtractParams& p, const ExtractPlan& P, int lane, int hq,
+                                               int64_t qrow_off, Issue&& issue_first) {
     constexpr int H = D / 2, QK = D / 64;
     const int r16 = lane & 15, g = lane >> 4;
     float lo[2][QK][8], hi[2][QK][8];
@@ -521,10 +539,7 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void extract_attn_ker
         for (int j = 0; j < 4; ++j) cs4[qb][k][j] = crow[16 * k + 4 * g + j];
       }
     }
-    // unconditional, so the wait below is not widened by a branch: a launched
-    // workgroup always has a tile (its wave 0 owns rows), and a DMA past the
-    // document's rows reads zeros through the buffer range check
-    issue(0, stage0);
+    issue_first();
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -535,53 +550,40 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void extract_attn_ker
           const float cc = ok[qb] ? c[2 * (e & 1)] : 1.f, sn = ok[qb] ? c[2 * (e & 1) + 1] : 0.f;
           float y0, y1;
           rope_pair(ok[qb] ? lo[qb][k][e] : 0.f, ok[qb] ? hi[qb][k][e] : 0.f, cc, sn, y0, y1);
-          W.qB[qb][k][e] = from_f32<T>(y0);
-          W.qB[qb][k + QK][e] = from_f32<T>(y1);
+          qB[qb][k][e] = from_f32<T>(y0);
+          qB[qb][k + QK][e] = from_f32<T>(y1);
         }
   }
 
-  auto compute = [&](int it, const char* stage) {
-    const TileSel ts = extract_tile(P, it);
-    if (!ts.active) return;
-    if (ts.masked) W.template tile<true>(stage, lane, p.scale_log2, ts.pred, P.q0, ts.key0);
-    else W.template tile<false>(stage, lane, p.scale_log2, ts.pred, P.q0, ts.key0);
-  };
-  for (int it = 0; it < ntiles; it += 2) {
-    wait_vmem();
-    __syncthreads();
-    if (it + 1 < ntiles) issue(it + 1, stage1);
-    compute(it, stage0);
-    if (it + 1 >= ntiles) break;
-    wait_vmem();
-    __syncthreads();
-    if (it + 2 < ntiles) issue(it + 2, stage0);
-    compute(it + 1, stage1);
-  }
-
-  // ---- normalise and write rows
-  if (!P.wvalid) return;
-  const int r16 = lane & 15, g = lane >> 4;
+  // Normalise and write the unit's rows (and their log-sum-exp).
+  __device__ __forceinline__ void write_rows(const ExtractParams& p, const ExtractPlan& P, int lane, int hq,
+                                             int64_t qrow_off) const {
+    const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float lt = W.ls[qb][0];   // every lane of a column holds its sum
-    const float inv = 1.f / lt;
-    const int ql = P.q0 + 16 * qb + r16;
-    if (ql < P.qend) {
-      const int64_t prow = P.row0 + qrow_off + ql;
-      T* orow = reinterpret_cast<T*>(p.o) + (prow * hq + P.head) * (int64_t)D;
+    for (int qb = 0; qb < 2; ++qb) {
+      const float lt = ls[qb][0];   // every lane of a column holds its sum
+      const float inv = 1.f / lt;
+      const int ql = P.q0 + 16 * qb + r16;
+      if (ql < P.qend) {
+        const int64_t prow = P.row0 + qrow_off + ql;
+        T* orow = reinterpret_cast<T*>(p.o) + (prow * hq + P.head) * (int64_t)D;
 #pragma unroll
-      for (int db = 0; db < XAttn<T, D>::DB; ++db) {
-        typename ElemTraits<T>::v4 outv;
+        for (int db = 0; db < DB; ++db) {
+          typename ElemTraits<T>::v4 outv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) outv[i] = from_f32<T>(W.o[db][qb][i] * inv);
-        *reinterpret_cast<typename ElemTraits<T>::v4*>(orow + 16 * db + 4 * g) = outv;
+          for (int i = 0; i < 4; ++i) outv[i] = from_f32<T>(o[db][qb][i] * inv);
+          *reinterpret_cast<typename ElemTraits<T>::v4*>(orow + 16 * db + 4 * g) = outv;
+        }
+        if (g == 0 && p.lse)
+          p.lse[(int64_t)P.head * p.total_rows + prow] =
+              (m[qb] * p.scale_log2 + __log2f(lt)) * 0.69314718055994531f;
       }
-      if (g == 0 && p.lse)
-        p.lse[(int64_t)P.head * p.total_rows + prow] =
-            (W.m[qb] * p.scale_log2 + __log2f(lt)) * 0.69314718055994531f;
     }
   }
-}
+};
+
+template <typename T, int D>
+constexpr int kXMinWaves = (2 * XTile<T, D>::STAGE * 2 <= 160 * 1024) ? 2 : 1;
 
 // --------------------------------------------- bf16 extraction, 32x32 tiles
 // The bf16 extraction tile on v_mfma_f32_32x32x16_bf16.  S^T = K Q^T puts the
@@ -709,51 +711,21 @@ struct XAttn32 {
       }
     }
   }
-};
 
-// The bf16 extraction kernel on XAttn32: the plan, tile enumeration, DMA
-// schedule and rotation of extract_attn_kernel, with the 32x32 tile's
-// swizzles, query operand layout and output layout.
-template <int D>
-__global__ __launch_bounds__(kThreads, (kXMinWaves<bf16, D>)) void extract_attn32_kernel(const ExtractParams p) {
-  using T = bf16;
-  using X = XTile<T, D>;
-  using A = XAttn32<D>;
-  __shared__ __attribute__((aligned(1024))) char stage0[X::STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[X::STAGE];
-  asm volatile("" : : "r"(stage0), "r"(stage1) : "memory");
-  const int L = xcd_logical(blockIdx.x, p.grid_wg);
-  if (L >= p.total_wg) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const ExtractPlan P = extract_plan(p, L, wave);
-  const int hq = p.hq, hkv = p.hkv;
-  const int64_t qrow_off = P.slot_region ? P.n : 0;
-  const int64_t doc_rows = (int64_t)P.n + P.m;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const char*>(p.krot) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
-      (int)(doc_rows * hkv * X::RB), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const char*>(p.v) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
-      (int)(doc_rows * hkv * X::RB), 0x00020000);
-  DmaLanes<T, D, true> lanes;
-  lanes.init(hkv, wave, lane);
-  auto issue = [&](int it, char* stage) {
-    const TileSel ts = extract_tile(P, it);
-    const int krow0 = (ts.is_slot ? P.n : 0) + ts.key0;
-    dma_tile<T, D>(stage, krs, vrs, lanes, krow0 * hkv * X::RB, krow0 * hkv * X::RB, wave);
-  };
-  const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
+  static constexpr bool kM32 = true;    // LDS swizzles of this tile (DmaLanes)
 
-  A W;
-  W.init();
-  const int r = lane & 31, h = lane >> 5;
-  // ---- queries: lane (r, h) loads dims 16 kk + 8 h .. +7 of each half of
-  // query q0 + r, rotates them at the extraction position and keeps them as
-  // the B operand; every load goes out before the first tile's DMA, and
-  // unconditionally (a row outside the wave's range reads the wave's first
-  // row and is zeroed), so one wait covers them while the tile is in flight.
-  {
-    constexpr int H = D / 2, QH = A::KS / 2;
+  // Queries of the wave's unit: lane (r, h) loads dims 16 kk + 8 h .. +7 of
+  // each half of query q0 + r, rotates them at the extraction position and
+  // keeps them as the B operand; every load goes out before issue_first()
+  // (the first tile's DMA), and unconditionally (a row outside the wave's
+  // range reads the wave's first row and is zeroed), so one wait covers them
+  // while the tile is in flight.
+  template <typename Issue>
+  __device__ __forceinline__ void load_queries(const ExtractParams& p, const ExtractPlan& P, int lane, int hq,
+                                               int64_t qrow_off, Issue&& issue_first) {
+    using T = bf16;
+    const int r = lane & 31, h = lane >> 5;
+    constexpr int H = D / 2, QH = KS / 2;
     float lo[QH][8], hi[QH][8];
     f32x4 cs4[QH][4];
     const int ql = P.q0 + r;
@@ -769,7 +741,7 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<bf16, D>)) void extract_attn3
 #pragma unroll
       for (int j = 0; j < 4; ++j) cs4[kk][j] = crow[8 * kk + 4 * h + j];
     }
-    issue(0, stage0);
+    issue_first();
 #pragma unroll
     for (int kk = 0; kk < QH; ++kk)
 #pragma unroll
@@ -778,10 +750,81 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<bf16, D>)) void extract_attn3
         const float cc = ok ? c[2 * (e & 1)] : 1.f, sn = ok ? c[2 * (e & 1) + 1] : 0.f;
         float y0, y1;
         rope_pair(ok ? lo[kk][e] : 0.f, ok ? hi[kk][e] : 0.f, cc, sn, y0, y1);
-        W.qB[kk][e] = from_f32<T>(y0);
-        W.qB[kk + QH][e] = from_f32<T>(y1);
+        qB[kk][e] = from_f32<T>(y0);
+        qB[kk + QH][e] = from_f32<T>(y1);
       }
   }
+
+  // Normalise and write the unit's rows: register i of block db is dim
+  // 32 db + 8 (i/4) + 4 h + i%4 of query q0 + r.
+  __device__ __forceinline__ void write_rows(const ExtractParams& p, const ExtractPlan& P, int lane, int hq,
+                                             int64_t qrow_off) const {
+    using T = bf16;
+    const int r = lane & 31, h = lane >> 5;
+    const float lt = half_sum_32(ls);
+    const float inv = 1.f / lt;
+    const int ql = P.q0 + r;
+    if (ql < P.qend) {
+      const int64_t prow = P.row0 + qrow_off + ql;
+      T* orow = reinterpret_cast<T*>(p.o) + (prow * hq + P.head) * (int64_t)D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 outv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) outv[e] = from_f32<T>(o[db][4 * g4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g4 + 4 * h) = outv;
+        }
+      if (h == 0 && p.lse)
+        p.lse[(int64_t)P.head * p.total_rows + prow] = (m * p.scale_log2 + __log2f(lt)) * 0.69314718055994531f;
+    }
+  }
+};
+
+// Extraction attention.  The plan, tile enumeration, DMA schedule and tile
+// loop are shared by both tiles; A (XAttn for fp32, XAttn32 for bf16)
+// supplies the query operand layout, the tile and the output layout, and
+// selects the LDS swizzles (A::kM32).
+template <typename T, int D, typename A>
+__global__ __launch_bounds__(kThreads, (kXMinWaves<T, D>)) void extract_attn_kernel(const ExtractParams p) {
+  using X = XTile<T, D>;
+  __shared__ __attribute__((aligned(1024))) char stage0[X::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[X::STAGE];
+  // The stages are written only by buffer_load ... lds; escape them so the
+  // compiler does not treat them as never-stored memory.
+  asm volatile("" : : "r"(stage0), "r"(stage1) : "memory");
+  const int L = xcd_logical(blockIdx.x, p.grid_wg);
+  if (L >= p.total_wg) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const ExtractPlan P = extract_plan(p, L, wave);
+  const int hq = p.hq, hkv = p.hkv;
+  const int64_t qrow_off = P.slot_region ? P.n : 0;
+  // buffer resources: this document's rotated keys and its values, KV head
+  // kvh; reads past the document's rows return zeros
+  const int64_t doc_rows = (int64_t)P.n + P.m;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(p.krot) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
+      (int)(doc_rows * hkv * X::RB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(p.v) + ((P.row0 * hkv + P.kvh) * (int64_t)X::RB)), 0,
+      (int)(doc_rows * hkv * X::RB), 0x00020000);
+  DmaLanes<T, D, A::kM32> lanes;
+  lanes.init(hkv, wave, lane);
+  auto issue = [&](int it, char* stage) {
+    const TileSel ts = extract_tile(P, it);
+    const int krow0 = (ts.is_slot ? P.n : 0) + ts.key0;
+    dma_tile<T, D>(stage, krs, vrs, lanes, krow0 * hkv * X::RB, krow0 * hkv * X::RB, wave, hkv);
+  };
+  const int ntiles = (P.nA1 - P.nA0) + (P.nB1 - P.nB0) + P.nS;
+
+  A W;
+  W.init();
+  // the first tile's DMA goes out between the query loads and their
+  // rotation, unconditionally, so the wait below is not widened by a branch:
+  // a launched workgroup always has a tile (its wave 0 owns rows), and a DMA
+  // past the document's rows reads zeros through the buffer range check
+  W.load_queries(p, P, lane, hq, qrow_off, [&] { issue(0, stage0); });
 
   auto compute = [&](int it, const char* stage) {
     const TileSel ts = extract_tile(P, it);
@@ -801,28 +844,10 @@ __global__ __launch_bounds__(kThreads, (kXMinWaves<bf16, D>)) void extract_attn3
     compute(it + 1, stage1);
   }
 
-  // ---- normalise and write rows: register i of block db is dim
-  // 32 db + 8 (i/4) + 4 h + i%4 of query q0 + r
   if (!P.wvalid) return;
-  const float lt = half_sum_32(W.ls);
-  const float inv = 1.f / lt;
-  const int ql = P.q0 + r;
-  if (ql < P.qend) {
-    const int64_t prow = P.row0 + qrow_off + ql;
-    T* orow = reinterpret_cast<T*>(p.o) + (prow * hq + P.head) * (int64_t)D;
-#pragma unroll
-    for (int db = 0; db < A::DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 outv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) outv[e] = from_f32<T>(W.o[db][4 * g4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g4 + 4 * h) = outv;
-      }
-    if (h == 0 && p.lse)
-      p.lse[(int64_t)P.head * p.total_rows + prow] = (W.m * p.scale_log2 + __log2f(lt)) * 0.69314718055994531f;
-  }
+  W.write_rows(p, P, lane, hq, qrow_off);
 }
+
 
 // Counting twin of the extraction kernel: the same plan, tile enumeration and
 // predicate, but each active (wave, tile) pair counts its visible cells.
@@ -1200,9 +1225,9 @@ static hipError_t launch_extract_t(const ExtractParams& p, int mode, hipStream_t
   } else if (mode == kExtractDump) {
     hipLaunchKernelGGL(tile_dump_kernel, dim3(p.grid_wg), dim3(kThreads), 0, st, p);
   } else if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((extract_attn32_kernel<D>), dim3(p.grid_wg), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((extract_attn_kernel<bf16, D, XAttn32<D>>), dim3(p.grid_wg), dim3(kThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL((extract_attn_kernel<T, D>), dim3(p.grid_wg), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((extract_attn_kernel<T, D, XAttn<T, D>>), dim3(p.grid_wg), dim3(kThreads), 0, st, p);
   }
   return hipGetLastError();
 }
