@@ -388,7 +388,7 @@ struct ComposeUnit {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 3) void compose_kernel(const ComposeParams p) {
+__global__ __launch_bounds__(256, 4) void compose_kernel(const ComposeParams p) {
   static_assert(kComposeHPT == 2, "two heads per thread");
   __shared__ ComposeTable tb;
   int u = blockIdx.x;
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(256, 3) void compose_kernel(const ComposeParams p) 
   compose_table_a(p, tb);
   const int total = tb.doc_unit0[p.num_docs];
   // one unit in flight per wave: a unit's loads are amortised over the
-  // stores of its whole occurrence group, and three workgroups per CU keep
+  // stores of its whole occurrence group, and four workgroups per CU keep
   // other waves' loads in flight meanwhile.  The first unit's loads are
   // issued before the second phase of the table, which runs under them.
   ComposeUnit<T, D> cur;
@@ -414,12 +414,13 @@ template <typename T, int D>
 static hipError_t launch_compose_t(const ComposeParams& p, bool host_src, hipStream_t st) {
   const int units = p.total_units;
   if (units == 0) return hipSuccess;
-  // device sources: three workgroups per CU (12 waves) is the measured
-  // optimum for 1k-2k units: fewer leaves HBM idle, more adds dispatch
-  // without more bytes in flight.  Host sources: 16 workgroups (about 1 MB in flight) keep the
+  // device sources: four workgroups per CU (16 waves).  Measured on one
+  // MI355X: the Qwen2.5 pool (about 6900 units) 101.3-101.6 us against
+  // 102.6-104.1 at three and 105-106 at two; the Llama layer (1024 units)
+  // 16.6-16.8 us at three or four, 18.6 at two.  Host sources: 16 workgroups (about 1 MB in flight) keep the
   // host link busy; more concurrent readers made its transfers slower
   // (56 GB/s at 12-16 workgroups, 48 GB/s at 192 or more).
-  const int blocks = min(units, host_src ? 16 : 3 * 256);
+  const int blocks = min(units, host_src ? 16 : 4 * 256);
   hipLaunchKernelGGL((compose_kernel<T, D>), dim3(blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
