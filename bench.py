@@ -123,13 +123,18 @@ def summarize(dirs, out, cmd, calib_mib):
     if not has_pmc:
         rows = con.execute("select name, count(*), avg(end-start), sum(end-start), min(end-start), max(end-start) "
                            "from kernels group by name order by sum(end-start) desc").fetchall()
+        durs = {}
+        for name, dt in con.execute("select name, end-start from kernels"):
+            durs.setdefault(name, []).append(dt)
         tot = sum(r[3] for r in rows)
         lines.append("# rocprofv3 kernel-trace summary (durations from the kernel dispatch records)")
         lines.append(f"# command: {cmd}")
-        lines.append("# calls    avg_us      min_us      max_us    total_ms   share  kernel")
+        lines.append("# calls    avg_us   median_us      min_us      max_us    total_ms   share  kernel")
         for r in rows:
-            lines.append(f"{r[1]:7d} {r[2] / 1e3:9.2f} {r[4] / 1e3:11.2f} {r[5] / 1e3:11.2f} {r[3] / 1e6:11.3f} "
-                         f"{100 * r[3] / tot:6.1f}%  {r[0][:110]}")
+            d = sorted(durs[r[0]])
+            med = d[len(d) // 2] if len(d) % 2 else 0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
+            lines.append(f"{r[1]:7d} {r[2] / 1e3:9.2f} {med / 1e3:11.2f} {r[4] / 1e3:11.2f} {r[5] / 1e3:11.2f} "
+                         f"{r[3] / 1e6:11.3f} {100 * r[3] / tot:6.1f}%  {r[0][:110]}")
     else:
         avg = {}
         for d in dirs:
