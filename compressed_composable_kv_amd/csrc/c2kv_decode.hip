@@ -199,30 +199,46 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
   __shared__ __attribute__((aligned(1024))) char s_raw[kDecLdsBytes<T, D>];
 
   const int L = blockIdx.x;
-  if (L >= p.total_wg) return;
+  // The kernel-argument fields of the prologue, with the first request's
+  // entry (the only one of a one-request launch), loaded in one round of
+  // scalar loads: the empty asm needs them all at once, so they complete at
+  // one wait instead of one dependent round per use.
+  const int total_wg = p.total_wg, num_reqs = p.num_reqs, req0 = p.req0, hq = p.hq, hkv = p.hkv, G = p.G;
+  const float sl2 = p.scale_log2;
+  const int64_t cap = p.cap;
+  const DecodeReq rq0 = p.reqs[0];
+  const void* const q_in = p.q;
+  const void* const kn_in = p.k_new;
+  const void* const vn_in = p.v_new;
+  void* const kc = p.kc;
+  void* const vc = p.vc;
+  asm volatile("" : : "s"(total_wg), "s"(num_reqs), "s"(req0), "s"(hq), "s"(hkv), "s"(G), "s"(sl2), "s"(cap), "s"(rq0.wg0),
+               "s"(rq0.cache_len), "s"(rq0.pos), "s"(rq0.nsplit), "s"(rq0.chunk), "s"(rq0.pbase), "s"(q_in),
+               "s"(kn_in), "s"(vn_in), "s"(kc), "s"(vc));
+  if (L >= total_wg) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  const int ri = request_of(p.reqs, p.num_reqs, L);
-  const DecodeReq rq = p.reqs[ri];
-  const int r = p.req0 + ri;
+  const int ri = request_of(p.reqs, num_reqs, L);
+  DecodeReq rq = rq0;
+  if (num_reqs != 1) rq = p.reqs[ri];
+  const int r = req0 + ri;
   const int local = L - rq.wg0;
   const int kvh = local / rq.nsplit, split = local % rq.nsplit;
-  const int G = p.G;
   const int newk = rq.cache_len;                       // row of the new token
   const int k0 = split * rq.chunk, k1 = min(newk + 1, k0 + rq.chunk);
   const int nsteps = (k1 - k0 + 31) / 32;
 
-  const int64_t head_base = ((int64_t)r * p.hkv + kvh) * p.cap;
-  const T* knew = reinterpret_cast<const T*>(p.k_new) + ((int64_t)r * p.hkv + kvh) * D;
-  const T* vnew = reinterpret_cast<const T*>(p.v_new) + ((int64_t)r * p.hkv + kvh) * D;
+  const int64_t head_base = ((int64_t)r * hkv + kvh) * cap;
+  const T* knew = reinterpret_cast<const T*>(kn_in) + ((int64_t)r * hkv + kvh) * D;
+  const T* vnew = reinterpret_cast<const T*>(vn_in) + ((int64_t)r * hkv + kvh) * D;
   char* vt = s_raw + wave * Tile::BYTES;
   // K and V rows of this head: rows at or past min(k1, newk) read as zeros
   // (the new token's key is loaded from k_new, its value patched in LDS)
   const int nrec = min(k1, newk) * RB;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const char*>(p.kc) + head_base * RB), 0, nrec, 0x00020000);
+      (void*)(reinterpret_cast<const char*>(kc) + head_base * RB), 0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const char*>(p.vc) + head_base * RB), 0, nrec, 0x00020000);
+      (void*)(reinterpret_cast<const char*>(vc) + head_base * RB), 0, nrec, 0x00020000);
   int voff[NDMA];
 #pragma unroll
   for (int j = 0; j < NDMA; ++j) {
@@ -239,7 +255,7 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
   V8 qraw[KS];
   {
     const bool ok = r16 < G;
-    const T* qrow = reinterpret_cast<const T*>(p.q) + ((int64_t)r * p.hq + kvh * G + (ok ? r16 : 0)) * D;
+    const T* qrow = reinterpret_cast<const T*>(q_in) + ((int64_t)r * hq + kvh * G + (ok ? r16 : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS / 2; ++ks) {
       qraw[ks] = *reinterpret_cast<const V8*>(qrow + 32 * ks + 8 * g);
@@ -337,7 +353,7 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = key0 + 16 * kb + 4 * g + i;
-        const float v = key < k1 ? s[kb][i] * p.scale_log2 : -INFINITY;
+        const float v = key < k1 ? s[kb][i] * sl2 : -INFINITY;
         x[kb][i] = v;
         mx = fmaxf(mx, v);
       }
@@ -450,15 +466,29 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   using VF = typename MergeVec<DPL>::type;
   __shared__ float s_red[WPR > 1 ? kWaves * (D + 1) : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the kernel-argument fields, with the first request's entries (the only
+  // ones of a one-request launch), in one round of scalar loads
+  const int num_rows = p.num_rows, hq = p.hq, tq = p.tq, req0 = p.req0, nsplit0 = p.nsplit[0], pbase0 = p.pbase[0];
+  const float* const part_o = p.part_o;
+  const float2* const part_ml = p.part_ml;
+  void* const out = p.o;
+  float* const lse = p.lse;
+  asm volatile("" : : "s"(num_rows), "s"(hq), "s"(tq), "s"(req0), "s"(nsplit0), "s"(pbase0), "s"(part_o),
+               "s"(part_ml), "s"(out), "s"(lse));
   const int row = WPR == 1 ? blockIdx.x * kWaves + wave : blockIdx.x;
-  if (row >= p.num_rows) return;
-  const int ri = row / (p.hq * p.tq);
-  const int rem = row % (p.hq * p.tq);          // head * tq + t
-  const int nsplit = p.nsplit[ri];
+  if (row >= num_rows) return;
+  const int rows_per_req = hq * tq;
+  const int ri = num_rows == rows_per_req ? 0 : row / rows_per_req;
+  const int rem = row - ri * rows_per_req;      // head * tq + t
+  int nsplit = nsplit0, pbase = pbase0;
+  if (ri != 0) {
+    nsplit = p.nsplit[ri];
+    pbase = p.pbase[ri];
+  }
   if (nsplit <= 1) return;        // single-chunk requests were written directly
-  const int64_t idx0 = (int64_t)p.pbase[ri] + (int64_t)rem * nsplit;
-  const float* base = p.part_o + idx0 * D;
-  const float2* ml = p.part_ml + idx0;
+  const int64_t idx0 = (int64_t)pbase + (int64_t)rem * nsplit;
+  const float* base = part_o + idx0 * D;
+  const float2* ml = part_ml + idx0;
   const int half = lane >> 5, col = (lane & 31) * DPL;
   const int hw = (WPR == 1 ? 0 : 2 * wave) + half;     // this half-wave's first split
   auto load_o = [&](int s) { return *reinterpret_cast<const VF*>(base + (int64_t)min(s, nsplit - 1) * D + col); };
@@ -520,14 +550,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     }
   }
   if (half == 0) {
-    const int head = rem / p.tq, t = rem % p.tq;
-    const int r = p.req0 + ri;
-    T* orow = reinterpret_cast<T*>(p.o) + (((int64_t)r * p.tq + t) * p.hq + head) * D + col;
+    const int head = rem / tq, t = rem % tq;
+    const int r = req0 + ri;
+    T* orow = reinterpret_cast<T*>(out) + (((int64_t)r * tq + t) * hq + head) * D + col;
     const float inv = 1.f / ls;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) orow[e] = from_f32<T>(acc[e] * inv);
-    if (lane == 0 && p.lse)
-      p.lse[((int64_t)r * p.hq + head) * p.tq + t] = (M + __log2f(ls)) * 0.69314718055994531f;
+    if (lane == 0 && lse)
+      lse[((int64_t)r * hq + head) * tq + t] = (M + __log2f(ls)) * 0.69314718055994531f;
   }
 }
 
