@@ -391,8 +391,19 @@ template <typename T, int D>
 __global__ __launch_bounds__(256, 4) void compose_kernel(const ComposeParams p) {
   static_assert(kComposeHPT == 2, "two heads per thread");
   __shared__ ComposeTable tb;
+  // the scalar kernel-argument fields, loaded in one round: the empty asm
+  // needs them all at once, so they complete at one wait instead of one
+  // dependent round per use (the table's per-lane loads follow separately)
+  const int total_units = p.total_units, num_docs = p.num_docs, num_occ = p.num_occ, num_runs = p.num_runs;
+  const int hkv = p.hkv, ratio_k = p.ratio_k, rpt = p.rpt, gpb = p.gpb, nblk = p.nblk;
+  const int64_t cap = p.cap;
+  void* const ck = p.cache_k;
+  void* const cv = p.cache_v;
+  int32_t* const pos_out = p.pos_out;
+  asm volatile("" : : "s"(total_units), "s"(num_docs), "s"(num_occ), "s"(num_runs), "s"(hkv), "s"(ratio_k),
+               "s"(rpt), "s"(gpb), "s"(nblk), "s"(cap), "s"(ck), "s"(cv), "s"(pos_out));
   int u = blockIdx.x;
-  if (u >= p.total_units) return;
+  if (u >= total_units) return;
   compose_table_a(p, tb);
   const int total = tb.doc_unit0[p.num_docs];
   // one unit in flight per wave: a unit's loads are amortised over the
