@@ -218,9 +218,21 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
   if (L >= total_wg) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  const int ri = request_of(p.reqs, num_reqs, L);
+  int ri = 0;
   DecodeReq rq = rq0;
-  if (num_reqs != 1) rq = p.reqs[ri];
+  if (num_reqs != 1) {
+    // each lane loads one request's entry; the ballot over the requests'
+    // first workgroups picks this workgroup's request, and its fields come
+    // from that lane (no second round of loads)
+    const DecodeReq e = p.reqs[min(lane, num_reqs - 1)];
+    ri = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane < num_reqs && e.wg0 <= L)) - 1);
+    rq.wg0 = __builtin_amdgcn_readlane(e.wg0, ri);
+    rq.cache_len = __builtin_amdgcn_readlane(e.cache_len, ri);
+    rq.pos = __builtin_amdgcn_readlane(e.pos, ri);
+    rq.nsplit = __builtin_amdgcn_readlane(e.nsplit, ri);
+    rq.chunk = __builtin_amdgcn_readlane(e.chunk, ri);
+    rq.pbase = __builtin_amdgcn_readlane(e.pbase, ri);
+  }
   const int r = req0 + ri;
   const int local = L - rq.wg0;
   const int kvh = local / rq.nsplit, split = local % rq.nsplit;
@@ -469,6 +481,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   // the kernel-argument fields, with the first request's entries (the only
   // ones of a one-request launch), in one round of scalar loads
   const int num_rows = p.num_rows, hq = p.hq, tq = p.tq, req0 = p.req0, nsplit0 = p.nsplit[0], pbase0 = p.pbase[0];
+  // (and every request's entries, one per lane, for launches of several)
+  static_assert(C2KV_MAX_BATCH == 64, "one lane per request of a launch");
+  const int nsplit_l = p.nsplit[lane], pbase_l = p.pbase[lane];
   const float* const part_o = p.part_o;
   const float2* const part_ml = p.part_ml;
   void* const out = p.o;
@@ -482,8 +497,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   const int rem = row - ri * rows_per_req;      // head * tq + t
   int nsplit = nsplit0, pbase = pbase0;
   if (ri != 0) {
-    nsplit = p.nsplit[ri];
-    pbase = p.pbase[ri];
+    nsplit = __shfl(nsplit_l, ri);
+    pbase = __shfl(pbase_l, ri);
   }
   if (nsplit <= 1) return;        // single-chunk requests were written directly
   const int64_t idx0 = (int64_t)pbase + (int64_t)rem * nsplit;
