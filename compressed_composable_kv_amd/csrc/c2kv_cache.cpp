@@ -30,11 +30,13 @@ namespace {
 //    step), so every workgroup streams about the same number of bytes and
 //    no second, partly filled round trails the first.
 constexpr int64_t kDecodeSlots = 3 * 256;   // decode workgroups resident at once on a 256-CU MI355X
-// Minimum 128-key workgroup steps per decode piece.  Measured on the Llama
-// layer's batch-1 decode (8 KV heads x 8193 keys) on one MI355X: 14.6 us per
-// step at 1 step per piece, 15.5 at 2, 13.0 at 3, 14.6 at 4, 18.1 at 6;
-// the Qwen2.5 pool (pieces of about 9 steps) is unaffected.
-constexpr int64_t kDecodeMinSteps = 3;
+// Minimum keys per decode piece (a multiple of one wave's 32-key step).
+// Measured on the Llama layer's batch-1 decode (8 KV heads x 8193 keys) on
+// one MI355X, per step: 12.1 us at 288 keys (232 workgroups), 12.2 at 320,
+// 12.3 at 352, 12.6 at 384, 13.3 at 416, and 15.1 at 256 (264 workgroups,
+// more than the CUs); the Qwen2.5 pool (pieces of about 1100 keys) is
+// unaffected.
+constexpr int64_t kDecodeMinKeys = 288;
 constexpr int64_t kPrefillSlots = 256;      // prefill workgroups per launch: one per CU (two measured slower)
 struct CachePlan {
   bool decode = false;
@@ -63,7 +65,9 @@ c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, i
     total_keys += c + tq;
     max_len = std::max(max_len, c + tq);
   }
-  const int64_t step = decode ? 4 * 32 : 2 * kBN;    // keys per workgroup step (all waves)
+  // keys per unit of the chunk search: one wave's step for decode, a
+  // workgroup's step (a tile per wave group) for prefill
+  const int64_t step = decode ? 32 : 2 * kBN;
   P.nsplit.resize(num_reqs);
   P.chunk_r.resize(num_reqs);
   if (!decode) {
@@ -90,9 +94,9 @@ c2kv_status cache_plan(const int32_t* cache_len, int32_t num_reqs, int32_t tq, i
       }
       return true;
     };
-    // (at least kDecodeMinSteps steps per piece: shorter pieces leave the
-    // first loads' latency and the partial write unamortised)
-    int64_t lo = std::max<int64_t>(kDecodeMinSteps, ceil_div(ceil_div(total_keys * hkv, kDecodeSlots), step));
+    // (at least kDecodeMinKeys per piece: shorter pieces leave the first
+    // loads' latency and the partial write unamortised)
+    int64_t lo = std::max<int64_t>(kDecodeMinKeys / step, ceil_div(ceil_div(total_keys * hkv, kDecodeSlots), step));
     lo = std::max<int64_t>(lo, ceil_div(ceil_div(max_len, C2KV_MAX_SPLITS), step));
     int64_t hi = std::max<int64_t>(lo, ceil_div(max_len, step));   // one piece per request: the fallback
     while (lo < hi) {
