@@ -199,10 +199,14 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
   __shared__ __attribute__((aligned(1024))) char s_raw[kDecLdsBytes<T, D>];
 
   const int L = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // The kernel-argument fields of the prologue, with the first request's
-  // entry (the only one of a one-request launch), loaded in one round of
-  // scalar loads: the empty asm needs them all at once, so they complete at
-  // one wait instead of one dependent round per use.
+  // entry (the only one of a one-request launch) and every request's entry
+  // one per lane (the host zeroes the unused ones), loaded in one round: the
+  // empty asm needs them all at once, so they complete at one wait instead
+  // of one dependent round per use.
+  static_assert(C2KV_MAX_BATCH == 64, "one lane per request of a launch");
+  const DecodeReq e = p.reqs[lane];
   const int total_wg = p.total_wg, num_reqs = p.num_reqs, req0 = p.req0, hq = p.hq, hkv = p.hkv, G = p.G;
   const float sl2 = p.scale_log2;
   const int64_t cap = p.cap;
@@ -214,17 +218,15 @@ __global__ __launch_bounds__(kThreads, (kDecMinWaves<T, D>)) void decode_attn_ke
   void* const vc = p.vc;
   asm volatile("" : : "s"(total_wg), "s"(num_reqs), "s"(req0), "s"(hq), "s"(hkv), "s"(G), "s"(sl2), "s"(cap), "s"(rq0.wg0),
                "s"(rq0.cache_len), "s"(rq0.pos), "s"(rq0.nsplit), "s"(rq0.chunk), "s"(rq0.pbase), "s"(q_in),
-               "s"(kn_in), "s"(vn_in), "s"(kc), "s"(vc));
+               "s"(kn_in), "s"(vn_in), "s"(kc), "s"(vc), "v"(e.wg0), "v"(e.cache_len), "v"(e.pos), "v"(e.nsplit),
+               "v"(e.chunk), "v"(e.pbase));
   if (L >= total_wg) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
   int ri = 0;
   DecodeReq rq = rq0;
   if (num_reqs != 1) {
-    // each lane loads one request's entry; the ballot over the requests'
-    // first workgroups picks this workgroup's request, and its fields come
-    // from that lane (no second round of loads)
-    const DecodeReq e = p.reqs[min(lane, num_reqs - 1)];
+    // the ballot over the requests' first workgroups picks this
+    // workgroup's request, and its fields come from that request's lane
     ri = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane < num_reqs && e.wg0 <= L)) - 1);
     rq.wg0 = __builtin_amdgcn_readlane(e.wg0, ri);
     rq.cache_len = __builtin_amdgcn_readlane(e.cache_len, ri);
@@ -489,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   void* const out = p.o;
   float* const lse = p.lse;
   asm volatile("" : : "s"(num_rows), "s"(hq), "s"(tq), "s"(req0), "s"(nsplit0), "s"(pbase0), "s"(part_o),
-               "s"(part_ml), "s"(out), "s"(lse));
+               "s"(part_ml), "s"(out), "s"(lse), "v"(nsplit_l), "v"(pbase_l));
   const int row = WPR == 1 ? blockIdx.x * kWaves + wave : blockIdx.x;
   if (row >= num_rows) return;
   const int rows_per_req = hq * tq;
