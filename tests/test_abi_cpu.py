@@ -107,6 +107,32 @@ def test_workspace_sizes(lib):
     assert lib.c2kv_workspace_size_compose(100) == 0
 
 
+def _decode_pieces(lib, lens, hq=32, hkv=8, d=128):
+    """Key pieces per request of a decode call, from the size of its split
+    partials: hq partial rows of d fp32 values and one (m, l) pair per piece
+    and head (each array 256-byte aligned; one piece needs none)."""
+    ws = lib.c2kv_workspace_size_decode(_arr(lens), len(lens), hq, hkv, d, 0)
+    per_piece = hq * d * 4 + hq * 8
+    return ws // per_piece if ws > 256 else 1
+
+
+def test_decode_split_plan(lib):
+    """One request: pieces of at least 288 keys (the budget is searched in
+    32-key units), at most 768 workgroups (one round of resident workgroups
+    at three per CU), one piece when that budget covers the request."""
+    # the Llama layer's batch-1 decode after the 64-token question: 29
+    # pieces per KV head (232 workgroups, fewer than the 256 CUs)
+    assert _decode_pieces(lib, [8192 + 64]) == 29
+    for L in list(range(0, 2000, 37)) + list(range(2000, 200000, 4099)):
+        n = _decode_pieces(lib, [L])
+        keys = L + 1
+        assert n <= max(1, -(-keys // 288)), (L, n)
+        if n > 1:
+            assert n * 8 <= 768, (L, n)
+        if keys <= 288:
+            assert n == 1, (L, n)
+
+
 def _compose(lib, segs, ptr, cap=100, k=4, d=128, hkv=2, theta=1e6, base=None):
     from compressed_composable_kv_amd._lib import Segment
     arr = (Segment * len(segs))(*[Segment(*s) for s in segs])
